@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for HCA attention.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+draws random tensors and document lengths and nothing else: it holds none of
+the method's arithmetic (no masking rule, no attention), so the oracle and the
+HIP path receive identical inputs without sharing any of the computation.
+
+Workloads (the five standard problem sizes; every one is synthetic, with the
+shapes, value distributions and document structure the method's pages and the
+problem statement give):
+
+  tiny_fp32    B=1 S=489 H=4  D=64  r=16  Sc=30   W=64  fp32, one document
+  packed_bf16  B=2 S=4096 H=16 D=128 r=128 Sc=32  W=128 bf16, documents with
+               lengths uniform on the integers 256..2048
+  mid_bf16     B=1 S=16384 H=64 D=512 r=128 Sc=128 W=128 bf16, one document,
+               q / kv / kv_comp scaled by 0.5
+  long_bf16    B=1 S=65536 H=64 D=512 r=128 Sc=512 W=128 bf16, one document
+  max_bf16     B=1 S=131063 H=64 D=512 r=128 Sc=1023 W=128 bf16, documents
+               with lengths log-uniform on [1024, 65536)
+
+Draw recipe: a torch generator seeded with the workload number draws q, kv,
+kv_comp and dout, in that order, as float32 N(0, 1) (times the workload's value
+scale for q / kv / kv_comp), then rounds to the workload dtype
+(round-to-nearest-even for bf16).  Document lengths come from
+numpy.random.default_rng(seed): per batch row, lengths are drawn until they
+cover S, and the last one is cut at S.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    S: int
+    H: int
+    D: int
+    r: int
+    Sc: int
+    W: int
+    dtype: str  # "f32" or "bf16"
+    docs: Optional[str] = None  # None, "uniform", "loguniform"
+    doc_lo: int = 0
+    doc_hi: int = 0
+    value_scale: float = 1.0
+    seed: int = 0
+
+
+WORKLOADS = {
+    1: Workload("tiny_fp32", 1, 489, 4, 64, 16, 30, 64, "f32", seed=1),
+    2: Workload("packed_bf16", 2, 4096, 16, 128, 128, 32, 128, "bf16", docs="uniform",
+                doc_lo=256, doc_hi=2048, seed=2),
+    3: Workload("mid_bf16", 1, 16384, 64, 512, 128, 128, 128, "bf16", value_scale=0.5,
+                seed=3),
+    4: Workload("long_bf16", 1, 65536, 64, 512, 128, 512, 128, "bf16", seed=4),
+    5: Workload("max_bf16", 1, 131063, 64, 512, 128, 1023, 128, "bf16", docs="loguniform",
+                doc_lo=1024, doc_hi=65536, seed=5),
+}
+
+
+def doc_lengths(wl: Workload) -> Optional[List[List[int]]]:
+    """Per batch row, the list of document lengths (None: one document)."""
+    if wl.docs is None:
+        return None
+    rng = np.random.default_rng(wl.seed)
+    out = []
+    for _ in range(wl.B):
+        lens, total = [], 0
+        while total < wl.S:
+            if wl.docs == "uniform":
+                L = int(rng.integers(wl.doc_lo, wl.doc_hi + 1))
+            else:
+                L = int(math.floor(math.exp(rng.uniform(math.log(wl.doc_lo),
+                                                        math.log(wl.doc_hi)))))
+            L = min(L, wl.S - total)
+            lens.append(L)
+            total += L
+        out.append(lens)
+    return out
+
+
+def starts_csr(lengths: Optional[List[List[int]]], B: int):
+    """Document start positions, concatenated over the batch, plus per-row counts."""
+    if lengths is None:
+        return None, None
+    starts, counts = [], []
+    for lens in lengths:
+        pos = 0
+        for L in lens:
+            starts.append(pos)
+            pos += L
+        counts.append(len(lens))
+    assert len(counts) == B
+    return np.asarray(starts, dtype=np.int32), np.asarray(counts, dtype=np.int32)
+
+
+def segment_ids(lengths: Optional[List[List[int]]], B: int, S: int) -> np.ndarray:
+    """Per-token document index [B, S] int32."""
+    seg = np.zeros((B, S), dtype=np.int32)
+    if lengths is None:
+        return seg
+    for b, lens in enumerate(lengths):
+        pos = 0
+        for j, L in enumerate(lens):
+            seg[b, pos:pos + L] = j
+            pos += L
+        assert pos == S
+    return seg
+
+
+def draw(B, S, H, D, Sc, dtype="bf16", seed=0, value_scale=1.0, device="cpu"):
+    """Draws q [B,H,S,D], kv [B,S,D], kv_comp [B,Sc,D], dout [B,H,S,D] (torch)."""
+    import torch
+
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def one(shape, scale):
+        t = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+        if scale != 1.0:
+            t.mul_(scale)
+        return t.to(tdt)
+
+    q = one((B, H, S, D), value_scale)
+    kv = one((B, S, D), value_scale)
+    kvc = one((B, Sc, D), value_scale)
+    dout = one((B, H, S, D), 1.0)
+    return q, kv, kvc, dout
+
+
+def draw_workload(wl: Workload, device="cpu"):
+    return draw(wl.B, wl.S, wl.H, wl.D, wl.Sc, wl.dtype, wl.seed, wl.value_scale, device)
+
+
+def random_lengths(rng: np.random.Generator, S: int, lo: int, hi: int) -> List[int]:
+    """Lengths drawn uniformly from lo..hi until they cover S (last one cut)."""
+    lens, total = [], 0
+    while total < S:
+        L = min(int(rng.integers(lo, hi + 1)), S - total)
+        lens.append(L)
+        total += L
+    return lens
+
+
+def to_host_bits(t):
+    """Host numpy view of a torch tensor for the oracle: float32, or bf16 bits as uint16."""
+    import torch
+
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.to(torch.float32).numpy()
