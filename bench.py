@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark: HCA attention forward + backward on one MI355X.
+
+A step is one pass of the whole hot path on one batch of synthetic input
+already resident in device memory: hca_attn_fwd (KV transposes + forward
+kernel) then hca_attn_bwd (transposes, dQ kernel, dKV kernel, reduction).  The
+block table is built once per sequence layout, outside the timed region
+(it depends only on S, r, W and the document starts), and its build time is
+reported as plan_build_ms.
+
+Prints one JSON line.  value = effective TFLOP/s of forward + backward
+= 14 * D * H * P / time, where P is the number of visible (position, key)
+pairs (forward 4 * D * H * P, backward 10 * D * H * P; masked work excluded).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_bf16",
+                    help="tiny_fp32 | packed_bf16 | mid_bf16 | long_bf16 | max_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, target_s):
+    """Times the oracle on the first S' positions of the workload (all heads), full
+    forward + backward in fp64, doubling S' until the run takes target_s."""
+    import numpy as np
+
+    import oracle
+    from hca_inputs import draw, segment_ids
+
+    oracle.build()
+    Sp = 64
+    best = None
+    while True:
+        Sp = min(Sp, wl.S)
+        Sc = Sp // wl.r
+        q, kv, kvc, dout = draw(1, Sp, wl.H, wl.D, Sc, wl.dtype, wl.seed, wl.value_scale, "cpu")
+        from hca_inputs import to_host_bits
+
+        host = [to_host_bits(t) for t in (q, kv, kvc, dout)]
+        prob = oracle.Problem(1, Sp, wl.H, wl.D, wl.r, wl.W, Sc, 1.0 / math.sqrt(wl.D),
+                              segment_ids(None, 1, Sp), oracle.STRICT, wl.dtype)
+        t0 = time.perf_counter()
+        oracle.full(prob, *host)
+        dt = time.perf_counter() - t0
+        pairs = oracle.count_pairs(prob, 0) + oracle.count_pairs(prob, 1)
+        flops = 14.0 * wl.D * wl.H * pairs
+        best = (Sp, dt, flops)
+        if dt >= target_s or Sp >= wl.S or Sp >= 8192:
+            break
+        Sp *= 2
+    Sp, dt, flops = best
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "first %d positions of %s (1 document, all %d heads), full forward + "
+                      "backward in fp64, %.1f s" % (Sp, wl.name, wl.H, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_sparse_compressed_amd as hca
+    from hca_inputs import WORKLOADS, doc_lengths, draw_workload, starts_csr
+
+    wl = {w.name: w for w in WORKLOADS.values()}[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lengths = doc_lengths(wl)
+    starts, counts = starts_csr(lengths, wl.B)
+
+    t0 = time.perf_counter()
+    plan_probe = hca.hca_block_mask_build(wl.B, wl.S, wl.r, wl.W, wl.Sc, starts, counts, wl.H,
+                                          wl.D, hca.HCA_BF16 if wl.dtype == "bf16" else hca.HCA_F32)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    del plan_probe
+
+    q, kv, kvc, dout = draw_workload(wl, device=dev)
+    torch.cuda.reset_peak_memory_stats()
+    att = hca.HcaAttention(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, wl.dtype, starts, counts)
+    info = att.info
+    scale = 1.0 / math.sqrt(wl.D)
+    o, lse = att.new_outputs()
+    grads = att.new_grads()
+
+    def step():
+        att.forward(q, kv, kvc, scale, o, lse)
+        att.backward(q, kv, kvc, o, lse, dout, scale, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Forward alone, for the forward-only figure.
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        att.forward(q, kv, kvc, scale, o, lse)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = ev[0].elapsed_time(ev[1]) / args.steps
+
+    # Timed region: K full steps; per-kernel HIP events recorded by the library on
+    # the launch stream.
+    hca.hca_timing_read()
+    hca.hca_timing_enable(True)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    hca.hca_timing_enable(False)
+    kernels = hca.hca_timing_read()
+    ms = start.elapsed_time(stop) / args.steps
+    peak_mem = torch.cuda.max_memory_allocated() / 2**30
+
+    P = info.pairs_raw + info.pairs_comp
+    fl_fwd = 4.0 * wl.D * wl.H * P
+    fl_all = 14.0 * wl.D * wl.H * P
+    # Algorithmic work per launch of each kernel (flops; bytes for the HBM-bound ones).
+    e = 2 if wl.dtype == "bf16" else 4
+    per_kernel_flops = {"fwd": fl_fwd, "bwd_dq": 6.0 * wl.D * wl.H * P,
+                        "bwd_dkv": 4.0 * wl.D * wl.H * P, "fwd_f32": fl_fwd,
+                        "bwd_f32": 10.0 * wl.D * wl.H * P}
+    kavg = {k: v[1] / v[0] for k, v in kernels.items() if v[0]}
+    per_step = {k: kernels[k][1] / args.steps for k in kernels}
+    dom = max((k for k in per_step if k in per_kernel_flops), key=lambda k: per_step[k])
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = per_kernel_flops[dom] / (kavg[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None, "avg_ms": round(kavg[dom], 4)}
+
+    out = {
+        "metric": "HCA attn fwd+bwd effective TFLOP/s",
+        "value": round(fl_all / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "H": wl.H, "D": wl.D, "r": wl.r,
+                   "W": wl.W, "S_c": wl.Sc,
+                   "documents": 1 if lengths is None else sum(len(x) for x in lengths),
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(wl.B * wl.S / (ms * 1e-3), 1),
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(fl_fwd / (fwd_ms * 1e-3) / 1e12, 3),
+        "fwd_tokens_per_s": round(wl.B * wl.S / (fwd_ms * 1e-3), 1),
+        "visible_pairs": P,
+        "plan_build_ms": round(plan_ms, 2),
+        "peak_mem_gib": round(peak_mem, 3),
+        "wall_s": round(wall, 3),
+        "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,349 @@
+"""Python binding of libhca.so -- MI355X (gfx950) Heavily Compressed Attention.
+
+Thin ctypes layer over the C ABI declared in ``include/hca.h``: the functions
+below carry the same names and marshal arguments (torch tensors become device
+pointers, the current torch stream becomes the HIP stream).  Every step of the
+computation runs inside libhca.so; nothing here computes attention, and there
+is no fallback: importing this package fails if the library is missing.
+
+PyTorch is used for device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhca.so")
+
+HCA_OK, HCA_ERR_INVALID_ARG, HCA_ERR_UNSUPPORTED = 0, 1, 2
+HCA_ERR_WORKSPACE, HCA_ERR_HIP, HCA_ERR_NOMEM, HCA_ERR_STATE = 3, 4, 5, 6
+HCA_F32, HCA_BF16 = 0, 1
+HCA_COMPSEG_STRICT, HCA_COMPSEG_LAST = 0, 1
+HCA_TILE_EMPTY, HCA_TILE_PARTIAL, HCA_TILE_FULL = 0, 1, 2
+
+# Declared in include/hca.h; the ABI test checks the header and this list agree.
+EXPORTS = (
+    "hca_block_mask_build", "hca_plan_get_info", "hca_plan_export_tiles",
+    "hca_plan_export_rows", "hca_plan_upload", "hca_plan_destroy", "hca_attn_fwd",
+    "hca_attn_bwd", "hca_timing_enable", "hca_timing_read", "hca_status_string",
+    "hca_last_error",
+)
+
+
+class HcaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class HcaInvalidArgument(HcaError, ValueError):
+    pass
+
+
+class HcaUnsupported(HcaError, NotImplementedError):
+    pass
+
+
+class _TileCfg(ctypes.Structure):
+    _fields_ = [("bq", ctypes.c_int32), ("bk_raw", ctypes.c_int32), ("bk_comp", ctypes.c_int32)]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "B", "S", "H", "D", "r", "W", "S_c", "dtype", "comp_mode", "bq", "bk_raw", "bk_comp",
+        "nqt", "nkt_raw", "nkt_comp", "kernel_ok")] + [(n, ctypes.c_int64) for n in (
+        "tiles_raw", "tiles_comp", "full_raw", "full_comp", "pairs_raw", "pairs_comp")] + [
+        (n, ctypes.c_uint64) for n in ("device_bytes", "ws_fwd_bytes", "ws_bwd_bytes")]
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libhca.so is not built (%s); run block_sparse_compressed_amd/_build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+    lib.hca_block_mask_build.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32,
+                                         vp, ctypes.POINTER(vp)]
+    lib.hca_block_mask_build.restype = ctypes.c_int
+    lib.hca_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
+    lib.hca_plan_get_info.restype = ctypes.c_int
+    lib.hca_plan_export_tiles.argtypes = [vp, vp, vp]
+    lib.hca_plan_export_tiles.restype = ctypes.c_int
+    lib.hca_plan_export_rows.argtypes = [vp, vp]
+    lib.hca_plan_export_rows.restype = ctypes.c_int
+    lib.hca_plan_upload.argtypes = [vp, vp, u64, vp]
+    lib.hca_plan_upload.restype = ctypes.c_int
+    lib.hca_plan_destroy.argtypes = [vp]
+    lib.hca_plan_destroy.restype = None
+    lib.hca_attn_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, u64, vp]
+    lib.hca_attn_fwd.restype = ctypes.c_int
+    lib.hca_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                 u64, vp]
+    lib.hca_attn_bwd.restype = ctypes.c_int
+    lib.hca_timing_enable.argtypes = [i32]
+    lib.hca_timing_enable.restype = ctypes.c_int
+    lib.hca_timing_read.argtypes = [ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32)]
+    lib.hca_timing_read.restype = ctypes.c_int
+    lib.hca_status_string.argtypes = [ctypes.c_int]
+    lib.hca_status_string.restype = ctypes.c_char_p
+    lib.hca_last_error.argtypes = []
+    lib.hca_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load_library()
+
+
+def library():
+    return _lib
+
+
+def _check(status: int):
+    if status == HCA_OK:
+        return
+    msg = "%s: %s" % (_lib.hca_status_string(status).decode(), _lib.hca_last_error().decode())
+    if status == HCA_ERR_INVALID_ARG:
+        raise HcaInvalidArgument(status, msg)
+    if status == HCA_ERR_UNSUPPORTED:
+        raise HcaUnsupported(status, msg)
+    raise HcaError(status, msg)
+
+
+def hca_status_string(status: int) -> str:
+    return _lib.hca_status_string(status).decode()
+
+
+def hca_last_error() -> str:
+    return _lib.hca_last_error().decode()
+
+
+@dataclass
+class PlanInfo:
+    B: int; S: int; H: int; D: int; r: int; W: int; S_c: int
+    dtype: int; comp_mode: int; bq: int; bk_raw: int; bk_comp: int
+    nqt: int; nkt_raw: int; nkt_comp: int; kernel_ok: int
+    tiles_raw: int; tiles_comp: int; full_raw: int; full_comp: int
+    pairs_raw: int; pairs_comp: int
+    device_bytes: int; ws_fwd_bytes: int; ws_bwd_bytes: int
+
+
+class Plan:
+    """Owns an ``hca_plan*``; released when the object is collected."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+        self.device_buffer = None  # keeps the uploaded torch buffer alive
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.hca_plan_destroy(h)
+            self._h = ctypes.c_void_p(0)
+
+
+def _i32(a: Optional[Sequence[int]]):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def hca_block_mask_build(B, S, r, W, S_c, seg_starts=None, seg_counts=None, H=1, D=64,
+                         dtype=HCA_BF16, mode=HCA_COMPSEG_STRICT, tiles=None) -> Plan:
+    starts, counts = _i32(seg_starts), _i32(seg_counts)
+    cfg = None
+    if tiles is not None:
+        cfg = _TileCfg(*tiles)
+    out = ctypes.c_void_p()
+    _check(_lib.hca_block_mask_build(
+        B, S, r, W, S_c,
+        starts.ctypes.data if starts is not None else None,
+        counts.ctypes.data if counts is not None else None,
+        H, D, dtype, mode, ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out)))
+    return Plan(out.value)
+
+
+def hca_plan_get_info(plan: Plan) -> PlanInfo:
+    info = _PlanInfo()
+    _check(_lib.hca_plan_get_info(plan.handle, ctypes.byref(info)))
+    return PlanInfo(**{n: getattr(info, n) for n, _ in _PlanInfo._fields_})
+
+
+def hca_plan_export_tiles(plan: Plan):
+    """Returns (raw [B, nqt, nkt_raw], comp [B, nqt, nkt_comp]) uint8 tables."""
+    i = hca_plan_get_info(plan)
+    raw = np.empty((i.B, i.nqt, i.nkt_raw), dtype=np.uint8)
+    comp = np.empty((i.B, i.nqt, i.nkt_comp), dtype=np.uint8)
+    _check(_lib.hca_plan_export_tiles(plan.handle, raw.ctypes.data if raw.size else None,
+                                      comp.ctypes.data if comp.size else None))
+    return raw, comp
+
+
+def hca_plan_export_rows(plan: Plan) -> np.ndarray:
+    """Per-position intervals [B, S, 3] int32: raw_lo, comp_lo, comp_hi."""
+    i = hca_plan_get_info(plan)
+    rows = np.empty((i.B, i.S, 3), dtype=np.int32)
+    _check(_lib.hca_plan_export_rows(plan.handle, rows.ctypes.data))
+    return rows
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def hca_plan_upload(plan: Plan, dev_buf, stream=None):
+    """Uploads the plan's device image into ``dev_buf`` (a uint8 CUDA tensor)."""
+    _check(_lib.hca_plan_upload(plan.handle, _ptr(dev_buf), _nbytes(dev_buf), _stream(stream)))
+    plan.device_buffer = dev_buf
+
+
+def _expect(t, name, shape, dtype):
+    """Host-side check that a torch tensor matches the plan before its pointer is passed."""
+    import torch
+
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise HcaInvalidArgument(HCA_ERR_INVALID_ARG, "%s must be a torch tensor" % name)
+    if t.device.type != "cuda" or not t.is_contiguous():
+        raise HcaInvalidArgument(HCA_ERR_INVALID_ARG, "%s must be a contiguous device tensor" % name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise HcaInvalidArgument(
+            HCA_ERR_INVALID_ARG, "%s: expected %s %s, got %s %s" % (name, tuple(shape), dtype,
+                                                                   tuple(t.shape), t.dtype))
+
+
+def _elem_dtype(info):
+    import torch
+
+    return torch.bfloat16 if info.dtype == HCA_BF16 else torch.float32
+
+
+def hca_attn_fwd(plan: Plan, q, kv, kv_comp, scale, o, lse, ws, stream=None):
+    import torch
+
+    i = hca_plan_get_info(plan)
+    et = _elem_dtype(i)
+    _expect(q, "q", (i.B, i.H, i.S, i.D), et)
+    _expect(kv, "kv", (i.B, i.S, i.D), et)
+    if i.S_c > 0:
+        _expect(kv_comp, "kv_comp", (i.B, i.S_c, i.D), et)
+    _expect(o, "o", (i.B, i.H, i.S, i.D), et)
+    _expect(lse, "lse", (i.B, i.H, i.S), torch.float32)
+    _check(_lib.hca_attn_fwd(plan.handle, _ptr(q), _ptr(kv), _ptr(kv_comp), float(scale),
+                             _ptr(o), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def hca_attn_bwd(plan: Plan, q, kv, kv_comp, o, lse, dout, scale, dq, dkv, dkv_comp, ws,
+                 stream=None):
+    import torch
+
+    i = hca_plan_get_info(plan)
+    et = _elem_dtype(i)
+    for t, n in ((q, "q"), (o, "o"), (dout, "dout"), (dq, "dq")):
+        _expect(t, n, (i.B, i.H, i.S, i.D), et)
+    for t, n in ((kv, "kv"), (dkv, "dkv")):
+        _expect(t, n, (i.B, i.S, i.D), et)
+    if i.S_c > 0:
+        _expect(kv_comp, "kv_comp", (i.B, i.S_c, i.D), et)
+        _expect(dkv_comp, "dkv_comp", (i.B, i.S_c, i.D), et)
+    _expect(lse, "lse", (i.B, i.H, i.S), torch.float32)
+    _check(_lib.hca_attn_bwd(plan.handle, _ptr(q), _ptr(kv), _ptr(kv_comp), _ptr(o), _ptr(lse),
+                             _ptr(dout), float(scale), _ptr(dq), _ptr(dkv), _ptr(dkv_comp),
+                             _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def hca_timing_enable(enable: bool = True):
+    _check(_lib.hca_timing_enable(1 if enable else 0))
+
+
+def hca_timing_read() -> dict:
+    """{kernel name: (launches, total_ms)} since the last read (waits for the events)."""
+    buf = (_KernelTime * 16)()
+    n = ctypes.c_int32()
+    _check(_lib.hca_timing_read(buf, 16, ctypes.byref(n)))
+    return {buf[k].name.decode(): (int(buf[k].launches), float(buf[k].total_ms))
+            for k in range(min(n.value, 16))}
+
+
+class HcaAttention:
+    """Convenience holder: one plan, its device image and workspaces (torch-allocated).
+
+    All computation goes through hca_attn_fwd / hca_attn_bwd.
+    """
+
+    def __init__(self, B, S, H, D, r, W, dtype="bf16", seg_starts=None, seg_counts=None,
+                 mode=HCA_COMPSEG_STRICT, tiles=None, device="cuda"):
+        import torch
+
+        self.B, self.S, self.H, self.D, self.r, self.W = B, S, H, D, r, W
+        self.S_c = S // r
+        self.dtype = HCA_BF16 if dtype == "bf16" else HCA_F32
+        self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.plan = hca_block_mask_build(B, S, r, W, self.S_c, seg_starts, seg_counts, H, D,
+                                         self.dtype, mode, tiles)
+        self.info = hca_plan_get_info(self.plan)
+        self.device = torch.device(device)
+        buf = torch.empty(max(1, self.info.device_bytes), dtype=torch.uint8, device=self.device)
+        hca_plan_upload(self.plan, buf)
+        self.ws_fwd = torch.empty(max(16, self.info.ws_fwd_bytes), dtype=torch.uint8,
+                                  device=self.device)
+        self.ws_bwd = torch.empty(max(16, self.info.ws_bwd_bytes), dtype=torch.uint8,
+                                  device=self.device)
+
+    def new_outputs(self):
+        import torch
+
+        o = torch.empty((self.B, self.H, self.S, self.D), dtype=self.torch_dtype,
+                        device=self.device)
+        lse = torch.empty((self.B, self.H, self.S), dtype=torch.float32, device=self.device)
+        return o, lse
+
+    def new_grads(self):
+        import torch
+
+        dq = torch.empty((self.B, self.H, self.S, self.D), dtype=self.torch_dtype,
+                         device=self.device)
+        dkv = torch.empty((self.B, self.S, self.D), dtype=self.torch_dtype, device=self.device)
+        dkvc = torch.empty((self.B, self.S_c, self.D), dtype=self.torch_dtype,
+                           device=self.device)
+        return dq, dkv, dkvc
+
+    def forward(self, q, kv, kv_comp, scale, o=None, lse=None, stream=None):
+        if o is None:
+            o, lse = self.new_outputs()
+        hca_attn_fwd(self.plan, q, kv, kv_comp if self.S_c > 0 else None, scale, o, lse,
+                     self.ws_fwd, stream)
+        return o, lse
+
+    def backward(self, q, kv, kv_comp, o, lse, dout, scale, grads=None, stream=None):
+        dq, dkv, dkvc = grads if grads is not None else self.new_grads()
+        hca_attn_bwd(self.plan, q, kv, kv_comp if self.S_c > 0 else None, o, lse, dout, scale,
+                     dq, dkv, dkvc if self.S_c > 0 else None, self.ws_bwd, stream)
+        return dq, dkv, dkvc

@@ -1,0 +1,510 @@
+// hca_bwd.hip -- HCA attention backward on gfx950 (bf16 MFMA, fp32 accumulation).
+//
+// Gradients of softmax attention with one shared key/value tensor ("[DeepSeek-V4]
+// Implement Compressed Attention Layers", review suggestions: k = kv, v = kv,
+// broadcast over heads), so each key's gradient is the sum of its key path and
+// its value path over every head:
+//   P = exp(scale <q, kv> - LSE),  dP = <dO, kv>,  delta = <dO, O>,
+//   dS = P (dP - delta),  dQ = scale sum_k dS kv_k,
+//   dKV_k = sum_rows scale dS q + P dO.
+//
+// Three kernels, all driven by the host-built block table:
+//  1. query-stationary dQ: same tiling and key-tile walk as the forward; the
+//     row's Q and dO fragments stay in VGPRs, delta is computed in the
+//     prologue from O and dO, and dQ is accumulated in registers and written
+//     once -- no atomics (the page on the static mask compiles the backward with
+//     an on-chip dQ reduction; here the whole dQ row stays on chip).
+//  2. key-stationary dKV: a workgroup owns one 32-key tile (raw or compressed)
+//     and walks the query tiles that see it, recomputing S and dP with the
+//     tile's K fragments held in VGPRs; long compressed-entry lists are split
+//     into several work items.  Each item writes a float32 partial.
+//  3. a fixed-order reduction of the partials into dKV and dKV_comp, so the
+//     result is bitwise reproducible.
+#include <climits>
+
+#include "hca_device.h"
+#include "hca_internal.h"
+
+namespace hca {
+
+namespace {
+
+constexpr int kBK = 32;
+
+template <int D, int NT>
+struct StageB {
+  static constexpr int KROW = D + 8;
+  static constexpr int TROW = kBK + 8;
+  static constexpr int KCH = kBK * D / 8;
+  static constexpr int TCH = D * kBK / 8;
+  static constexpr int KPT = (KCH + NT - 1) / NT;
+  static constexpr int TPT = (TCH + NT - 1) / NT;
+
+  __device__ __forceinline__ static void load(uint4 (&pk)[KPT], uint4 (&pt)[TPT], int tid,
+                                              const bf16raw *src, int nk, const bf16raw *srct,
+                                              int ts, int k0) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int c = tid + u * NT;
+      if (KCH % NT == 0 || c < KCH) {
+        const int row = c / (D / 8), col = c % (D / 8);
+        const int key = k0 + row;
+        pk[u] = key < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)key * D + col * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int c = tid + u * NT;
+      if (TCH % NT == 0 || c < TCH) {
+        const int dd = c / (kBK / 8), col = c % (kBK / 8);
+        pt[u] = *reinterpret_cast<const uint4 *>(srct + (size_t)dd * ts + k0 + col * 8);
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void store(const uint4 (&pk)[KPT], const uint4 (&pt)[TPT],
+                                               int tid, bf16raw *k_lds, bf16raw *t_lds) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int c = tid + u * NT;
+      if (KCH % NT == 0 || c < KCH) {
+        const int row = c / (D / 8), col = c % (D / 8);
+        *reinterpret_cast<uint4 *>(k_lds + row * KROW + col * 8) = pk[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int c = tid + u * NT;
+      if (TCH % NT == 0 || c < TCH) {
+        const int dd = c / (kBK / 8), col = c % (kBK / 8);
+        *reinterpret_cast<uint4 *>(t_lds + dd * TROW + col * 8) = pt[u];
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+  const bf16raw *x = reinterpret_cast<const bf16raw *>(&a);
+  const bf16raw *y = reinterpret_cast<const bf16raw *>(&b);
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) s += bf2f(x[t]) * bf2f(y[t]);
+  return s;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 1. dQ (+ delta), query-stationary.
+// ---------------------------------------------------------------------------
+template <int D, int NW, int MB>
+__global__ void __launch_bounds__(NW * 64, 1)
+    hca_bwd_dq_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                      const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
+                      const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
+                      const bf16raw *__restrict__ o, const float *__restrict__ lse,
+                      const bf16raw *__restrict__ dout, float scale_log2, float scale,
+                      bf16raw *__restrict__ dq, float *__restrict__ delta) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int M = NW * MB * 16;
+  using St = StageB<D, NT>;
+  __shared__ __attribute__((aligned(16))) bf16raw k_lds[kBK * St::KROW];
+  __shared__ __attribute__((aligned(16))) bf16raw t_lds[D * St::TROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int nslices = d.bq * d.H / M;
+  const int nitems = d.B * d.nqt;
+  const int li = blockIdx.x / nslices, sl = blockIdx.x - li * nslices;
+  const int item = p.qorder[xcd_remap(li, nitems)];
+  const int b = item / d.nqt, qt = item - b * d.nqt;
+
+  int pos[MB], hh[MB], rlo[MB], clo[MB], chi[MB];
+  bool valid[MB];
+  float lse2[MB], dl[MB];
+  bf16x8 qf[MB][KS], dof[MB][KS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int rho = sl * M + (wave * MB + mb) * 16 + j;
+    pos[mb] = qt * d.bq + rho / d.H;
+    hh[mb] = rho % d.H;
+    valid[mb] = pos[mb] < d.S;
+    const size_t row = ((size_t)b * d.H + hh[mb]) * d.S + pos[mb];
+    if (valid[mb]) {
+      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos[mb]];
+      rlo[mb] = rw.x;
+      clo[mb] = rw.y;
+      chi[mb] = rw.z;
+      lse2[mb] = lse[row] * kLog2e;
+    } else {
+      rlo[mb] = INT_MAX;
+      clo[mb] = 0;
+      chi[mb] = 0;
+      lse2[mb] = -INFINITY;
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 qv = make_uint4(0, 0, 0, 0), dv = qv, ov = qv;
+      if (valid[mb]) {
+        qv = *reinterpret_cast<const uint4 *>(q + row * D + 32 * ks + 8 * g);
+        dv = *reinterpret_cast<const uint4 *>(dout + row * D + 32 * ks + 8 * g);
+        ov = *reinterpret_cast<const uint4 *>(o + row * D + 32 * ks + 8 * g);
+      }
+      qf[mb][ks] = as_bf16x8(qv);
+      dof[mb][ks] = as_bf16x8(dv);
+      part += dot8(dv, ov);
+    }
+    part = xor_sum(part, 16);
+    part = xor_sum(part, 32);
+    dl[mb] = part;
+    if (valid[mb] && g == 0) delta[row] = part;
+  }
+
+  floatx4 acc[MB][DB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[mb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int e_begin = p.qptr[item], e_end = p.qptr[item + 1];
+  const bf16raw *kv_b = kv + (size_t)b * d.S * D;
+  const bf16raw *kvc_b = kvc + (size_t)b * d.Sc * D;
+  const bf16raw *kvt_b = kvt + (size_t)b * D * d.S_pad;
+  const bf16raw *kvct_b = kvct + (size_t)b * D * d.Sc_pad;
+  uint4 pk[St::KPT], pt[St::TPT];
+  auto issue = [&](int e) {
+    const uint32_t ent = p.qent[e];
+    const bool comp = ent & kEntComp;
+    const int k0 = (int)(ent & kEntIdx) * kBK;
+    St::load(pk, pt, tid, comp ? kvc_b : kv_b, comp ? d.Sc : d.S, comp ? kvct_b : kvt_b,
+             comp ? d.Sc_pad : d.S_pad, k0);
+  };
+  if (e_begin < e_end) issue(e_begin);
+  const int r0 = 8 * (j >> 2) + (j & 3), r1 = r0 + 4;
+
+  for (int e = e_begin; e < e_end; ++e) {
+    const uint32_t ent = p.qent[e];
+    const bool comp = ent & kEntComp;
+    const bool full = ent & kEntFull;
+    const int k0 = (int)(ent & kEntIdx) * kBK;
+    __syncthreads();
+    St::store(pk, pt, tid, k_lds, t_lds);
+    __syncthreads();
+    if (e + 1 < e_end) issue(e + 1);
+
+    floatx4 s0[MB], s1[MB], p0[MB], p1[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      s0[mb] = s1[mb] = p0[mb] = p1[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a0 = as_bf16x8(lds_load16(k_lds + r0 * St::KROW + 32 * ks + 8 * g));
+      const bf16x8 a1 = as_bf16x8(lds_load16(k_lds + r1 * St::KROW + 32 * ks + 8 * g));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        s0[mb] = mfma16x16x32(a0, qf[mb][ks], s0[mb]);
+        s1[mb] = mfma16x16x32(a1, qf[mb][ks], s1[mb]);
+        p0[mb] = mfma16x16x32(a0, dof[mb][ks], p0[mb]);
+        p1[mb] = mfma16x16x32(a1, dof[mb][ks], p1[mb]);
+      }
+    }
+    bf16x8 dsb[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float x[8], dp[8];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[v] = s0[mb][v] * scale_log2;
+        x[4 + v] = s1[mb][v] * scale_log2;
+        dp[v] = p0[mb][v];
+        dp[4 + v] = p1[mb][v];
+      }
+      const int kb = k0 + 8 * g;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        bool vis = true;
+        if (!full) {
+          const int key = kb + t;
+          vis = comp ? (key >= clo[mb] && key < chi[mb]) : (key >= rlo[mb] && key <= pos[mb]);
+        }
+        const float pr = vis ? fast_exp2(x[t] - lse2[mb]) : 0.f;
+        x[t] = pr * (dp[t] - dl[mb]);
+      }
+      dsb[mb] = pack8(x);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 a = as_bf16x8(lds_load16(t_lds + (16 * db + j) * St::TROW + 8 * g));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][db] = mfma16x16x32(a, dsb[mb], acc[mb][db]);
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (!valid[mb]) continue;
+    bf16raw *drow = dq + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      ushort4 w;
+      w.x = f2bf(acc[mb][db][0] * scale);
+      w.y = f2bf(acc[mb][db][1] * scale);
+      w.z = f2bf(acc[mb][db][2] * scale);
+      w.w = f2bf(acc[mb][db][3] * scale);
+      *reinterpret_cast<ushort4 *>(drow + 16 * db + 4 * g) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dKV, key-stationary.  4 waves: wave & 1 selects 16 of the tile's 32 keys,
+//    wave >> 1 selects one 32-row half of each 64-row step.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256, 1)
+    hca_bwd_dkv_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                       const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
+                       const float *__restrict__ lse, const float *__restrict__ delta,
+                       const bf16raw *__restrict__ dout, float scale_log2, float scale,
+                       float *__restrict__ part) {
+  constexpr int KS = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int STEP = 64;           // query rows staged per step
+  constexpr int QROW = D + 8;        // padded LDS row (bf16)
+  constexpr int RCH = STEP * D / 8;  // 16-B chunks per staged tensor
+  static_assert(STEP * QROW * 2 >= 2 * D * 16 * 4, "reduction scratch fits in q_lds");
+  __shared__ __attribute__((aligned(16))) bf16raw q_lds[STEP * QROW];
+  __shared__ __attribute__((aligned(16))) bf16raw o_lds[STEP * QROW];  // dO rows
+  __shared__ float lse_lds[STEP], dl_lds[STEP];
+  __shared__ int4 info_lds[STEP];  // rlo, clo, chi, pos (pos = INT_MAX if padded)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int kh = wave & 1, rh = wave >> 1;
+  const KvItem it = p.kvitem[p.kvorder[blockIdx.x]];
+  const int b = it.b;
+  const bool comp = it.kind != 0;
+  const int k0 = it.kt * kBK;
+  const int nk = comp ? d.Sc : d.S;
+  const bf16raw *src = (comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D);
+  const int mykey = k0 + kh * 16 + j;  // this lane's key (B-operand column)
+
+  // Stationary K fragments: B[k = d][n = key].
+  bf16x8 kf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    kf[ks] = as_bf16x8(mykey < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)mykey * D +
+                                                                        32 * ks + 8 * g)
+                                  : make_uint4(0, 0, 0, 0));
+  floatx4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int rows_per_qt = d.bq * d.H;
+  const int r0 = 8 * (j >> 2) + (j & 3);  // A-operand row for the first 16-row block
+  for (int e = it.e0; e < it.e1; ++e) {
+    const uint32_t ent = p.kvent[e];
+    const int qt = (int)(ent & kEntIdx);
+    const bool full = ent & kEntFull;
+    for (int base = 0; base < rows_per_qt; base += STEP) {
+      __syncthreads();
+      // Stage rows base .. base+STEP-1 of query tile qt.
+      for (int c = tid; c < RCH; c += 256) {
+        const int r = c / (D / 8), col = c % (D / 8);
+        const int rho = base + r;
+        const int pos = qt * d.bq + rho / d.H, h = rho % d.H;
+        uint4 qv = make_uint4(0, 0, 0, 0), dv = qv;
+        if (pos < d.S) {
+          const size_t row = ((size_t)b * d.H + h) * d.S + pos;
+          qv = *reinterpret_cast<const uint4 *>(q + row * D + col * 8);
+          dv = *reinterpret_cast<const uint4 *>(dout + row * D + col * 8);
+        }
+        *reinterpret_cast<uint4 *>(q_lds + r * QROW + col * 8) = qv;
+        *reinterpret_cast<uint4 *>(o_lds + r * QROW + col * 8) = dv;
+      }
+      if (tid < STEP) {
+        const int rho = base + tid;
+        const int pos = qt * d.bq + rho / d.H, h = rho % d.H;
+        if (pos < d.S) {
+          const size_t row = ((size_t)b * d.H + h) * d.S + pos;
+          const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos];
+          info_lds[tid] = make_int4(rw.x, rw.y, rw.z, pos);
+          lse_lds[tid] = lse[row] * kLog2e;
+          dl_lds[tid] = delta[row];
+        } else {
+          info_lds[tid] = make_int4(INT_MAX, 0, 0, INT_MAX);
+          lse_lds[tid] = -INFINITY;
+          dl_lds[tid] = 0.f;
+        }
+      }
+      __syncthreads();
+
+      // S and dP for this wave's 32 rows x 16 keys.
+      const int wr = rh * 32;  // first staged row of this wave
+      floatx4 s[2], t[2];
+      s[0] = s[1] = t[0] = t[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int arow = wr + r0 + 4 * rb;
+          const bf16x8 aq = as_bf16x8(lds_load16(q_lds + arow * QROW + 32 * ks + 8 * g));
+          const bf16x8 ad = as_bf16x8(lds_load16(o_lds + arow * QROW + 32 * ks + 8 * g));
+          s[rb] = mfma16x16x32(aq, kf[ks], s[rb]);
+          t[rb] = mfma16x16x32(ad, kf[ks], t[rb]);
+        }
+      }
+      // Lane holds rows wr + 8g + {0..3} (rb 0) and wr + 8g + 4 + {0..3} (rb 1)
+      // for key `mykey`.
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int rr = wr + 8 * g + 4 * rb + v;
+          const int4 inf = info_lds[rr];
+          bool vis = true;
+          if (!full)
+            vis = comp ? (mykey >= inf.y && mykey < inf.z) : (mykey >= inf.x && mykey <= inf.w);
+          const float pr = vis ? fast_exp2(s[rb][v] * scale_log2 - lse_lds[rr]) : 0.f;
+          pv[4 * rb + v] = pr;
+          dsv[4 * rb + v] = pr * (t[rb][v] - dl_lds[rr]) * scale;
+        }
+      const bf16x8 pb = pack8(pv), dsb = pack8(dsv);
+      // dKV^T[d][key] += Q^T[d][rows] dS[rows][key] + dO^T[d][rows] P[rows][key]
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        bf16x8 aq, ad;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int rr = wr + 8 * g + u;
+          aq[u] = __builtin_bit_cast(__bf16, q_lds[rr * QROW + 16 * db + j]);
+          ad[u] = __builtin_bit_cast(__bf16, o_lds[rr * QROW + 16 * db + j]);
+        }
+        acc[db] = mfma16x16x32(aq, dsb, acc[db]);
+        acc[db] = mfma16x16x32(ad, pb, acc[db]);
+      }
+    }
+  }
+
+  // Sum the two row-half partials of each key half, then write the item's
+  // float32 partial [32 keys][D].
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(q_lds);  // [2 key halves][D][16 keys]
+  if (rh == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(kh * D + 16 * db + 4 * g + v) * 16 + j] = acc[db][v];
+  }
+  __syncthreads();
+  if (rh == 0) {
+    float *out = part + it.part_off + (size_t)(kh * 16 + j) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      float4 w;
+      w.x = acc[db][0] + red[(kh * D + 16 * db + 4 * g + 0) * 16 + j];
+      w.y = acc[db][1] + red[(kh * D + 16 * db + 4 * g + 1) * 16 + j];
+      w.z = acc[db][2] + red[(kh * D + 16 * db + 4 * g + 2) * 16 + j];
+      w.w = acc[db][3] + red[(kh * D + 16 * db + 4 * g + 3) * 16 + j];
+      *reinterpret_cast<float4 *>(out + 16 * db + 4 * g) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Fixed-order sum of the partials of every key tile -> dKV / dKV_comp.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+    hca_dkv_reduce_kernel(Dims d, DevPlan p, const float *__restrict__ part, int dtype,
+                          void *__restrict__ dkv, void *__restrict__ dkvc) {
+  const int nkt = d.nkt_raw + d.nkt_comp;
+  const int b = blockIdx.x / nkt, t = blockIdx.x - b * nkt;
+  const bool comp = t >= d.nkt_raw;
+  const int kt = comp ? t - d.nkt_raw : t;
+  const int bk = comp ? d.bk_comp : d.bk_raw;
+  const int nk = comp ? d.Sc : d.S;
+  const int first = p.kvtile[2 * (b * nkt + t)], n = p.kvtile[2 * (b * nkt + t) + 1];
+  const int D = d.D;
+  for (int e = threadIdx.x * 4; e < bk * D; e += 256 * 4) {
+    const int key = kt * bk + e / D, col = e % D;
+    if (key >= nk) continue;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < n; ++i) {
+      const float4 v = *reinterpret_cast<const float4 *>(part + p.kvitem[first + i].part_off + e);
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    const size_t off = ((size_t)b * nk + key) * D + col;
+    if (dtype == HCA_BF16) {
+      ushort4 w;
+      w.x = f2bf(a.x);
+      w.y = f2bf(a.y);
+      w.z = f2bf(a.z);
+      w.w = f2bf(a.w);
+      *reinterpret_cast<ushort4 *>((bf16raw *)(comp ? dkvc : dkv) + off) = w;
+    } else {
+      *reinterpret_cast<float4 *>((float *)(comp ? dkvc : dkv) + off) = a;
+    }
+  }
+}
+
+int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
+                       const void *kvc, const void *kvt, const void *kvct, const void *o,
+                       const float *lse, const void *dout, float scale, void *dq, float *delta,
+                       void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const float sl2 = scale * kLog2e;
+  auto go = [&](auto kernel, int nw, int m) {
+    const dim3 grid(d.B * d.nqt * (d.bq * d.H / m));
+    hipLaunchKernelGGL(kernel, grid, dim3(nw * 64), 0, s, d, p, (const bf16raw *)q,
+                       (const bf16raw *)kv, (const bf16raw *)kvc, (const bf16raw *)kvt,
+                       (const bf16raw *)kvct, (const bf16raw *)o, lse, (const bf16raw *)dout, sl2,
+                       scale, (bf16raw *)dq, delta);
+  };
+  switch (d.D) {
+    case 512: go(hca_bwd_dq_kernel<512, 4, 1>, 4, 64); break;
+    case 128: go(hca_bwd_dq_kernel<128, 8, 1>, 8, 128); break;
+    case 64: go(hca_bwd_dq_kernel<64, 8, 1>, 8, 128); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
+                        const void *kvc, const float *lse, const float *delta,
+                        const void *dout, float scale, float *part, void *stream) {
+  if (d.n_items == 0) return hipSuccess;
+  hipStream_t s = (hipStream_t)stream;
+  const float sl2 = scale * kLog2e;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(d.n_items), dim3(256), 0, s, d, p, (const bf16raw *)q,
+                       (const bf16raw *)kv, (const bf16raw *)kvc, lse, delta,
+                       (const bf16raw *)dout, sl2, scale, part);
+  };
+  switch (d.D) {
+    case 512: go(hca_bwd_dkv_kernel<512>); break;
+    case 128: go(hca_bwd_dkv_kernel<128>); break;
+    case 64: go(hca_bwd_dkv_kernel<64>); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_dkv_reduce(const Dims &d, const DevPlan &p, const float *part, int dtype, void *dkv,
+                      void *dkvc, void *stream) {
+  const int nblk = d.B * (d.nkt_raw + d.nkt_comp);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(hca_dkv_reduce_kernel, dim3(nblk), dim3(256), 0, (hipStream_t)stream, d, p,
+                     part, dtype, dkv, dkvc);
+  return (int)hipGetLastError();
+}
+
+}  // namespace hca

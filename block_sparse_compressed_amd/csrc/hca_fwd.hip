@@ -1,0 +1,302 @@
+// hca_fwd.hip -- HCA attention forward on gfx950 (bf16 MFMA, fp32 accumulation).
+//
+// One workgroup owns one query tile: bq positions x all H heads = 128 query
+// rows (single KV head, so every head of a position sees the same keys; the
+// shared-KV einsum form of "[DeepSeek-V4] Implement Compressed Attention
+// Layers", review suggestions).  It walks the tile's list of non-empty key
+// tiles from the host-built block table (EMPTY tiles never appear; "Add HCA
+// Static Compilation for Splash Attention [Deepseek v4]", Description), stages
+// each 32-key tile of the shared K = V tensor in LDS once for all heads, and
+// runs
+//   S^T = K Q^T      (v_mfma_f32_16x16x32_bf16, Q fragments held in VGPRs)
+//   online softmax   (PARTIAL tiles masked in registers from per-row intervals)
+//   O^T += K^T P^T   (P rounded to bf16, K^T read from a transposed LDS copy)
+// Computing S transposed leaves each lane holding one query row and 8
+// consecutive keys, which is exactly the B operand layout the PV product
+// needs, so P never goes through LDS.
+#include <climits>
+
+#include "hca_device.h"
+#include "hca_internal.h"
+
+namespace hca {
+
+constexpr int kBK = 32;  // keys per tile (raw and compressed)
+
+// K tile chunks: BK rows x D; transposed tile chunks: D rows x BK.  16 B each.
+template <int D, int NT>
+struct Stage {
+  static constexpr int KROW = D + 8;    // padded LDS row of the K tile (bf16)
+  static constexpr int TROW = kBK + 8;  // padded LDS row of the transposed tile
+  static constexpr int KCH = kBK * D / 8;
+  static constexpr int TCH = D * kBK / 8;
+  static constexpr int KPT = (KCH + NT - 1) / NT;
+  static constexpr int TPT = (TCH + NT - 1) / NT;
+
+  __device__ __forceinline__ static void load(uint4 (&pk)[KPT], uint4 (&pt)[TPT], int tid,
+                                              const bf16raw *src, int nk, const bf16raw *srct,
+                                              int ts, int k0) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int c = tid + u * NT;
+      if (KCH % NT == 0 || c < KCH) {
+        const int row = c / (D / 8), col = c % (D / 8);
+        const int key = k0 + row;
+        pk[u] = key < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)key * D + col * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int c = tid + u * NT;
+      if (TCH % NT == 0 || c < TCH) {
+        const int dd = c / (kBK / 8), col = c % (kBK / 8);
+        pt[u] = *reinterpret_cast<const uint4 *>(srct + (size_t)dd * ts + k0 + col * 8);
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void store(const uint4 (&pk)[KPT], const uint4 (&pt)[TPT],
+                                               int tid, bf16raw *k_lds, bf16raw *t_lds) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int c = tid + u * NT;
+      if (KCH % NT == 0 || c < KCH) {
+        const int row = c / (D / 8), col = c % (D / 8);
+        *reinterpret_cast<uint4 *>(k_lds + row * KROW + col * 8) = pk[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int c = tid + u * NT;
+      if (TCH % NT == 0 || c < TCH) {
+        const int dd = c / (kBK / 8), col = c % (kBK / 8);
+        *reinterpret_cast<uint4 *>(t_lds + dd * TROW + col * 8) = pt[u];
+      }
+    }
+  }
+};
+
+template <int D, int NW, int MB>
+__global__ void __launch_bounds__(NW * 64, 1)
+    hca_fwd_bf16_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                        const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
+                        const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
+                        float scale_log2, bf16raw *__restrict__ o, float *__restrict__ lse) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D / 32;
+  constexpr int DB = D / 16;
+  using St = Stage<D, NT>;
+  __shared__ __attribute__((aligned(16))) bf16raw k_lds[kBK * St::KROW];
+  __shared__ __attribute__((aligned(16))) bf16raw t_lds[D * St::TROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int nitems = d.B * d.nqt;
+  const int item = p.qorder[xcd_remap(blockIdx.x, nitems)];
+  const int b = item / d.nqt, qt = item - b * d.nqt;
+
+  int pos[MB], hh[MB], rlo[MB], clo[MB], chi[MB];
+  bool valid[MB];
+  bf16x8 qf[MB][KS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int rho = (wave * MB + mb) * 16 + j;
+    pos[mb] = qt * d.bq + rho / d.H;
+    hh[mb] = rho % d.H;
+    valid[mb] = pos[mb] < d.S;
+    if (valid[mb]) {
+      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos[mb]];
+      rlo[mb] = rw.x;
+      clo[mb] = rw.y;
+      chi[mb] = rw.z;
+    } else {
+      rlo[mb] = INT_MAX;
+      clo[mb] = 0;
+      chi[mb] = 0;
+    }
+    const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[mb][ks] = valid[mb] ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g))
+                             : as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+
+  float m_run[MB], l_run[MB];
+  floatx4 oacc[MB][DB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    m_run[mb] = -INFINITY;
+    l_run[mb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[mb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int e_begin = p.qptr[item], e_end = p.qptr[item + 1];
+  const bf16raw *kv_b = kv + (size_t)b * d.S * D;
+  const bf16raw *kvc_b = kvc + (size_t)b * d.Sc * D;
+  const bf16raw *kvt_b = kvt + (size_t)b * D * d.S_pad;
+  const bf16raw *kvct_b = kvct + (size_t)b * D * d.Sc_pad;
+
+  uint4 pk[St::KPT], pt[St::TPT];
+  auto issue = [&](int e) {
+    const uint32_t ent = p.qent[e];
+    const bool comp = ent & kEntComp;
+    const int k0 = (int)(ent & kEntIdx) * kBK;
+    St::load(pk, pt, tid, comp ? kvc_b : kv_b, comp ? d.Sc : d.S, comp ? kvct_b : kvt_b,
+             comp ? d.Sc_pad : d.S_pad, k0);
+  };
+  if (e_begin < e_end) issue(e_begin);
+
+  // A-operand rows of the two 16-key halves: lane group g ends up holding
+  // keys 8g .. 8g+7 of the 32-key tile for its query row.
+  const int r0 = 8 * (j >> 2) + (j & 3), r1 = r0 + 4;
+
+  for (int e = e_begin; e < e_end; ++e) {
+    const uint32_t ent = p.qent[e];
+    const bool comp = ent & kEntComp;
+    const bool full = ent & kEntFull;
+    const int k0 = (int)(ent & kEntIdx) * kBK;
+    __syncthreads();
+    St::store(pk, pt, tid, k_lds, t_lds);
+    __syncthreads();
+    if (e + 1 < e_end) issue(e + 1);
+
+    floatx4 s0[MB], s1[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      s0[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      s1[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a0 = as_bf16x8(lds_load16(k_lds + r0 * St::KROW + 32 * ks + 8 * g));
+      const bf16x8 a1 = as_bf16x8(lds_load16(k_lds + r1 * St::KROW + 32 * ks + 8 * g));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        s0[mb] = mfma16x16x32(a0, qf[mb][ks], s0[mb]);
+        s1[mb] = mfma16x16x32(a1, qf[mb][ks], s1[mb]);
+      }
+    }
+
+    bf16x8 pb[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float x[8];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[v] = s0[mb][v] * scale_log2;
+        x[4 + v] = s1[mb][v] * scale_log2;
+      }
+      if (!full) {
+        const int kb = k0 + 8 * g;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int key = kb + t;
+          const bool vis = comp ? (key >= clo[mb] && key < chi[mb])
+                                : (key >= rlo[mb] && key <= pos[mb]);
+          if (!vis) x[t] = -INFINITY;
+        }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
+      mx = xor_max(mx, 16);
+      mx = xor_max(mx, 32);
+      const float m_new = fmaxf(m_run[mb], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[mb] - m_use);
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        x[t] = fast_exp2(x[t] - m_use);
+        ps += x[t];
+      }
+      l_run[mb] = l_run[mb] * alpha + ps;
+      m_run[mb] = m_new;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[mb][db] *= alpha;
+      pb[mb] = pack8(x);
+    }
+
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 a = as_bf16x8(lds_load16(t_lds + (16 * db + j) * St::TROW + 8 * g));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb][db] = mfma16x16x32(a, pb[mb], oacc[mb][db]);
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float l = l_run[mb];
+    l = xor_sum(l, 16);
+    l = xor_sum(l, 32);
+    if (valid[mb]) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      bf16raw *orow = o + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        ushort4 w;
+        w.x = f2bf(oacc[mb][db][0] * inv);
+        w.y = f2bf(oacc[mb][db][1] * inv);
+        w.z = f2bf(oacc[mb][db][2] * inv);
+        w.w = f2bf(oacc[mb][db][3] * inv);
+        *reinterpret_cast<ushort4 *>(orow + 16 * db + 4 * g) = w;
+      }
+      if (g == 0)
+        lse[((size_t)b * d.H + hh[mb]) * d.S + pos[mb]] =
+            l > 0.f ? (m_run[mb] + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// dst[b][d][t] = src[b][t][d] for t < N, 0 for N <= t < N_pad.
+__global__ void __launch_bounds__(256) hca_transpose_kernel(const bf16raw *__restrict__ src,
+                                                            bf16raw *__restrict__ dst, int N,
+                                                            int N_pad, int D) {
+  __shared__ bf16raw tile[64][66];
+  const int b = blockIdx.z, t0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+  const bf16raw *s = src + (size_t)b * N * D;
+  bf16raw *o = dst + (size_t)b * D * N_pad;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int tt = i / 64, dd = i % 64, t = t0 + tt, dx = d0 + dd;
+    tile[tt][dd] = (t < N && dx < D) ? s[(size_t)t * D + dx] : (bf16raw)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int dd = i / 64, tt = i % 64, t = t0 + tt, dx = d0 + dd;
+    if (dx < D && t < N_pad) o[(size_t)dx * N_pad + t] = tile[tt][dd];
+  }
+}
+
+int launch_transpose_kv(const void *src, void *dst, int B, int N, int N_pad, int D,
+                        void *stream) {
+  if (N_pad == 0) return hipSuccess;
+  dim3 grid((N_pad + 63) / 64, (D + 63) / 64, B);
+  hipLaunchKernelGGL(hca_transpose_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                     (const bf16raw *)src, (bf16raw *)dst, N, N_pad, D);
+  return (int)hipGetLastError();
+}
+
+int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
+                    const void *kvc, const void *kvt, const void *kvct, float scale, void *o,
+                    float *lse, void *stream) {
+  const dim3 grid(d.B * d.nqt);
+  const float sl2 = scale * kLog2e;
+  hipStream_t s = (hipStream_t)stream;
+  auto args = [&](auto kernel, int nw) {
+    hipLaunchKernelGGL(kernel, grid, dim3(nw * 64), 0, s, d, p, (const bf16raw *)q,
+                       (const bf16raw *)kv, (const bf16raw *)kvc, (const bf16raw *)kvt,
+                       (const bf16raw *)kvct, sl2, (bf16raw *)o, lse);
+  };
+  switch (d.D) {
+    case 512: args(hca_fwd_bf16_kernel<512, 8, 1>, 8); break;
+    case 128: args(hca_fwd_bf16_kernel<128, 8, 1>, 8); break;
+    case 64: args(hca_fwd_bf16_kernel<64, 8, 1>, 8); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace hca

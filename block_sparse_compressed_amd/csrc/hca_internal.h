@@ -1,0 +1,115 @@
+// hca_internal.h -- host-side plan structure and kernel launcher declarations
+// shared by the planner, the C-ABI shim and the HIP kernels.  Not installed.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "hca.h"
+
+namespace hca {
+
+// Query-tile schedule entry (one per non-empty (query tile, key tile) pair):
+//   bit 31: key kind (0 raw, 1 compressed)   bit 30: tile is FULL
+//   bits 0..29: key tile index
+constexpr uint32_t kEntComp = 1u << 31;
+constexpr uint32_t kEntFull = 1u << 30;
+constexpr uint32_t kEntIdx = (1u << 30) - 1;
+
+// Key-tile work item for the key-stationary backward kernel: the query tiles
+// kv_ent[e0, e1) that see key tile `kt` of kind `kind` in batch row `b`; the
+// item's float32 partial gradient [bk][D] is written at `part_off` floats into
+// the partial area of the backward workspace.
+struct KvItem {
+  int32_t b, kind, kt, e0, e1, pad;
+  int64_t part_off;
+};
+static_assert(sizeof(KvItem) == 32, "KvItem layout");
+
+// Byte offsets of the sections of the plan's device image (256-B aligned).
+struct DevLayout {
+  uint64_t rows = 0;     // int4 [B][S]: raw_lo, comp_lo, comp_hi, 0
+  uint64_t qptr = 0;     // int32 [B*nqt + 1]
+  uint64_t qent = 0;     // uint32 [n_qent]
+  uint64_t qorder = 0;   // int32 [B*nqt]: query-tile launch order
+  uint64_t kvitem = 0;   // KvItem [n_items] (tile-major)
+  uint64_t kvorder = 0;  // int32 [n_items]: item launch order
+  uint64_t kvent = 0;    // uint32 [n_kvent]: bit 30 FULL, bits 0..29 query tile
+  uint64_t kvtile = 0;   // int32 [B][nkt_raw + nkt_comp][2]: first item, item count
+  uint64_t total = 0;
+};
+
+// Byte offsets inside the caller's workspaces.
+struct WsLayout {
+  uint64_t kvt = 0;     // transposed raw kv [B][D][S_pad] (bf16 path)
+  uint64_t kvct = 0;    // transposed compressed kv [B][D][Sc_pad]
+  uint64_t delta = 0;   // float32 [B][H][S] (backward)
+  uint64_t part = 0;    // float32 partial key gradients (backward)
+  uint64_t fwd_total = 0;
+  uint64_t bwd_total = 0;
+};
+
+// Parameters every kernel receives (by value).
+struct Dims {
+  int32_t B, S, H, D, r, W, Sc;
+  int32_t bq, bk_raw, bk_comp, nqt, nkt_raw, nkt_comp;
+  int32_t S_pad, Sc_pad;  // nkt_raw * bk_raw, nkt_comp * bk_comp
+  int32_t n_items;
+};
+
+struct DevPlan {
+  const int32_t *rows;  // int4 per position
+  const int32_t *qptr;
+  const uint32_t *qent;
+  const int32_t *qorder;
+  const KvItem *kvitem;
+  const int32_t *kvorder;
+  const uint32_t *kvent;
+  const int32_t *kvtile;
+};
+
+// Launchers (defined in the .hip files).  Each returns a hipError_t as int.
+int launch_transpose_kv(const void *src, void *dst, int B, int N, int N_pad, int D,
+                        void *stream);
+int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
+                    const void *kvc, const void *kvt, const void *kvct, float scale, void *o,
+                    float *lse, void *stream);
+int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
+                       const void *kvc, const void *kvt, const void *kvct, const void *o,
+                       const float *lse, const void *dout, float scale, void *dq, float *delta,
+                       void *stream);
+int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
+                        const void *kvc, const float *lse, const float *delta,
+                        const void *dout, float scale, float *part, void *stream);
+int launch_dkv_reduce(const Dims &d, const DevPlan &p, const float *part, int dtype, void *dkv,
+                      void *dkvc, void *stream);
+int launch_fwd_f32(const Dims &d, const DevPlan &p, const float *q, const float *kv,
+                   const float *kvc, float scale, float *o, float *lse, void *stream);
+int launch_bwd_f32(const Dims &d, const DevPlan &p, const float *q, const float *kv,
+                   const float *kvc, const float *o, const float *lse, const float *dout,
+                   float scale, float *dq, float *dkv, float *dkvc, float *delta, void *stream);
+
+// Tile shapes the GPU kernels are built for.
+bool kernel_supports(int dtype, int D, int H, int bq, int bk_raw, int bk_comp);
+void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp);
+
+void set_error(const std::string &msg);
+
+}  // namespace hca
+
+struct hca_plan {
+  hca_plan_info info{};
+  std::vector<int32_t> rows;  // [B][S][4]
+  std::vector<int32_t> qptr;
+  std::vector<uint32_t> qent;
+  std::vector<int32_t> qorder;
+  std::vector<hca::KvItem> kvitem;
+  std::vector<int32_t> kvorder;
+  std::vector<uint32_t> kvent;
+  std::vector<int32_t> kvtile;
+  hca::DevLayout lay;
+  hca::WsLayout ws;
+  std::vector<uint8_t> image;  // the device image, built once
+  void *dev = nullptr;         // caller's device buffer after upload
+};

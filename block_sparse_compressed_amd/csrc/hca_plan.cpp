@@ -1,0 +1,408 @@
+// hca_plan.cpp -- analytic block table and schedules for HCA attention (host only).
+//
+// The HCA pattern is deterministic, so the tile-level block mask can be built
+// from coordinates on the host ahead of time, with no S x S mask anywhere
+// ("Add HCA Static Compilation for Splash Attention [Deepseek v4]",
+// Description: the static block mask is evaluated on the CPU from coordinates
+// rather than materialised in device memory).  Each query position i of a
+// document starting at a_i sees
+//   raw keys          [max(i - W + 1, a_i), i]                    (none if W = 0)
+//   compressed entries [lo_c, floor((i + 1) / r))
+// with lo_c = ceil(a_i / r) under the STRICT document rule (the entry's whole
+// window lies in the document) and floor(a_i / r) under the LAST rule (the
+// window's last position lies in the document).  Both follow from the element
+// rule (entry c is complete for i iff (c+1) r <= i + 1) for contiguous
+// documents.  Tiles are classified from these intervals row by row; the
+// element predicate itself is never evaluated here.
+#include <algorithm>
+#include <climits>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "hca_internal.h"
+
+namespace hca {
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+inline uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Positions covered by one compressed-tile work item of the key-stationary
+// backward kernel; longer query-tile lists are split into several items whose
+// partial gradients are summed afterwards in a fixed order.
+constexpr int64_t kItemPositions = 512;
+
+}  // namespace
+
+void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp) {
+  (void)D;
+  if (dtype == HCA_BF16 && H >= 1 && H <= 128 && 128 % H == 0) {
+    *bq = 128 / H;
+  } else {
+    *bq = 16;
+  }
+  *bk_raw = 32;
+  *bk_comp = 32;
+}
+
+bool kernel_supports(int dtype, int D, int H, int bq, int bk_raw, int bk_comp) {
+  if (dtype == HCA_BF16) {
+    if (D != 64 && D != 128 && D != 512) return false;
+    if ((int64_t)bq * H != 128) return false;
+    return bk_raw == 32 && bk_comp == 32;
+  }
+  // float32 path: vector kernels, any tile shape.
+  return D % 64 == 0 && D >= 64 && D <= 512;
+}
+
+}  // namespace hca
+
+using namespace hca;
+
+extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int32_t W,
+                                           int32_t S_c, const int32_t *seg_starts,
+                                           const int32_t *seg_counts, int32_t H, int32_t D,
+                                           hca_dtype dtype, hca_compseg_mode mode,
+                                           const hca_tile_cfg *tiles, hca_plan **out) {
+  if (!out) {
+    set_error("hca_block_mask_build: out is NULL");
+    return HCA_ERR_INVALID_ARG;
+  }
+  *out = nullptr;
+  if (B < 1 || S < 1 || H < 1 || D < 1) {
+    set_error("hca_block_mask_build: B, S, H and D must all be >= 1");
+    return HCA_ERR_INVALID_ARG;
+  }
+  if (r < 1) {
+    set_error("hca_block_mask_build: compression ratio r must be >= 1");
+    return HCA_ERR_INVALID_ARG;
+  }
+  if (W < 0) {
+    set_error("hca_block_mask_build: window W must be >= 0");
+    return HCA_ERR_INVALID_ARG;
+  }
+  if (S_c != S / r) {
+    set_error("hca_block_mask_build: S_c must equal floor(S / r) = " + std::to_string(S / r) +
+              ", got " + std::to_string(S_c));
+    return HCA_ERR_INVALID_ARG;
+  }
+  if (dtype != HCA_F32 && dtype != HCA_BF16) {
+    set_error("hca_block_mask_build: unknown dtype");
+    return HCA_ERR_INVALID_ARG;
+  }
+  if (mode != HCA_COMPSEG_STRICT && mode != HCA_COMPSEG_LAST) {
+    set_error("hca_block_mask_build: unknown compressed-segment mode");
+    return HCA_ERR_INVALID_ARG;
+  }
+  if ((seg_starts == nullptr) != (seg_counts == nullptr)) {
+    set_error("hca_block_mask_build: seg_starts and seg_counts must both be NULL or both set");
+    return HCA_ERR_INVALID_ARG;
+  }
+  // Document lists: per row strictly increasing, first 0, all < S.
+  std::vector<int64_t> seg_off(B + 1, 0);
+  if (seg_counts) {
+    for (int b = 0; b < B; ++b) {
+      if (seg_counts[b] < 1 || seg_counts[b] > S) {
+        set_error("hca_block_mask_build: seg_counts[" + std::to_string(b) +
+                  "] must be in [1, S]");
+        return HCA_ERR_INVALID_ARG;
+      }
+      seg_off[b + 1] = seg_off[b] + seg_counts[b];
+    }
+    for (int b = 0; b < B; ++b) {
+      const int32_t *st = seg_starts + seg_off[b];
+      int64_t n = seg_off[b + 1] - seg_off[b];
+      if (st[0] != 0) {
+        set_error("hca_block_mask_build: first document start of row " + std::to_string(b) +
+                  " must be 0");
+        return HCA_ERR_INVALID_ARG;
+      }
+      for (int64_t j = 1; j < n; ++j) {
+        if (st[j] <= st[j - 1] || st[j] >= S) {
+          set_error("hca_block_mask_build: document starts of row " + std::to_string(b) +
+                    " must be strictly increasing and < S");
+          return HCA_ERR_INVALID_ARG;
+        }
+      }
+    }
+  }
+  int bq, bkr, bkc;
+  default_tiles(dtype, D, H, &bq, &bkr, &bkc);
+  if (tiles) {
+    if (tiles->bq < 0 || tiles->bk_raw < 0 || tiles->bk_comp < 0) {
+      set_error("hca_block_mask_build: tile sizes must be >= 0");
+      return HCA_ERR_INVALID_ARG;
+    }
+    if (tiles->bq) bq = tiles->bq;
+    if (tiles->bk_raw) bkr = tiles->bk_raw;
+    if (tiles->bk_comp) bkc = tiles->bk_comp;
+  }
+  // Work-list entries pack tile indices into 30 bits.
+  if (ceil_div(S, bq) >= (1 << 29) || ceil_div(S, bkr) >= (1 << 29)) {
+    set_error("hca_block_mask_build: too many tiles");
+    return HCA_ERR_INVALID_ARG;
+  }
+
+  hca_plan *p = new (std::nothrow) hca_plan();
+  if (!p) {
+    set_error("hca_block_mask_build: out of host memory");
+    return HCA_ERR_NOMEM;
+  }
+  try {
+    const int64_t nqt = ceil_div(S, bq);
+    const int64_t nktr = ceil_div(S, bkr);
+    const int64_t nktc = ceil_div(S_c, bkc);
+    hca_plan_info &in = p->info;
+    in.B = B; in.S = S; in.H = H; in.D = D; in.r = r; in.W = W; in.S_c = S_c;
+    in.dtype = dtype; in.comp_mode = mode;
+    in.bq = bq; in.bk_raw = bkr; in.bk_comp = bkc;
+    in.nqt = (int32_t)nqt; in.nkt_raw = (int32_t)nktr; in.nkt_comp = (int32_t)nktc;
+    in.kernel_ok = kernel_supports(dtype, D, H, bq, bkr, bkc) ? 1 : 0;
+
+    // ---- per-position visible intervals --------------------------------- //
+    p->rows.assign((size_t)B * S * 4, 0);
+    int64_t pairs_raw = 0, pairs_comp = 0;
+    for (int b = 0; b < B; ++b) {
+      const int32_t *st = seg_starts ? seg_starts + seg_off[b] : nullptr;
+      const int64_t nseg = seg_starts ? seg_off[b + 1] - seg_off[b] : 1;
+      int64_t next = 1, a = 0;
+      for (int64_t i = 0; i < S; ++i) {
+        while (st && next < nseg && st[next] <= i) a = st[next++];
+        int64_t rlo = W == 0 ? i + 1 : std::max<int64_t>(i - W + 1, a);
+        int64_t chi = std::min<int64_t>((i + 1) / r, S_c);
+        int64_t clo = mode == HCA_COMPSEG_STRICT ? ceil_div(a, r) : a / r;
+        if (clo > chi) clo = chi;
+        int32_t *row = &p->rows[((size_t)b * S + i) * 4];
+        row[0] = (int32_t)rlo; row[1] = (int32_t)clo; row[2] = (int32_t)chi; row[3] = 0;
+        pairs_raw += std::max<int64_t>(0, i - rlo + 1);
+        pairs_comp += chi - clo;
+      }
+    }
+    in.pairs_raw = pairs_raw;
+    in.pairs_comp = pairs_comp;
+
+    // ---- query-tile schedule (CSR) ---------------------------------------- //
+    p->qptr.assign((size_t)B * nqt + 1, 0);
+    std::vector<int64_t> cost((size_t)B * nqt, 0);
+    int64_t full_raw = 0, full_comp = 0;
+    for (int b = 0; b < B; ++b) {
+      for (int64_t qt = 0; qt < nqt; ++qt) {
+        const int64_t i0 = qt * bq, i1 = std::min<int64_t>(S, i0 + bq);
+        const bool nominal_q = i0 + bq <= S;
+        const int32_t *rw = &p->rows[((size_t)b * S) * 4];
+        // raw key tiles
+        int64_t lo = INT64_MAX, hi = -1;
+        for (int64_t i = i0; i < i1; ++i) {
+          if (rw[i * 4] <= i) {
+            lo = std::min<int64_t>(lo, rw[i * 4]);
+            hi = std::max<int64_t>(hi, i);
+          }
+        }
+        if (hi >= 0) {
+          for (int64_t kt = lo / bkr; kt <= hi / bkr; ++kt) {
+            const int64_t k0 = kt * bkr, k1 = k0 + bkr, kend = std::min<int64_t>(k1, S);
+            bool any = false, all = nominal_q && k1 <= S;
+            for (int64_t i = i0; i < i1; ++i) {
+              const int64_t rlo = rw[i * 4];
+              if (std::max(rlo, k0) <= std::min(i, kend - 1)) any = true;
+              if (!(rlo <= k0 && k1 - 1 <= i)) all = false;
+            }
+            if (!any) continue;
+            uint32_t e = (uint32_t)kt | (all ? kEntFull : 0u);
+            p->qent.push_back(e);
+            full_raw += all;
+            cost[(size_t)b * nqt + qt] += bkr;
+          }
+        }
+        // compressed entry tiles
+        lo = INT64_MAX;
+        hi = -1;
+        for (int64_t i = i0; i < i1; ++i) {
+          const int64_t clo = rw[i * 4 + 1], chi = rw[i * 4 + 2];
+          if (clo < chi) {
+            lo = std::min(lo, clo);
+            hi = std::max(hi, chi - 1);
+          }
+        }
+        if (hi >= 0) {
+          for (int64_t kt = lo / bkc; kt <= hi / bkc; ++kt) {
+            const int64_t k0 = kt * bkc, k1 = k0 + bkc, kend = std::min<int64_t>(k1, S_c);
+            bool any = false, all = nominal_q && k1 <= S_c;
+            for (int64_t i = i0; i < i1; ++i) {
+              const int64_t clo = rw[i * 4 + 1], chi = rw[i * 4 + 2];
+              if (std::max(clo, k0) < std::min(chi, kend)) any = true;
+              if (!(clo <= k0 && k1 <= chi)) all = false;
+            }
+            if (!any) continue;
+            uint32_t e = (uint32_t)kt | kEntComp | (all ? kEntFull : 0u);
+            p->qent.push_back(e);
+            full_comp += all;
+            cost[(size_t)b * nqt + qt] += bkc;
+          }
+        }
+        p->qptr[(size_t)b * nqt + qt + 1] = (int32_t)p->qent.size();
+      }
+    }
+    if (p->qent.size() >= (size_t)INT32_MAX) throw std::bad_alloc();
+    in.full_raw = full_raw;
+    in.full_comp = full_comp;
+    int64_t ent_comp = 0;
+    for (uint32_t e : p->qent) ent_comp += (e & kEntComp) ? 1 : 0;
+    in.tiles_raw = (int64_t)p->qent.size() - ent_comp;
+    in.tiles_comp = ent_comp;
+
+    // Heaviest query tiles first.
+    p->qorder.resize((size_t)B * nqt);
+    std::iota(p->qorder.begin(), p->qorder.end(), 0);
+    std::stable_sort(p->qorder.begin(), p->qorder.end(),
+                     [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+
+    // ---- key-tile lists (transpose of the query-tile schedule) ---------- //
+    const int64_t nkt = nktr + nktc;
+    std::vector<int64_t> kcount((size_t)B * nkt + 1, 0);
+    for (int b = 0; b < B; ++b)
+      for (int64_t qt = 0; qt < nqt; ++qt)
+        for (int32_t e = p->qptr[(size_t)b * nqt + qt]; e < p->qptr[(size_t)b * nqt + qt + 1]; ++e) {
+          uint32_t v = p->qent[e];
+          int64_t t = (v & kEntComp) ? nktr + (v & kEntIdx) : (v & kEntIdx);
+          kcount[(size_t)b * nkt + t + 1]++;
+        }
+    for (size_t j = 1; j < kcount.size(); ++j) kcount[j] += kcount[j - 1];
+    p->kvent.assign(p->qent.size(), 0);
+    {
+      std::vector<int64_t> fill(kcount.begin(), kcount.end() - 1);
+      for (int b = 0; b < B; ++b)
+        for (int64_t qt = 0; qt < nqt; ++qt)  // ascending qt within each key tile
+          for (int32_t e = p->qptr[(size_t)b * nqt + qt]; e < p->qptr[(size_t)b * nqt + qt + 1]; ++e) {
+            uint32_t v = p->qent[e];
+            int64_t t = (v & kEntComp) ? nktr + (v & kEntIdx) : (v & kEntIdx);
+            p->kvent[fill[(size_t)b * nkt + t]++] = (uint32_t)qt | (v & kEntFull);
+          }
+    }
+    // Work items: each key tile's list, split every kItemPositions positions.
+    const int64_t chunk = std::max<int64_t>(1, kItemPositions / bq);
+    p->kvtile.assign((size_t)B * nkt * 2, 0);
+    int64_t part_off = 0;
+    for (int b = 0; b < B; ++b) {
+      for (int64_t t = 0; t < nkt; ++t) {
+        const int kind = t < nktr ? 0 : 1;
+        const int64_t kt = kind ? t - nktr : t;
+        const int64_t s0 = kcount[(size_t)b * nkt + t], s1 = kcount[(size_t)b * nkt + t + 1];
+        p->kvtile[((size_t)b * nkt + t) * 2] = (int32_t)p->kvitem.size();
+        int32_t n = 0;
+        for (int64_t s = s0; s < s1; s += chunk) {
+          KvItem it{};
+          it.b = b; it.kind = kind; it.kt = (int32_t)kt;
+          it.e0 = (int32_t)s; it.e1 = (int32_t)std::min(s1, s + chunk);
+          it.part_off = part_off;
+          part_off += (int64_t)(kind ? bkc : bkr) * D;
+          p->kvitem.push_back(it);
+          ++n;
+        }
+        p->kvtile[((size_t)b * nkt + t) * 2 + 1] = n;
+      }
+    }
+    p->kvorder.resize(p->kvitem.size());
+    std::iota(p->kvorder.begin(), p->kvorder.end(), 0);
+    std::stable_sort(p->kvorder.begin(), p->kvorder.end(), [&](int32_t x, int32_t y) {
+      return (p->kvitem[x].e1 - p->kvitem[x].e0) > (p->kvitem[y].e1 - p->kvitem[y].e0);
+    });
+
+    // ---- device image ----------------------------------------------------- //
+    DevLayout &L = p->lay;
+    uint64_t off = 0;
+    auto place = [&](uint64_t bytes) { uint64_t o = off; off = align_up(off + bytes); return o; };
+    L.rows = place(p->rows.size() * 4);
+    L.qptr = place(p->qptr.size() * 4);
+    L.qent = place(std::max<size_t>(1, p->qent.size()) * 4);
+    L.qorder = place(p->qorder.size() * 4);
+    L.kvitem = place(std::max<size_t>(1, p->kvitem.size()) * sizeof(KvItem));
+    L.kvorder = place(std::max<size_t>(1, p->kvorder.size()) * 4);
+    L.kvent = place(std::max<size_t>(1, p->kvent.size()) * 4);
+    L.kvtile = place(p->kvtile.size() * 4);
+    L.total = off;
+    p->image.assign(L.total, 0);
+    auto put = [&](uint64_t o, const void *src, size_t bytes) {
+      if (bytes) std::memcpy(p->image.data() + o, src, bytes);
+    };
+    put(L.rows, p->rows.data(), p->rows.size() * 4);
+    put(L.qptr, p->qptr.data(), p->qptr.size() * 4);
+    put(L.qent, p->qent.data(), p->qent.size() * 4);
+    put(L.qorder, p->qorder.data(), p->qorder.size() * 4);
+    put(L.kvitem, p->kvitem.data(), p->kvitem.size() * sizeof(KvItem));
+    put(L.kvorder, p->kvorder.data(), p->kvorder.size() * 4);
+    put(L.kvent, p->kvent.data(), p->kvent.size() * 4);
+    put(L.kvtile, p->kvtile.data(), p->kvtile.size() * 4);
+    in.device_bytes = L.total;
+
+    // ---- workspaces ------------------------------------------------------- //
+    WsLayout &w = p->ws;
+    off = 0;
+    if (dtype == HCA_BF16) {
+      w.kvt = place((uint64_t)B * D * (nktr * bkr) * 2);
+      w.kvct = place((uint64_t)B * D * std::max<int64_t>(1, nktc * bkc) * 2);
+    }
+    w.fwd_total = dtype == HCA_BF16 ? off : 0;
+    w.delta = place((uint64_t)B * H * S * 4);
+    w.part = place((uint64_t)std::max<int64_t>(1, part_off) * 4);
+    w.bwd_total = off;
+    in.ws_fwd_bytes = w.fwd_total;
+    in.ws_bwd_bytes = w.bwd_total;
+  } catch (const std::bad_alloc &) {
+    delete p;
+    set_error("hca_block_mask_build: out of host memory");
+    return HCA_ERR_NOMEM;
+  }
+  *out = p;
+  return HCA_OK;
+}
+
+extern "C" hca_status hca_plan_get_info(const hca_plan *plan, hca_plan_info *out) {
+  if (!plan || !out) {
+    set_error("hca_plan_get_info: NULL argument");
+    return HCA_ERR_INVALID_ARG;
+  }
+  *out = plan->info;
+  return HCA_OK;
+}
+
+extern "C" hca_status hca_plan_export_tiles(const hca_plan *plan, uint8_t *raw_states,
+                                            uint8_t *comp_states) {
+  if (!plan) {
+    set_error("hca_plan_export_tiles: plan is NULL");
+    return HCA_ERR_INVALID_ARG;
+  }
+  const hca_plan_info &in = plan->info;
+  const size_t nqt = in.nqt, nktr = in.nkt_raw, nktc = in.nkt_comp;
+  if (raw_states) std::memset(raw_states, HCA_TILE_EMPTY, (size_t)in.B * nqt * nktr);
+  if (comp_states) std::memset(comp_states, HCA_TILE_EMPTY, (size_t)in.B * nqt * nktc);
+  for (int b = 0; b < in.B; ++b)
+    for (size_t qt = 0; qt < nqt; ++qt)
+      for (int32_t e = plan->qptr[b * nqt + qt]; e < plan->qptr[b * nqt + qt + 1]; ++e) {
+        uint32_t v = plan->qent[e];
+        uint8_t st = (v & kEntFull) ? HCA_TILE_FULL : HCA_TILE_PARTIAL;
+        size_t kt = v & kEntIdx;
+        if (v & kEntComp) {
+          if (comp_states) comp_states[((size_t)b * nqt + qt) * nktc + kt] = st;
+        } else if (raw_states) {
+          raw_states[((size_t)b * nqt + qt) * nktr + kt] = st;
+        }
+      }
+  return HCA_OK;
+}
+
+extern "C" hca_status hca_plan_export_rows(const hca_plan *plan, int32_t *rows) {
+  if (!plan || !rows) {
+    set_error("hca_plan_export_rows: NULL argument");
+    return HCA_ERR_INVALID_ARG;
+  }
+  const size_t n = (size_t)plan->info.B * plan->info.S;
+  for (size_t j = 0; j < n; ++j)
+    for (int c = 0; c < 3; ++c) rows[j * 3 + c] = plan->rows[j * 4 + c];
+  return HCA_OK;
+}
+
+extern "C" void hca_plan_destroy(hca_plan *plan) { delete plan; }

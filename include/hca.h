@@ -1,0 +1,228 @@
+/*
+ * hca.h -- C ABI of the MI355X (gfx950) Heavily Compressed Attention library.
+ *
+ * The operation.  DeepSeek-V4 Heavily Compressed Attention (HCA) is
+ * single-KV-head (MQA) softmax attention in which each query attends to a
+ * local sliding window of raw keys plus every compressed KV entry whose
+ * compression window has completed at or before the query; the pattern is
+ * deterministic, with no indexer ("Add HCA Static Compilation for Splash
+ * Attention [Deepseek v4]", Description).  Keys and values are one shared
+ * tensor broadcast over all query heads ("[DeepSeek-V4] Implement Compressed
+ * Attention Layers", review suggestions replacing the per-head repeat by an
+ * einsum broadcast with k = v = kv).  Conventions fixed by this library:
+ *
+ *   raw key t is visible to query i       iff  i - W < t <= i, same document
+ *   entry c covers raw positions [c*r, (c+1)*r) and is visible to query i
+ *                                          iff  (c+1)*r <= i+1, same document
+ *   document of an entry: HCA_COMPSEG_STRICT -- the document that contains
+ *   the entry's whole window (no document if it straddles a boundary);
+ *   HCA_COMPSEG_LAST -- the document of the window's last raw position.
+ *
+ * One softmax runs over the union of both key sets.  Outputs:
+ *   O[b,h,i]   = sum_k P_k kv_k,   P = softmax_k(scale * <q[b,h,i], kv_k>)
+ *   LSE[b,h,i] = natural log of sum_k exp(scale * <q, kv_k>)
+ * A query with no visible key gets O = 0, LSE = -inf and no gradient.
+ * Backward (loss gradient dO given): dQ, and one gradient for the shared raw
+ * kv and one for the compressed kv, each the sum of its key-path and
+ * value-path parts over all heads.
+ *
+ * Memory and ownership.
+ *   - The caller owns every device buffer (inputs, outputs, workspace, the
+ *     plan's device image) and the stream.  The library never allocates
+ *     device memory; a plan owns host memory only.
+ *   - All device pointers must be 16-byte aligned.  Tensors are contiguous,
+ *     row-major:  q, o, dout, dq [B][H][S][D];  kv, dkv [B][S][D];
+ *     kv_comp, dkv_comp [B][S_c][D];  lse [B][H][S] float32.
+ *     Element type of q, kv, kv_comp, o, dout, dq, dkv, dkv_comp: the plan's
+ *     dtype (float32 or bfloat16).  Accumulation is float32 throughout.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Work is enqueued on the given HIP stream (NULL = default stream) and is
+ *     asynchronous: results are ready after the caller synchronises.  Faults
+ *     inside kernels surface at that synchronisation.
+ *
+ * Errors.  Every entry point validates all of its arguments before it makes
+ * any HIP call, and returns a status; no exception crosses the ABI.  A
+ * thread-local message (hca_last_error) describes the last failure.
+ */
+#ifndef HCA_H_
+#define HCA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hca_status {
+  HCA_OK = 0,
+  HCA_ERR_INVALID_ARG = 1, /* a size, pointer, layout or segment list is invalid */
+  HCA_ERR_UNSUPPORTED = 2, /* valid, but outside what the GPU kernels implement  */
+  HCA_ERR_WORKSPACE = 3,   /* workspace or plan buffer smaller than required     */
+  HCA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed         */
+  HCA_ERR_NOMEM = 5,       /* host allocation failed                             */
+  HCA_ERR_STATE = 6        /* plan used before hca_plan_upload                   */
+} hca_status;
+
+typedef enum hca_dtype { HCA_F32 = 0, HCA_BF16 = 1 } hca_dtype;
+
+typedef enum hca_compseg_mode { HCA_COMPSEG_STRICT = 0, HCA_COMPSEG_LAST = 1 } hca_compseg_mode;
+
+/* Tile states of the block table (one byte each). */
+enum { HCA_TILE_EMPTY = 0, HCA_TILE_PARTIAL = 1, HCA_TILE_FULL = 2 };
+
+/*
+ * Tile shape of the block table: bq query positions (all heads) by bk_raw raw
+ * keys, or by bk_comp compressed entries.  A zero field selects the library's
+ * choice for (D, H, dtype).  Any positive shape is accepted by the planner;
+ * the GPU entry points run only the shapes their kernels are built for
+ * (hca_plan_info.kernel_ok).
+ */
+typedef struct hca_tile_cfg {
+  int32_t bq;
+  int32_t bk_raw;
+  int32_t bk_comp;
+} hca_tile_cfg;
+
+typedef struct hca_plan hca_plan; /* opaque, host-owned */
+
+typedef struct hca_plan_info {
+  int32_t B, S, H, D, r, W, S_c;
+  int32_t dtype;     /* hca_dtype */
+  int32_t comp_mode; /* hca_compseg_mode */
+  int32_t bq, bk_raw, bk_comp;
+  int32_t nqt;       /* ceil(S / bq) query tiles per batch row */
+  int32_t nkt_raw;   /* ceil(S / bk_raw) */
+  int32_t nkt_comp;  /* ceil(S_c / bk_comp) */
+  int32_t kernel_ok; /* 1: hca_attn_fwd / hca_attn_bwd run this plan */
+  int64_t tiles_raw, tiles_comp;   /* non-empty tiles, summed over the batch */
+  int64_t full_raw, full_comp;     /* of which FULL */
+  int64_t pairs_raw, pairs_comp;   /* visible (query position, key) pairs, summed over the
+                                      batch; multiply by H for (query row, key) pairs */
+  uint64_t device_bytes;           /* size of the plan's device image */
+  uint64_t ws_fwd_bytes;           /* workspace hca_attn_fwd needs */
+  uint64_t ws_bwd_bytes;           /* workspace hca_attn_bwd needs */
+} hca_plan_info;
+
+/*
+ * Builds the tile-level sparsity table analytically on the host, from
+ * (S, r, W, document starts) alone; no S x S mask is formed anywhere.
+ * Passage: "Add HCA Static Compilation for Splash Attention [Deepseek v4]",
+ * Description -- the block mask of the deterministic HCA pattern is computed
+ * from coordinates on the CPU ahead of time instead of being materialised in
+ * device memory; ceiling-division padding for unaligned S; segment IDs for
+ * packed documents.  The compression ratio is an explicit argument (a review
+ * on the same page notes it must not be inferred from S).
+ *
+ *   B, S, H, D    batch, sequence length, query heads, head dim (all >= 1)
+ *   r             compression ratio (>= 1);  W  window (>= 0, 0 = no raw keys)
+ *   S_c           number of compressed entries; must equal floor(S / r)
+ *   seg_starts    document start positions of every batch row, concatenated;
+ *                 per row strictly increasing, first 0, all < S.  NULL: one
+ *                 document per row (seg_counts must then be NULL too)
+ *   seg_counts    [B] number of documents in each row
+ *   dtype, mode   element type and compressed-entry document rule
+ *   tiles         NULL or a tile shape (0 fields = library choice)
+ *   out           receives the plan; release it with hca_plan_destroy
+ * Errors: HCA_ERR_INVALID_ARG for any violated rule above, HCA_ERR_NOMEM.
+ */
+hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int32_t W, int32_t S_c,
+                                const int32_t *seg_starts, const int32_t *seg_counts,
+                                int32_t H, int32_t D, hca_dtype dtype, hca_compseg_mode mode,
+                                const hca_tile_cfg *tiles, hca_plan **out);
+
+/* Fills *out with the plan's sizes and counts.  HCA_ERR_INVALID_ARG on NULL. */
+hca_status hca_plan_get_info(const hca_plan *plan, hca_plan_info *out);
+
+/*
+ * Copies the block table to host arrays: raw_states [B][nqt][nkt_raw] and
+ * comp_states [B][nqt][nkt_comp], one HCA_TILE_* byte each.  Either pointer
+ * may be NULL to skip that table.  Same rule as the planner: EMPTY when no
+ * in-range element is visible, FULL when every element of the nominal bq x bk
+ * rectangle is in range and visible, PARTIAL otherwise.
+ */
+hca_status hca_plan_export_tiles(const hca_plan *plan, uint8_t *raw_states,
+                                 uint8_t *comp_states);
+
+/*
+ * Copies the per-position visible intervals to a host array [B][S][3] of
+ * int32: {raw_lo, comp_lo, comp_hi}.  Query i sees raw keys raw_lo..i
+ * (none when raw_lo > i) and compressed entries comp_lo..comp_hi-1.
+ */
+hca_status hca_plan_export_rows(const hca_plan *plan, int32_t *rows);
+
+/*
+ * Copies the plan's device image (schedule lists and per-position
+ * intervals, info.device_bytes bytes) into the caller's device buffer with an
+ * asynchronous copy on `hip_stream`, and records the buffer in the plan.  The
+ * buffer must stay valid, and the plan alive, for every later call that uses
+ * the plan.  HCA_ERR_WORKSPACE if bytes < info.device_bytes; HCA_ERR_HIP if
+ * the copy cannot be enqueued.
+ */
+hca_status hca_plan_upload(hca_plan *plan, void *dev_buf, uint64_t bytes, void *hip_stream);
+
+/* Releases the plan's host memory (not the caller's device buffer).  NULL is a no-op. */
+void hca_plan_destroy(hca_plan *plan);
+
+/*
+ * Forward pass: o (plan dtype) and lse (float32).
+ * Passages: the HCA pattern ("Add HCA Static Compilation for Splash Attention
+ * [Deepseek v4]", Description); the shared-KV einsum form ("[DeepSeek-V4]
+ * Implement Compressed Attention Layers", review suggestions).
+ *   scale      logit scale (usually 1/sqrt(D)); must be finite and > 0
+ *   kv_comp    may be NULL only when S_c == 0
+ *   ws         device workspace of at least info.ws_fwd_bytes (may be NULL when 0)
+ * Errors: HCA_ERR_INVALID_ARG (NULL or misaligned pointer, bad scale),
+ * HCA_ERR_STATE (plan not uploaded), HCA_ERR_UNSUPPORTED (kernel_ok == 0),
+ * HCA_ERR_WORKSPACE, HCA_ERR_HIP (launch failure).
+ */
+hca_status hca_attn_fwd(const hca_plan *plan, const void *q, const void *kv, const void *kv_comp,
+                        float scale, void *o, float *lse, void *ws, uint64_t ws_bytes,
+                        void *hip_stream);
+
+/*
+ * Backward pass: dq, dkv (raw) and dkv_comp (compressed), all in the plan
+ * dtype, given the forward's o and lse and the loss gradient dout.
+ *   dq[b,h,i]  = scale * sum_k dS_k kv_k
+ *   dkv_k      = sum over (h, i) that see k of scale * dS_k q[b,h,i] + P_k dout[b,h,i]
+ * with dS_k = P_k (<dout, kv_k> - <dout, o>).  Key K and value V are one
+ * tensor, so each key's two gradient paths are summed ("[DeepSeek-V4]
+ * Implement Compressed Attention Layers", review suggestions: k = kv, v = kv).
+ * dQ is accumulated in registers, never through atomics to device memory.
+ *   ws   device workspace of at least info.ws_bwd_bytes
+ *   dkv_comp / kv_comp may be NULL only when S_c == 0.
+ * Errors as for hca_attn_fwd.
+ */
+hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const void *kv, const void *kv_comp,
+                        const void *o, const float *lse, const void *dout, float scale, void *dq,
+                        void *dkv, void *dkv_comp, void *ws, uint64_t ws_bytes, void *hip_stream);
+
+/*
+ * Kernel timing (instrumentation).  While enabled, every kernel the library
+ * launches is bracketed by a pair of HIP events recorded on that launch's
+ * stream.  hca_timing_read waits for the recorded events, writes per-kernel
+ * totals (up to `capacity` entries, *count = number of kernels with launches)
+ * and clears them.  Not thread-safe against concurrent hca_attn_* calls on
+ * other threads while enabled.  Errors: HCA_ERR_INVALID_ARG on NULL output
+ * pointers, HCA_ERR_HIP if an event cannot be created or read.
+ */
+typedef struct hca_kernel_time {
+  char name[32];    /* kernel family, e.g. "fwd", "bwd_dq", "bwd_dkv" */
+  int64_t launches; /* number of timed launches since the last read */
+  double total_ms;  /* summed event-to-event duration */
+} hca_kernel_time;
+
+hca_status hca_timing_enable(int32_t enable);
+hca_status hca_timing_read(hca_kernel_time *out, int32_t capacity, int32_t *count);
+
+/* Static description of a status code. */
+const char *hca_status_string(hca_status s);
+
+/* Detail message of the last failed call on this thread ("" if none). */
+const char *hca_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCA_H_ */

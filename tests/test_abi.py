@@ -1,0 +1,175 @@
+"""C ABI: exported symbols match include/hca.h, and every error path returns the
+documented status before any HIP call (so these run on a CPU-only host)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_compressed_amd as hca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hca.h")
+lib = hca.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hca_\w+)\s*\(", text)))
+
+
+def test_header_and_library_agree():
+    names = declared_functions()
+    assert names == sorted(hca.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_library_exports_via_nm():
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", hca.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (hca_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def status_of(fn, *args):
+    return fn(*args)
+
+
+def build_raw(B=1, S=64, r=8, W=4, Sc=None, starts=None, counts=None, H=4, D=64,
+              dtype=hca.HCA_BF16, mode=0, tiles=None):
+    out = ctypes.c_void_p()
+    st = np.asarray(starts, np.int32) if starts is not None else None
+    ct = np.asarray(counts, np.int32) if counts is not None else None
+    cfg = hca._TileCfg(*tiles) if tiles is not None else None
+    s = lib.hca_block_mask_build(B, S, r, W, (S // r if r > 0 else 0) if Sc is None else Sc,
+                                 st.ctypes.data if st is not None else None,
+                                 ct.ctypes.data if ct is not None else None, H, D, dtype, mode,
+                                 ctypes.byref(cfg) if cfg is not None else None,
+                                 ctypes.byref(out))
+    return s, out
+
+
+@pytest.mark.parametrize("kw", [
+    dict(S=0), dict(B=0), dict(H=0), dict(D=0), dict(r=0), dict(W=-1), dict(Sc=7),
+    dict(S=64, r=8, Sc=9), dict(starts=[0, 10], counts=None), dict(starts=None, counts=[1]),
+    dict(starts=[1, 10], counts=[2]), dict(starts=[0, 10, 10], counts=[3]),
+    dict(starts=[0, 30, 20], counts=[3]), dict(starts=[0, 64], counts=[2]),
+    dict(starts=[0], counts=[0]), dict(dtype=7), dict(mode=5), dict(tiles=(-1, 0, 0)),
+])
+def test_build_rejects_invalid(kw):
+    s, out = build_raw(**kw)
+    assert s == hca.HCA_ERR_INVALID_ARG
+    assert out.value is None
+    assert lib.hca_last_error().decode()
+
+
+def test_build_null_out():
+    assert lib.hca_block_mask_build(1, 8, 2, 2, 4, None, None, 1, 64, 1, 0, None, None) == \
+        hca.HCA_ERR_INVALID_ARG
+
+
+def test_python_layer_raises_value_error():
+    with pytest.raises(ValueError):
+        hca.hca_block_mask_build(1, 64, 8, 4, 7, H=4, D=64)
+
+
+FAKE = 0x100000  # an aligned address that is never dereferenced: checks fail first
+
+
+def fwd_args(plan, **over):
+    a = dict(q=FAKE, kv=FAKE, kvc=FAKE, scale=0.125, o=FAKE, lse=FAKE, ws=FAKE,
+             ws_bytes=1 << 40)
+    a.update(over)
+    return (plan.handle, a["q"], a["kv"], a["kvc"], ctypes.c_float(a["scale"]), a["o"],
+            a["lse"], a["ws"], ctypes.c_uint64(a["ws_bytes"]), None)
+
+
+def bwd_args(plan, **over):
+    a = dict(q=FAKE, kv=FAKE, kvc=FAKE, o=FAKE, lse=FAKE, dout=FAKE, scale=0.125, dq=FAKE,
+             dkv=FAKE, dkvc=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(over)
+    return (plan.handle, a["q"], a["kv"], a["kvc"], a["o"], a["lse"], a["dout"],
+            ctypes.c_float(a["scale"]), a["dq"], a["dkv"], a["dkvc"], a["ws"],
+            ctypes.c_uint64(a["ws_bytes"]), None)
+
+
+@pytest.fixture
+def plan():
+    return hca.hca_block_mask_build(1, 64, 8, 4, 8, H=4, D=64, dtype=hca.HCA_BF16, tiles=(32, 32, 32))
+
+
+def test_plan_is_kernel_ready(plan):
+    assert hca.hca_plan_get_info(plan).kernel_ok == 1
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), hca.HCA_ERR_INVALID_ARG), (dict(kv=FAKE + 8), hca.HCA_ERR_INVALID_ARG),
+    (dict(kvc=None), hca.HCA_ERR_INVALID_ARG), (dict(o=None), hca.HCA_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 4), hca.HCA_ERR_INVALID_ARG), (dict(scale=0.0), hca.HCA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), hca.HCA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), hca.HCA_ERR_WORKSPACE), (dict(ws=None), hca.HCA_ERR_INVALID_ARG),
+    (dict(), hca.HCA_ERR_STATE),
+])
+def test_fwd_error_paths(plan, over, status):
+    assert lib.hca_attn_fwd(*fwd_args(plan, **over)) == status
+    assert lib.hca_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dout=None), hca.HCA_ERR_INVALID_ARG), (dict(dq=FAKE + 2), hca.HCA_ERR_INVALID_ARG),
+    (dict(dkv=None), hca.HCA_ERR_INVALID_ARG), (dict(dkvc=None), hca.HCA_ERR_INVALID_ARG),
+    (dict(o=None), hca.HCA_ERR_INVALID_ARG), (dict(scale=-1.0), hca.HCA_ERR_INVALID_ARG),
+    (dict(ws_bytes=100), hca.HCA_ERR_WORKSPACE), (dict(), hca.HCA_ERR_STATE),
+])
+def test_bwd_error_paths(plan, over, status):
+    assert lib.hca_attn_bwd(*bwd_args(plan, **over)) == status
+
+
+def test_null_plan():
+    assert lib.hca_attn_fwd(None, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE, FAKE,
+                            ctypes.c_uint64(1 << 40), None) == hca.HCA_ERR_INVALID_ARG
+    assert lib.hca_plan_get_info(None, None) == hca.HCA_ERR_INVALID_ARG
+    lib.hca_plan_destroy(None)
+
+
+def test_compressed_pointers_optional_without_entries():
+    plan = hca.hca_block_mask_build(1, 64, 100, 4, 0, H=4, D=64, dtype=hca.HCA_BF16,
+                                    tiles=(32, 32, 32))
+    # kv_comp = NULL is fine when S_c = 0: the call proceeds to the upload check
+    assert lib.hca_attn_fwd(*fwd_args(plan, kvc=None)) == hca.HCA_ERR_STATE
+    assert lib.hca_attn_bwd(*bwd_args(plan, kvc=None, dkvc=None)) == hca.HCA_ERR_STATE
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=hca.HCA_BF16, H=3, D=64),        # 128 rows per tile not reachable
+    dict(dtype=hca.HCA_BF16, H=4, D=96),        # head dim without a kernel
+    dict(dtype=hca.HCA_F32, H=4, D=96),
+    dict(dtype=hca.HCA_BF16, H=4, D=64, tiles=(32, 16, 32)),
+])
+def test_unsupported_configurations(kw):
+    plan = hca.hca_block_mask_build(1, 64, 8, 4, 8, **kw)
+    assert hca.hca_plan_get_info(plan).kernel_ok == 0
+    assert lib.hca_attn_fwd(*fwd_args(plan)) == hca.HCA_ERR_UNSUPPORTED
+    assert lib.hca_attn_bwd(*bwd_args(plan)) == hca.HCA_ERR_UNSUPPORTED
+
+
+def test_upload_checks(plan):
+    info = hca.hca_plan_get_info(plan)
+    assert lib.hca_plan_upload(plan.handle, None, info.device_bytes, None) == \
+        hca.HCA_ERR_INVALID_ARG
+    assert lib.hca_plan_upload(plan.handle, FAKE + 1, info.device_bytes, None) == \
+        hca.HCA_ERR_INVALID_ARG
+    assert lib.hca_plan_upload(plan.handle, FAKE, info.device_bytes - 1, None) == \
+        hca.HCA_ERR_WORKSPACE
+    assert lib.hca_plan_upload(None, FAKE, info.device_bytes, None) == hca.HCA_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(7):
+        assert hca.hca_status_string(s).startswith("HCA_")

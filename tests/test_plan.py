@@ -1,0 +1,164 @@
+"""Block table and per-position intervals of the planner vs the oracle's element predicate.
+
+The planner (libhca.so, host code) builds the table analytically from
+intervals; the oracle classifies tiles by brute force over every element.  The
+two must agree bit for bit.  Runs on the CPU (no GPU call is made).
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import block_sparse_compressed_amd as hca
+import oracle
+from hca_inputs import WORKLOADS, doc_lengths, random_lengths, segment_ids, starts_csr
+
+
+def build_both(B, S, H, D, r, W, lengths, mode, tiles=None, dtype=hca.HCA_BF16):
+    starts, counts = starts_csr(lengths, B)
+    plan = hca.hca_block_mask_build(B, S, r, W, S // r, starts, counts, H, D, dtype, mode,
+                                    tiles)
+    seg = segment_ids(lengths, B, S)
+    prob = oracle.Problem(B, S, H, D, r, W, S // r, 1.0 / math.sqrt(D), seg,
+                          oracle.STRICT if mode == hca.HCA_COMPSEG_STRICT else oracle.LAST)
+    return plan, prob
+
+
+def check_full_tables(plan, prob):
+    info = hca.hca_plan_get_info(plan)
+    raw, comp = hca.hca_plan_export_tiles(plan)
+    want_raw = oracle.tile_states(prob, 0, info.bq, info.bk_raw)
+    want_comp = oracle.tile_states(prob, 1, info.bq, info.bk_comp)
+    assert raw.shape == want_raw.shape and comp.shape == want_comp.shape
+    np.testing.assert_array_equal(raw, want_raw)
+    np.testing.assert_array_equal(comp, want_comp)
+    assert info.tiles_raw == int((raw > 0).sum()) and info.full_raw == int((raw == 2).sum())
+    assert info.tiles_comp == int((comp > 0).sum()) and info.full_comp == int((comp == 2).sum())
+
+
+def check_rows(plan, prob, positions=None):
+    """Exported intervals reproduce the oracle's visible sets position by position."""
+    rows = hca.hca_plan_export_rows(plan)
+    B, S, W, Sc = prob.B, prob.S, prob.W, prob.Sc
+    for b in range(B):
+        for i in (range(S) if positions is None else positions):
+            lo, clo, chi = rows[b, i]
+            cand = range(max(0, i - W - 1), min(S, i + 2))
+            got_raw = [t for t in cand if lo <= t <= i]
+            want_raw = [t for t in cand if oracle.vis_raw(prob, b, i, t)]
+            assert got_raw == want_raw, (b, i)
+            want_comp = [c for c in range(Sc) if oracle.vis_comp(prob, b, i, c)]
+            assert list(range(clo, chi)) == want_comp, (b, i)
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_workload_tables_bit_exact(wid):
+    wl = WORKLOADS[wid]
+    dtype = hca.HCA_F32 if wl.dtype == "f32" else hca.HCA_BF16
+    plan, prob = build_both(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, doc_lengths(wl),
+                            hca.HCA_COMPSEG_STRICT, dtype=dtype)
+    check_full_tables(plan, prob)
+    info = hca.hca_plan_get_info(plan)
+    assert info.kernel_ok == 1
+    if wid <= 2:
+        assert info.pairs_raw == oracle.count_pairs(prob, 0)
+        assert info.pairs_comp == oracle.count_pairs(prob, 1)
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_workload_tables_sampled(wid):
+    """Full-size tables: every non-empty tile, the tiles around them and a random sample."""
+    wl = WORKLOADS[wid]
+    plan, prob = build_both(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, doc_lengths(wl),
+                            hca.HCA_COMPSEG_STRICT)
+    info = hca.hca_plan_get_info(plan)
+    assert info.kernel_ok == 1
+    raw, comp = hca.hca_plan_export_tiles(plan)
+    rng = np.random.default_rng(wid)
+    for kind, table, bk in [(0, raw, info.bk_raw), (1, comp, info.bk_comp)]:
+        nz = np.flatnonzero(table.reshape(-1))
+        nkt = table.shape[2]
+        # neighbours of non-empty tiles along the key axis (band edges)
+        neigh = np.concatenate([nz - 1, nz + 1])
+        neigh = neigh[(neigh >= 0) & (neigh < table.size)]
+        sample = rng.integers(0, table.size, size=20000)
+        # every tile of a few random query tiles
+        qts = rng.integers(0, info.nqt, size=8)
+        rowsel = (qts[:, None] * nkt + np.arange(nkt)[None, :]).reshape(-1)
+        flat = np.unique(np.concatenate([nz, neigh, sample, rowsel]))
+        want = oracle.tile_states_at(prob, kind, info.bq, bk, flat)
+        np.testing.assert_array_equal(table.reshape(-1)[flat], want)
+    positions = sorted(set(rng.integers(0, wl.S, size=64).tolist()) | {0, wl.S - 1, wl.r - 1,
+                                                                        wl.r, wl.r - 2})
+    check_rows(plan, prob, positions)
+
+
+def sweep_cases():
+    rng = np.random.default_rng(1234)
+    out = []
+    tiles_list = [None, (1, 1, 1), (4, 8, 4), (16, 32, 32), (3, 5, 7)]
+    for S, r, W in itertools.product([1, 2, 15, 16, 17, 31, 33, 489, 4133],
+                                     [1, 3, 16, 128, 5000], [0, 1, 5, 64, 128, 10000]):
+        if rng.random() > 0.22:
+            continue
+        B = 2 if rng.random() < 0.3 else 1
+        kind = rng.integers(0, 5)
+        lengths = None
+        if kind == 1:  # random documents
+            lengths = [random_lengths(rng, S, 1, max(1, S // 3)) for _ in range(B)]
+        elif kind == 2 and S > r:  # boundaries on multiples of r
+            lengths = [[L for L in np.diff(sorted({0, S} | set(range(0, S, r * 2)))).tolist()]
+                       for _ in range(B)]
+        elif kind == 3:  # boundaries on tile edges (16)
+            lengths = [[L for L in np.diff(sorted({0, S} | set(range(0, S, 16)))).tolist()]
+                       for _ in range(B)]
+        elif kind == 4:  # many length-1 documents then one long one
+            lengths = [[1] * min(S - 1, 5) + ([S - min(S - 1, 5)] if S > 1 else [])
+                       for _ in range(B)]
+            lengths = [[L for L in ls if L > 0] for ls in lengths]
+        tiles = tiles_list[rng.integers(0, len(tiles_list))]
+        mode = int(rng.integers(0, 2))
+        H = int(rng.choice([1, 4, 16, 64]))
+        out.append((B, S, H, r, W, lengths, mode, tiles))
+    return out
+
+
+@pytest.mark.parametrize("case", sweep_cases(), ids=lambda c: "B%dS%dH%dr%dW%d" % c[:5])
+def test_sweep_bit_exact(case):
+    B, S, H, r, W, lengths, mode, tiles = case
+    plan, prob = build_both(B, S, H, 128, r, W, lengths, mode, tiles)
+    check_full_tables(plan, prob)
+    if S <= 600:
+        check_rows(plan, prob)
+        info = hca.hca_plan_get_info(plan)
+        assert info.pairs_raw == oracle.count_pairs(prob, 0)
+        assert info.pairs_comp == oracle.count_pairs(prob, 1)
+
+
+def test_unaligned_lengths_cover_padding_branches():
+    """S = 489 with 2-, 16- and 32-wide tiles: padded rows and keys are never FULL."""
+    for tiles in [(2, 32, 32), (16, 32, 32), (32, 16, 8)]:
+        plan, prob = build_both(1, 489, 4, 64, 16, 64, None, hca.HCA_COMPSEG_STRICT, tiles)
+        check_full_tables(plan, prob)
+        raw, comp = hca.hca_plan_export_tiles(plan)
+        info = hca.hca_plan_get_info(plan)
+        last_q = raw[0, info.nqt - 1]
+        if 489 % info.bq:
+            assert not (last_q == hca.HCA_TILE_FULL).any()
+        if 489 % info.bk_raw:
+            assert not (raw[0, :, info.nkt_raw - 1] == hca.HCA_TILE_FULL).any()
+
+
+def test_schedule_is_consistent():
+    """Query-tile lists and key-tile work items cover the same non-empty tiles."""
+    wl = WORKLOADS[2]
+    lengths = doc_lengths(wl)
+    starts, counts = starts_csr(lengths, wl.B)
+    plan = hca.hca_block_mask_build(wl.B, wl.S, wl.r, wl.W, wl.Sc, starts, counts, wl.H, wl.D,
+                                    hca.HCA_BF16, hca.HCA_COMPSEG_STRICT)
+    info = hca.hca_plan_get_info(plan)
+    assert info.device_bytes > 0 and info.ws_bwd_bytes > info.ws_fwd_bytes > 0
+    # no device buffer is O(S^2): the plan image is linear in S
+    assert info.device_bytes < 64 * wl.B * wl.S + 16 * (info.tiles_raw + info.tiles_comp) + 8192
