@@ -18,10 +18,19 @@
 
 #include "hca_device.h"
 #include "hca_internal.h"
+#include "hca_stage.h"
 
 namespace hca {
 
 constexpr int kBK = 32;  // keys per tile (raw and compressed)
+
+#ifndef HCA_FWD_NW
+#define HCA_FWD_NW 8  // waves of the D = 512 forward (two per SIMD)
+#endif
+#ifndef HCA_FWD_MB
+#define HCA_FWD_MB 1  // 16-row blocks per wave of the D = 512 forward
+#endif
+
 
 // K tile chunks: BK rows x D; transposed tile chunks: D rows x BK.  16 B each.
 template <int D, int NT>
@@ -251,6 +260,230 @@ __global__ void __launch_bounds__(NW * 64, 1)
   }
 }
 
+// ---------------------------------------------------------------------------
+// D = 512 forward: 8 waves x 16 rows = 128 rows per workgroup.
+//
+// Software pipeline per wave: while the softmax and the PV product of tile t
+// run, the S^T = K Q^T MFMAs of tile t+1 are already in flight, so the VALU
+// and transcendental work of the softmax overlaps matrix-core work instead of
+// idling it.  K tiles and K^T tiles therefore live one tile apart: during
+// iteration t the LDS holds K(t+1) (being read), K(t+2) (arriving), K^T(t)
+// (being read) and K^T(t+1) (arriving) -- 4 x 32 KiB -- with one barrier per
+// tile.  Loads go global -> LDS directly (no VGPR staging), in swizzled layouts
+// that make every operand read conflict-free.  O is rescaled lazily: a row's
+// reference max only moves when its tile max exceeds it by more than kLazy
+// (log2 units), so P stays below 2^kLazy and rescales are rare.
+// ---------------------------------------------------------------------------
+// Lazy rescaling: a row's reference max m_run only moves when the tile max
+// exceeds it by more than kLazy (log2 units), so P = 2^(x - m_run) stays below
+// 2^kLazy and the O rescale (a wave-uniform branch) is rare.
+constexpr float kLazy = 8.f;
+
+template <int NW, int MB>
+__global__ void __launch_bounds__(NW * 64, 1)
+    hca_fwd512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                      const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
+                      const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
+                      float scale_log2, bf16raw *__restrict__ o, float *__restrict__ lse) {
+  constexpr int D = 512, KS = D / 32, DB = D / 16;
+  constexpr int M = NW * MB * 16;  // rows per workgroup
+  // [K buffer 0][K buffer 1][K^T buffer 0][K^T buffer 1]
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes512];
+  char *const kbase = smem;
+  char *const tbase = smem + 2 * kTileBytes512;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int nslices = d.bq * d.H / M;
+  const int nitems = d.B * d.nqt;
+  const int li = blockIdx.x / nslices, sl = blockIdx.x - li * nslices;
+  const int item = p.qorder[xcd_remap(li, nitems)];
+  const int b = item / d.nqt, qt = item - b * d.nqt;
+
+  int pos[MB], hh[MB], rlo[MB], clo[MB], chi[MB];
+  bool valid[MB];
+  bf16x8 qf[MB][KS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int rho = sl * M + (wave * MB + mb) * 16 + j;
+    pos[mb] = qt * d.bq + rho / d.H;
+    hh[mb] = rho % d.H;
+    valid[mb] = pos[mb] < d.S;
+    rlo[mb] = INT_MAX;
+    clo[mb] = chi[mb] = 0;
+    if (valid[mb]) {
+      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos[mb]];
+      rlo[mb] = rw.x;
+      clo[mb] = rw.y;
+      chi[mb] = rw.z;
+    }
+    const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[mb][ks] = valid[mb]
+                       ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g))
+                       : as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+
+  const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
+  // The tile's list, one entry per lane: entries are fetched with readlane,
+  // not with a dependent memory load per tile (lists longer than 64 fall back
+  // to memory for the tail).
+  const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
+  auto entry = [&](int t) -> uint32_t {
+    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t) : p.qent[e_begin + t];
+  };
+  const __amdgpu_buffer_rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
+  const __amdgpu_buffer_rsrc_t r_kvc =
+      make_rsrc(kvc + (size_t)b * d.Sc * D, (uint32_t)d.Sc * D * 2);
+  const __amdgpu_buffer_rsrc_t r_kvt =
+      make_rsrc(kvt + (size_t)b * D * d.S_pad, (uint32_t)d.S_pad * D * 2);
+  const __amdgpu_buffer_rsrc_t r_kvct =
+      make_rsrc(kvct + (size_t)b * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 2);
+  auto stage_k = [&](int t) {  // K of list entry t -> K buffer t & 1
+    if (t >= nent) return;
+    const uint32_t ent = entry(t);
+    stage_k512<NW>((ent & kEntComp) ? r_kvc : r_kv, (int)(ent & kEntIdx) * kBK,
+                   kbase + (t & 1) * kTileBytes512, wave, lane);
+  };
+  auto stage_t = [&](int t) {  // K^T of list entry t -> K^T buffer t & 1
+    if (t >= nent) return;
+    const uint32_t ent = entry(t);
+    const bool comp = ent & kEntComp;
+    stage_kt512<NW>(comp ? r_kvct : r_kvt, comp ? d.Sc_pad : d.S_pad, (int)(ent & kEntIdx) * kBK,
+                    tbase + (t & 1) * kTileBytes512, wave, lane);
+  };
+
+  // Lane-constant parts of the operand addresses.  QK^T A operand of k-step
+  // ks = 4 m + n: key row 8 (j >> 2) + (j & 3) (+4 for the second 16 keys),
+  // slot (4 ks + g) ^ j = 4 (m*4 + (n ^ (j >> 2))) + (g ^ (j & 3)).
+  int qk_off[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+    qk_off[n] = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
+  const int pv_off = (4 * j + (g ^ kt_swz(j))) * 16;
+
+  // S^T of tile t for every row block: two 16-key halves per block.
+  auto qk = [&](int t, floatx4 (&s)[MB][2]) {
+    const char *kb = kbase + (t & 1) * kTileBytes512;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) s[mb][0] = s[mb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const char *a = kb + qk_off[ks & 3] + 256 * (ks >> 2);
+      const bf16x8 a0 = lds_frag(a), a1 = lds_frag(a + 4096);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        s[mb][0] = mfma16x16x32(a0, qf[mb][ks], s[mb][0]);
+        s[mb][1] = mfma16x16x32(a1, qf[mb][ks], s[mb][1]);
+      }
+    }
+  };
+
+  float m_run[MB], l_run[MB];
+  floatx4 oacc[MB][DB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    m_run[mb] = -INFINITY;
+    l_run[mb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[mb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  stage_k(0);
+  stage_k(1);
+  stage_t(0);
+  wait_all_loads();
+  __syncthreads();
+  floatx4 sc[MB][2];
+  if (nent > 0) qk(0, sc);
+  __syncthreads();
+  stage_k(2);
+  stage_t(1);
+
+  for (int it = 0; it < nent; ++it) {
+    floatx4 sn[MB][2];
+    if (it + 1 < nent) qk(it + 1, sn);
+
+    const uint32_t ent = entry(it);
+    const bool comp = ent & kEntComp;
+    const int k0 = (int)(ent & kEntIdx) * kBK;
+    bf16x8 pb[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float x[8];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[v] = sc[mb][0][v] * scale_log2;
+        x[4 + v] = sc[mb][1][v] * scale_log2;
+      }
+      if (!(ent & kEntFull)) {
+        // visible keys of this row: [lo, hi) relative to this lane's 8 keys
+        const int lo = (comp ? clo[mb] : rlo[mb]) - (k0 + 8 * g);
+        const int hi = (comp ? chi[mb] : pos[mb] + 1) - (k0 + 8 * g);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mx = group_max(mx);
+      const bool up = mx > m_run[mb] + kLazy;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float m_new = up ? mx : m_run[mb];
+        const float alpha = fast_exp2(m_run[mb] - (m_new == -INFINITY ? 0.f : m_new));
+        l_run[mb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[mb][db] *= alpha;
+        m_run[mb] = m_new;
+      }
+      const float m_use = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        x[t] = fast_exp2(x[t] - m_use);
+        l_run[mb] += x[t];
+      }
+      pb[mb] = pack8(x);
+    }
+    const char *tb = tbase + (it & 1) * kTileBytes512 + pv_off;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 a = lds_frag(tb + db * 1024);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb][db] = mfma16x16x32(a, pb[mb], oacc[mb][db]);
+    }
+
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      sc[mb][0] = sn[mb][0];
+      sc[mb][1] = sn[mb][1];
+    }
+    wait_all_loads();
+    __syncthreads();
+    stage_k(it + 3);
+    stage_t(it + 2);
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const float l = group_sum(l_run[mb]);
+    if (!valid[mb]) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16raw *orow = o + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      ushort4 w;
+      w.x = f2bf(oacc[mb][db][0] * inv);
+      w.y = f2bf(oacc[mb][db][1] * inv);
+      w.z = f2bf(oacc[mb][db][2] * inv);
+      w.w = f2bf(oacc[mb][db][3] * inv);
+      *reinterpret_cast<ushort4 *>(orow + 16 * db + 4 * g) = w;
+    }
+    if (g == 0)
+      lse[((size_t)b * d.H + hh[mb]) * d.S + pos[mb]] =
+          l > 0.f ? (m_run[mb] + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
 // dst[b][d][t] = src[b][t][d] for t < N, 0 for N <= t < N_pad.
 __global__ void __launch_bounds__(256) hca_transpose_kernel(const bf16raw *__restrict__ src,
                                                             bf16raw *__restrict__ dst, int N,
@@ -291,7 +524,14 @@ int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *
                        (const bf16raw *)kvct, sl2, (bf16raw *)o, lse);
   };
   switch (d.D) {
-    case 512: args(hca_fwd_bf16_kernel<512, 8, 1>, 8); break;
+    case 512: {
+      constexpr int NW = HCA_FWD_NW, MB = HCA_FWD_MB;
+      const dim3 g512(d.B * d.nqt * (d.bq * d.H / (NW * MB * 16)));
+      hipLaunchKernelGGL((hca_fwd512_kernel<NW, MB>), g512, dim3(NW * 64), 0, s, d, p,
+                         (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc,
+                         (const bf16raw *)kvt, (const bf16raw *)kvct, sl2, (bf16raw *)o, lse);
+      break;
+    }
     case 128: args(hca_fwd_bf16_kernel<128, 8, 1>, 8); break;
     case 64: args(hca_fwd_bf16_kernel<64, 8, 1>, 8); break;
     default: return (int)hipErrorInvalidValue;

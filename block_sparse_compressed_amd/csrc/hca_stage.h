@@ -1,0 +1,97 @@
+// hca_stage.h -- asynchronous staging of 32-key K/V tiles (D = 512) into LDS.
+//
+// Tiles move global -> LDS with buffer_load_dwordx4 ... lds: each wave
+// instruction deposits 64 lanes x 16 B = 1 KiB contiguously at its LDS base
+// (lane l at base + 16 l), bypassing VGPRs; the buffer range check returns
+// zeros for rows past the end of the tensor.  The layouts below permute which
+// global 16-byte chunk each lane fetches so that the MFMA operand reads that
+// follow are free of LDS bank conflicts:
+//
+//   K tile  [32 keys][64 chunks]: key row rho holds chunk c at slot
+//           c ^ hk(rho), hk(rho) = (rho & 3) | ((rho >> 3) & 3) << 2.
+//           The QK^T A-operand read of lane (g, j) -- key row
+//           8 (j >> 2) + 4 b + (j & 3), chunk 4 ks + g -- lands on slot
+//           (4 ks + g) ^ j: sixteen distinct bank groups per 16 lanes.
+//   K^T tile [512 d][4 chunks of 8 keys], 16 d-rows per 1 KiB block: row jr
+//           of a block holds chunk c at slot c ^ tk(jr),
+//           tk(jr) = (jr >> 2) ^ (jr & 2).  The PV A-operand read of lane
+//           (g, j) -- d-row j of the block, chunk g -- is again conflict-free.
+#pragma once
+
+#include "hca_device.h"
+
+namespace hca {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int k_swz(int rho) { return (rho & 3) | (((rho >> 3) & 3) << 2); }
+__device__ __forceinline__ int kt_swz(int jr) { return (jr >> 2) ^ (jr & 2); }
+
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+constexpr int kTileBytes512 = 32 * 1024;  // one K tile or one K^T tile at D = 512
+
+// Buffer resource over `bytes` bytes at `base`; loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+// All of the offset goes in the per-lane operand (scalar offset 0), so the
+// range check covers the whole address.
+__device__ __forceinline__ void buf_load16(__amdgpu_buffer_rsrc_t r, void *lds_base, int voff,
+                                           int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, voff, soff, 0, 0);
+}
+
+// Stages key rows k0 .. k0+31 of a [nk][512] tensor (resource `r` covers
+// exactly nk rows, so rows past the end load as zeros) into `kbuf` (32 KiB).
+template <int NW>
+__device__ __forceinline__ void stage_k512(__amdgpu_buffer_rsrc_t r, int k0, char *kbuf, int wave,
+                                           int lane) {
+  static_assert(32 % NW == 0, "waves must divide the tile rows");
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int rho = wave * (32 / NW) + i;
+    buf_load16(r, kbuf + rho * 1024, (k0 + rho) * 1024 + ((lane ^ k_swz(rho)) << 4), 0);
+  }
+}
+
+// Stages columns k0 .. k0+31 of a transposed copy [512][ts] (ts a multiple of
+// 32, padding zero-filled) into `tbuf` (32 KiB).
+template <int NW>
+__device__ __forceinline__ void stage_kt512(__amdgpu_buffer_rsrc_t r, int ts, int k0, char *tbuf,
+                                            int wave, int lane) {
+  const int jr = lane >> 2;
+  const int voff = jr * ts * 2 + k0 * 2 + (((lane & 3) ^ kt_swz(jr)) << 4);
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int blk = wave * (32 / NW) + i;
+    buf_load16(r, tbuf + blk * 1024, voff + blk * 16 * ts * 2, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const char *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// Cross-lane max / sum over lanes i ^ 16 and i ^ 32 (the four lane groups of a
+// 16x16 MFMA output column) with the gfx950 permlane swaps.
+__device__ __forceinline__ float group_max(float v) {
+  unsigned u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  u = __float_as_uint(v);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float group_sum(float v) {
+  unsigned u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  u = __float_as_uint(v);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace hca
