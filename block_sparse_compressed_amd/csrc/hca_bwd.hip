@@ -24,6 +24,7 @@
 
 #include "hca_device.h"
 #include "hca_internal.h"
+#include "hca_stage.h"
 
 namespace hca {
 
@@ -262,6 +263,185 @@ __global__ void __launch_bounds__(NW * 64, 1)
 }
 
 // ---------------------------------------------------------------------------
+// 1b. dQ (+ delta) at D = 512: NW waves x 16 rows, one wave per SIMD (Q, dO
+//     and the dQ accumulator take ~260 registers).  Same staging as the
+//     forward: K and K^T tiles double-buffered in LDS one tile apart, filled
+//     by buffer-to-LDS loads in conflict-free swizzled layouts, one barrier per
+//     tile.  The S^T and dP^T products of tile t+1 share their K A-operands and
+//     are issued before dS and the dQ product of tile t, so VALU work overlaps
+//     matrix-core work.
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
+    hca_bwd_dq512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                         const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
+                         const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
+                         const bf16raw *__restrict__ o, const float *__restrict__ lse,
+                         const bf16raw *__restrict__ dout, float scale_log2, float scale,
+                         bf16raw *__restrict__ dq, float *__restrict__ delta) {
+  constexpr int D = 512, KS = D / 32, DB = D / 16;
+  constexpr int M = NW * 16;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes512];
+  char *const kbase = smem;
+  char *const tbase = smem + 2 * kTileBytes512;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int nslices = d.bq * d.H / M;
+  const int nitems = d.B * d.nqt;
+  const int li = blockIdx.x / nslices, sl = blockIdx.x - li * nslices;
+  const int item = p.qorder[xcd_remap(li, nitems)];
+  const int b = item / d.nqt, qt = item - b * d.nqt;
+
+  const int rho = sl * M + wave * 16 + j;
+  const int pos = qt * d.bq + rho / d.H, hh = rho % d.H;
+  const bool valid = pos < d.S;
+  const size_t row = ((size_t)b * d.H + hh) * d.S + pos;
+  int rlo = INT_MAX, clo = 0, chi = 0;
+  float lse2 = -INFINITY;
+  if (valid) {
+    const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos];
+    rlo = rw.x;
+    clo = rw.y;
+    chi = rw.z;
+    lse2 = lse[row] * kLog2e;
+  }
+  bf16x8 qf[KS], dof[KS];
+  float dl;
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 qv = make_uint4(0, 0, 0, 0), dv = qv, ov = qv;
+      if (valid) {
+        qv = *reinterpret_cast<const uint4 *>(q + row * D + 32 * ks + 8 * g);
+        dv = *reinterpret_cast<const uint4 *>(dout + row * D + 32 * ks + 8 * g);
+        ov = *reinterpret_cast<const uint4 *>(o + row * D + 32 * ks + 8 * g);
+      }
+      qf[ks] = as_bf16x8(qv);
+      dof[ks] = as_bf16x8(dv);
+      part += dot8(dv, ov);
+    }
+    dl = group_sum(part);
+    if (valid && g == 0) delta[row] = dl;
+  }
+
+  const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
+  const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
+  auto entry = [&](int t) -> uint32_t {
+    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t) : p.qent[e_begin + t];
+  };
+  const __amdgpu_buffer_rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
+  const __amdgpu_buffer_rsrc_t r_kvc =
+      make_rsrc(kvc + (size_t)b * d.Sc * D, (uint32_t)d.Sc * D * 2);
+  const __amdgpu_buffer_rsrc_t r_kvt =
+      make_rsrc(kvt + (size_t)b * D * d.S_pad, (uint32_t)d.S_pad * D * 2);
+  const __amdgpu_buffer_rsrc_t r_kvct =
+      make_rsrc(kvct + (size_t)b * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 2);
+  auto stage_k = [&](int t) {
+    if (t >= nent) return;
+    const uint32_t ent = entry(t);
+    stage_k512<NW>((ent & kEntComp) ? r_kvc : r_kv, (int)(ent & kEntIdx) * kBK,
+                   kbase + (t & 1) * kTileBytes512, wave, lane);
+  };
+  auto stage_t = [&](int t) {
+    if (t >= nent) return;
+    const uint32_t ent = entry(t);
+    const bool comp = ent & kEntComp;
+    stage_kt512<NW>(comp ? r_kvct : r_kvt, comp ? d.Sc_pad : d.S_pad, (int)(ent & kEntIdx) * kBK,
+                    tbase + (t & 1) * kTileBytes512, wave, lane);
+  };
+
+  int qk_off[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+    qk_off[n] = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
+  const int pv_off = (4 * j + (g ^ kt_swz(j))) * 16;
+
+  // S^T and dP^T of tile t (shared K A-operands): [0] keys 0-15, [1] keys 16-31.
+  auto sdp = [&](int t, floatx4 (&s)[2], floatx4 (&dp)[2]) {
+    const char *kb = kbase + (t & 1) * kTileBytes512;
+    s[0] = s[1] = dp[0] = dp[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const char *a = kb + qk_off[ks & 3] + 256 * (ks >> 2);
+      const bf16x8 a0 = lds_frag(a), a1 = lds_frag(a + 4096);
+      s[0] = mfma16x16x32(a0, qf[ks], s[0]);
+      s[1] = mfma16x16x32(a1, qf[ks], s[1]);
+      dp[0] = mfma16x16x32(a0, dof[ks], dp[0]);
+      dp[1] = mfma16x16x32(a1, dof[ks], dp[1]);
+    }
+  };
+
+  floatx4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  stage_k(0);
+  stage_k(1);
+  stage_t(0);
+  wait_all_loads();
+  __syncthreads();
+  floatx4 sc[2], pc[2];
+  if (nent > 0) sdp(0, sc, pc);
+  __syncthreads();
+  stage_k(2);
+  stage_t(1);
+
+  for (int it = 0; it < nent; ++it) {
+    floatx4 sn[2], pn[2];
+    if (it + 1 < nent) sdp(it + 1, sn, pn);
+
+    const uint32_t ent = entry(it);
+    const bool comp = ent & kEntComp;
+    const int k0 = (int)(ent & kEntIdx) * kBK;
+    float x[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      x[v] = sc[0][v] * scale_log2 - lse2;
+      x[4 + v] = sc[1][v] * scale_log2 - lse2;
+    }
+    if (!(ent & kEntFull)) {
+      const int lo = (comp ? clo : rlo) - (k0 + 8 * g);
+      const int hi = (comp ? chi : pos + 1) - (k0 + 8 * g);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      x[v] = fast_exp2(x[v]) * (pc[0][v] - dl);
+      x[4 + v] = fast_exp2(x[4 + v]) * (pc[1][v] - dl);
+    }
+    const bf16x8 dsb = pack8(x);
+    const char *tb = tbase + (it & 1) * kTileBytes512 + pv_off;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = mfma16x16x32(lds_frag(tb + db * 1024), dsb, acc[db]);
+
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+    pc[0] = pn[0];
+    pc[1] = pn[1];
+    wait_all_loads();
+    __syncthreads();
+    stage_k(it + 3);
+    stage_t(it + 2);
+  }
+
+  if (valid) {
+    bf16raw *drow = dq + row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      ushort4 w;
+      w.x = f2bf(acc[db][0] * scale);
+      w.y = f2bf(acc[db][1] * scale);
+      w.z = f2bf(acc[db][2] * scale);
+      w.w = f2bf(acc[db][3] * scale);
+      *reinterpret_cast<ushort4 *>(drow + 16 * db + 4 * g) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 2. dKV, key-stationary.  4 waves: wave & 1 selects 16 of the tile's 32 keys,
 //    wave >> 1 selects one 32-row half of each 64-row step.
 // ---------------------------------------------------------------------------
@@ -470,7 +650,7 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
                        scale, (bf16raw *)dq, delta);
   };
   switch (d.D) {
-    case 512: go(hca_bwd_dq_kernel<512, 4, 1>, 4, 64); break;
+    case 512: go(hca_bwd_dq512_kernel<4>, 4, 64); break;
     case 128: go(hca_bwd_dq_kernel<128, 8, 1>, 8, 128); break;
     case 64: go(hca_bwd_dq_kernel<64, 8, 1>, 8, 128); break;
     default: return (int)hipErrorInvalidValue;
