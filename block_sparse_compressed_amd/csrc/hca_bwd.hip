@@ -598,41 +598,275 @@ __global__ void __launch_bounds__(256, 1)
 }
 
 // ---------------------------------------------------------------------------
+// 2b. dKV at D = 512, key-stationary.  A work item is a 64-key tile and a run
+//     of query tiles that see it; each of the 4 waves (one per SIMD) owns 16
+//     keys: their K fragments stay in VGPRs and their [16 keys][512] fp32
+//     gradient in accumulation registers (32 keys per wave would not fit the
+//     register file at D = 512).  Query rows stream through LDS in
+//     32-row steps (Q and dO, 64 KiB, double-buffered, direct global->LDS
+//     loads, swizzled rows).  Per step and wave:
+//       S = Q K^T, dP = dO K^T          (A operands: ds_read_b128, conflict-free)
+//       P = 2^(S log2e scale - LSE log2e), dS = scale P (dP - delta)
+//       dKV^T += Q^T dS + dO^T P        (A operands: ds_read_b64_tr_b16 of the
+//                                        same row-major tiles)
+//     Waves whose 32 keys are invisible to a step skip its arithmetic.
+// ---------------------------------------------------------------------------
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// Transposed A operand (d-row j of a 16-wide column block, rows 8g..8g+7 of
+// the step) from a swizzled row-major [rows][512] tile: two transpose reads.
+__device__ __forceinline__ bf16x8 tr_frag(const char *p) {
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(p));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(p + 4096));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
+    hca_bwd_dkv512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                          const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
+                          const float *__restrict__ lse, const float *__restrict__ delta,
+                          const bf16raw *__restrict__ dout, float scale_log2, float scale,
+                          float *__restrict__ part) {
+  constexpr int D = 512, KS = D / 32, DB = D / 16;
+  constexpr int STEP = 32, STEP_BYTES = STEP * 1024;
+  static_assert(NW * 16 == 64, "4 waves x 16 keys");
+  constexpr int KB = 1;  // 16-key blocks per wave
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * STEP_BYTES];  // [buf][Q | dO]
+  __shared__ float lse_s[2][STEP], dl_s[2][STEP];
+  __shared__ int lo_s[2][STEP], hi_s[2][STEP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const KvItem it = p.kvitem[p.kvorder[blockIdx.x]];
+  const int b = it.b;
+  const bool comp = it.kind != 0;
+  const int nk = comp ? d.Sc : d.S;
+  const int kw0 = it.kt * d.kv_bk + 16 * KB * wave;  // this wave's first key
+  const bf16raw *src = comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D;
+
+  // Stationary K fragments, B[k = d][n = key] of S = Q K^T.
+  bf16x8 kf[KB][KS];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw0 + 16 * kb + j;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[kb][ks] = as_bf16x8(key < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)key * D +
+                                                                           32 * ks + 8 * g)
+                                      : make_uint4(0, 0, 0, 0));
+  }
+  floatx4 acc[KB][DB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[kb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int nq = it.e1 - it.e0;
+  const int spq = d.bq * d.H / STEP;  // steps per query tile
+  const int nsteps = nq * spq;
+  const uint32_t ent_lane = lane < nq ? p.kvent[it.e0 + lane] : 0u;
+  auto entry = [&](int e) -> uint32_t {
+    return e < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, e) : p.kvent[it.e0 + e];
+  };
+  // Step s covers rows u*32 .. u*32+31 of query tile entry e = s / spq.
+  auto stage = [&](int s) {
+    const int e = s / spq, u = s - e * spq;
+    const int qt = (int)(entry(e) & kEntIdx);
+    char *qb = smem + (s & 1) * 2 * STEP_BYTES;
+#pragma unroll
+    for (int i = 0; i < STEP / NW; ++i) {
+      const int r = wave * (STEP / NW) + i;
+      const int rho = u * STEP + r;
+      const int pos = min(qt * d.bq + rho / d.H, d.S - 1), h = rho % d.H;
+      const size_t off = (((size_t)b * d.H + h) * d.S + pos) * D + ((lane ^ k_swz(r)) << 3);
+      __builtin_amdgcn_global_load_lds(q + off, (lds_void_t *)(qb + r * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dout + off, (lds_void_t *)(qb + STEP_BYTES + r * 1024), 16,
+                                       0, 0);
+    }
+  };
+  float nl2 = 0.f, ndl = 0.f;
+  int nlo = INT_MAX, nhi = 0;
+  auto rowinfo = [&](int s) {  // wave 0, lanes < STEP: row lane of step s
+    const int e = s / spq, u = s - e * spq;
+    const int qt = (int)(entry(e) & kEntIdx);
+    const int rho = u * STEP + lane;
+    const int pos = qt * d.bq + rho / d.H, h = rho % d.H;
+    nl2 = 0.f;
+    ndl = 0.f;
+    nlo = INT_MAX;
+    nhi = 0;
+    if (lane < STEP && pos < d.S) {
+      const size_t row = ((size_t)b * d.H + h) * d.S + pos;
+      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos];
+      nl2 = lse[row] * kLog2e;
+      ndl = delta[row];
+      nlo = comp ? rw.y : rw.x;
+      nhi = comp ? rw.z : pos + 1;
+    }
+  };
+  auto put_rowinfo = [&](int slot) {
+    if (lane < STEP) {
+      lse_s[slot][lane] = nl2;
+      dl_s[slot][lane] = ndl;
+      lo_s[slot][lane] = nlo;
+      hi_s[slot][lane] = nhi;
+    }
+  };
+
+  int qk_off[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+    qk_off[n] = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
+  // Transpose-read offsets for d-column blocks db = 8 dh + dl (dh via +256 dh).
+  int tr_off[8];
+  {
+    const int u = j >> 2, c0 = (j & 3) >> 1;
+#pragma unroll
+    for (int dl = 0; dl < 8; ++dl)
+      tr_off[dl] = (8 * g + u) * 1024 + (((2 * dl + c0) ^ (u + 4 * g)) << 4) + ((j & 1) << 3);
+  }
+
+  if (nsteps > 0) stage(0);
+  if (wave == 0 && nsteps > 0) {
+    rowinfo(0);
+    put_rowinfo(0);
+  }
+  wait_all_loads();
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) {
+      stage(s + 1);
+      if (wave == 0) rowinfo(s + 1);
+    }
+    const int slot = s & 1;
+    const bool full = entry(s / spq) & kEntFull;
+    const char *qb = smem + slot * 2 * STEP_BYTES;
+    const char *ob = qb + STEP_BYTES;
+    float l2r[8], dlr[8];
+    bool vis[KB][8];
+    bool any = false;
+#pragma unroll
+    for (int u8 = 0; u8 < 8; ++u8) {
+      const int rr = 8 * g + u8;
+      l2r[u8] = lse_s[slot][rr];
+      dlr[u8] = dl_s[slot][rr];
+      const int lo = lo_s[slot][rr], hi = hi_s[slot][rr];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int key = kw0 + 16 * kb + j;
+        vis[kb][u8] = full || (key >= lo && key < hi);
+        any |= vis[kb][u8];
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(any)) {
+      floatx4 sv[2][KB], pv[2][KB];  // [row block][key block]
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sv[rb][kb] = pv[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = qk_off[ks & 3] + 256 * (ks >> 2);
+        const bf16x8 aq0 = lds_frag(qb + off), aq1 = lds_frag(qb + off + 4096);
+        const bf16x8 ad0 = lds_frag(ob + off), ad1 = lds_frag(ob + off + 4096);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          sv[0][kb] = mfma16x16x32(aq0, kf[kb][ks], sv[0][kb]);
+          sv[1][kb] = mfma16x16x32(aq1, kf[kb][ks], sv[1][kb]);
+          pv[0][kb] = mfma16x16x32(ad0, kf[kb][ks], pv[0][kb]);
+          pv[1][kb] = mfma16x16x32(ad1, kf[kb][ks], pv[1][kb]);
+        }
+      }
+      // Lane (g, j) holds rows 8g + 4 rb + v of the step for key 16 kb + j.
+      bf16x8 pb[KB], dsb[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float pr[8], ds[8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int u8 = 4 * rb + v;
+            const float e = vis[kb][u8] ? fast_exp2(sv[rb][kb][v] * scale_log2 - l2r[u8]) : 0.f;
+            pr[u8] = e;
+            ds[u8] = e * (pv[rb][kb][v] - dlr[u8]) * scale;
+          }
+        pb[kb] = pack8(pr);
+        dsb[kb] = pack8(ds);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int off = tr_off[db & 7] + 256 * (db >> 3);
+        const bf16x8 aqt = tr_frag(qb + off), adt = tr_frag(ob + off);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          acc[kb][db] = mfma16x16x32(aqt, dsb[kb], acc[kb][db]);
+          acc[kb][db] = mfma16x16x32(adt, pb[kb], acc[kb][db]);
+        }
+      }
+    }
+    if (s + 1 < nsteps && wave == 0) put_rowinfo((s + 1) & 1);
+    wait_all_loads();
+    __syncthreads();
+  }
+
+  // Partial [64 keys][512] of this item: this wave's 16 keys.
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    float *out = part + it.part_off + (size_t)(16 * KB * wave + 16 * kb + j) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      float4 w;
+      w.x = acc[kb][db][0];
+      w.y = acc[kb][db][1];
+      w.z = acc[kb][db][2];
+      w.w = acc[kb][db][3];
+      *reinterpret_cast<float4 *>(out + 16 * db + 4 * g) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. Fixed-order sum of the partials of every key tile -> dKV / dKV_comp.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
     hca_dkv_reduce_kernel(Dims d, DevPlan p, const float *__restrict__ part, int dtype,
                           void *__restrict__ dkv, void *__restrict__ dkvc) {
-  const int nkt = d.nkt_raw + d.nkt_comp;
-  const int b = blockIdx.x / nkt, t = blockIdx.x - b * nkt;
-  const bool comp = t >= d.nkt_raw;
-  const int kt = comp ? t - d.nkt_raw : t;
-  const int bk = comp ? d.bk_comp : d.bk_raw;
+  // One workgroup per (key tile, 1024-element chunk of the tile's [kv_bk][D] block).
+  const int nkt = d.nkv_raw + d.nkv_comp;
+  const int per_tile = d.kv_bk * d.D / 1024;
+  const int tile = blockIdx.x / per_tile, chunk = blockIdx.x - tile * per_tile;
+  const int b = tile / nkt, t = tile - b * nkt;
+  const bool comp = t >= d.nkv_raw;
+  const int kt = comp ? t - d.nkv_raw : t;
   const int nk = comp ? d.Sc : d.S;
   const int first = p.kvtile[2 * (b * nkt + t)], n = p.kvtile[2 * (b * nkt + t) + 1];
   const int D = d.D;
-  for (int e = threadIdx.x * 4; e < bk * D; e += 256 * 4) {
-    const int key = kt * bk + e / D, col = e % D;
-    if (key >= nk) continue;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = 0; i < n; ++i) {
-      const float4 v = *reinterpret_cast<const float4 *>(part + p.kvitem[first + i].part_off + e);
-      a.x += v.x;
-      a.y += v.y;
-      a.z += v.z;
-      a.w += v.w;
-    }
-    const size_t off = ((size_t)b * nk + key) * D + col;
-    if (dtype == HCA_BF16) {
-      ushort4 w;
-      w.x = f2bf(a.x);
-      w.y = f2bf(a.y);
-      w.z = f2bf(a.z);
-      w.w = f2bf(a.w);
-      *reinterpret_cast<ushort4 *>((bf16raw *)(comp ? dkvc : dkv) + off) = w;
-    } else {
-      *reinterpret_cast<float4 *>((float *)(comp ? dkvc : dkv) + off) = a;
-    }
+  const int e = chunk * 1024 + threadIdx.x * 4;
+  const int key = kt * d.kv_bk + e / D, col = e % D;
+  if (key >= nk) return;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < n; ++i) {
+    const float4 v = *reinterpret_cast<const float4 *>(part + p.kvitem[first + i].part_off + e);
+    a.x += v.x;
+    a.y += v.y;
+    a.z += v.z;
+    a.w += v.w;
+  }
+  const size_t off = ((size_t)b * nk + key) * D + col;
+  if (dtype == HCA_BF16) {
+    ushort4 w;
+    w.x = f2bf(a.x);
+    w.y = f2bf(a.y);
+    w.z = f2bf(a.z);
+    w.w = f2bf(a.w);
+    *reinterpret_cast<ushort4 *>((bf16raw *)(comp ? dkvc : dkv) + off) = w;
+  } else {
+    *reinterpret_cast<float4 *>((float *)(comp ? dkvc : dkv) + off) = a;
   }
 }
 
@@ -670,7 +904,11 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
                        (const bf16raw *)dout, sl2, scale, part);
   };
   switch (d.D) {
-    case 512: go(hca_bwd_dkv_kernel<512>); break;
+    case 512:
+      hipLaunchKernelGGL(hca_bwd_dkv512_kernel<4>, dim3(d.n_items), dim3(256), 0, s, d, p,
+                         (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc, lse, delta,
+                         (const bf16raw *)dout, sl2, scale, part);
+      break;
     case 128: go(hca_bwd_dkv_kernel<128>); break;
     case 64: go(hca_bwd_dkv_kernel<64>); break;
     default: return (int)hipErrorInvalidValue;
@@ -680,7 +918,8 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
 
 int launch_dkv_reduce(const Dims &d, const DevPlan &p, const float *part, int dtype, void *dkv,
                       void *dkvc, void *stream) {
-  const int nblk = d.B * (d.nkt_raw + d.nkt_comp);
+  // kv_bk * D is a multiple of 1024 for every kernel configuration (kv_bk >= 32, D >= 64).
+  const int nblk = d.B * (d.nkv_raw + d.nkv_comp) * (d.kv_bk * d.D / 1024);
   if (nblk == 0) return hipSuccess;
   hipLaunchKernelGGL(hca_dkv_reduce_kernel, dim3(nblk), dim3(256), 0, (hipStream_t)stream, d, p,
                      part, dtype, dkv, dkvc);

@@ -18,9 +18,9 @@ constexpr uint32_t kEntFull = 1u << 30;
 constexpr uint32_t kEntIdx = (1u << 30) - 1;
 
 // Key-tile work item for the key-stationary backward kernel: the query tiles
-// kv_ent[e0, e1) that see key tile `kt` of kind `kind` in batch row `b`; the
-// item's float32 partial gradient [bk][D] is written at `part_off` floats into
-// the partial area of the backward workspace.
+// kv_ent[e0, e1) that see key tile `kt` (kv_bk keys) of kind `kind` in batch
+// row `b`; the item's float32 partial gradient [kv_bk][D] is written at
+// `part_off` floats into the partial area of the backward workspace.
 struct KvItem {
   int32_t b, kind, kt, e0, e1, pad;
   int64_t part_off;
@@ -36,7 +36,7 @@ struct DevLayout {
   uint64_t kvitem = 0;   // KvItem [n_items] (tile-major)
   uint64_t kvorder = 0;  // int32 [n_items]: item launch order
   uint64_t kvent = 0;    // uint32 [n_kvent]: bit 30 FULL, bits 0..29 query tile
-  uint64_t kvtile = 0;   // int32 [B][nkt_raw + nkt_comp][2]: first item, item count
+  uint64_t kvtile = 0;   // int32 [B][nkv_raw + nkv_comp][2]: first item, item count
   uint64_t total = 0;
 };
 
@@ -56,6 +56,7 @@ struct Dims {
   int32_t bq, bk_raw, bk_comp, nqt, nkt_raw, nkt_comp;
   int32_t S_pad, Sc_pad;  // nkt_raw * bk_raw, nkt_comp * bk_comp
   int32_t n_items;
+  int32_t kv_bk, nkv_raw, nkv_comp;  // key tiles of the key-stationary backward
 };
 
 struct DevPlan {
@@ -108,6 +109,7 @@ struct hca_plan {
   std::vector<int32_t> kvorder;
   std::vector<uint32_t> kvent;
   std::vector<int32_t> kvtile;
+  int32_t kv_bk = 32, nkv_raw = 0, nkv_comp = 0;  // key-stationary backward tiling
   hca::DevLayout lay;
   hca::WsLayout ws;
   std::vector<uint8_t> image;  // the device image, built once

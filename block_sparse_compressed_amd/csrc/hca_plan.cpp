@@ -35,7 +35,27 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // partial gradients are summed afterwards in a fixed order.
 constexpr int64_t kItemPositions = 512;
 
+// State of query tile qt (positions qt*bq .. +bq-1) against keys [k0, k0+bk)
+// of `kind`, from the per-position intervals `rw` ([S][4]).
+int classify_tile(const int32_t *rw, int64_t S, int64_t qt, int bq, int kind, int64_t k0,
+                  int64_t bk, int64_t nk) {
+  const int64_t i0 = qt * bq, i1 = std::min<int64_t>(S, i0 + bq);
+  const int64_t k1 = k0 + bk, kend = std::min<int64_t>(k1, nk);
+  bool any = false, all = i0 + bq <= S && k1 <= nk;
+  for (int64_t i = i0; i < i1; ++i) {
+    const int64_t lo = kind ? rw[i * 4 + 1] : rw[i * 4];
+    const int64_t hi = kind ? rw[i * 4 + 2] : i + 1;
+    if (std::max(lo, k0) < std::min(hi, kend)) any = true;
+    if (!(lo <= k0 && k1 <= hi)) all = false;
+  }
+  return any ? (all ? HCA_TILE_FULL : HCA_TILE_PARTIAL) : HCA_TILE_EMPTY;
+}
+
 }  // namespace
+
+// Keys per work item of the key-stationary backward: 64 (4 waves x 16 keys)
+// for the D = 512 bf16 kernel, otherwise the forward's 32-key tile.
+int kv_tile_keys(int dtype, int D) { return (dtype == HCA_BF16 && D == 512) ? 64 : 32; }
 
 void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp) {
   (void)D;
@@ -161,6 +181,7 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     in.bq = bq; in.bk_raw = bkr; in.bk_comp = bkc;
     in.nqt = (int32_t)nqt; in.nkt_raw = (int32_t)nktr; in.nkt_comp = (int32_t)nktc;
     in.kernel_ok = kernel_supports(dtype, D, H, bq, bkr, bkc) ? 1 : 0;
+    p->kv_bk = kv_tile_keys(dtype, D);
 
     // ---- per-position visible intervals --------------------------------- //
     p->rows.assign((size_t)B * S * 4, 0);
@@ -260,51 +281,61 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     std::stable_sort(p->qorder.begin(), p->qorder.end(),
                      [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
 
-    // ---- key-tile lists (transpose of the query-tile schedule) ---------- //
-    const int64_t nkt = nktr + nktc;
-    std::vector<int64_t> kcount((size_t)B * nkt + 1, 0);
-    for (int b = 0; b < B; ++b)
-      for (int64_t qt = 0; qt < nqt; ++qt)
-        for (int32_t e = p->qptr[(size_t)b * nqt + qt]; e < p->qptr[(size_t)b * nqt + qt + 1]; ++e) {
-          uint32_t v = p->qent[e];
-          int64_t t = (v & kEntComp) ? nktr + (v & kEntIdx) : (v & kEntIdx);
-          kcount[(size_t)b * nkt + t + 1]++;
-        }
-    for (size_t j = 1; j < kcount.size(); ++j) kcount[j] += kcount[j - 1];
-    p->kvent.assign(p->qent.size(), 0);
-    {
-      std::vector<int64_t> fill(kcount.begin(), kcount.end() - 1);
-      for (int b = 0; b < B; ++b)
-        for (int64_t qt = 0; qt < nqt; ++qt)  // ascending qt within each key tile
-          for (int32_t e = p->qptr[(size_t)b * nqt + qt]; e < p->qptr[(size_t)b * nqt + qt + 1]; ++e) {
-            uint32_t v = p->qent[e];
-            int64_t t = (v & kEntComp) ? nktr + (v & kEntIdx) : (v & kEntIdx);
-            p->kvent[fill[(size_t)b * nkt + t]++] = (uint32_t)qt | (v & kEntFull);
-          }
-    }
-    // Work items: each key tile's list, split every kItemPositions positions.
-    const int64_t chunk = std::max<int64_t>(1, kItemPositions / bq);
-    p->kvtile.assign((size_t)B * nkt * 2, 0);
+    // ---- key-tile work lists for the key-stationary backward ------------ //
+    // Key tiles of kv_bk keys (wider than the forward's tiles at D = 512, so
+    // one workgroup's waves each own 32 of them); for each, the query tiles
+    // that see any of its keys, classified from the same intervals.
+    const int64_t kvb = p->kv_bk;
+    const int64_t nkvr = ceil_div(S, kvb), nkvc = ceil_div(S_c, kvb);
+    const int64_t nkv = nkvr + nkvc;
+    const int64_t chunk = std::max<int64_t>(1, (kvb >= 64 ? 128 : kItemPositions) / bq);
+    p->kvtile.assign((size_t)B * nkv * 2, 0);
     int64_t part_off = 0;
+    std::vector<uint32_t> list;
     for (int b = 0; b < B; ++b) {
-      for (int64_t t = 0; t < nkt; ++t) {
-        const int kind = t < nktr ? 0 : 1;
-        const int64_t kt = kind ? t - nktr : t;
-        const int64_t s0 = kcount[(size_t)b * nkt + t], s1 = kcount[(size_t)b * nkt + t + 1];
-        p->kvtile[((size_t)b * nkt + t) * 2] = (int32_t)p->kvitem.size();
+      const int32_t *rw = &p->rows[((size_t)b * S) * 4];
+      for (int64_t t = 0; t < nkv; ++t) {
+        const int kind = t < nkvr ? 0 : 1;
+        const int64_t kt = kind ? t - nkvr : t;
+        const int64_t k0 = kt * kvb;
+        const int64_t nk = kind ? S_c : S;
+        // positions that can see a key of [k0, k0 + kvb)
+        int64_t p0, p1;
+        if (kind == 0) {
+          p0 = k0;
+          p1 = W > 0 ? std::min<int64_t>(S - 1, k0 + kvb - 1 + W - 1) : -1;
+        } else {
+          p0 = (k0 + 1) * r - 1;
+          p1 = S - 1;
+        }
+        list.clear();
+        for (int64_t qt = p0 >= 0 && p0 <= p1 ? p0 / bq : 0; p0 <= p1 && qt <= p1 / bq; ++qt) {
+          const int st = classify_tile(rw, S, qt, bq, kind, k0, kvb, nk);
+          if (st != HCA_TILE_EMPTY)
+            list.push_back((uint32_t)qt | (st == HCA_TILE_FULL ? kEntFull : 0u));
+        }
+        p->kvtile[((size_t)b * nkv + t) * 2] = (int32_t)p->kvitem.size();
         int32_t n = 0;
-        for (int64_t s = s0; s < s1; s += chunk) {
+        for (size_t s0 = 0; s0 < list.size(); s0 += chunk) {
+          const size_t s1 = std::min(list.size(), s0 + (size_t)chunk);
           KvItem it{};
-          it.b = b; it.kind = kind; it.kt = (int32_t)kt;
-          it.e0 = (int32_t)s; it.e1 = (int32_t)std::min(s1, s + chunk);
+          it.b = b;
+          it.kind = kind;
+          it.kt = (int32_t)kt;
+          it.e0 = (int32_t)p->kvent.size();
+          p->kvent.insert(p->kvent.end(), list.begin() + s0, list.begin() + s1);
+          it.e1 = (int32_t)p->kvent.size();
           it.part_off = part_off;
-          part_off += (int64_t)(kind ? bkc : bkr) * D;
+          part_off += kvb * D;
           p->kvitem.push_back(it);
           ++n;
         }
-        p->kvtile[((size_t)b * nkt + t) * 2 + 1] = n;
+        p->kvtile[((size_t)b * nkv + t) * 2 + 1] = n;
       }
     }
+    if (p->kvent.size() >= (size_t)INT32_MAX) throw std::bad_alloc();
+    p->nkv_raw = (int32_t)nkvr;
+    p->nkv_comp = (int32_t)nkvc;
     p->kvorder.resize(p->kvitem.size());
     std::iota(p->kvorder.begin(), p->kvorder.end(), 0);
     std::stable_sort(p->kvorder.begin(), p->kvorder.end(), [&](int32_t x, int32_t y) {
