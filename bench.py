@@ -37,7 +37,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times), the "
+                         "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size: reads and writes exactly mib MiB per launch."""
+    import torch
+
+    n = mib * 2**20 // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert bool((dst[-4:] == src[-4:]).all())
+    print(json.dumps({"copy_probe_bytes": n * 4, "launches": 3}), flush=True)
 
 
 def cpu_baseline(wl, target_s):
@@ -82,6 +99,9 @@ def main():
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     import torch
 
     import block_sparse_compressed_amd as hca

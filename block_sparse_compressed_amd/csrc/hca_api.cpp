@@ -30,7 +30,7 @@ Dims make_dims(const hca_plan *plan) {
   d.nqt = in.nqt; d.nkt_raw = in.nkt_raw; d.nkt_comp = in.nkt_comp;
   d.S_pad = in.nkt_raw * in.bk_raw;
   d.Sc_pad = in.nkt_comp * in.bk_comp;
-  d.n_items = (int32_t)plan->kvitem.size();
+  d.n_items = (int32_t)plan->kvorder.size();  // launch slots (items + padding)
   d.kv_bk = plan->kv_bk;
   d.nkv_raw = plan->nkv_raw;
   d.nkv_comp = plan->nkv_comp;

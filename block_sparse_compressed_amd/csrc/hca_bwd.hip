@@ -329,7 +329,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
   const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
   auto entry = [&](int t) -> uint32_t {
-    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t) : p.qent[e_begin + t];
+    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
+                  : uniform_load(p.qent, e_begin + t);
   };
   const __amdgpu_buffer_rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
   const __amdgpu_buffer_rsrc_t r_kvc =
@@ -466,7 +467,9 @@ __global__ void __launch_bounds__(256, 1)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
   const int kh = wave & 1, rh = wave >> 1;
-  const KvItem it = p.kvitem[p.kvorder[blockIdx.x]];
+  const int item = p.kvorder[blockIdx.x];
+  if (item < 0) return;  // padding slot of the launch order
+  const KvItem it = p.kvitem[item];
   const int b = it.b;
   const bool comp = it.kind != 0;
   const int k0 = it.kt * kBK;
@@ -599,17 +602,23 @@ __global__ void __launch_bounds__(256, 1)
 
 // ---------------------------------------------------------------------------
 // 2b. dKV at D = 512, key-stationary.  A work item is a 64-key tile and a run
-//     of query tiles that see it; each of the 4 waves (one per SIMD) owns 16
-//     keys: their K fragments stay in VGPRs and their [16 keys][512] fp32
-//     gradient in accumulation registers (32 keys per wave would not fit the
-//     register file at D = 512).  Query rows stream through LDS in
-//     32-row steps (Q and dO, 64 KiB, double-buffered, direct global->LDS
-//     loads, swizzled rows).  Per step and wave:
-//       S = Q K^T, dP = dO K^T          (A operands: ds_read_b128, conflict-free)
-//       P = 2^(S log2e scale - LSE log2e), dS = scale P (dP - delta)
-//       dKV^T += Q^T dS + dO^T P        (A operands: ds_read_b64_tr_b16 of the
-//                                        same row-major tiles)
-//     Waves whose 32 keys are invisible to a step skip its arithmetic.
+//     of query tiles that see it.  Query rows stream through LDS in 32-row
+//     steps (Q and dO, 64 KiB, double-buffered, direct global->LDS loads,
+//     swizzled rows).  Each step has two phases:
+//       scores    wave (rh, kh) forms S = Q K^T and dP = dO K^T for 16 of the
+//                 32 rows (half rh) and 32 of the 64 keys (half kh), with the K
+//                 fragments of its keys held in VGPRs; then
+//                 P = 2^(S log2e scale - LSE log2e), dS = scale P (dP - delta),
+//                 stored as bf16 in a [key][row] exchange tile in LDS;
+//       gradient  wave w accumulates dKV^T[d][key] += Q^T dS + dO^T P over the
+//                 step's rows for its quarter of the columns, d in
+//                 [128 w, 128 w + 128), and all 64 keys: A operands are
+//                 ds_read_b64_tr_b16 reads of the row-major Q / dO tiles,
+//                 B operands come from the exchange tile, fp32 sums stay in
+//                 accumulation registers for the whole item.
+//     Splitting the gradient over columns means each wave reads a quarter of
+//     the transposed tiles instead of all of them; steps whose rows see none of
+//     the 64 keys are skipped.
 // ---------------------------------------------------------------------------
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
@@ -623,6 +632,11 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *p) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Exchange tile [64 keys][32 rows] bf16, 64 B per key: rows 8c .. 8c + 7 of
+// key k sit in 16-byte slot c ^ ((k >> 2) & 3), so the 16 lanes that read one
+// slot index for 16 consecutive keys touch 16 distinct bank groups.
+__device__ __forceinline__ int x_off(int key, int c) { return key * 64 + ((c ^ ((key >> 2) & 3)) << 4); }
+
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, 1)
     hca_bwd_dkv512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
@@ -630,107 +644,134 @@ __global__ void __launch_bounds__(NW * 64, 1)
                           const float *__restrict__ lse, const float *__restrict__ delta,
                           const bf16raw *__restrict__ dout, float scale_log2, float scale,
                           float *__restrict__ part) {
-  constexpr int D = 512, KS = D / 32, DB = D / 16;
-  constexpr int STEP = 32, STEP_BYTES = STEP * 1024;
-  static_assert(NW * 16 == 64, "4 waves x 16 keys");
-  constexpr int KB = 1;  // 16-key blocks per wave
+  constexpr int D = 512, KS = D / 32;
+  constexpr int KEYS = 64, STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = KEYS * STEP * 2;
+  static_assert(NW == 4, "2 row halves x 2 key halves; 4 column quarters");
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * STEP_BYTES];  // [buf][Q | dO]
-  __shared__ float lse_s[2][STEP], dl_s[2][STEP];
-  __shared__ int lo_s[2][STEP], hi_s[2][STEP];
+  __shared__ __attribute__((aligned(16))) char xs[2 * XBYTES];             // [P | dS]
+  // Row table per step slot: lse log2e, delta, first and one-past-last key.
+  __shared__ float4 ri_s[2][STEP];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is made visibly wave-uniform so that the row bookkeeping
+  // below runs on the scalar unit.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
-  const KvItem it = p.kvitem[p.kvorder[blockIdx.x]];
+  const int rh = wave & 1, kh = wave >> 1;
+  const int item = p.kvorder[blockIdx.x];
+  if (item < 0) return;  // padding slot of the launch order
+  const KvItem it = p.kvitem[item];
   const int b = it.b;
   const bool comp = it.kind != 0;
   const int nk = comp ? d.Sc : d.S;
-  const int kw0 = it.kt * d.kv_bk + 16 * KB * wave;  // this wave's first key
+  const int k0 = it.kt * KEYS;   // first key of the item
+  const int kw = k0 + 32 * kh;   // first key of this wave's score half
   const bf16raw *src = comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D;
 
-  // Stationary K fragments, B[k = d][n = key] of S = Q K^T.
-  bf16x8 kf[KB][KS];
+  // K fragments of this wave's 32 keys, B[k = d][n = key] of S = Q K^T.
+  bf16x8 kf[2][KS];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int key = kw0 + 16 * kb + j;
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kw + 16 * kb + j;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       kf[kb][ks] = as_bf16x8(key < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)key * D +
                                                                            32 * ks + 8 * g)
                                       : make_uint4(0, 0, 0, 0));
   }
-  floatx4 acc[KB][DB];
+  floatx4 acc[4][8];  // [16-key block][16-column block of this wave's quarter]
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[kb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int nq = it.e1 - it.e0;
-  const int spq = d.bq * d.H / STEP;  // steps per query tile
-  const int nsteps = nq * spq;
+  // A query tile holds bq * H = 128 rows (so H, a divisor of 128, is a power
+  // of two): 4 steps of 32 rows; row rho is position qt * bq + (rho >> lh),
+  // head rho & (H - 1).
+  constexpr int SPQ = 128 / STEP;
+  const int lh = __builtin_ctz(d.H);
+  const int nsteps = nq * SPQ;
+  // An item lists at most 64 query tiles: lane e holds entry e.
   const uint32_t ent_lane = lane < nq ? p.kvent[it.e0 + lane] : 0u;
   auto entry = [&](int e) -> uint32_t {
-    return e < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, e) : p.kvent[it.e0 + e];
+    return (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, e);
   };
-  // Step s covers rows u*32 .. u*32+31 of query tile entry e = s / spq.
+  const size_t bat = (size_t)b * d.H * d.S * D;
+  // Byte offset of this lane's 16-byte chunk in a staged row: row r = 8 wave + i
+  // is stored with swizzle k_swz(r) = (i & 3) | (wave << 2).
+  uint32_t lane_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lane_off[i] = (uint32_t)((lane ^ (i | (wave << 2))) << 4);
+  // Step s covers rows u*32 .. u*32+31 of query tile entry e = s / SPQ.
   auto stage = [&](int s) {
-    const int e = s / spq, u = s - e * spq;
+    const int e = s / SPQ, u = s % SPQ;
     const int qt = (int)(entry(e) & kEntIdx);
-    char *qb = smem + (s & 1) * 2 * STEP_BYTES;
+    const uint32_t qb = lds_addr(smem + (s & 1) * 2 * STEP_BYTES);
 #pragma unroll
     for (int i = 0; i < STEP / NW; ++i) {
       const int r = wave * (STEP / NW) + i;
       const int rho = u * STEP + r;
-      const int pos = min(qt * d.bq + rho / d.H, d.S - 1), h = rho % d.H;
-      const size_t off = (((size_t)b * d.H + h) * d.S + pos) * D + ((lane ^ k_swz(r)) << 3);
-      __builtin_amdgcn_global_load_lds(q + off, (lds_void_t *)(qb + r * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dout + off, (lds_void_t *)(qb + STEP_BYTES + r * 1024), 16,
-                                       0, 0);
+      const int pos = min(qt * d.bq + (rho >> lh), d.S - 1), h = rho & (d.H - 1);
+      const size_t rowoff = bat + ((size_t)h * d.S + pos) * D;  // wave-uniform
+      dma16(q + rowoff, lane_off[i & 3], qb + r * 1024);
+      dma16(dout + rowoff, lane_off[i & 3], qb + STEP_BYTES + r * 1024);
     }
   };
-  float nl2 = 0.f, ndl = 0.f;
-  int nlo = INT_MAX, nhi = 0;
-  auto rowinfo = [&](int s) {  // wave 0, lanes < STEP: row lane of step s
-    const int e = s / spq, u = s - e * spq;
+  // Row table of the next step (lse log2e, delta, key interval), loaded by
+  // every wave while the current step computes and written to LDS by wave 0
+  // at its end.  The loads are unconditional (clamped position) and their
+  // values are not touched until then, so no wait for them lands mid-step.
+  int4 nrw = make_int4(0, 0, 0, 0);
+  float nl = 0.f, nd = 0.f;
+  int npos = 0;
+  auto rowinfo = [&](int s) {  // row (lane & 31) of step s
+    const int e = s / SPQ, u = s % SPQ;
     const int qt = (int)(entry(e) & kEntIdx);
-    const int rho = u * STEP + lane;
-    const int pos = qt * d.bq + rho / d.H, h = rho % d.H;
-    nl2 = 0.f;
-    ndl = 0.f;
-    nlo = INT_MAX;
-    nhi = 0;
-    if (lane < STEP && pos < d.S) {
-      const size_t row = ((size_t)b * d.H + h) * d.S + pos;
-      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos];
-      nl2 = lse[row] * kLog2e;
-      ndl = delta[row];
-      nlo = comp ? rw.y : rw.x;
-      nhi = comp ? rw.z : pos + 1;
-    }
+    const int rho = u * STEP + (lane & (STEP - 1));
+    npos = qt * d.bq + (rho >> lh);
+    const int h = rho & (d.H - 1), pc = min(npos, d.S - 1);
+    const size_t row = ((size_t)b * d.H + h) * d.S + pc;
+    nrw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
+    nl = lse[row];
+    nd = delta[row];
   };
   auto put_rowinfo = [&](int slot) {
-    if (lane < STEP) {
-      lse_s[slot][lane] = nl2;
-      dl_s[slot][lane] = ndl;
-      lo_s[slot][lane] = nlo;
-      hi_s[slot][lane] = nhi;
+    if (wave == 0 && lane < STEP) {
+      const bool ok = npos < d.S;
+      float4 w;
+      w.x = ok ? nl * kLog2e : 0.f;
+      w.y = ok ? nd : 0.f;
+      w.z = __int_as_float(ok ? (comp ? nrw.y : nrw.x) : INT_MAX);
+      w.w = __int_as_float(ok ? (comp ? nrw.z : npos + 1) : 0);
+      ri_s[slot][lane] = w;
     }
   };
 
+  // Score-phase A operands: row i of the wave's 16 maps to step row
+  // 8 (i >> 2) + 4 rh + (i & 3), so lane (g, j) ends up holding rows
+  // 8 g + 4 rh + v, v = 0..3, of key j of each 16-key block.
   int qk_off[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n)
-    qk_off[n] = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
-  // Transpose-read offsets for d-column blocks db = 8 dh + dl (dh via +256 dh).
+    qk_off[n] = (8 * (j >> 2) + 4 * rh + (j & 3)) * 1024 +
+                16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
+  // Transpose-read offsets for the column blocks 8 wave + dl of this quarter.
   int tr_off[8];
   {
     const int u = j >> 2, c0 = (j & 3) >> 1;
 #pragma unroll
     for (int dl = 0; dl < 8; ++dl)
-      tr_off[dl] = (8 * g + u) * 1024 + (((2 * dl + c0) ^ (u + 4 * g)) << 4) + ((j & 1) << 3);
+      tr_off[dl] = (8 * g + u) * 1024 + (((2 * dl + c0) ^ (u + 4 * g)) << 4) + ((j & 1) << 3) +
+                   256 * wave;
   }
+  int xw_off[2], xr_off[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) xw_off[kb] = x_off(32 * kh + 16 * kb + j, g) + 8 * rh;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) xr_off[kb] = x_off(16 * kb + j, g);
 
-  if (nsteps > 0) stage(0);
-  if (wave == 0 && nsteps > 0) {
+  if (nsteps > 0) {
+    stage(0);
     rowinfo(0);
     put_rowinfo(0);
   }
@@ -740,92 +781,121 @@ __global__ void __launch_bounds__(NW * 64, 1)
   for (int s = 0; s < nsteps; ++s) {
     if (s + 1 < nsteps) {
       stage(s + 1);
-      if (wave == 0) rowinfo(s + 1);
+      rowinfo(s + 1);
     }
     const int slot = s & 1;
-    const bool full = entry(s / spq) & kEntFull;
+    const bool full = entry(s / SPQ) & kEntFull;
     const char *qb = smem + slot * 2 * STEP_BYTES;
     const char *ob = qb + STEP_BYTES;
-    float l2r[8], dlr[8];
-    bool vis[KB][8];
-    bool any = false;
+    // Rows 8 g + 4 rh + v of the step (v = 0..3), as held after the scores.
+    float4 ri[4];
 #pragma unroll
-    for (int u8 = 0; u8 < 8; ++u8) {
-      const int rr = 8 * g + u8;
-      l2r[u8] = lse_s[slot][rr];
-      dlr[u8] = dl_s[slot][rr];
-      const int lo = lo_s[slot][rr], hi = hi_s[slot][rr];
+    for (int v = 0; v < 4; ++v) ri[v] = ri_s[slot][8 * g + 4 * rh + v];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Scores: operand fragments are read PF k-steps ahead of their MFMAs.
+    constexpr int PF = 3;
+    floatx4 sv[2], pv[2];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int key = kw0 + 16 * kb + j;
-        vis[kb][u8] = full || (key >= lo && key < hi);
-        any |= vis[kb][u8];
+    for (int kb = 0; kb < 2; ++kb) sv[kb] = pv[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      bf16x8 fq[KS], fo[KS];
+      auto qk_at = [&](int ks) { return qk_off[ks & 3] + 256 * (ks >> 2); };
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) {
+        fq[ks] = lds_frag(qb + qk_at(ks));
+        fo[ks] = lds_frag(ob + qk_at(ks));
       }
-    }
-    if (__builtin_amdgcn_ballot_w64(any)) {
-      floatx4 sv[2][KB], pv[2][KB];  // [row block][key block]
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sv[rb][kb] = pv[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = qk_off[ks & 3] + 256 * (ks >> 2);
-        const bf16x8 aq0 = lds_frag(qb + off), aq1 = lds_frag(qb + off + 4096);
-        const bf16x8 ad0 = lds_frag(ob + off), ad1 = lds_frag(ob + off + 4096);
+        if (ks + PF < KS) {
+          fq[ks + PF] = lds_frag(qb + qk_at(ks + PF));
+          fo[ks + PF] = lds_frag(ob + qk_at(ks + PF));
+        }
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          sv[0][kb] = mfma16x16x32(aq0, kf[kb][ks], sv[0][kb]);
-          sv[1][kb] = mfma16x16x32(aq1, kf[kb][ks], sv[1][kb]);
-          pv[0][kb] = mfma16x16x32(ad0, kf[kb][ks], pv[0][kb]);
-          pv[1][kb] = mfma16x16x32(ad1, kf[kb][ks], pv[1][kb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          sv[kb] = mfma16x16x32(fq[ks], kf[kb][ks], sv[kb]);
+          pv[kb] = mfma16x16x32(fo[ks], kf[kb][ks], pv[kb]);
         }
       }
-      // Lane (g, j) holds rows 8g + 4 rb + v of the step for key 16 kb + j.
-      bf16x8 pb[KB], dsb[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        float pr[8], ds[8];
+      for (int ks = 0; ks < PF; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int u8 = 4 * rb + v;
-            const float e = vis[kb][u8] ? fast_exp2(sv[rb][kb][v] * scale_log2 - l2r[u8]) : 0.f;
-            pr[u8] = e;
-            ds[u8] = e * (pv[rb][kb][v] - dlr[u8]) * scale;
-          }
-        pb[kb] = pack8(pr);
-        dsb[kb] = pack8(ds);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int off = tr_off[db & 7] + 256 * (db >> 3);
-        const bf16x8 aqt = tr_frag(qb + off), adt = tr_frag(ob + off);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          acc[kb][db] = mfma16x16x32(aqt, dsb[kb], acc[kb][db]);
-          acc[kb][db] = mfma16x16x32(adt, pb[kb], acc[kb][db]);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
     }
-    if (s + 1 < nsteps && wave == 0) put_rowinfo((s + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // P and dS of this wave's rows and keys -> exchange tile.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = kw + 16 * kb + j;
+      bf16x4 pw, dw;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bool vis =
+            full || (key >= __float_as_int(ri[v].z) && key < __float_as_int(ri[v].w));
+        const float e = vis ? fast_exp2(sv[kb][v] * scale_log2 - ri[v].x) : 0.f;
+        pw[v] = (__bf16)e;
+        dw[v] = (__bf16)(e * (pv[kb][v] - ri[v].y) * scale);
+      }
+      *reinterpret_cast<bf16x4 *>(xs + xw_off[kb]) = pw;
+      *reinterpret_cast<bf16x4 *>(xs + XBYTES + xw_off[kb]) = dw;
+    }
+    lds_barrier();  // exchange tile complete; the next step's copies stay in flight
+
+    // Gradient: transpose-read fragments PF2 column blocks ahead.
+    {
+      constexpr int PF2 = 2;
+      bf16x8 xp[4], xd[4], tq[8], to[8];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        xd[kb] = lds_frag(xs + XBYTES + xr_off[kb]);
+        xp[kb] = lds_frag(xs + xr_off[kb]);
+      }
+#pragma unroll
+      for (int dl = 0; dl < PF2; ++dl) {
+        tq[dl] = tr_frag(qb + tr_off[dl]);
+        to[dl] = tr_frag(ob + tr_off[dl]);
+      }
+#pragma unroll
+      for (int dl = 0; dl < 8; ++dl) {
+        if (dl + PF2 < 8) {
+          tq[dl + PF2] = tr_frag(qb + tr_off[dl + PF2]);
+          to[dl + PF2] = tr_frag(ob + tr_off[dl + PF2]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[kb][dl] = mfma16x16x32(tq[dl], xd[kb], acc[kb][dl]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[kb][dl] = mfma16x16x32(to[dl], xp[kb], acc[kb][dl]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4 * PF2, 0);
+#pragma unroll
+      for (int dl = 0; dl < 8; ++dl) {
+        if (dl + PF2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < nsteps) put_rowinfo((s + 1) & 1);
     wait_all_loads();
     __syncthreads();
   }
 
-  // Partial [64 keys][512] of this item: this wave's 16 keys.
+  // Partial [64 keys][512] of this item: this wave's 128 columns of every key.
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    float *out = part + it.part_off + (size_t)(16 * KB * wave + 16 * kb + j) * D;
+  for (int kb = 0; kb < 4; ++kb) {
+    float *out = part + it.part_off + (size_t)(16 * kb + j) * D + 128 * wave;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int dl = 0; dl < 8; ++dl) {
       float4 w;
-      w.x = acc[kb][db][0];
-      w.y = acc[kb][db][1];
-      w.z = acc[kb][db][2];
-      w.w = acc[kb][db][3];
-      *reinterpret_cast<float4 *>(out + 16 * db + 4 * g) = w;
+      w.x = acc[kb][dl][0];
+      w.y = acc[kb][dl][1];
+      w.z = acc[kb][dl][2];
+      w.w = acc[kb][dl][3];
+      *reinterpret_cast<float4 *>(out + 16 * dl + 4 * g) = w;
     }
   }
 }

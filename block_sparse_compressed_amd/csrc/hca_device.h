@@ -42,6 +42,13 @@ __device__ __forceinline__ bf16raw f2bf(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wave-uniform read of a table the kernel never writes, through the scalar
+// cache (counted by lgkmcnt, so waiting for it does not also wait for the
+// vector-memory tile loads in flight).
+__device__ __forceinline__ uint32_t uniform_load(const uint32_t *p, int i) {
+  return ((const __attribute__((address_space(4))) uint32_t *)p)[i];
+}
+
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
 

@@ -331,7 +331,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
   // to memory for the tail).
   const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
   auto entry = [&](int t) -> uint32_t {
-    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t) : p.qent[e_begin + t];
+    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
+                  : uniform_load(p.qent, e_begin + t);
   };
   const __amdgpu_buffer_rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
   const __amdgpu_buffer_rsrc_t r_kvc =

@@ -34,7 +34,7 @@ struct DevLayout {
   uint64_t qent = 0;     // uint32 [n_qent]
   uint64_t qorder = 0;   // int32 [B*nqt]: query-tile launch order
   uint64_t kvitem = 0;   // KvItem [n_items] (tile-major)
-  uint64_t kvorder = 0;  // int32 [n_items]: item launch order
+  uint64_t kvorder = 0;  // int32 [n_items]: launch slot -> item, -1 = none
   uint64_t kvent = 0;    // uint32 [n_kvent]: bit 30 FULL, bits 0..29 query tile
   uint64_t kvtile = 0;   // int32 [B][nkv_raw + nkv_comp][2]: first item, item count
   uint64_t total = 0;
@@ -55,7 +55,7 @@ struct Dims {
   int32_t B, S, H, D, r, W, Sc;
   int32_t bq, bk_raw, bk_comp, nqt, nkt_raw, nkt_comp;
   int32_t S_pad, Sc_pad;  // nkt_raw * bk_raw, nkt_comp * bk_comp
-  int32_t n_items;
+  int32_t n_items;  // launch slots of the key-stationary backward
   int32_t kv_bk, nkv_raw, nkv_comp;  // key tiles of the key-stationary backward
 };
 

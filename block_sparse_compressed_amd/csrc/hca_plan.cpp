@@ -288,9 +288,14 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     const int64_t kvb = p->kv_bk;
     const int64_t nkvr = ceil_div(S, kvb), nkvc = ceil_div(S_c, kvb);
     const int64_t nkv = nkvr + nkvc;
-    const int64_t chunk = std::max<int64_t>(1, (kvb >= 64 ? 128 : kItemPositions) / bq);
+    // Query tiles per item; at most 64 so that the key-stationary kernels can
+    // hold an item's whole list in one register across the wave.
+    const int64_t chunk =
+        std::min<int64_t>(64, std::max<int64_t>(1, (kvb >= 64 ? 128 : kItemPositions) / bq));
+    const int64_t nchunk = ceil_div(nqt, chunk);
     p->kvtile.assign((size_t)B * nkv * 2, 0);
     int64_t part_off = 0;
+    std::vector<int64_t> item_group;  // (b, chunk) of each item
     std::vector<uint32_t> list;
     for (int b = 0; b < B; ++b) {
       const int32_t *rw = &p->rows[((size_t)b * S) * 4];
@@ -316,8 +321,13 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
         }
         p->kvtile[((size_t)b * nkv + t) * 2] = (int32_t)p->kvitem.size();
         int32_t n = 0;
-        for (size_t s0 = 0; s0 < list.size(); s0 += chunk) {
-          const size_t s1 = std::min(list.size(), s0 + (size_t)chunk);
+        // Items break at multiples of `chunk` query tiles, the same grid for
+        // every key tile, so the items of different key tiles over one chunk
+        // stream exactly the same query rows.
+        for (size_t s0 = 0; s0 < list.size();) {
+          const int64_t ck = (int64_t)(list[s0] & kEntIdx) / chunk;
+          size_t s1 = s0 + 1;
+          while (s1 < list.size() && (int64_t)(list[s1] & kEntIdx) / chunk == ck) ++s1;
           KvItem it{};
           it.b = b;
           it.kind = kind;
@@ -328,7 +338,9 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
           it.part_off = part_off;
           part_off += kvb * D;
           p->kvitem.push_back(it);
+          item_group.push_back((int64_t)b * nchunk + ck);
           ++n;
+          s0 = s1;
         }
         p->kvtile[((size_t)b * nkv + t) * 2 + 1] = n;
       }
@@ -336,11 +348,44 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     if (p->kvent.size() >= (size_t)INT32_MAX) throw std::bad_alloc();
     p->nkv_raw = (int32_t)nkvr;
     p->nkv_comp = (int32_t)nkvc;
-    p->kvorder.resize(p->kvitem.size());
-    std::iota(p->kvorder.begin(), p->kvorder.end(), 0);
-    std::stable_sort(p->kvorder.begin(), p->kvorder.end(), [&](int32_t x, int32_t y) {
-      return (p->kvitem[x].e1 - p->kvitem[x].e0) > (p->kvitem[y].e1 - p->kvitem[y].e0);
-    });
+
+    // Launch order.  Workgroup i of a launch goes to XCD i % kXcd, and each
+    // XCD runs its share in order.  The items of one chunk (its group) read
+    // the same query rows at about the same pace, so a group is kept together
+    // on one XCD, where its L2 serves the repeated reads.  Groups go, heaviest
+    // first, to the least-loaded XCD; slots past the end of a short XCD queue
+    // hold -1 (no work).
+    {
+      constexpr int kXcd = 8;
+      const int64_t ngroup = (int64_t)B * nchunk;
+      std::vector<int64_t> gwork(ngroup, 0);
+      std::vector<std::vector<int32_t>> gitems(ngroup);
+      for (size_t i = 0; i < p->kvitem.size(); ++i) {
+        gwork[item_group[i]] += p->kvitem[i].e1 - p->kvitem[i].e0;
+        gitems[item_group[i]].push_back((int32_t)i);
+      }
+      std::vector<int64_t> gorder;
+      for (int64_t gi = 0; gi < ngroup; ++gi)
+        if (!gitems[gi].empty()) gorder.push_back(gi);
+      std::stable_sort(gorder.begin(), gorder.end(),
+                       [&](int64_t x, int64_t y) { return gwork[x] > gwork[y]; });
+      std::vector<std::vector<int32_t>> queue(kXcd);
+      std::vector<int64_t> load(kXcd, 0);
+      for (int64_t gi : gorder) {
+        std::vector<int32_t> &its = gitems[gi];
+        std::stable_sort(its.begin(), its.end(), [&](int32_t x, int32_t y) {
+          return (p->kvitem[x].e1 - p->kvitem[x].e0) > (p->kvitem[y].e1 - p->kvitem[y].e0);
+        });
+        const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+        queue[x].insert(queue[x].end(), its.begin(), its.end());
+        load[x] += gwork[gi];
+      }
+      size_t qmax = 0;
+      for (const auto &qq : queue) qmax = std::max(qmax, qq.size());
+      p->kvorder.assign(qmax * kXcd, -1);
+      for (int x = 0; x < kXcd; ++x)
+        for (size_t k = 0; k < queue[x].size(); ++k) p->kvorder[k * kXcd + x] = queue[x][k];
+    }
 
     // ---- device image ----------------------------------------------------- //
     DevLayout &L = p->lay;

@@ -70,6 +70,34 @@ __device__ __forceinline__ void stage_kt512(__amdgpu_buffer_rsrc_t r, int ts, in
   }
 }
 
+// 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4, SGPR base +
+// per-lane byte offset; lane l lands at LDS byte address lds + 16 l).  Issued
+// from inline assembly on purpose: the compiler's wait-count pass treats an
+// LDS-DMA in flight as aliasing every LDS read and would wait for it before
+// each of them (and at every barrier), serialising the copy with the math it
+// is meant to overlap.  Callers wait for these copies themselves with
+// wait_all_loads() before the barrier that publishes the buffer.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(lds_void_t *)p;
+}
+
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads (an ordinary __syncthreads() would also
+// drain the tile copies in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 lds_frag(const char *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
