@@ -285,16 +285,20 @@ __global__ void __launch_bounds__(NW * 64, 1)
   char *const kbase = smem;
   char *const tbase = smem + 2 * kTileBytes512;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
+  // Query tile = bq positions x H heads, rows position-fastest, in slices of
+  // M rows (one wave = 16 consecutive positions of one head); the slices of
+  // two neighbouring tiles run back to back on one XCD.
   const int nslices = d.bq * d.H / M;
-  const int nitems = d.B * d.nqt;
-  const int li = blockIdx.x / nslices, sl = blockIdx.x - li * nslices;
-  const int item = p.qorder[xcd_remap(li, nitems)];
+  const int lbq = __builtin_ctz(d.bq);
+  const int u = xcd_remap(blockIdx.x, d.B * d.nqt * nslices, 2 * nslices);
+  const int li = u / nslices, sl = u - li * nslices;
+  const int item = p.qorder[li];
   const int b = item / d.nqt, qt = item - b * d.nqt;
 
   const int rho = sl * M + wave * 16 + j;
-  const int pos = qt * d.bq + rho / d.H, hh = rho % d.H;
+  const int pos = qt * d.bq + (rho & (d.bq - 1)), hh = rho >> lbq;
   const bool valid = pos < d.S;
   const size_t row = ((size_t)b * d.H + hh) * d.S + pos;
   int rlo = INT_MAX, clo = 0, chi = 0;
@@ -332,12 +336,12 @@ __global__ void __launch_bounds__(NW * 64, 1)
     return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
                   : uniform_load(p.qent, e_begin + t);
   };
-  const __amdgpu_buffer_rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
-  const __amdgpu_buffer_rsrc_t r_kvc =
+  const rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
+  const rsrc_t r_kvc =
       make_rsrc(kvc + (size_t)b * d.Sc * D, (uint32_t)d.Sc * D * 2);
-  const __amdgpu_buffer_rsrc_t r_kvt =
+  const rsrc_t r_kvt =
       make_rsrc(kvt + (size_t)b * D * d.S_pad, (uint32_t)d.S_pad * D * 2);
-  const __amdgpu_buffer_rsrc_t r_kvct =
+  const rsrc_t r_kvct =
       make_rsrc(kvct + (size_t)b * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 2);
   auto stage_k = [&](int t) {
     if (t >= nent) return;
@@ -360,17 +364,35 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const int pv_off = (4 * j + (g ^ kt_swz(j))) * 16;
 
   // S^T and dP^T of tile t (shared K A-operands): [0] keys 0-15, [1] keys 16-31.
+  // Operand fragments are read PF k-steps ahead of their MFMAs.
   auto sdp = [&](int t, floatx4 (&s)[2], floatx4 (&dp)[2]) {
+    constexpr int PF = 3;
     const char *kb = kbase + (t & 1) * kTileBytes512;
     s[0] = s[1] = dp[0] = dp[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a0[KS], a1[KS];
+    auto at = [&](int ks) { return kb + qk_off[ks & 3] + 256 * (ks >> 2); };
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) {
+      a0[ks] = lds_frag(at(ks));
+      a1[ks] = lds_frag(at(ks) + 4096);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const char *a = kb + qk_off[ks & 3] + 256 * (ks >> 2);
-      const bf16x8 a0 = lds_frag(a), a1 = lds_frag(a + 4096);
-      s[0] = mfma16x16x32(a0, qf[ks], s[0]);
-      s[1] = mfma16x16x32(a1, qf[ks], s[1]);
-      dp[0] = mfma16x16x32(a0, dof[ks], dp[0]);
-      dp[1] = mfma16x16x32(a1, dof[ks], dp[1]);
+      if (ks + PF < KS) {
+        a0[ks + PF] = lds_frag(at(ks + PF));
+        a1[ks + PF] = lds_frag(at(ks + PF) + 4096);
+      }
+      s[0] = mfma16x16x32(a0[ks], qf[ks], s[0]);
+      s[1] = mfma16x16x32(a1[ks], qf[ks], s[1]);
+      dp[0] = mfma16x16x32(a0[ks], dof[ks], dp[0]);
+      dp[1] = mfma16x16x32(a1[ks], dof[ks], dp[1]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
   };
 
@@ -389,11 +411,13 @@ __global__ void __launch_bounds__(NW * 64, 1)
   stage_k(2);
   stage_t(1);
 
+  // List entries are read only right after the barrier (where a wait for a
+  // scalar load costs nothing): ent holds the entry of the current tile.
+  uint32_t ent = nent > 0 ? entry(0) : 0u;
   for (int it = 0; it < nent; ++it) {
     floatx4 sn[2], pn[2];
     if (it + 1 < nent) sdp(it + 1, sn, pn);
 
-    const uint32_t ent = entry(it);
     const bool comp = ent & kEntComp;
     const int k0 = (int)(ent & kEntIdx) * kBK;
     float x[8];
@@ -414,9 +438,27 @@ __global__ void __launch_bounds__(NW * 64, 1)
       x[4 + v] = fast_exp2(x[4 + v]) * (pc[1][v] - dl);
     }
     const bf16x8 dsb = pack8(x);
-    const char *tb = tbase + (it & 1) * kTileBytes512 + pv_off;
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      // dQ^T += K^T dS^T: fragments read PV column blocks ahead.
+      constexpr int PV = 8;
+      const char *tb = tbase + (it & 1) * kTileBytes512 + pv_off;
+      bf16x8 kt[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = mfma16x16x32(lds_frag(tb + db * 1024), dsb, acc[db]);
+      for (int db = 0; db < PV; ++db) kt[db] = lds_frag(tb + db * 1024);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        if (db + PV < DB) kt[db + PV] = lds_frag(tb + (db + PV) * 1024);
+        acc[db] = mfma16x16x32(kt[db], dsb, acc[db]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, PV, 0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        if (db + PV < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     sc[0] = sn[0];
     sc[1] = sn[1];
@@ -424,6 +466,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     pc[1] = pn[1];
     wait_all_loads();
     __syncthreads();
+    if (it + 1 < nent) ent = entry(it + 1);
     stage_k(it + 3);
     stage_t(it + 2);
   }
@@ -685,11 +728,11 @@ __global__ void __launch_bounds__(NW * 64, 1)
     for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int nq = it.e1 - it.e0;
-  // A query tile holds bq * H = 128 rows (so H, a divisor of 128, is a power
-  // of two): 4 steps of 32 rows; row rho is position qt * bq + (rho >> lh),
-  // head rho & (H - 1).
-  constexpr int SPQ = 128 / STEP;
-  const int lh = __builtin_ctz(d.H);
+  // A query tile is bq positions x H heads (bq a power of two, bq * H a
+  // multiple of 128), rows ordered position-fastest: row rho is position
+  // qt * bq + (rho & (bq - 1)), head rho >> lbq.  SPQ steps of 32 rows each.
+  const int lbq = __builtin_ctz(d.bq);
+  const int SPQ = d.bq * d.H / STEP, lspq = __builtin_ctz(SPQ);
   const int nsteps = nq * SPQ;
   // An item lists at most 64 query tiles: lane e holds entry e.
   const uint32_t ent_lane = lane < nq ? p.kvent[it.e0 + lane] : 0u;
@@ -704,14 +747,14 @@ __global__ void __launch_bounds__(NW * 64, 1)
   for (int i = 0; i < 4; ++i) lane_off[i] = (uint32_t)((lane ^ (i | (wave << 2))) << 4);
   // Step s covers rows u*32 .. u*32+31 of query tile entry e = s / SPQ.
   auto stage = [&](int s) {
-    const int e = s / SPQ, u = s % SPQ;
+    const int e = s >> lspq, u = s & (SPQ - 1);
     const int qt = (int)(entry(e) & kEntIdx);
     const uint32_t qb = lds_addr(smem + (s & 1) * 2 * STEP_BYTES);
 #pragma unroll
     for (int i = 0; i < STEP / NW; ++i) {
       const int r = wave * (STEP / NW) + i;
       const int rho = u * STEP + r;
-      const int pos = min(qt * d.bq + (rho >> lh), d.S - 1), h = rho & (d.H - 1);
+      const int pos = min(qt * d.bq + (rho & (d.bq - 1)), d.S - 1), h = rho >> lbq;
       const size_t rowoff = bat + ((size_t)h * d.S + pos) * D;  // wave-uniform
       dma16(q + rowoff, lane_off[i & 3], qb + r * 1024);
       dma16(dout + rowoff, lane_off[i & 3], qb + STEP_BYTES + r * 1024);
@@ -725,11 +768,11 @@ __global__ void __launch_bounds__(NW * 64, 1)
   float nl = 0.f, nd = 0.f;
   int npos = 0;
   auto rowinfo = [&](int s) {  // row (lane & 31) of step s
-    const int e = s / SPQ, u = s % SPQ;
+    const int e = s >> lspq, u = s & (SPQ - 1);
     const int qt = (int)(entry(e) & kEntIdx);
     const int rho = u * STEP + (lane & (STEP - 1));
-    npos = qt * d.bq + (rho >> lh);
-    const int h = rho & (d.H - 1), pc = min(npos, d.S - 1);
+    npos = qt * d.bq + (rho & (d.bq - 1));
+    const int h = rho >> lbq, pc = min(npos, d.S - 1);
     const size_t row = ((size_t)b * d.H + h) * d.S + pc;
     nrw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
     nl = lse[row];
@@ -784,7 +827,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
       rowinfo(s + 1);
     }
     const int slot = s & 1;
-    const bool full = entry(s / SPQ) & kEntFull;
+    const bool full = entry(s >> lspq) & kEntFull;
     const char *qb = smem + slot * 2 * STEP_BYTES;
     const char *ob = qb + STEP_BYTES;
     // Rows 8 g + 4 rh + v of the step (v = 0..3), as held after the scores.

@@ -56,8 +56,8 @@ __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor
 // consecutive block ids land on different L2s.  This bijection on [0, n)
 // gives each XCD runs of G consecutive list entries (neighbouring query tiles
 // share key tiles), while the list order (heaviest first) is kept across runs.
-__device__ __forceinline__ int xcd_remap(int x, int n) {
-  constexpr int X = 8, G = 4;
+__device__ __forceinline__ int xcd_remap(int x, int n, int G = 4) {
+  constexpr int X = 8;
   const int full = n / (X * G) * (X * G);
   if (x >= full) return x;
   const int r = x / X;

@@ -292,12 +292,17 @@ __global__ void __launch_bounds__(NW * 64, 1)
   char *const kbase = smem;
   char *const tbase = smem + 2 * kTileBytes512;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
+  // A query tile is bq positions x H heads, rows ordered position-fastest
+  // (row rho = position rho % bq, head rho / bq), cut into slices of M rows;
+  // one wave's 16 rows are 16 consecutive positions of one head.  The slices
+  // of two neighbouring tiles run back to back on one XCD.
   const int nslices = d.bq * d.H / M;
-  const int nitems = d.B * d.nqt;
-  const int li = blockIdx.x / nslices, sl = blockIdx.x - li * nslices;
-  const int item = p.qorder[xcd_remap(li, nitems)];
+  const int lbq = __builtin_ctz(d.bq);
+  const int u = xcd_remap(blockIdx.x, d.B * d.nqt * nslices, 2 * nslices);
+  const int li = u / nslices, sl = u - li * nslices;
+  const int item = p.qorder[li];
   const int b = item / d.nqt, qt = item - b * d.nqt;
 
   int pos[MB], hh[MB], rlo[MB], clo[MB], chi[MB];
@@ -306,8 +311,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int rho = sl * M + (wave * MB + mb) * 16 + j;
-    pos[mb] = qt * d.bq + rho / d.H;
-    hh[mb] = rho % d.H;
+    pos[mb] = qt * d.bq + (rho & (d.bq - 1));
+    hh[mb] = rho >> lbq;
     valid[mb] = pos[mb] < d.S;
     rlo[mb] = INT_MAX;
     clo[mb] = chi[mb] = 0;
@@ -334,12 +339,12 @@ __global__ void __launch_bounds__(NW * 64, 1)
     return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
                   : uniform_load(p.qent, e_begin + t);
   };
-  const __amdgpu_buffer_rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
-  const __amdgpu_buffer_rsrc_t r_kvc =
+  const rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
+  const rsrc_t r_kvc =
       make_rsrc(kvc + (size_t)b * d.Sc * D, (uint32_t)d.Sc * D * 2);
-  const __amdgpu_buffer_rsrc_t r_kvt =
+  const rsrc_t r_kvt =
       make_rsrc(kvt + (size_t)b * D * d.S_pad, (uint32_t)d.S_pad * D * 2);
-  const __amdgpu_buffer_rsrc_t r_kvct =
+  const rsrc_t r_kvct =
       make_rsrc(kvct + (size_t)b * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 2);
   auto stage_k = [&](int t) {  // K of list entry t -> K buffer t & 1
     if (t >= nent) return;
@@ -402,11 +407,13 @@ __global__ void __launch_bounds__(NW * 64, 1)
   stage_k(2);
   stage_t(1);
 
+  // List entries are read only right after the barrier (where a wait for a
+  // scalar load costs nothing): ent holds the entry of the current tile.
+  uint32_t ent = nent > 0 ? entry(0) : 0u;
   for (int it = 0; it < nent; ++it) {
     floatx4 sn[MB][2];
     if (it + 1 < nent) qk(it + 1, sn);
 
-    const uint32_t ent = entry(it);
     const bool comp = ent & kEntComp;
     const int k0 = (int)(ent & kEntIdx) * kBK;
     bf16x8 pb[MB];
@@ -460,6 +467,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     }
     wait_all_loads();
     __syncthreads();
+    if (it + 1 < nent) ent = entry(it + 1);
     stage_k(it + 3);
     stage_t(it + 2);
   }

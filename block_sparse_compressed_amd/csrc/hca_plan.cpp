@@ -58,9 +58,10 @@ int classify_tile(const int32_t *rw, int64_t S, int64_t qt, int bq, int kind, in
 int kv_tile_keys(int dtype, int D) { return (dtype == HCA_BF16 && D == 512) ? 64 : 32; }
 
 void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp) {
-  (void)D;
   if (dtype == HCA_BF16 && H >= 1 && H <= 128 && 128 % H == 0) {
-    *bq = 128 / H;
+    // D = 512 kernels want at least 16 positions per tile (one wave = 16
+    // consecutive positions of one head); the others take 128 rows per tile.
+    *bq = D == 512 ? std::max(16, 128 / H) : 128 / H;
   } else {
     *bq = 16;
   }
@@ -70,9 +71,14 @@ void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp) 
 
 bool kernel_supports(int dtype, int D, int H, int bq, int bk_raw, int bk_comp) {
   if (dtype == HCA_BF16) {
-    if (D != 64 && D != 128 && D != 512) return false;
-    if ((int64_t)bq * H != 128) return false;
-    return bk_raw == 32 && bk_comp == 32;
+    if (bk_raw != 32 || bk_comp != 32) return false;
+    if (D == 64 || D == 128) return (int64_t)bq * H == 128;
+    // D = 512: bq >= 16 and bq * H >= 128, both powers of two.
+    const int64_t rows = (int64_t)bq * H;
+    if (D == 512)
+      return bq >= 16 && (bq & (bq - 1)) == 0 && rows >= 128 && (rows & (rows - 1)) == 0 &&
+             rows <= 1 << 20;
+    return false;
   }
   // float32 path: vector kernels, any tile shape.
   return D % 64 == 0 && D >= 64 && D <= 512;
@@ -280,6 +286,29 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     std::iota(p->qorder.begin(), p->qorder.end(), 0);
     std::stable_sort(p->qorder.begin(), p->qorder.end(),
                      [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+    // Staggered first round: every workgroup loads its query rows before its
+    // tile loop and stores its output rows after it.  If the first round of
+    // workgroups all cost the same, all of them hit memory at the same time,
+    // then all compute, and the rounds stay in lock step.  Taking the first
+    // round's tiles from across the heavier half of the list spreads their
+    // finishing times; the rest follow heaviest first, so the tail stays light.
+    {
+      constexpr int64_t kFirstRound = 256;
+      const int64_t n = (int64_t)p->qorder.size();
+      if (n >= 4 * kFirstRound) {
+        std::vector<int32_t> order;
+        order.reserve(n);
+        std::vector<char> taken(n, 0);
+        for (int64_t i = 0; i < kFirstRound; ++i) {
+          const int64_t at = i * (n / 2) / kFirstRound;
+          order.push_back(p->qorder[at]);
+          taken[at] = 1;
+        }
+        for (int64_t i = 0; i < n; ++i)
+          if (!taken[i]) order.push_back(p->qorder[i]);
+        p->qorder.swap(order);
+      }
+    }
 
     // ---- key-tile work lists for the key-stationary backward ------------ //
     // Key tiles of kv_bk keys (wider than the forward's tiles at D = 512, so

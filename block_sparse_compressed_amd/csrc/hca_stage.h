@@ -31,45 +31,6 @@ __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0)
 
 constexpr int kTileBytes512 = 32 * 1024;  // one K tile or one K^T tile at D = 512
 
-// Buffer resource over `bytes` bytes at `base`; loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-}
-
-// All of the offset goes in the per-lane operand (scalar offset 0), so the
-// range check covers the whole address.
-__device__ __forceinline__ void buf_load16(__amdgpu_buffer_rsrc_t r, void *lds_base, int voff,
-                                           int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, voff, soff, 0, 0);
-}
-
-// Stages key rows k0 .. k0+31 of a [nk][512] tensor (resource `r` covers
-// exactly nk rows, so rows past the end load as zeros) into `kbuf` (32 KiB).
-template <int NW>
-__device__ __forceinline__ void stage_k512(__amdgpu_buffer_rsrc_t r, int k0, char *kbuf, int wave,
-                                           int lane) {
-  static_assert(32 % NW == 0, "waves must divide the tile rows");
-#pragma unroll
-  for (int i = 0; i < 32 / NW; ++i) {
-    const int rho = wave * (32 / NW) + i;
-    buf_load16(r, kbuf + rho * 1024, (k0 + rho) * 1024 + ((lane ^ k_swz(rho)) << 4), 0);
-  }
-}
-
-// Stages columns k0 .. k0+31 of a transposed copy [512][ts] (ts a multiple of
-// 32, padding zero-filled) into `tbuf` (32 KiB).
-template <int NW>
-__device__ __forceinline__ void stage_kt512(__amdgpu_buffer_rsrc_t r, int ts, int k0, char *tbuf,
-                                            int wave, int lane) {
-  const int jr = lane >> 2;
-  const int voff = jr * ts * 2 + k0 * 2 + (((lane & 3) ^ kt_swz(jr)) << 4);
-#pragma unroll
-  for (int i = 0; i < 32 / NW; ++i) {
-    const int blk = wave * (32 / NW) + i;
-    buf_load16(r, tbuf + blk * 1024, voff + blk * 16 * ts * 2, 0);
-  }
-}
-
 // 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4, SGPR base +
 // per-lane byte offset; lane l lands at LDS byte address lds + 16 l).  Issued
 // from inline assembly on purpose: the compiler's wait-count pass treats an
@@ -96,6 +57,53 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // drain the tile copies in flight).
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Buffer resource (4 dwords: base, stride 0, size in bytes, format word) over
+// `bytes` bytes at `base`; loads at offsets past `bytes` return zeros.
+typedef unsigned int rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return rsrc_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16-byte-per-lane buffer -> LDS copy (buffer_load_dwordx4 ... offen lds; lane
+// l lands at LDS byte address lds + 16 l).  The whole offset is the per-lane
+// operand (scalar offset 0), so the range check covers all of it.  Issued
+// from inline assembly for the same reason as dma16 below.
+__device__ __forceinline__ void buf_load16(rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff),
+               "s"(r), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Stages key rows k0 .. k0+31 of a [nk][512] tensor (resource `r` covers
+// exactly nk rows, so rows past the end load as zeros) into `kbuf` (32 KiB).
+template <int NW>
+__device__ __forceinline__ void stage_k512(rsrc_t r, int k0, char *kbuf, int wave, int lane) {
+  static_assert(32 % NW == 0, "waves must divide the tile rows");
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int rho = wave * (32 / NW) + i;
+    buf_load16(r, lds_addr(kbuf + rho * 1024), (k0 + rho) * 1024 + ((lane ^ k_swz(rho)) << 4));
+  }
+}
+
+// Stages columns k0 .. k0+31 of a transposed copy [512][ts] (ts a multiple of
+// 32, padding zero-filled) into `tbuf` (32 KiB).
+template <int NW>
+__device__ __forceinline__ void stage_kt512(rsrc_t r, int ts, int k0, char *tbuf, int wave,
+                                            int lane) {
+  const int jr = lane >> 2;
+  const int voff = jr * ts * 2 + k0 * 2 + (((lane & 3) ^ kt_swz(jr)) << 4);
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int blk = wave * (32 / NW) + i;
+    buf_load16(r, lds_addr(tbuf + blk * 1024), voff + blk * 16 * ts * 2);
+  }
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const char *p) {

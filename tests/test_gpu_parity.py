@@ -126,6 +126,10 @@ SMALL = [
     (1, 97, 4, 128, 4, 9, "f32", "random", 1),
     (1, 64, 64, 512, 1, 0, "bf16", None, 0),   # compressed only (W = 0, r = 1)
     (1, 70, 16, 128, 100, 70, "bf16", None, 0),  # no compressed entries, causal
+    # D = 512 tiles at other head counts: 16 x 8, 16 x 128 and 32 x 4 (positions x heads)
+    (1, 250, 8, 512, 16, 40, "bf16", None, 0),
+    (1, 100, 128, 512, 8, 30, "bf16", [[40, 60]], 1),
+    (1, 150, 4, 512, 32, 64, "bf16", "random", 0),
 ]
 
 
