@@ -16,6 +16,7 @@ pairs (forward 4 * D * H * P, backward 10 * D * H * P; masked work excluded).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -25,6 +26,42 @@ import time
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "block_sparse_compressed_amd", "csrc")
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+# (scaled by a plain copy of known size); one "traffic:" JSON line per kernel.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_bf16.md")
+KERNEL_SOURCES = {"fwd": "hca_fwd.hip", "bwd_dq": "hca_bwd.hip", "bwd_dkv": "hca_bwd.hip",
+                  "dkv_reduce": "hca_bwd.hip", "transpose": "hca_fwd.hip"}
+
+
+def source_hash(kernel):
+    """Hash of the sources that decide a kernel's memory traffic: its .hip file, the
+    shared device headers and the planner (launch order)."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "hca_stage.h", "hca_device.h", "hca_internal.h",
+              "hca_plan.cpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """Measured HBM bytes per launch for this kernel and workload, or None when no
+    measurement exists for the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = [ln[len("traffic:"):] for ln in fh if ln.startswith("traffic:")]
+    except OSError:
+        return None
+    want = source_hash(kernel) if kernel in KERNEL_SOURCES else None
+    for ln in lines:
+        rec = json.loads(ln)
+        if rec.get("kernel") == kernel and rec.get("workload") == workload and \
+                rec.get("source") == want:
+            return rec["bytes_per_launch"]
+    return None
 
 
 def parse():
@@ -37,6 +74,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--source-hashes", action="store_true",
+                    help="print the source hash of each kernel and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), the "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -99,6 +138,9 @@ def main():
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.source_hashes:
+        print(json.dumps({k: source_hash(k) for k in KERNEL_SOURCES}))
+        return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
         return
@@ -177,9 +219,10 @@ def main():
     dom = max((k for k in per_step if k in per_kernel_flops), key=lambda k: per_step[k])
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = per_kernel_flops[dom] / (kavg[dom] * 1e-3) / 1e12
+    traffic = recorded_traffic(dom, wl.name)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None, "avg_ms": round(kavg[dom], 4)}
+                "traffic": traffic, "avg_ms": round(kavg[dom], 4)}
 
     out = {
         "metric": "HCA attn fwd+bwd effective TFLOP/s",

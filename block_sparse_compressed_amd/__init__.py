@@ -71,6 +71,12 @@ def _load_library():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             "libhca.so is not built (%s); run block_sparse_compressed_amd/_build.py" % LIB_PATH)
+    # One HIP runtime per process: PyTorch ships its own libamdhip64, and if
+    # libhca.so were loaded first it would pull in the system copy as well; the
+    # two runtimes then disagree about the device.  Importing torch first makes
+    # libhca.so bind to the runtime torch has already loaded.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
     lib.hca_block_mask_build.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32,

@@ -312,23 +312,6 @@ __global__ void __launch_bounds__(NW * 64, 1)
   }
   bf16x8 qf[KS], dof[KS];
   float dl;
-  {
-    float part = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 qv = make_uint4(0, 0, 0, 0), dv = qv, ov = qv;
-      if (valid) {
-        qv = *reinterpret_cast<const uint4 *>(q + row * D + 32 * ks + 8 * g);
-        dv = *reinterpret_cast<const uint4 *>(dout + row * D + 32 * ks + 8 * g);
-        ov = *reinterpret_cast<const uint4 *>(o + row * D + 32 * ks + 8 * g);
-      }
-      qf[ks] = as_bf16x8(qv);
-      dof[ks] = as_bf16x8(dv);
-      part += dot8(dv, ov);
-    }
-    dl = group_sum(part);
-    if (valid && g == 0) delta[row] = dl;
-  }
 
   const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
   const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
@@ -400,9 +383,27 @@ __global__ void __launch_bounds__(NW * 64, 1)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // First tile copies go out before the row loads, so the two latencies overlap.
   stage_k(0);
   stage_k(1);
   stage_t(0);
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 qv = make_uint4(0, 0, 0, 0), dv = qv, ov = qv;
+      if (valid) {
+        qv = *reinterpret_cast<const uint4 *>(q + row * D + 32 * ks + 8 * g);
+        dv = *reinterpret_cast<const uint4 *>(dout + row * D + 32 * ks + 8 * g);
+        ov = *reinterpret_cast<const uint4 *>(o + row * D + 32 * ks + 8 * g);
+      }
+      qf[ks] = as_bf16x8(qv);
+      dof[ks] = as_bf16x8(dv);
+      part += dot8(dv, ov);
+    }
+    dl = group_sum(part);
+    if (valid && g == 0) delta[row] = dl;
+  }
   wait_all_loads();
   __syncthreads();
   floatx4 sc[2], pc[2];

@@ -322,12 +322,6 @@ __global__ void __launch_bounds__(NW * 64, 1)
       clo[mb] = rw.y;
       chi[mb] = rw.z;
     }
-    const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[mb][ks] = valid[mb]
-                       ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g))
-                       : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
   const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
@@ -396,9 +390,20 @@ __global__ void __launch_bounds__(NW * 64, 1)
     for (int db = 0; db < DB; ++db) oacc[mb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // First tile copies go out before the query-row loads, so the two latencies
+  // overlap.
   stage_k(0);
   stage_k(1);
   stage_t(0);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[mb][ks] = valid[mb]
+                       ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g))
+                       : as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
   wait_all_loads();
   __syncthreads();
   floatx4 sc[MB][2];

@@ -173,3 +173,16 @@ def test_upload_checks(plan):
 def test_status_strings():
     for s in range(7):
         assert hca.hca_status_string(s).startswith("HCA_")
+
+
+def test_binding_binds_to_torch_hip_runtime():
+    """Importing the binding on its own loads torch first, so libhca.so binds to the
+    HIP runtime torch ships instead of pulling in a second one."""
+    import subprocess
+    import sys
+
+    code = ("import sys; import block_sparse_compressed_amd; "
+            "print('torch' in sys.modules)")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=ROOT, check=True).stdout
+    assert out.strip().splitlines()[-1] == "True"
