@@ -645,24 +645,22 @@ __global__ void __launch_bounds__(256, 1)
 }
 
 // ---------------------------------------------------------------------------
-// 2b. dKV at D = 512, key-stationary.  A work item is a 64-key tile and a run
+// 2b. dKV at D = 512, key-stationary.  A work item is a 128-key tile and a run
 //     of query tiles that see it.  Query rows stream through LDS in 32-row
-//     steps (Q and dO, 64 KiB, double-buffered, direct global->LDS loads,
+//     steps (Q and dO, 64 KiB, double-buffered, direct global->LDS copies,
 //     swizzled rows).  Each step has two phases:
-//       scores    wave (rh, kh) forms S = Q K^T and dP = dO K^T for 16 of the
-//                 32 rows (half rh) and 32 of the 64 keys (half kh), with the K
-//                 fragments of its keys held in VGPRs; then
+//       scores    wave w forms S = Q K^T and dP = dO K^T for all 32 rows and
+//                 its 32 keys (K fragments of those keys held in VGPRs); then
 //                 P = 2^(S log2e scale - LSE log2e), dS = scale P (dP - delta),
 //                 stored as bf16 in a [key][row] exchange tile in LDS;
 //       gradient  wave w accumulates dKV^T[d][key] += Q^T dS + dO^T P over the
 //                 step's rows for its quarter of the columns, d in
-//                 [128 w, 128 w + 128), and all 64 keys: A operands are
-//                 ds_read_b64_tr_b16 reads of the row-major Q / dO tiles,
-//                 B operands come from the exchange tile, fp32 sums stay in
-//                 accumulation registers for the whole item.
-//     Splitting the gradient over columns means each wave reads a quarter of
-//     the transposed tiles instead of all of them; steps whose rows see none of
-//     the 64 keys are skipped.
+//                 [128 w, 128 w + 128), and all 128 keys: A operands are
+//                 ds_read_b64_tr_b16 reads of the row-major Q / dO tiles, B
+//                 operands come from the exchange tile, and the fp32 sums
+//                 (256 per lane) stay in accumulation registers for the item.
+//     128 keys per item give each 64 KiB row copy 2 x 256 MFMAs per wave of
+//     work, long enough to hide the copy of the next step behind it.
 // ---------------------------------------------------------------------------
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
@@ -689,8 +687,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
                           const bf16raw *__restrict__ dout, float scale_log2, float scale,
                           float *__restrict__ part) {
   constexpr int D = 512, KS = D / 32;
-  constexpr int KEYS = 64, STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = KEYS * STEP * 2;
-  static_assert(NW == 4, "2 row halves x 2 key halves; 4 column quarters");
+  constexpr int KEYS = 128, STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = KEYS * STEP * 2;
+  static_assert(NW == 4, "4 waves: 32 score keys and one column quarter each");
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * STEP_BYTES];  // [buf][Q | dO]
   __shared__ __attribute__((aligned(16))) char xs[2 * XBYTES];             // [P | dS]
   // Row table per step slot: lse log2e, delta, first and one-past-last key.
@@ -700,7 +698,6 @@ __global__ void __launch_bounds__(NW * 64, 1)
   // below runs on the scalar unit.
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
-  const int rh = wave & 1, kh = wave >> 1;
   const int item = p.kvorder[blockIdx.x];
   if (item < 0) return;  // padding slot of the launch order
   const KvItem it = p.kvitem[item];
@@ -708,7 +705,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const bool comp = it.kind != 0;
   const int nk = comp ? d.Sc : d.S;
   const int k0 = it.kt * KEYS;   // first key of the item
-  const int kw = k0 + 32 * kh;   // first key of this wave's score half
+  const int kw = k0 + 32 * wave;  // first of this wave's score keys
   const bf16raw *src = comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D;
 
   // K fragments of this wave's 32 keys, B[k = d][n = key] of S = Q K^T.
@@ -722,9 +719,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
                                                                            32 * ks + 8 * g)
                                       : make_uint4(0, 0, 0, 0));
   }
-  floatx4 acc[4][8];  // [16-key block][16-column block of this wave's quarter]
+  floatx4 acc[8][8];  // [16-key block][16-column block of this wave's quarter]
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
     for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -791,14 +788,13 @@ __global__ void __launch_bounds__(NW * 64, 1)
     }
   };
 
-  // Score-phase A operands: row i of the wave's 16 maps to step row
-  // 8 (i >> 2) + 4 rh + (i & 3), so lane (g, j) ends up holding rows
-  // 8 g + 4 rh + v, v = 0..3, of key j of each 16-key block.
+  // Score-phase A operands: row i of row block rb maps to step row
+  // 8 (i >> 2) + 4 rb + (i & 3), so lane (g, j) ends up holding rows
+  // 8 g .. 8 g + 7 of key j of each 16-key block (4 rb + v for block rb).
   int qk_off[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n)
-    qk_off[n] = (8 * (j >> 2) + 4 * rh + (j & 3)) * 1024 +
-                16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
+    qk_off[n] = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
   // Transpose-read offsets for the column blocks 8 wave + dl of this quarter.
   int tr_off[8];
   {
@@ -808,11 +804,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
       tr_off[dl] = (8 * g + u) * 1024 + (((2 * dl + c0) ^ (u + 4 * g)) << 4) + ((j & 1) << 3) +
                    256 * wave;
   }
-  int xw_off[2], xr_off[4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) xw_off[kb] = x_off(32 * kh + 16 * kb + j, g) + 8 * rh;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) xr_off[kb] = x_off(16 * kb + j, g);
+  // Exchange-tile offsets: key 16 kb + j lives at 1024 kb + x_off(j, g).
+  const int xw0 = x_off(j, g) + 2048 * wave;  // this wave's keys 32 wave + 16 kb + j
+  const int xr0 = x_off(j, g);
 
   if (nsteps > 0) {
     stage(0);
@@ -831,96 +825,106 @@ __global__ void __launch_bounds__(NW * 64, 1)
     const bool full = entry(s >> lspq) & kEntFull;
     const char *qb = smem + slot * 2 * STEP_BYTES;
     const char *ob = qb + STEP_BYTES;
-    // Rows 8 g + 4 rh + v of the step (v = 0..3), as held after the scores.
-    float4 ri[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) ri[v] = ri_s[slot][8 * g + 4 * rh + v];
     __builtin_amdgcn_sched_barrier(0);
 
     // Scores: operand fragments are read PF k-steps ahead of their MFMAs.
-    constexpr int PF = 3;
-    floatx4 sv[2], pv[2];
+    constexpr int PF = 1;
+    floatx4 sv[2][2], pv[2][2];  // [row block][key block]
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sv[kb] = pv[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sv[rb][kb] = pv[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
     {
-      bf16x8 fq[KS], fo[KS];
+      bf16x8 fq[2][KS], fo[2][KS];
       auto qk_at = [&](int ks) { return qk_off[ks & 3] + 256 * (ks >> 2); };
+      auto fetch = [&](int ks) {
 #pragma unroll
-      for (int ks = 0; ks < PF; ++ks) {
-        fq[ks] = lds_frag(qb + qk_at(ks));
-        fo[ks] = lds_frag(ob + qk_at(ks));
-      }
+        for (int rb = 0; rb < 2; ++rb) {
+          fq[rb][ks] = lds_frag(qb + qk_at(ks) + 4096 * rb);
+          fo[rb][ks] = lds_frag(ob + qk_at(ks) + 4096 * rb);
+        }
+      };
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) fetch(ks);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks + PF < KS) {
-          fq[ks + PF] = lds_frag(qb + qk_at(ks + PF));
-          fo[ks + PF] = lds_frag(ob + qk_at(ks + PF));
-        }
+        if (ks + PF < KS) fetch(ks + PF);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          sv[kb] = mfma16x16x32(fq[ks], kf[kb][ks], sv[kb]);
-          pv[kb] = mfma16x16x32(fo[ks], kf[kb][ks], pv[kb]);
-        }
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            sv[rb][kb] = mfma16x16x32(fq[rb][ks], kf[kb][ks], sv[rb][kb]);
+            pv[rb][kb] = mfma16x16x32(fo[rb][ks], kf[kb][ks], pv[rb][kb]);
+          }
       }
 #pragma unroll
-      for (int ks = 0; ks < PF; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int ks = 0; ks < PF; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // P and dS of this wave's rows and keys -> exchange tile.
+    // P and dS of rows 8 g .. 8 g + 7 for this wave's keys -> exchange tile.
+    {
+      float4 ri[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = kw + 16 * kb + j;
-      bf16x4 pw, dw;
+      for (int r = 0; r < 8; ++r) ri[r] = ri_s[slot][8 * g + r];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const bool vis =
-            full || (key >= __float_as_int(ri[v].z) && key < __float_as_int(ri[v].w));
-        const float e = vis ? fast_exp2(sv[kb][v] * scale_log2 - ri[v].x) : 0.f;
-        pw[v] = (__bf16)e;
-        dw[v] = (__bf16)(e * (pv[kb][v] - ri[v].y) * scale);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw + 16 * kb + j;
+        float pr[8], ds[8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float4 rr = ri[4 * rb + v];
+            const bool vis = full || (key >= __float_as_int(rr.z) && key < __float_as_int(rr.w));
+            const float e = vis ? fast_exp2(sv[rb][kb][v] * scale_log2 - rr.x) : 0.f;
+            pr[4 * rb + v] = e;
+            ds[4 * rb + v] = e * (pv[rb][kb][v] - rr.y) * scale;
+          }
+        *reinterpret_cast<bf16x8 *>(xs + xw0 + 1024 * kb) = pack8(pr);
+        *reinterpret_cast<bf16x8 *>(xs + XBYTES + xw0 + 1024 * kb) = pack8(ds);
       }
-      *reinterpret_cast<bf16x4 *>(xs + xw_off[kb]) = pw;
-      *reinterpret_cast<bf16x4 *>(xs + XBYTES + xw_off[kb]) = dw;
     }
     lds_barrier();  // exchange tile complete; the next step's copies stay in flight
 
-    // Gradient: transpose-read fragments PF2 column blocks ahead.
-    {
-      constexpr int PF2 = 2;
-      bf16x8 xp[4], xd[4], tq[8], to[8];
+    // Gradient, in two passes of four column blocks: the pass's transpose-read
+    // fragments are held, the exchange fragments stream through (read one
+    // key block ahead).
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        xd[kb] = lds_frag(xs + XBYTES + xr_off[kb]);
-        xp[kb] = lds_frag(xs + xr_off[kb]);
+    for (int ps = 0; ps < 2; ++ps) {
+      bf16x8 tq[4], to[4], xp[8], xd[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        tq[c] = tr_frag(qb + tr_off[4 * ps + c]);
+        to[c] = tr_frag(ob + tr_off[4 * ps + c]);
       }
+      xd[0] = lds_frag(xs + XBYTES + xr0);
+      xp[0] = lds_frag(xs + xr0);
 #pragma unroll
-      for (int dl = 0; dl < PF2; ++dl) {
-        tq[dl] = tr_frag(qb + tr_off[dl]);
-        to[dl] = tr_frag(ob + tr_off[dl]);
-      }
-#pragma unroll
-      for (int dl = 0; dl < 8; ++dl) {
-        if (dl + PF2 < 8) {
-          tq[dl + PF2] = tr_frag(qb + tr_off[dl + PF2]);
-          to[dl + PF2] = tr_frag(ob + tr_off[dl + PF2]);
+      for (int kb = 0; kb < 8; ++kb) {
+        if (kb + 1 < 8) {
+          xd[kb + 1] = lds_frag(xs + XBYTES + xr0 + 1024 * (kb + 1));
+          xp[kb + 1] = lds_frag(xs + xr0 + 1024 * (kb + 1));
         }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc[kb][dl] = mfma16x16x32(tq[dl], xd[kb], acc[kb][dl]);
+        for (int c = 0; c < 4; ++c)
+          acc[kb][4 * ps + c] = mfma16x16x32(tq[c], xd[kb], acc[kb][4 * ps + c]);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc[kb][dl] = mfma16x16x32(to[dl], xp[kb], acc[kb][dl]);
+        for (int c = 0; c < 4; ++c)
+          acc[kb][4 * ps + c] = mfma16x16x32(to[c], xp[kb], acc[kb][4 * ps + c]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4 * PF2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16 + 2, 0);
 #pragma unroll
-      for (int dl = 0; dl < 8; ++dl) {
-        if (dl + PF2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      for (int kb = 0; kb < 8; ++kb) {
+        if (kb + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < nsteps) put_rowinfo((s + 1) & 1);
@@ -928,9 +932,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
     __syncthreads();
   }
 
-  // Partial [64 keys][512] of this item: this wave's 128 columns of every key.
+  // Partial [128 keys][512] of this item: this wave's 128 columns of every key.
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < 8; ++kb) {
     float *out = part + it.part_off + (size_t)(16 * kb + j) * D + 128 * wave;
 #pragma unroll
     for (int dl = 0; dl < 8; ++dl) {

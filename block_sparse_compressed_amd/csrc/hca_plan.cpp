@@ -53,9 +53,9 @@ int classify_tile(const int32_t *rw, int64_t S, int64_t qt, int bq, int kind, in
 
 }  // namespace
 
-// Keys per work item of the key-stationary backward: 64 (4 waves x 16 keys)
+// Keys per work item of the key-stationary backward: 128 (4 waves x 32 keys)
 // for the D = 512 bf16 kernel, otherwise the forward's 32-key tile.
-int kv_tile_keys(int dtype, int D) { return (dtype == HCA_BF16 && D == 512) ? 64 : 32; }
+int kv_tile_keys(int dtype, int D) { return (dtype == HCA_BF16 && D == 512) ? 128 : 32; }
 
 void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp) {
   if (dtype == HCA_BF16 && H >= 1 && H <= 128 && 128 % H == 0) {
