@@ -818,8 +818,11 @@ __global__ void __launch_bounds__(NW * 64, 1)
 
   for (int s = 0; s < nsteps; ++s) {
     if (s + 1 < nsteps) {
-      stage(s + 1);
+      // Row-table loads first: anything the step must wait for at its top
+      // (these addresses, a reload) then waits before the tile copies are in
+      // flight, not behind them.
       rowinfo(s + 1);
+      stage(s + 1);
     }
     const int slot = s & 1;
     const bool full = entry(s >> lspq) & kEntFull;
@@ -881,8 +884,12 @@ __global__ void __launch_bounds__(NW * 64, 1)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const float4 rr = ri[4 * rb + v];
-            const bool vis = full || (key >= __float_as_int(rr.z) && key < __float_as_int(rr.w));
-            const float e = vis ? fast_exp2(sv[rb][kb][v] * scale_log2 - rr.x) : 0.f;
+            // Branch-free: exp2 always, then a select (a branch per value would
+            // cost more than the exp2 it skips).
+            const bool vis =
+                full | ((key >= __float_as_int(rr.z)) & (key < __float_as_int(rr.w)));
+            const float ex = fast_exp2(sv[rb][kb][v] * scale_log2 - rr.x);
+            const float e = vis ? ex : 0.f;
             pr[4 * rb + v] = e;
             ds[4 * rb + v] = e * (pv[rb][kb][v] - rr.y) * scale;
           }

@@ -25,7 +25,7 @@ namespace hca {
 constexpr int kBK = 32;  // keys per tile (raw and compressed)
 
 #ifndef HCA_FWD_NW
-#define HCA_FWD_NW 8  // waves of the D = 512 forward (two per SIMD)
+#define HCA_FWD_NW 4  // waves of the D = 512 forward: 4 (two workgroups per CU) or 8
 #endif
 #ifndef HCA_FWD_MB
 #define HCA_FWD_MB 1  // 16-row blocks per wave of the D = 512 forward
@@ -279,8 +279,11 @@ __global__ void __launch_bounds__(NW * 64, 1)
 // 2^kLazy and the O rescale (a wave-uniform branch) is rare.
 constexpr float kLazy = 8.f;
 
+// NW = 8: one workgroup per CU, K and K^T double-buffered (128 KiB of LDS).
+// NW = 4: two workgroups per CU, K and K^T single-buffered (64 KiB each), so
+// one workgroup's row loads, barriers and tile waits overlap the other's math.
 template <int NW, int MB>
-__global__ void __launch_bounds__(NW * 64, 1)
+__global__ void __launch_bounds__(NW * 64, 8 / NW)
     hca_fwd512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                       const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
                       const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
@@ -288,9 +291,11 @@ __global__ void __launch_bounds__(NW * 64, 1)
   constexpr int D = 512, KS = D / 32, DB = D / 16;
   constexpr int M = NW * MB * 16;  // rows per workgroup
   // [K buffer 0][K buffer 1][K^T buffer 0][K^T buffer 1]
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes512];
+  constexpr bool kSingle = NW == 4;
+  constexpr int kBufs = kSingle ? 1 : 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufs * kTileBytes512];
   char *const kbase = smem;
-  char *const tbase = smem + 2 * kTileBytes512;
+  char *const tbase = smem + kBufs * kTileBytes512;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
@@ -344,14 +349,14 @@ __global__ void __launch_bounds__(NW * 64, 1)
     if (t >= nent) return;
     const uint32_t ent = entry(t);
     stage_k512<NW>((ent & kEntComp) ? r_kvc : r_kv, (int)(ent & kEntIdx) * kBK,
-                   kbase + (t & 1) * kTileBytes512, wave, lane);
+                   kbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
   };
   auto stage_t = [&](int t) {  // K^T of list entry t -> K^T buffer t & 1
     if (t >= nent) return;
     const uint32_t ent = entry(t);
     const bool comp = ent & kEntComp;
     stage_kt512<NW>(comp ? r_kvct : r_kvt, comp ? d.Sc_pad : d.S_pad, (int)(ent & kEntIdx) * kBK,
-                    tbase + (t & 1) * kTileBytes512, wave, lane);
+                    tbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
   };
 
   // Lane-constant parts of the operand addresses.  QK^T A operand of k-step
@@ -365,7 +370,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 
   // S^T of tile t for every row block: two 16-key halves per block.
   auto qk = [&](int t, floatx4 (&s)[MB][2]) {
-    const char *kb = kbase + (t & 1) * kTileBytes512;
+    const char *kb = kbase + (t & (kBufs - 1)) * kTileBytes512;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) s[mb][0] = s[mb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -390,35 +395,19 @@ __global__ void __launch_bounds__(NW * 64, 1)
     for (int db = 0; db < DB; ++db) oacc[mb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // First tile copies go out before the query-row loads, so the two latencies
-  // overlap.
-  stage_k(0);
-  stage_k(1);
-  stage_t(0);
+  auto load_q = [&]() {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
+    for (int mb = 0; mb < MB; ++mb) {
+      const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[mb][ks] = valid[mb]
-                       ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g))
-                       : as_bf16x8(make_uint4(0, 0, 0, 0));
-  }
-  wait_all_loads();
-  __syncthreads();
-  floatx4 sc[MB][2];
-  if (nent > 0) qk(0, sc);
-  __syncthreads();
-  stage_k(2);
-  stage_t(1);
-
-  // List entries are read only right after the barrier (where a wait for a
-  // scalar load costs nothing): ent holds the entry of the current tile.
-  uint32_t ent = nent > 0 ? entry(0) : 0u;
-  for (int it = 0; it < nent; ++it) {
-    floatx4 sn[MB][2];
-    if (it + 1 < nent) qk(it + 1, sn);
-
+      for (int ks = 0; ks < KS; ++ks)
+        qf[mb][ks] = valid[mb]
+                         ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g))
+                         : as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  };
+  // Online softmax of tile `it` (scores sc, list entry ent) and O^T += K^T P^T.
+  auto soft_pv = [&](int it, const floatx4 (&sc)[MB][2], uint32_t ent) {
     const bool comp = ent & kEntComp;
     const int k0 = (int)(ent & kEntIdx) * kBK;
     bf16x8 pb[MB];
@@ -457,24 +446,77 @@ __global__ void __launch_bounds__(NW * 64, 1)
       }
       pb[mb] = pack8(x);
     }
-    const char *tb = tbase + (it & 1) * kTileBytes512 + pv_off;
+    const char *tb = tbase + (it & (kBufs - 1)) * kTileBytes512 + pv_off;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const bf16x8 a = lds_frag(tb + db * 1024);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb][db] = mfma16x16x32(a, pb[mb], oacc[mb][db]);
     }
+  };
 
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      sc[mb][0] = sn[mb][0];
-      sc[mb][1] = sn[mb][1];
-    }
+  if constexpr (!kSingle) {
+    // Double-buffered: K runs two tiles ahead, K^T one; S of tile t+1 is
+    // issued before the softmax and PV of tile t; one barrier per tile.
+    // First tile copies go out before the query-row loads, so the two
+    // latencies overlap.
+    stage_k(0);
+    stage_k(1);
+    stage_t(0);
+    load_q();
     wait_all_loads();
     __syncthreads();
-    if (it + 1 < nent) ent = entry(it + 1);
-    stage_k(it + 3);
-    stage_t(it + 2);
+    floatx4 sc[MB][2];
+    if (nent > 0) qk(0, sc);
+    __syncthreads();
+    stage_k(2);
+    stage_t(1);
+
+    // List entries are read only right after the barrier (where a wait for a
+    // scalar load costs nothing): ent holds the entry of the current tile.
+    uint32_t ent = nent > 0 ? entry(0) : 0u;
+    for (int it = 0; it < nent; ++it) {
+      floatx4 sn[MB][2];
+      if (it + 1 < nent) qk(it + 1, sn);
+      soft_pv(it, sc, ent);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        sc[mb][0] = sn[mb][0];
+        sc[mb][1] = sn[mb][1];
+      }
+      wait_all_loads();
+      __syncthreads();
+      if (it + 1 < nent) ent = entry(it + 1);
+      stage_k(it + 3);
+      stage_t(it + 2);
+    }
+  } else {
+    // Single-buffered: the copy of K for tile t+1 overlaps the softmax and PV
+    // of tile t, the copy of K^T for tile t+1 overlaps S of tile t+1; two
+    // barriers per tile.  The second workgroup on the CU covers the rest.
+    stage_k(0);
+    stage_t(0);
+    load_q();
+    wait_all_loads();
+    __syncthreads();
+    floatx4 sc[MB][2];
+    if (nent > 0) qk(0, sc);
+    __syncthreads();  // K buffer free
+    stage_k(1);
+    uint32_t ent = nent > 0 ? entry(0) : 0u;
+    for (int it = 0; it < nent; ++it) {
+      soft_pv(it, sc, ent);
+      wait_all_loads();  // K of tile it + 1
+      __syncthreads();   // K^T buffer free, K of tile it + 1 visible
+      if (it + 1 < nent) {
+        ent = entry(it + 1);
+        stage_t(it + 1);
+        qk(it + 1, sc);
+        wait_all_loads();  // K^T of tile it + 1
+        __syncthreads();   // K buffer free, K^T of tile it + 1 visible
+        stage_k(it + 2);
+      }
+    }
   }
 
 #pragma unroll
