@@ -472,18 +472,13 @@ __global__ void __launch_bounds__(NW * 64, 1)
     stage_t(it + 2);
   }
 
-  if (valid) {
-    bf16raw *drow = dq + row * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      ushort4 w;
-      w.x = f2bf(acc[db][0] * scale);
-      w.y = f2bf(acc[db][1] * scale);
-      w.z = f2bf(acc[db][2] * scale);
-      w.w = f2bf(acc[db][3] * scale);
-      *reinterpret_cast<ushort4 *>(drow + 16 * db + 4 * g) = w;
-    }
-  }
+  // The tile buffers are free (the loop ended on a barrier with no copy in
+  // flight): each wave stages its 16 rows of dQ there and stores whole rows.
+  store_rows512(acc, scale, smem + wave * 16384, lane, [&](int r) -> bf16raw * {
+    const int rr = sl * M + wave * 16 + r;
+    const int pr = qt * d.bq + (rr & (d.bq - 1)), hr = rr >> lbq;
+    return pr < d.S ? dq + (((size_t)b * d.H + hr) * d.S + pr) * D : nullptr;
+  });
 }
 
 // ---------------------------------------------------------------------------

@@ -519,22 +519,19 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     }
   }
 
+  // The tile buffers are free (the loop ended on a barrier with no copy in
+  // flight): each 16-row block is staged there and stored as whole rows.
+  static_assert(NW * MB * 16384 <= 2 * kBufs * kTileBytes512, "row staging fits the tiles");
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const float l = group_sum(l_run[mb]);
-    if (!valid[mb]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    bf16raw *orow = o + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      ushort4 w;
-      w.x = f2bf(oacc[mb][db][0] * inv);
-      w.y = f2bf(oacc[mb][db][1] * inv);
-      w.z = f2bf(oacc[mb][db][2] * inv);
-      w.w = f2bf(oacc[mb][db][3] * inv);
-      *reinterpret_cast<ushort4 *>(orow + 16 * db + 4 * g) = w;
-    }
-    if (g == 0)
+    store_rows512(oacc[mb], inv, smem + (wave * MB + mb) * 16384, lane, [&](int r) -> bf16raw * {
+      const int rr = sl * M + (wave * MB + mb) * 16 + r;
+      const int pr = qt * d.bq + (rr & (d.bq - 1)), hr = rr >> lbq;
+      return pr < d.S ? o + (((size_t)b * d.H + hr) * d.S + pr) * D : nullptr;
+    });
+    if (valid[mb] && g == 0)
       lse[((size_t)b * d.H + hh[mb]) * d.S + pos[mb]] =
           l > 0.f ? (m_run[mb] + __log2f(l)) * kLn2 : -INFINITY;
   }

@@ -106,6 +106,39 @@ __device__ __forceinline__ void stage_kt512(rsrc_t r, int ts, int k0, char *tbuf
   }
 }
 
+// Stores a wave's 16 output rows of 512 as bf16.  acc[db] is the transposed
+// MFMA layout: lane (g, j) holds elements 16 db + 4 g + v (v = 0..3) of row j.
+// The rows go through `buf` (16 KiB of LDS used by this wave only), with the
+// 16-byte chunks of row r stored at chunk index c ^ r so both the scattered
+// writes and the row reads are free of bank conflicts, and then leave as one
+// fully coalesced 1 KiB store per row instead of 32 partial-line writes.
+// row_ptr(r) gives the destination of row r, or nullptr to skip it; it must be
+// wave-uniform.
+template <typename RowPtr>
+__device__ __forceinline__ void store_rows512(const floatx4 (&acc)[32], float mul, char *buf,
+                                              int lane, RowPtr row_ptr) {
+  const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+  for (int db = 0; db < 32; ++db) {
+    ushort4 w;
+    w.x = f2bf(acc[db][0] * mul);
+    w.y = f2bf(acc[db][1] * mul);
+    w.z = f2bf(acc[db][2] * mul);
+    w.w = f2bf(acc[db][3] * mul);
+    const int c = 2 * db + (g >> 1);
+    *reinterpret_cast<ushort4 *>(buf + j * 1024 + ((c ^ j) << 4) + 8 * (g & 1)) = w;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    bf16raw *dst = row_ptr(r);
+    if (dst) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(buf + r * 1024 + ((lane ^ r) << 4));
+      *reinterpret_cast<uint4 *>(dst + 8 * lane) = v;
+    }
+  }
+}
+
 __device__ __forceinline__ bf16x8 lds_frag(const char *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
