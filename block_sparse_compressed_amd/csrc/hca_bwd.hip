@@ -301,20 +301,19 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const int pos = qt * d.bq + (rho & (d.bq - 1)), hh = rho >> lbq;
   const bool valid = pos < d.S;
   const size_t row = ((size_t)b * d.H + hh) * d.S + pos;
+  // Padded rows (pos >= S) read a real row and are zeroed / masked below:
+  // every prologue load is unconditional, so none of them waits for another.
+  const size_t rowc = ((size_t)b * d.H + hh) * d.S + min(pos, d.S - 1);
   int rlo = INT_MAX, clo = 0, chi = 0;
   float lse2 = -INFINITY;
-  if (valid) {
-    const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos];
-    rlo = rw.x;
-    clo = rw.y;
-    chi = rw.z;
-    lse2 = lse[row] * kLog2e;
-  }
   bf16x8 qf[KS], dof[KS];
   float dl;
 
+  // The list entries are needed for the first tile copies: load them first
+  // and wait for them once, before any copy is in flight.
   const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
   const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
+  __builtin_amdgcn_s_waitcnt(0);
   auto entry = [&](int t) -> uint32_t {
     return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
                   : uniform_load(p.qent, e_begin + t);
@@ -388,20 +387,30 @@ __global__ void __launch_bounds__(NW * 64, 1)
   stage_k(1);
   stage_t(0);
   {
+    const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + min(pos, d.S - 1)];
+    const float lv = lse[rowc];
+    uint4 qv[KS], dv[KS], ov[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qv[ks] = *reinterpret_cast<const uint4 *>(q + rowc * D + 32 * ks + 8 * g);
+      dv[ks] = *reinterpret_cast<const uint4 *>(dout + rowc * D + 32 * ks + 8 * g);
+      ov[ks] = *reinterpret_cast<const uint4 *>(o + rowc * D + 32 * ks + 8 * g);
+    }
+    // A padded row keeps the clamped row's data: its key interval is empty
+    // (and a tile holding it is never FULL), so its P and dS are zero, and its
+    // dQ and delta are never stored.
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 qv = make_uint4(0, 0, 0, 0), dv = qv, ov = qv;
-      if (valid) {
-        qv = *reinterpret_cast<const uint4 *>(q + row * D + 32 * ks + 8 * g);
-        dv = *reinterpret_cast<const uint4 *>(dout + row * D + 32 * ks + 8 * g);
-        ov = *reinterpret_cast<const uint4 *>(o + row * D + 32 * ks + 8 * g);
-      }
-      qf[ks] = as_bf16x8(qv);
-      dof[ks] = as_bf16x8(dv);
-      part += dot8(dv, ov);
+      qf[ks] = as_bf16x8(qv[ks]);
+      dof[ks] = as_bf16x8(dv[ks]);
+      part += dot8(dv[ks], ov[ks]);
     }
     dl = group_sum(part);
+    rlo = valid ? rw.x : INT_MAX;
+    clo = valid ? rw.y : 0;
+    chi = valid ? rw.z : 0;
+    lse2 = valid ? lv * kLog2e : -INFINITY;
     if (valid && g == 0) delta[row] = dl;
   }
   wait_all_loads();
@@ -704,15 +713,18 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const bf16raw *src = comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D;
 
   // K fragments of this wave's 32 keys, B[k = d][n = key] of S = Q K^T.
+  // (Unconditional loads of a clamped key, zeroed past the end, so that all
+  // 32 loads are in flight together.)
   bf16x8 kf[2][KS];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kw + 16 * kb + j;
+    const bf16raw *krow = src + (size_t)min(key, nk - 1) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[kb][ks] = as_bf16x8(key < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)key * D +
-                                                                           32 * ks + 8 * g)
-                                      : make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(krow + 32 * ks + 8 * g);
+      kf[kb][ks] = as_bf16x8(key < nk ? v : make_uint4(0, 0, 0, 0));
+    }
   }
   floatx4 acc[8][8];  // [16-key block][16-column block of this wave's quarter]
 #pragma unroll

@@ -321,19 +321,15 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     valid[mb] = pos[mb] < d.S;
     rlo[mb] = INT_MAX;
     clo[mb] = chi[mb] = 0;
-    if (valid[mb]) {
-      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos[mb]];
-      rlo[mb] = rw.x;
-      clo[mb] = rw.y;
-      chi[mb] = rw.z;
-    }
   }
 
   const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
   // The tile's list, one entry per lane: entries are fetched with readlane,
   // not with a dependent memory load per tile (lists longer than 64 fall back
-  // to memory for the tail).
+  // to memory for the tail).  They are needed for the first tile copies: load
+  // them first and wait for them once, before any copy is in flight.
   const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
+  __builtin_amdgcn_s_waitcnt(0);
   auto entry = [&](int t) -> uint32_t {
     return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
                   : uniform_load(p.qent, e_begin + t);
@@ -395,15 +391,22 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     for (int db = 0; db < DB; ++db) oacc[mb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // Query rows and their key intervals.  All loads are unconditional (a padded
+  // row, pos >= S, reads the last row): issued back to back, waited for once.
+  // A padded row's interval is empty and a tile holding it is never FULL, so
+  // it contributes nothing, and it is never stored.
   auto load_q = [&]() {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
+      const int pc = min(pos[mb], d.S - 1);
+      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
+      rlo[mb] = valid[mb] ? rw.x : INT_MAX;
+      clo[mb] = valid[mb] ? rw.y : 0;
+      chi[mb] = valid[mb] ? rw.z : 0;
+      const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pc) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qf[mb][ks] = valid[mb]
-                         ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g))
-                         : as_bf16x8(make_uint4(0, 0, 0, 0));
+        qf[mb][ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g));
     }
   };
   // Online softmax of tile `it` (scores sc, list entry ent) and O^T += K^T P^T.
