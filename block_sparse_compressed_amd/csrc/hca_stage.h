@@ -129,13 +129,19 @@ __device__ __forceinline__ void store_rows512(const floatx4 (&acc)[32], float mu
     *reinterpret_cast<ushort4 *>(buf + j * 1024 + ((c ^ j) << 4) + 8 * (g & 1)) = w;
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // Rows in batches of four: four reads (one wait), then four stores.
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    bf16raw *dst = row_ptr(r);
-    if (dst) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(buf + r * 1024 + ((lane ^ r) << 4));
-      *reinterpret_cast<uint4 *>(dst + 8 * lane) = v;
-    }
+  for (int r0 = 0; r0 < 16; r0 += 4) {
+    const uint4 v0 = *reinterpret_cast<const uint4 *>(buf + (r0 + 0) * 1024 + ((lane ^ (r0 + 0)) << 4));
+    const uint4 v1 = *reinterpret_cast<const uint4 *>(buf + (r0 + 1) * 1024 + ((lane ^ (r0 + 1)) << 4));
+    const uint4 v2 = *reinterpret_cast<const uint4 *>(buf + (r0 + 2) * 1024 + ((lane ^ (r0 + 2)) << 4));
+    const uint4 v3 = *reinterpret_cast<const uint4 *>(buf + (r0 + 3) * 1024 + ((lane ^ (r0 + 3)) << 4));
+    bf16raw *d0 = row_ptr(r0 + 0), *d1 = row_ptr(r0 + 1), *d2 = row_ptr(r0 + 2),
+            *d3 = row_ptr(r0 + 3);
+    if (d0) *reinterpret_cast<uint4 *>(d0 + 8 * lane) = v0;
+    if (d1) *reinterpret_cast<uint4 *>(d1 + 8 * lane) = v1;
+    if (d2) *reinterpret_cast<uint4 *>(d2 + 8 * lane) = v2;
+    if (d3) *reinterpret_cast<uint4 *>(d3 + 8 * lane) = v3;
   }
 }
 
