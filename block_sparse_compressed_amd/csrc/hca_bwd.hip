@@ -59,7 +59,7 @@ struct StageB {
       const int c = tid + u * NT;
       if (TCH % NT == 0 || c < TCH) {
         const int dd = c / (kBK / 8), col = c % (kBK / 8);
-        pt[u] = *reinterpret_cast<const uint4 *>(srct + (size_t)dd * ts + k0 + col * 8);
+        pt[u] = *reinterpret_cast<const uint4 *>(srct + (size_t)k0 * D + dd * kBK + col * 8);
       }
     }
   }
@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     if (t >= nent) return;
     const uint32_t ent = entry(t);
     const bool comp = ent & kEntComp;
-    stage_kt512<NW>(comp ? r_kvct : r_kvt, comp ? d.Sc_pad : d.S_pad, (int)(ent & kEntIdx) * kBK,
+    stage_kt512<NW>(comp ? r_kvct : r_kvt, (int)(ent & kEntIdx) * kBK,
                     tbase + (t & 1) * kTileBytes512, wave, lane);
   };
 

@@ -60,7 +60,7 @@ struct Stage {
       const int c = tid + u * NT;
       if (TCH % NT == 0 || c < TCH) {
         const int dd = c / (kBK / 8), col = c % (kBK / 8);
-        pt[u] = *reinterpret_cast<const uint4 *>(srct + (size_t)dd * ts + k0 + col * 8);
+        pt[u] = *reinterpret_cast<const uint4 *>(srct + (size_t)k0 * D + dd * kBK + col * 8);
       }
     }
   }
@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     if (t >= nent) return;
     const uint32_t ent = entry(t);
     const bool comp = ent & kEntComp;
-    stage_kt512<NW>(comp ? r_kvct : r_kvt, comp ? d.Sc_pad : d.S_pad, (int)(ent & kEntIdx) * kBK,
+    stage_kt512<NW>(comp ? r_kvct : r_kvt, (int)(ent & kEntIdx) * kBK,
                     tbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
   };
 
@@ -540,7 +540,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
   }
 }
 
-// dst[b][d][t] = src[b][t][d] for t < N, 0 for N <= t < N_pad.
+// Tile-major transpose: dst[b][t / 32][d][t % 32] = src[b][t][d] for t < N, 0 for
+// N <= t < N_pad (N_pad a multiple of 32).  Each 32-key tile's transpose is one
+// contiguous D x 32 block, so a kernel stages it with contiguous copies.
 __global__ void __launch_bounds__(256) hca_transpose_kernel(const bf16raw *__restrict__ src,
                                                             bf16raw *__restrict__ dst, int N,
                                                             int N_pad, int D) {
@@ -555,7 +557,7 @@ __global__ void __launch_bounds__(256) hca_transpose_kernel(const bf16raw *__res
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int dd = i / 64, tt = i % 64, t = t0 + tt, dx = d0 + dd;
-    if (dx < D && t < N_pad) o[(size_t)dx * N_pad + t] = tile[tt][dd];
+    if (dx < D && t < N_pad) o[(size_t)(t / kBK) * D * kBK + (size_t)dx * kBK + t % kBK] = tile[tt][dd];
   }
 }
 

@@ -92,17 +92,17 @@ __device__ __forceinline__ void stage_k512(rsrc_t r, int k0, char *kbuf, int wav
   }
 }
 
-// Stages columns k0 .. k0+31 of a transposed copy [512][ts] (ts a multiple of
-// 32, padding zero-filled) into `tbuf` (32 KiB).
+// Stages the transpose of key tile k0 .. k0+31 from a tile-major transposed
+// copy ([tile][512][32], tiles of the padding zero-filled) into `tbuf`
+// (32 KiB): each instruction moves 16 d-rows, one contiguous KiB.
 template <int NW>
-__device__ __forceinline__ void stage_kt512(rsrc_t r, int ts, int k0, char *tbuf, int wave,
-                                            int lane) {
+__device__ __forceinline__ void stage_kt512(rsrc_t r, int k0, char *tbuf, int wave, int lane) {
   const int jr = lane >> 2;
-  const int voff = jr * ts * 2 + k0 * 2 + (((lane & 3) ^ kt_swz(jr)) << 4);
+  const int voff = k0 * 1024 + jr * 64 + (((lane & 3) ^ kt_swz(jr)) << 4);
 #pragma unroll
   for (int i = 0; i < 32 / NW; ++i) {
     const int blk = wave * (32 / NW) + i;
-    buf_load16(r, lds_addr(tbuf + blk * 1024), voff + blk * 16 * ts * 2);
+    buf_load16(r, lds_addr(tbuf + blk * 1024), voff + blk * 1024);
   }
 }
 
