@@ -824,13 +824,22 @@ __global__ void __launch_bounds__(NW * 64, 1)
   __syncthreads();
 
   for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) {
-      // Row-table loads first: anything the step must wait for at its top
-      // (these addresses, a reload) then waits before the tile copies are in
-      // flight, not behind them.
-      rowinfo(s + 1);
-      stage(s + 1);
-    }
+    if (s + 1 < nsteps) rowinfo(s + 1);
+    // Rows of the next step (on the last step: this step's rows again, into
+    // the idle buffer), copied one instruction per score k-step below so the
+    // wave never stalls issuing a burst of 16 copies.
+    const int sn = min(s + 1, nsteps - 1);
+    const int qt_n = (int)(entry(sn >> lspq) & kEntIdx), u_n = sn & (SPQ - 1);
+    const uint32_t qb_n = lds_addr(smem + ((s + 1) & 1) * 2 * STEP_BYTES);
+    auto copy_one = [&](int ks) {  // row ks >> 1 of this wave's 8, Q (even) or dO (odd)
+      const int i = ks >> 1, r = wave * (STEP / NW) + i, rho = u_n * STEP + r;
+      const int pos = min(qt_n * d.bq + (rho & (d.bq - 1)), d.S - 1), h = rho >> lbq;
+      const size_t rowoff = bat + ((size_t)h * d.S + pos) * D;  // wave-uniform
+      if (ks & 1)
+        dma16(dout + rowoff, lane_off[i & 3], qb_n + STEP_BYTES + r * 1024);
+      else
+        dma16(q + rowoff, lane_off[i & 3], qb_n + r * 1024);
+    };
     const int slot = s & 1;
     const bool full = entry(s >> lspq) & kEntFull;
     const char *qb = smem + slot * 2 * STEP_BYTES;
@@ -858,6 +867,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
       for (int ks = 0; ks < PF; ++ks) fetch(ks);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        copy_one(ks);
         if (ks + PF < KS) fetch(ks + PF);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
