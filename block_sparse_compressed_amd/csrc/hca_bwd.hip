@@ -678,7 +678,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *p) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Exchange tile [64 keys][32 rows] bf16, 64 B per key: rows 8c .. 8c + 7 of
+// Exchange tile [128 keys][32 rows] bf16, 64 B per key: rows 8c .. 8c + 7 of
 // key k sit in 16-byte slot c ^ ((k >> 2) & 3), so the 16 lanes that read one
 // slot index for 16 consecutive keys touch 16 distinct bank groups.
 __device__ __forceinline__ int x_off(int key, int c) { return key * 64 + ((c ^ ((key >> 2) & 3)) << 4); }
