@@ -130,6 +130,8 @@ SMALL = [
     (1, 250, 8, 512, 16, 40, "bf16", None, 0),
     (1, 100, 128, 512, 8, 30, "bf16", [[40, 60]], 1),
     (1, 150, 4, 512, 32, 64, "bf16", "random", 0),
+    # more 64-row slices (1104) than CUs: persistent dQ workgroups walk several
+    (1, 1100, 64, 512, 16, 64, "bf16", [[300, 800]], 0),
 ]
 
 
@@ -141,6 +143,14 @@ def test_small_every_element(spec):
         rng = np.random.default_rng(S)
         lengths = [random_lengths(rng, S, 1, S // 2) for _ in range(B)]
     check_full(Case(B, S, H, D, r, W, dtype, lengths, mode, seed=S + D))
+
+
+def test_long_key_lists_every_element():
+    """Query tiles listing up to 13 key tiles (r = 8) with a peaked softmax
+    (value scale 2, so delta matters), 512 row slices of 64 rows: the
+    persistent dQ workgroups walk several slices, each prefetching the next
+    one's rows over its first tiles."""
+    check_full(Case(1, 2048, 16, 512, 8, 64, "bf16", [[700, 1348]], seed=11, value_scale=2.0))
 
 
 def test_single_position():
