@@ -24,7 +24,7 @@ import sys
 import time
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-PEAK_F32_TFLOPS = 157.3
+PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector ALU, published
 PEAK_HBM_GBS = 8000.0
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -209,20 +209,47 @@ def main():
     P = info.pairs_raw + info.pairs_comp
     fl_fwd = 4.0 * wl.D * wl.H * P
     fl_all = 14.0 * wl.D * wl.H * P
-    # Algorithmic work per launch of each kernel (flops; bytes for the HBM-bound ones).
+    # Algorithmic work per launch of each kernel: flops, and the bytes it must move
+    # (inputs read once, outputs written once; transposed copies and fp32 partial
+    # sums are workspace, not counted).  A kernel's roofline is whichever of
+    # flops / peak and bytes / HBM bandwidth takes longer.
     e = 2 if wl.dtype == "bf16" else 4
-    per_kernel_flops = {"fwd": fl_fwd, "bwd_dq": 6.0 * wl.D * wl.H * P,
-                        "bwd_dkv": 4.0 * wl.D * wl.H * P, "fwd_f32": fl_fwd,
-                        "bwd_f32": 10.0 * wl.D * wl.H * P}
+    qb = wl.B * wl.H * wl.S * wl.D * e          # one [B,H,S,D] tensor
+    kb = (wl.B * wl.S + wl.B * wl.Sc) * wl.D * e  # kv and kv_comp
+    rb = 4 * wl.B * wl.H * wl.S                  # one fp32 value per row (LSE, delta)
+    per_kernel = {  # kernel: (flops, bytes)
+        "fwd": (fl_fwd, 2 * qb + kb + rb),                          # Q, K -> O, LSE
+        "bwd_dq": (6.0 * wl.D * wl.H * P, 4 * qb + kb + 2 * rb),    # Q, dO, O, LSE, K -> dQ, delta
+        "bwd_dkv": (4.0 * wl.D * wl.H * P, 2 * qb + kb + 2 * rb),   # Q, dO, LSE, delta, K
+        "fwd_f32": (fl_fwd, 2 * qb + kb + rb),
+        "bwd_f32": (10.0 * wl.D * wl.H * P, 5 * qb + 2 * kb + rb),
+    }
     kavg = {k: v[1] / v[0] for k, v in kernels.items() if v[0]}
     per_step = {k: kernels[k][1] / args.steps for k in kernels}
-    dom = max((k for k in per_step if k in per_kernel_flops), key=lambda k: per_step[k])
+    dom = max((k for k in per_step if k in per_kernel), key=lambda k: per_step[k])
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
-    achieved = per_kernel_flops[dom] / (kavg[dom] * 1e-3) / 1e12
-    traffic = recorded_traffic(dom, wl.name)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic, "avg_ms": round(kavg[dom], 4)}
+
+    def roof(flops, nbytes, t_ms):
+        t_mfma = flops / (peak * 1e12)
+        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+        if t_hbm > t_mfma:
+            return dict(bound="hbm", achieved=round(nbytes / (t_ms * 1e-3) / 1e9, 2),
+                        peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(t_hbm / (t_ms * 1e-3), 4))
+        # bf16 runs on the matrix cores; the float32 path is vector-ALU code
+        # (peak: fp32 vector rate of 256 CUs at 2.4 GHz).
+        return dict(bound="mfma" if wl.dtype == "bf16" else "alu",
+                    achieved=round(flops / (t_ms * 1e-3) / 1e12, 2), peak=peak,
+                    unit="TFLOP/s", frac=round(t_mfma / (t_ms * 1e-3), 4))
+
+    roofline = roof(*per_kernel[dom], kavg[dom])
+    roofline.update(kernel=dom, traffic=recorded_traffic(dom, wl.name),
+                    avg_ms=round(kavg[dom], 4), alg_flops=per_kernel[dom][0],
+                    alg_bytes=per_kernel[dom][1])
+    # The whole step (forward + backward) against the same two limits.
+    step_bytes = (2 * qb + kb + rb) + (4 * qb + 2 * kb + rb)
+    step_roof = roof(fl_all, step_bytes, ms)
+    step_roof.update(alg_flops=fl_all, alg_bytes=step_bytes)
 
     out = {
         "metric": "HCA attn fwd+bwd effective TFLOP/s",
@@ -246,6 +273,7 @@ def main():
         "wall_s": round(wall, 3),
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
         "roofline": roofline,
+        "step_roofline": step_roof,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

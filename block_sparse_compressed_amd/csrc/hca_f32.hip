@@ -1,8 +1,9 @@
-// hca_f32.hip -- float32 HCA attention on gfx950 (vector ALU, one wavefront per row or key).
+// hca_f32.hip -- float32 HCA attention on gfx950 (vector ALU, one workgroup per row or key).
 //
 // The float32 path serves small problems that need float32 accuracy; every
-// product and sum is float32.  A wavefront owns one query row (forward, dQ)
-// or one key (dKV); its 64 lanes split the head dimension.  Each row walks
+// product and sum is float32.  A workgroup owns one query row (forward, dQ)
+// or one key (dKV); its wavefronts share out the row's keys (or the key's
+// rows) and the 64 lanes of each split the head dimension.  Each row walks
 // exactly its visible intervals -- raw keys raw_lo..i and compressed entries
 // comp_lo..comp_hi-1 from the host plan -- so nothing invisible is touched.
 // Same mathematics as the bf16 path: one softmax over the union of the sliding
@@ -25,13 +26,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 }  // namespace
 
+// Forward and dQ: one workgroup of kRowWaves wavefronts per query row; wave w
+// takes every kRowWaves-th visible key (raw window first, then compressed
+// entries), so the chains of dependent loads and wave-wide sums run side by
+// side.  The waves' partial results are merged in a fixed order.
+constexpr int kRowWaves = 4;
+
 template <int NDU>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRowWaves * 64)
     hca_fwd_f32_kernel(Dims d, DevPlan p, const float *__restrict__ q, const float *__restrict__ kv,
                        const float *__restrict__ kvc, float scale_log2, float *__restrict__ o,
                        float *__restrict__ lse) {
+  __shared__ float red_acc[kRowWaves][NDU * 64];
+  __shared__ float red_ml[kRowWaves][2];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t row = blockIdx.x;  // whole workgroup: same row
   if (row >= (int64_t)d.B * d.H * d.S) return;
   const int D = NDU * 64;
   const int i = (int)(row % d.S);
@@ -43,6 +52,7 @@ __global__ void __launch_bounds__(256)
     qv[u] = q[row * D + lane + 64 * u];
     acc[u] = 0.f;
   }
+  // Online softmax of this wave's keys (log2 units).
   float m = -INFINITY, l = 0.f;
   auto visit = [&](const float *krow) {
     float kr[NDU], s = 0.f;
@@ -59,23 +69,49 @@ __global__ void __launch_bounds__(256)
     for (int u = 0; u < NDU; ++u) acc[u] = acc[u] * a + pr * kr[u];
     m = mn;
   };
-  for (int t = rw.x; t <= i; ++t) visit(kv + ((size_t)b * d.S + t) * D);
-  for (int c = rw.y; c < rw.z; ++c) visit(kvc + ((size_t)b * d.Sc + c) * D);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int nraw = max(i + 1 - rw.x, 0);
+  const int nkeys = nraw + max(rw.z - rw.y, 0);
+  for (int n = wave; n < nkeys; n += kRowWaves)
+    visit(n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
+                   : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D);
+  // Merge: M = max m_w, L = sum l_w 2^(m_w - M), acc = sum acc_w 2^(m_w - M).
 #pragma unroll
-  for (int u = 0; u < NDU; ++u) o[row * D + lane + 64 * u] = acc[u] * inv;
-  if (lane == 0) lse[row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  for (int u = 0; u < NDU; ++u) red_acc[wave][lane + 64 * u] = acc[u];
+  if (lane == 0) {
+    red_ml[wave][0] = m;
+    red_ml[wave][1] = l;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = -INFINITY;
+    for (int w = 0; w < kRowWaves; ++w) M = fmaxf(M, red_ml[w][0]);
+    float L = 0.f, out[NDU];
+#pragma unroll
+    for (int u = 0; u < NDU; ++u) out[u] = 0.f;
+    for (int w = 0; w < kRowWaves; ++w) {
+      const float mw = red_ml[w][0];
+      const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      L += red_ml[w][1] * f;
+#pragma unroll
+      for (int u = 0; u < NDU; ++u) out[u] += red_acc[w][lane + 64 * u] * f;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int u = 0; u < NDU; ++u) o[row * D + lane + 64 * u] = out[u] * inv;
+    if (lane == 0) lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  }
 }
 
 template <int NDU>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRowWaves * 64)
     hca_bwd_dq_f32_kernel(Dims d, DevPlan p, const float *__restrict__ q,
                           const float *__restrict__ kv, const float *__restrict__ kvc,
                           const float *__restrict__ o, const float *__restrict__ lse,
                           const float *__restrict__ dout, float scale_log2, float scale,
                           float *__restrict__ dq, float *__restrict__ delta) {
+  __shared__ float red_acc[kRowWaves - 1][NDU * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t row = blockIdx.x;  // whole workgroup: same row
   if (row >= (int64_t)d.B * d.H * d.S) return;
   const int D = NDU * 64;
   const int i = (int)(row % d.S);
@@ -89,8 +125,8 @@ __global__ void __launch_bounds__(256)
     dl += dv[u] * o[row * D + lane + 64 * u];
     acc[u] = 0.f;
   }
-  dl = wave_sum(dl);
-  if (lane == 0) delta[row] = dl;
+  dl = wave_sum(dl);  // every wave computes delta; wave 0 stores it
+  if (wave == 0 && lane == 0) delta[row] = dl;
   const float lse2 = lse[row] * kLog2e;
   auto visit = [&](const float *krow) {
     float kr[NDU], s = 0.f, t = 0.f;
@@ -107,22 +143,44 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int u = 0; u < NDU; ++u) acc[u] += ds * kr[u];
   };
-  for (int t = rw.x; t <= i; ++t) visit(kv + ((size_t)b * d.S + t) * D);
-  for (int c = rw.y; c < rw.z; ++c) visit(kvc + ((size_t)b * d.Sc + c) * D);
+  const int nraw = max(i + 1 - rw.x, 0);
+  const int nkeys = nraw + max(rw.z - rw.y, 0);
+  for (int n = wave; n < nkeys; n += kRowWaves)
+    visit(n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
+                   : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D);
+  if (wave > 0) {
 #pragma unroll
-  for (int u = 0; u < NDU; ++u) dq[row * D + lane + 64 * u] = acc[u];
+    for (int u = 0; u < NDU; ++u) red_acc[wave - 1][lane + 64 * u] = acc[u];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 0; w < kRowWaves - 1; ++w)
+#pragma unroll
+      for (int u = 0; u < NDU; ++u) acc[u] += red_acc[w][lane + 64 * u];
+#pragma unroll
+    for (int u = 0; u < NDU; ++u) dq[row * D + lane + 64 * u] = acc[u];
+  }
 }
 
+// dKV: one workgroup of kDkvWaves wavefronts per key.  A compressed entry is
+// seen by every later position of its document, so a single wavefront walking
+// its rows one by one (each a chain of loads and wave-wide sums) took most of
+// the backward; the waves take interleaved positions and their partial sums are
+// added in a fixed order (wave 0, then 1, 2, ...), so the result is the same on
+// every run.
+constexpr int kDkvWaves = 16;
+
 template <int NDU>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kDkvWaves * 64)
     hca_bwd_dkv_f32_kernel(Dims d, DevPlan p, const float *__restrict__ q,
                            const float *__restrict__ kv, const float *__restrict__ kvc,
                            const float *__restrict__ lse, const float *__restrict__ delta,
                            const float *__restrict__ dout, float scale_log2, float scale,
                            float *__restrict__ dkv, float *__restrict__ dkvc) {
+  __shared__ float red[kDkvWaves - 1][NDU * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int per_b = d.S + d.Sc;
-  const int64_t kk = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t kk = blockIdx.x;  // whole workgroup: same key
   if (kk >= (int64_t)d.B * per_b) return;
   const int D = NDU * 64;
   const int b = (int)(kk / per_b), idx = (int)(kk % per_b);
@@ -145,7 +203,7 @@ __global__ void __launch_bounds__(256)
     i0 = k;
     i1 = d.W > 0 ? min(d.S - 1, k + d.W - 1) : k - 1;
   }
-  for (int i = i0; i <= i1; ++i) {
+  for (int i = i0 + wave; i <= i1; i += kDkvWaves) {
     const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + i];
     const bool vis = comp ? (rw.y <= k && k < rw.z) : (rw.x <= k);
     if (!vis) continue;
@@ -167,9 +225,19 @@ __global__ void __launch_bounds__(256)
       for (int u = 0; u < NDU; ++u) acc[u] += ds * qv[u] + pr * dv[u];
     }
   }
-  float *out = comp ? dkvc + ((size_t)b * d.Sc + k) * D : dkv + ((size_t)b * d.S + k) * D;
+  if (wave > 0) {
 #pragma unroll
-  for (int u = 0; u < NDU; ++u) out[lane + 64 * u] = acc[u];
+    for (int u = 0; u < NDU; ++u) red[wave - 1][lane + 64 * u] = acc[u];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 0; w < kDkvWaves - 1; ++w)
+#pragma unroll
+      for (int u = 0; u < NDU; ++u) acc[u] += red[w][lane + 64 * u];
+    float *out = comp ? dkvc + ((size_t)b * d.Sc + k) * D : dkv + ((size_t)b * d.S + k) * D;
+#pragma unroll
+    for (int u = 0; u < NDU; ++u) out[lane + 64 * u] = acc[u];
+  }
 }
 
 #define HCA_F32_SWITCH(D, CALL) \
@@ -188,11 +256,12 @@ __global__ void __launch_bounds__(256)
 int launch_fwd_f32(const Dims &d, const DevPlan &p, const float *q, const float *kv,
                    const float *kvc, float scale, float *o, float *lse, void *stream) {
   const int64_t rows = (int64_t)d.B * d.H * d.S;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const dim3 grid((unsigned)rows);
   hipStream_t s = (hipStream_t)stream;
   const float sl2 = scale * kLog2e;
-#define CALL(N) \
-  hipLaunchKernelGGL(hca_fwd_f32_kernel<N>, grid, dim3(256), 0, s, d, p, q, kv, kvc, sl2, o, lse)
+#define CALL(N)                                                                              \
+  hipLaunchKernelGGL(hca_fwd_f32_kernel<N>, grid, dim3(kRowWaves * 64), 0, s, d, p, q, kv, kvc, \
+                     sl2, o, lse)
   HCA_F32_SWITCH(d.D, CALL)
 #undef CALL
   return (int)hipGetLastError();
@@ -206,14 +275,14 @@ int launch_bwd_f32(const Dims &d, const DevPlan &p, const float *q, const float 
   hipStream_t s = (hipStream_t)stream;
   const float sl2 = scale * kLog2e;
 #define CALL(N)                                                                              \
-  hipLaunchKernelGGL(hca_bwd_dq_f32_kernel<N>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, \
+  hipLaunchKernelGGL(hca_bwd_dq_f32_kernel<N>, dim3((unsigned)rows), dim3(kRowWaves * 64), 0, \
                      s, d, p, q, kv, kvc, o, lse, dout, sl2, scale, dq, delta)
   HCA_F32_SWITCH(d.D, CALL)
 #undef CALL
   int err = (int)hipGetLastError();
   if (err) return err;
 #define CALL(N)                                                                                \
-  hipLaunchKernelGGL(hca_bwd_dkv_f32_kernel<N>, dim3((unsigned)((keys + 3) / 4)), dim3(256), 0, \
+  hipLaunchKernelGGL(hca_bwd_dkv_f32_kernel<N>, dim3((unsigned)keys), dim3(kDkvWaves * 64), 0, \
                      s, d, p, q, kv, kvc, lse, delta, dout, sl2, scale, dkv, dkvc)
   HCA_F32_SWITCH(d.D, CALL)
 #undef CALL
