@@ -1,9 +1,10 @@
 // hca_fwd.hip -- HCA attention forward on gfx950 (bf16 MFMA, fp32 accumulation).
 //
-// One workgroup owns one query tile: bq positions x all H heads = 128 query
-// rows (single KV head, so every head of a position sees the same keys; the
-// shared-KV einsum form of "[DeepSeek-V4] Implement Compressed Attention
-// Layers", review suggestions).  It walks the tile's list of non-empty key
+// A query tile is bq positions x all H heads (single KV head, so every head of
+// a position sees the same keys; the shared-KV einsum form of "[DeepSeek-V4]
+// Implement Compressed Attention Layers", review suggestions); a workgroup
+// owns the tile (D = 64 / 128: 128 rows) or a slice of it (D = 512: 64 rows of
+// a 16-position x 64-head tile).  It walks the tile's list of non-empty key
 // tiles from the host-built block table (EMPTY tiles never appear; "Add HCA
 // Static Compilation for Splash Attention [Deepseek v4]", Description), stages
 // each 32-key tile of the shared K = V tensor in LDS once for all heads, and
@@ -261,18 +262,19 @@ __global__ void __launch_bounds__(NW * 64, 1)
 }
 
 // ---------------------------------------------------------------------------
-// D = 512 forward: 8 waves x 16 rows = 128 rows per workgroup.
+// D = 512 forward: NW waves x 16 rows per workgroup (one wave = 16 consecutive
+// positions of one head).
 //
-// Software pipeline per wave: while the softmax and the PV product of tile t
-// run, the S^T = K Q^T MFMAs of tile t+1 are already in flight, so the VALU
-// and transcendental work of the softmax overlaps matrix-core work instead of
-// idling it.  K tiles and K^T tiles therefore live one tile apart: during
-// iteration t the LDS holds K(t+1) (being read), K(t+2) (arriving), K^T(t)
-// (being read) and K^T(t+1) (arriving) -- 4 x 32 KiB -- with one barrier per
-// tile.  Loads go global -> LDS directly (no VGPR staging), in swizzled layouts
-// that make every operand read conflict-free.  O is rescaled lazily: a row's
-// reference max only moves when its tile max exceeds it by more than kLazy
-// (log2 units), so P stays below 2^kLazy and rescales are rare.
+// NW = 4 (the default): 64 rows, two workgroups per CU, K and K^T tiles
+// single-buffered (32 KiB each).  Per tile: softmax and O^T += K^T P^T of tile
+// t (K of tile t+1 arriving meanwhile), barrier, copy K^T of tile t+1 while
+// S^T = K Q^T of tile t+1 runs, barrier, copy K of tile t+2.  The second
+// workgroup on the CU fills this one's waits and its row loads.
+// NW = 8: 128 rows, one workgroup per CU, K and K^T double-buffered and one
+// tile apart (4 x 32 KiB), one barrier per tile, the S^T MFMAs of tile t+1
+// issued before the softmax and PV of tile t.
+// Tiles go global -> LDS directly (no VGPR staging), in swizzled layouts that
+// make every operand read conflict-free.
 // ---------------------------------------------------------------------------
 // Lazy rescaling: a row's reference max m_run only moves when the tile max
 // exceeds it by more than kLazy (log2 units), so P = 2^(x - m_run) stays below
