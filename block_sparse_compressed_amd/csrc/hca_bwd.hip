@@ -318,32 +318,27 @@ __global__ void __launch_bounds__(NW * 64, 1)
     return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
                   : uniform_load(p.qent, e_begin + t);
   };
-  const rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
-  const rsrc_t r_kvc =
-      make_rsrc(kvc + (size_t)b * d.Sc * D, (uint32_t)d.Sc * D * 2);
-  const rsrc_t r_kvt =
-      make_rsrc(kvt + (size_t)b * D * d.S_pad, (uint32_t)d.S_pad * D * 2);
-  const rsrc_t r_kvct =
-      make_rsrc(kvct + (size_t)b * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 2);
-  auto stage_k = [&](int t) {
+  // K and K^T tiles come from the tile images (kvt, kvct) that the image
+  // kernel wrote at the start of the call.
+  const rsrc_t r_img =
+      make_rsrc(kvt + (size_t)b * 2 * D * d.S_pad, (uint32_t)d.S_pad * D * 4);
+  const rsrc_t r_imgc =
+      make_rsrc(kvct + (size_t)b * 2 * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 4);
+  auto stage_k = [&](int t) {  // K of list entry t
     if (t >= nent) return;
     const uint32_t ent = entry(t);
-    stage_k512<NW>((ent & kEntComp) ? r_kvc : r_kv, (int)(ent & kEntIdx) * kBK,
-                   kbase + (t & 1) * kTileBytes512, wave, lane);
+    stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 0,
+                     kbase + (t & 1) * kTileBytes512, wave, lane);
   };
-  auto stage_t = [&](int t) {
+  auto stage_t = [&](int t) {  // K^T of list entry t
     if (t >= nent) return;
     const uint32_t ent = entry(t);
-    const bool comp = ent & kEntComp;
-    stage_kt512<NW>(comp ? r_kvct : r_kvt, (int)(ent & kEntIdx) * kBK,
-                    tbase + (t & 1) * kTileBytes512, wave, lane);
+    stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 1,
+                     tbase + (t & 1) * kTileBytes512, wave, lane);
   };
 
-  int qk_off[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n)
-    qk_off[n] = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
-  const int pv_off = (4 * j + (g ^ kt_swz(j))) * 16;
+  // Operand reads are flat: lane l reads bytes 16 l .. 16 l + 15 of a block.
+  const int frag_off = 16 * lane;
 
   // S^T and dP^T of tile t (shared K A-operands): [0] keys 0-15, [1] keys 16-31.
   // Operand fragments are read PF k-steps ahead of their MFMAs.
@@ -352,17 +347,17 @@ __global__ void __launch_bounds__(NW * 64, 1)
     const char *kb = kbase + (t & 1) * kTileBytes512;
     s[0] = s[1] = dp[0] = dp[1] = floatx4{0.f, 0.f, 0.f, 0.f};
     bf16x8 a0[KS], a1[KS];
-    auto at = [&](int ks) { return kb + qk_off[ks & 3] + 256 * (ks >> 2); };
+    auto at = [&](int ks) { return kb + 2048 * ks + frag_off; };
 #pragma unroll
     for (int ks = 0; ks < PF; ++ks) {
       a0[ks] = lds_frag(at(ks));
-      a1[ks] = lds_frag(at(ks) + 4096);
+      a1[ks] = lds_frag(at(ks) + 1024);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + PF < KS) {
         a0[ks + PF] = lds_frag(at(ks + PF));
-        a1[ks + PF] = lds_frag(at(ks + PF) + 4096);
+        a1[ks + PF] = lds_frag(at(ks + PF) + 1024);
       }
       s[0] = mfma16x16x32(a0[ks], qf[ks], s[0]);
       s[1] = mfma16x16x32(a1[ks], qf[ks], s[1]);
@@ -452,7 +447,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     {
       // dQ^T += K^T dS^T: fragments read PV column blocks ahead.
       constexpr int PV = 8;
-      const char *tb = tbase + (it & 1) * kTileBytes512 + pv_off;
+      const char *tb = tbase + (it & 1) * kTileBytes512 + frag_off;
       bf16x8 kt[DB];
 #pragma unroll
       for (int db = 0; db < PV; ++db) kt[db] = lds_frag(tb + db * 1024);
@@ -746,7 +741,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
   };
   const size_t bat = (size_t)b * d.H * d.S * D;
   // Byte offset of this lane's 16-byte chunk in a staged row: row r = 8 wave + i
-  // is stored with swizzle k_swz(r) = (i & 3) | (wave << 2).
+  // is stored with swizzle (i & 3) | (wave << 2).
   uint32_t lane_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lane_off[i] = (uint32_t)((lane ^ (i | (wave << 2))) << 4);

@@ -336,35 +336,27 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
                   : uniform_load(p.qent, e_begin + t);
   };
-  const rsrc_t r_kv = make_rsrc(kv + (size_t)b * d.S * D, (uint32_t)d.S * D * 2);
-  const rsrc_t r_kvc =
-      make_rsrc(kvc + (size_t)b * d.Sc * D, (uint32_t)d.Sc * D * 2);
-  const rsrc_t r_kvt =
-      make_rsrc(kvt + (size_t)b * D * d.S_pad, (uint32_t)d.S_pad * D * 2);
-  const rsrc_t r_kvct =
-      make_rsrc(kvct + (size_t)b * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 2);
-  auto stage_k = [&](int t) {  // K of list entry t -> K buffer t & 1
+  // K and K^T tiles come from the tile images (kvt, kvct) that the image
+  // kernel wrote at the start of the call.
+  const rsrc_t r_img =
+      make_rsrc(kvt + (size_t)b * 2 * D * d.S_pad, (uint32_t)d.S_pad * D * 4);
+  const rsrc_t r_imgc =
+      make_rsrc(kvct + (size_t)b * 2 * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 4);
+  auto stage_k = [&](int t) {  // K of list entry t
     if (t >= nent) return;
     const uint32_t ent = entry(t);
-    stage_k512<NW>((ent & kEntComp) ? r_kvc : r_kv, (int)(ent & kEntIdx) * kBK,
-                   kbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
+    stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 0,
+                     kbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
   };
-  auto stage_t = [&](int t) {  // K^T of list entry t -> K^T buffer t & 1
+  auto stage_t = [&](int t) {  // K^T of list entry t
     if (t >= nent) return;
     const uint32_t ent = entry(t);
-    const bool comp = ent & kEntComp;
-    stage_kt512<NW>(comp ? r_kvct : r_kvt, (int)(ent & kEntIdx) * kBK,
-                    tbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
+    stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 1,
+                     tbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
   };
 
-  // Lane-constant parts of the operand addresses.  QK^T A operand of k-step
-  // ks = 4 m + n: key row 8 (j >> 2) + (j & 3) (+4 for the second 16 keys),
-  // slot (4 ks + g) ^ j = 4 (m*4 + (n ^ (j >> 2))) + (g ^ (j & 3)).
-  int qk_off[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n)
-    qk_off[n] = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
-  const int pv_off = (4 * j + (g ^ kt_swz(j))) * 16;
+  // Operand reads are flat: lane l reads bytes 16 l .. 16 l + 15 of a block.
+  const int frag_off = 16 * lane;
 
   // S^T of tile t for every row block: two 16-key halves per block.
   auto qk = [&](int t, floatx4 (&s)[MB][2]) {
@@ -373,8 +365,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     for (int mb = 0; mb < MB; ++mb) s[mb][0] = s[mb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const char *a = kb + qk_off[ks & 3] + 256 * (ks >> 2);
-      const bf16x8 a0 = lds_frag(a), a1 = lds_frag(a + 4096);
+      const char *a = kb + 2048 * ks + frag_off;
+      const bf16x8 a0 = lds_frag(a), a1 = lds_frag(a + 1024);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         s[mb][0] = mfma16x16x32(a0, qf[mb][ks], s[mb][0]);
@@ -451,7 +443,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
       }
       pb[mb] = pack8(x);
     }
-    const char *tb = tbase + (it & (kBufs - 1)) * kTileBytes512 + pv_off;
+    const char *tb = tbase + (it & (kBufs - 1)) * kTileBytes512 + frag_off;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const bf16x8 a = lds_frag(tb + db * 1024);
@@ -563,9 +555,57 @@ __global__ void __launch_bounds__(256) hca_transpose_kernel(const bf16raw *__res
   }
 }
 
+// Tile images at D = 512: dst[b][t] (64 KiB) = the K tile t (keys 32 t ..
+// 32 t + 31, zero past N) in MFMA fragment order, then its transpose in
+// fragment order (block and lane layout as the D = 512 kernels read them).
+// One workgroup per tile: the tile goes through LDS once, both orders are
+// written as contiguous 16-byte pieces.
+__global__ void __launch_bounds__(256) hca_image512_kernel(const bf16raw *__restrict__ src,
+                                                           bf16raw *__restrict__ dst, int N,
+                                                           int N_pad) {
+  constexpr int D = 512, PITCH = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16raw tile[32 * PITCH];
+  const int b = blockIdx.y, t = blockIdx.x;
+  const bf16raw *s = src + (size_t)b * N * D;
+  uint4 *out = reinterpret_cast<uint4 *>(dst + ((size_t)b * N_pad + (size_t)t * 32) * 2 * D);
+  for (int c = threadIdx.x; c < 32 * D / 8; c += 256) {
+    const int key = c / (D / 8), col = (c % (D / 8)) * 8, gk = t * 32 + key;
+    *reinterpret_cast<uint4 *>(tile + key * PITCH + col) =
+        gk < N ? *reinterpret_cast<const uint4 *>(s + (size_t)gk * D + col)
+               : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  // Block blk, lane l = 16 g + j.  K: k-step blk / 2, key half blk % 2, key
+  // 8 (j / 4) + j % 4 + 4 (blk % 2), columns 32 (blk / 2) + 8 g ...; K^T:
+  // d-row 16 blk + j, keys 8 g ... 8 g + 7.
+  for (int c = threadIdx.x; c < 2048; c += 256) {
+    const int blk = c >> 6, l = c & 63, j = l & 15, g = l >> 4;
+    const int key = 8 * (j >> 2) + (j & 3) + 4 * (blk & 1);
+    out[c] = *reinterpret_cast<const uint4 *>(tile + key * PITCH + 32 * (blk >> 1) + 8 * g);
+    const int dc = 16 * blk + j;
+    ushort4 lo, hi;
+    lo.x = tile[(8 * g + 0) * PITCH + dc];
+    lo.y = tile[(8 * g + 1) * PITCH + dc];
+    lo.z = tile[(8 * g + 2) * PITCH + dc];
+    lo.w = tile[(8 * g + 3) * PITCH + dc];
+    hi.x = tile[(8 * g + 4) * PITCH + dc];
+    hi.y = tile[(8 * g + 5) * PITCH + dc];
+    hi.z = tile[(8 * g + 6) * PITCH + dc];
+    hi.w = tile[(8 * g + 7) * PITCH + dc];
+    out[2048 + c] = make_uint4(lo.x | ((unsigned)lo.y << 16), lo.z | ((unsigned)lo.w << 16),
+                               hi.x | ((unsigned)hi.y << 16), hi.z | ((unsigned)hi.w << 16));
+  }
+}
+
 int launch_transpose_kv(const void *src, void *dst, int B, int N, int N_pad, int D,
                         void *stream) {
   if (N_pad == 0) return hipSuccess;
+  if (D == 512) {
+    if (N_pad % 32) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(hca_image512_kernel, dim3(N_pad / 32, B), dim3(256), 0,
+                       (hipStream_t)stream, (const bf16raw *)src, (bf16raw *)dst, N, N_pad);
+    return (int)hipGetLastError();
+  }
   dim3 grid((N_pad + 63) / 64, (D + 63) / 64, B);
   hipLaunchKernelGGL(hca_transpose_kernel, grid, dim3(256), 0, (hipStream_t)stream,
                      (const bf16raw *)src, (bf16raw *)dst, N, N_pad, D);

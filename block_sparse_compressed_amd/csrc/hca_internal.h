@@ -42,8 +42,9 @@ struct DevLayout {
 
 // Byte offsets inside the caller's workspaces.
 struct WsLayout {
-  uint64_t kvt = 0;     // transposed raw kv [B][D][S_pad] (bf16 path)
-  uint64_t kvct = 0;    // transposed compressed kv [B][D][Sc_pad]
+  uint64_t kvt = 0;     // raw kv tile images (bf16 path): D = 512 [B][S_pad/32][K | K^T
+                        // fragments, 64 KiB], else transposed [B][S_pad/32][D][32]
+  uint64_t kvct = 0;    // the same for compressed kv, Sc_pad entries
   uint64_t delta = 0;   // float32 [B][H][S] (backward)
   uint64_t part = 0;    // float32 partial key gradients (backward)
   uint64_t fwd_total = 0;

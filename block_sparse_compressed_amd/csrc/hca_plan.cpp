@@ -451,8 +451,11 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     WsLayout &w = p->ws;
     off = 0;
     if (dtype == HCA_BF16) {
-      w.kvt = place((uint64_t)B * D * (nktr * bkr) * 2);
-      w.kvct = place((uint64_t)B * D * std::max<int64_t>(1, nktc * bkc) * 2);
+      // D = 512: K and K^T of every tile in MFMA fragment order (two copies);
+      // other head dims: K^T only.
+      const uint64_t copies = D == 512 ? 2 : 1;
+      w.kvt = place(copies * B * D * (nktr * bkr) * 2);
+      w.kvct = place(copies * B * D * std::max<int64_t>(1, nktc * bkc) * 2);
     }
     w.fwd_total = dtype == HCA_BF16 ? off : 0;
     w.delta = place((uint64_t)B * H * S * 4);

@@ -3,19 +3,23 @@
 // Tiles move global -> LDS with buffer_load_dwordx4 ... lds: each wave
 // instruction deposits 64 lanes x 16 B = 1 KiB contiguously at its LDS base
 // (lane l at base + 16 l), bypassing VGPRs; the buffer range check returns
-// zeros for rows past the end of the tensor.  The layouts below permute which
-// global 16-byte chunk each lane fetches so that the MFMA operand reads that
-// follow are free of LDS bank conflicts:
+// zeros for rows past the end of the tensor.  Each lane chooses which global
+// 16-byte chunk it fetches, so the tiles land in LDS in MFMA fragment order:
+// every 1 KiB block is one A operand of v_mfma_f32_16x16x32_bf16, lane l's 8
+// values at byte 16 l, and each operand read is a flat, conflict-free
+// ds_read_b128 of 64 consecutive 16-byte pieces.
 //
-//   K tile  [32 keys][64 chunks]: key row rho holds chunk c at slot
-//           c ^ hk(rho), hk(rho) = (rho & 3) | ((rho >> 3) & 3) << 2.
-//           The QK^T A-operand read of lane (g, j) -- key row
-//           8 (j >> 2) + 4 b + (j & 3), chunk 4 ks + g -- lands on slot
-//           (4 ks + g) ^ j: sixteen distinct bank groups per 16 lanes.
-//   K^T tile [512 d][4 chunks of 8 keys], 16 d-rows per 1 KiB block: row jr
-//           of a block holds chunk c at slot c ^ tk(jr),
-//           tk(jr) = (jr >> 2) ^ (jr & 2).  The PV A-operand read of lane
-//           (g, j) -- d-row j of the block, chunk g -- is again conflict-free.
+//   K tile   block 2 ks + h (k-step ks = 0..15, key half h = 0..1) holds, for
+//            lane l = 16 g + j, key 8 (j >> 2) + (j & 3) + 4 h of the tile and
+//            columns 32 ks + 8 g .. 32 ks + 8 g + 7.  With this key order the
+//            S^T product leaves lane group g holding keys 8 g .. 8 g + 7 of its
+//            query row, the B operand layout of the PV product.
+//   K^T tile block db (16 d-rows) holds, for lane l = 16 g + j, d-row
+//            16 db + j and keys 8 g .. 8 g + 7.
+// Both orders are laid out in HBM by a small image kernel at the start of
+// each call (gathering them per lane straight from the row-major tensor made
+// every copy instruction touch 16 rows and ran far slower), so every copy
+// instruction reads one contiguous KiB.
 #pragma once
 
 #include "hca_device.h"
@@ -23,9 +27,6 @@
 namespace hca {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ int k_swz(int rho) { return (rho & 3) | (((rho >> 3) & 3) << 2); }
-__device__ __forceinline__ int kt_swz(int jr) { return (jr >> 2) ^ (jr & 2); }
 
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -80,29 +81,24 @@ __device__ __forceinline__ void buf_load16(rsrc_t r, uint32_t lds, uint32_t voff
 }
 #pragma clang diagnostic pop
 
-// Stages key rows k0 .. k0+31 of a [nk][512] tensor (resource `r` covers
-// exactly nk rows, so rows past the end load as zeros) into `kbuf` (32 KiB).
-template <int NW>
-__device__ __forceinline__ void stage_k512(rsrc_t r, int k0, char *kbuf, int wave, int lane) {
-  static_assert(32 % NW == 0, "waves must divide the tile rows");
-#pragma unroll
-  for (int i = 0; i < 32 / NW; ++i) {
-    const int rho = wave * (32 / NW) + i;
-    buf_load16(r, lds_addr(kbuf + rho * 1024), (k0 + rho) * 1024 + ((lane ^ k_swz(rho)) << 4));
-  }
-}
+// Tile images at D = 512: per 32-key tile 64 KiB, the K tile in fragment order
+// (32 KiB) followed by the K^T tile in fragment order (32 KiB), written by the
+// image kernel at the start of each forward / backward call; tiles of the
+// padding are zero.
+constexpr int kImageBytes512 = 2 * kTileBytes512;
 
-// Stages the transpose of key tile k0 .. k0+31 from a tile-major transposed
-// copy ([tile][512][32], tiles of the padding zero-filled) into `tbuf`
-// (32 KiB): each instruction moves 16 d-rows, one contiguous KiB.
+// Stages one half of the image of key tile k0 .. k0+31 (`part` 0: K, 1: K^T)
+// into `buf` (32 KiB): each instruction copies one contiguous KiB, lane l's
+// 16 bytes landing at buf + 1024 blk + 16 l.
 template <int NW>
-__device__ __forceinline__ void stage_kt512(rsrc_t r, int k0, char *tbuf, int wave, int lane) {
-  const int jr = lane >> 2;
-  const int voff = k0 * 1024 + jr * 64 + (((lane & 3) ^ kt_swz(jr)) << 4);
+__device__ __forceinline__ void stage_img512(rsrc_t r, int k0, int part, char *buf, int wave,
+                                             int lane) {
+  static_assert(32 % NW == 0, "waves must divide the tile blocks");
+  const int voff = (k0 / 32) * kImageBytes512 + part * kTileBytes512 + 16 * lane;
 #pragma unroll
   for (int i = 0; i < 32 / NW; ++i) {
     const int blk = wave * (32 / NW) + i;
-    buf_load16(r, lds_addr(tbuf + blk * 1024), voff + blk * 1024);
+    buf_load16(r, lds_addr(buf + blk * 1024), voff + blk * 1024);
   }
 }
 
