@@ -651,7 +651,7 @@ __global__ void __launch_bounds__(256, 1)
 //       scores    wave w forms S = Q K^T and dP = dO K^T for all 32 rows and
 //                 its 32 keys (K fragments of those keys held in VGPRs); then
 //                 P = 2^(S log2e scale - LSE log2e), dS = scale P (dP - delta),
-//                 stored as bf16 in a [key][row] exchange tile in LDS;
+//                 stored as bf16 in exchange tiles in LDS (fragment order);
 //       gradient  wave w accumulates dKV^T[d][key] += Q^T dS + dO^T P over the
 //                 step's rows for its quarter of the columns, d in
 //                 [128 w, 128 w + 128), and all 128 keys: A operands are
@@ -673,10 +673,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *p) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Exchange tile [128 keys][32 rows] bf16, 64 B per key: rows 8c .. 8c + 7 of
-// key k sit in 16-byte slot c ^ ((k >> 2) & 3), so the 16 lanes that read one
-// slot index for 16 consecutive keys touch 16 distinct bank groups.
-__device__ __forceinline__ int x_off(int key, int c) { return key * 64 + ((c ^ ((key >> 2) & 3)) << 4); }
 
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, 1)
@@ -806,9 +802,12 @@ __global__ void __launch_bounds__(NW * 64, 1)
       tr_off[dl] = (8 * g + u) * 1024 + (((2 * dl + c0) ^ (u + 4 * g)) << 4) + ((j & 1) << 3) +
                    256 * wave;
   }
-  // Exchange-tile offsets: key 16 kb + j lives at 1024 kb + x_off(j, g).
-  const int xw0 = x_off(j, g) + 2048 * wave;  // this wave's keys 32 wave + 16 kb + j
-  const int xr0 = x_off(j, g);
+  // Exchange tiles (P and dS, [8 key blocks][1 KiB]) in fragment order: block
+  // kb holds keys 16 kb + j, rows 8 g .. 8 g + 7 at byte 16 l of lane
+  // l = 16 g + j, both as the score phase produces them and as the gradient
+  // reads them as B operands, so writes and reads are flat.
+  const int xw0 = 16 * lane + 2048 * wave;  // this wave's keys 32 wave + 16 kb + j
+  const int xr0 = 16 * lane;
 
   if (nsteps > 0) {
     stage(0);
