@@ -29,9 +29,12 @@ PEAK_HBM_GBS = 8000.0
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_sparse_compressed_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE counters
-# (scaled by a plain copy of known size); one "traffic:" JSON line per kernel.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_bf16.md")
+# (scaled by a plain copy of known size): "traffic:" JSON lines, one per kernel and
+# workload, in profiles/hbm_traffic_<workload>.md.  MFMA and LDS utilisation from
+# rocprofv3's derived counters: "mfma:" JSON lines in profiles/mfma_util.md.
+MFMA_FILE = os.path.join(PROFILES, "mfma_util.md")
 KERNEL_SOURCES = {"fwd": "hca_fwd.hip", "bwd_dq": "hca_bwd.hip", "bwd_dkv": "hca_bwd.hip",
                   "dkv_reduce": "hca_bwd.hip", "transpose": "hca_fwd.hip"}
 
@@ -47,12 +50,12 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel, workload):
-    """Measured HBM bytes per launch for this kernel and workload, or None when no
-    measurement exists for the current sources."""
+def _records(path, tag, kernel, workload):
+    """The "tag:" JSON record of this kernel and workload in a profile summary, or
+    None when there is none for the kernel's current sources."""
     try:
-        with open(TRAFFIC_FILE) as fh:
-            lines = [ln[len("traffic:"):] for ln in fh if ln.startswith("traffic:")]
+        with open(path) as fh:
+            lines = [ln[len(tag):] for ln in fh if ln.startswith(tag)]
     except OSError:
         return None
     want = source_hash(kernel) if kernel in KERNEL_SOURCES else None
@@ -60,8 +63,21 @@ def recorded_traffic(kernel, workload):
         rec = json.loads(ln)
         if rec.get("kernel") == kernel and rec.get("workload") == workload and \
                 rec.get("source") == want:
-            return rec["bytes_per_launch"]
+            return rec
     return None
+
+
+def recorded_traffic(kernel, workload):
+    """Measured HBM bytes per launch for this kernel and workload, or None."""
+    rec = _records(os.path.join(PROFILES, "hbm_traffic_%s.md" % workload), "traffic:",
+                   kernel, workload)
+    return rec["bytes_per_launch"] if rec else None
+
+
+def recorded_util(kernel, workload):
+    """Measured MfmaUtil / LdsUtil / LDSBankConflict (fractions) or None."""
+    rec = _records(MFMA_FILE, "mfma:", kernel, workload)
+    return {k: rec[k] for k in ("mfma_util", "lds_util", "lds_bank_conflict")} if rec else None
 
 
 def parse():
@@ -243,7 +259,9 @@ def main():
                     unit="TFLOP/s", frac=round(t_mfma / (t_ms * 1e-3), 4))
 
     roofline = roof(*per_kernel[dom], kavg[dom])
+    util = recorded_util(dom, wl.name)
     roofline.update(kernel=dom, traffic=recorded_traffic(dom, wl.name),
+                    mfma_util=util["mfma_util"] if util else None,
                     avg_ms=round(kavg[dom], 4), alg_flops=per_kernel[dom][0],
                     alg_bytes=per_kernel[dom][1])
     # The whole step (forward + backward) against the same two limits.
@@ -274,6 +292,11 @@ def main():
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
         "roofline": roofline,
         "step_roofline": step_roof,
+        # rocprofv3 counters recorded for these kernel sources (separate runs).
+        "counters": {k: dict(recorded_util(k, wl.name) or {},
+                             hbm_bytes=recorded_traffic(k, wl.name))
+                     for k in per_step if recorded_util(k, wl.name) or
+                     recorded_traffic(k, wl.name)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
