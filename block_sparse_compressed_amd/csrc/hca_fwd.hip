@@ -31,6 +31,12 @@ constexpr int kBK = 32;  // keys per tile (raw and compressed)
 #ifndef HCA_FWD_MB
 #define HCA_FWD_MB 1  // 16-row blocks per wave of the D = 512 forward
 #endif
+#ifndef HCA_FWD_QK_PF
+#define HCA_FWD_QK_PF 3  // k-steps of K fragments in flight ahead of the S^T MFMAs
+#endif
+#ifndef HCA_FWD_PV_PF
+#define HCA_FWD_PV_PF 4  // column blocks of K^T fragments in flight ahead of the PV MFMAs
+#endif
 
 
 // K tile chunks: BK rows x D; transposed tile chunks: D rows x BK.  16 B each.
@@ -359,19 +365,37 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
   const int frag_off = 16 * lane;
 
   // S^T of tile t for every row block: two 16-key halves per block.
+  // Operand fragments are read QK_PF k-steps ahead of their MFMAs (the
+  // group barriers keep the compiler from collapsing the distance), so each
+  // MFMA finds its operand landed instead of waiting out an LDS round trip.
   auto qk = [&](int t, floatx4 (&s)[MB][2]) {
-    const char *kb = kbase + (t & (kBufs - 1)) * kTileBytes512;
+    constexpr int PF = HCA_FWD_QK_PF;
+    const char *kb = kbase + (t & (kBufs - 1)) * kTileBytes512 + frag_off;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) s[mb][0] = s[mb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a0[KS], a1[KS];
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) {
+      a0[ks] = lds_frag(kb + 2048 * ks);
+      a1[ks] = lds_frag(kb + 2048 * ks + 1024);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const char *a = kb + 2048 * ks + frag_off;
-      const bf16x8 a0 = lds_frag(a), a1 = lds_frag(a + 1024);
+      if (ks + PF < KS) {
+        a0[ks + PF] = lds_frag(kb + 2048 * (ks + PF));
+        a1[ks + PF] = lds_frag(kb + 2048 * (ks + PF) + 1024);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        s[mb][0] = mfma16x16x32(a0, qf[mb][ks], s[mb][0]);
-        s[mb][1] = mfma16x16x32(a1, qf[mb][ks], s[mb][1]);
+        s[mb][0] = mfma16x16x32(a0[ks], qf[mb][ks], s[mb][0]);
+        s[mb][1] = mfma16x16x32(a1[ks], qf[mb][ks], s[mb][1]);
       }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * MB, 0);
     }
   };
 
@@ -443,12 +467,23 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
       }
       pb[mb] = pack8(x);
     }
+    // K^T fragments read PV_PF column blocks ahead of their MFMAs.
+    constexpr int PV = HCA_FWD_PV_PF;
     const char *tb = tbase + (it & (kBufs - 1)) * kTileBytes512 + frag_off;
+    bf16x8 kt[DB];
+#pragma unroll
+    for (int db = 0; db < PV; ++db) kt[db] = lds_frag(tb + db * 1024);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = lds_frag(tb + db * 1024);
+      if (db + PV < DB) kt[db + PV] = lds_frag(tb + (db + PV) * 1024);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oacc[mb][db] = mfma16x16x32(a, pb[mb], oacc[mb][db]);
+      for (int mb = 0; mb < MB; ++mb) oacc[mb][db] = mfma16x16x32(kt[db], pb[mb], oacc[mb][db]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, PV, 0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (db + PV < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
     }
   };
 
