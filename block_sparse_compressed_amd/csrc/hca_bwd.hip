@@ -969,30 +969,62 @@ __global__ void __launch_bounds__(NW * 64, 1)
 // ---------------------------------------------------------------------------
 // 3. Fixed-order sum of the partials of every key tile -> dKV / dKV_comp.
 // ---------------------------------------------------------------------------
+// One launch for the raw key tiles, one for the compressed ones; a workgroup
+// takes one (key tile, chunk of the tile's [kv_bk][D] block).  Thread (g, c)
+// sums the float4 column c of the tile's items i = g, g + G, g + 2 G, ... in
+// increasing order (eight loads in flight), and the G group sums are added in
+// group order.  The grouping is fixed, so the result is bitwise reproducible.
+// Raw tiles have a few items each (G = 1, 1024-element chunks); a compressed
+// tile has hundreds, streamed by G = 8 groups over 128-element chunks.
+template <int G>
 __global__ void __launch_bounds__(256)
     hca_dkv_reduce_kernel(Dims d, DevPlan p, const float *__restrict__ part, int dtype,
-                          void *__restrict__ dkv, void *__restrict__ dkvc) {
-  // One workgroup per (key tile, 1024-element chunk of the tile's [kv_bk][D] block).
+                          void *__restrict__ dkv, void *__restrict__ dkvc, int comp) {
+  constexpr int C = 256 / G, CHUNK = 4 * C;  // float4 columns per group, elements per workgroup
+  __shared__ float4 red[G][C];
   const int nkt = d.nkv_raw + d.nkv_comp;
-  const int per_tile = d.kv_bk * d.D / 1024;
+  const int ntl = comp ? d.nkv_comp : d.nkv_raw;  // tiles of this launch per batch row
+  const int per_tile = d.kv_bk * d.D / CHUNK;
   const int tile = blockIdx.x / per_tile, chunk = blockIdx.x - tile * per_tile;
-  const int b = tile / nkt, t = tile - b * nkt;
-  const bool comp = t >= d.nkv_raw;
-  const int kt = comp ? t - d.nkv_raw : t;
+  const int b = tile / ntl, kt = tile - b * ntl;
+  const int t = comp ? d.nkv_raw + kt : kt;
   const int nk = comp ? d.Sc : d.S;
   const int first = p.kvtile[2 * (b * nkt + t)], n = p.kvtile[2 * (b * nkt + t) + 1];
   const int D = d.D;
-  const int e = chunk * 1024 + threadIdx.x * 4;
+  const int g = threadIdx.x / C, c = threadIdx.x % C;
+  const int e = chunk * CHUNK + c * 4;
   const int key = kt * d.kv_bk + e / D, col = e % D;
-  if (key >= nk) return;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = 0; i < n; ++i) {
-    const float4 v = *reinterpret_cast<const float4 *>(part + p.kvitem[first + i].part_off + e);
+  auto add = [&](const float4 v) {
     a.x += v.x;
     a.y += v.y;
     a.z += v.z;
     a.w += v.w;
+  };
+  if (n > g) {
+    // The planner gives a tile's items consecutive partial blocks, so item i of
+    // the tile sits i blocks after the first (no per-item table load).
+    const size_t blk = (size_t)d.kv_bk * D;
+    const float *src = part + p.kvitem[first].part_off + e;
+    int i = g;
+    for (; i + 7 * G < n; i += 8 * G) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4 *>(src + (i + u * G) * blk);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) add(v[u]);
+    }
+    for (; i < n; i += G) add(*reinterpret_cast<const float4 *>(src + i * blk));
   }
+  if constexpr (G > 1) {
+    red[g][c] = a;
+    __syncthreads();
+    if (g != 0) return;
+    a = red[0][c];
+#pragma unroll
+    for (int h = 1; h < G; ++h) add(red[h][c]);
+  }
+  if (key >= nk) return;
   const size_t off = ((size_t)b * nk + key) * D + col;
   if (dtype == HCA_BF16) {
     ushort4 w;
@@ -1055,10 +1087,15 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
 int launch_dkv_reduce(const Dims &d, const DevPlan &p, const float *part, int dtype, void *dkv,
                       void *dkvc, void *stream) {
   // kv_bk * D is a multiple of 1024 for every kernel configuration (kv_bk >= 32, D >= 64).
-  const int nblk = d.B * (d.nkv_raw + d.nkv_comp) * (d.kv_bk * d.D / 1024);
-  if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(hca_dkv_reduce_kernel, dim3(nblk), dim3(256), 0, (hipStream_t)stream, d, p,
-                     part, dtype, dkv, dkvc);
+  hipStream_t s = (hipStream_t)stream;
+  const int raw_blk = d.B * d.nkv_raw * (d.kv_bk * d.D / 1024);
+  const int comp_blk = d.B * d.nkv_comp * (d.kv_bk * d.D / 128);
+  if (raw_blk > 0)
+    hipLaunchKernelGGL(hca_dkv_reduce_kernel<1>, dim3(raw_blk), dim3(256), 0, s, d, p, part,
+                       dtype, dkv, dkvc, 0);
+  if (comp_blk > 0)
+    hipLaunchKernelGGL(hca_dkv_reduce_kernel<8>, dim3(comp_blk), dim3(256), 0, s, d, p, part,
+                       dtype, dkv, dkvc, 1);
   return (int)hipGetLastError();
 }
 

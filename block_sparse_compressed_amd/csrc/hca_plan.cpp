@@ -32,12 +32,13 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Positions covered by one work item of the key-stationary backward kernels;
 // longer query-tile lists are split into several items whose partial
-// gradients are summed afterwards in a fixed order.  128 positions keep a
-// compressed tile's items about as long as a raw tile's (whose keys are seen
-// by at most W + bk - 1 positions), so no few long items form the tail.  The
-// 32-key items of the smaller head dims use half as many positions: their
-// steps are short, and more items spread better over the CUs.
-constexpr int64_t kItemPositions = 128;
+// gradients are summed afterwards in a fixed order.  64 positions keep a
+// compressed tile's items about as short as a raw tile's (whose keys are seen
+// by at most W + bk - 1 positions), so no few long items form the tail, and
+// give enough items to fill every CU at S = 16384 (128 positions left its
+// launch at 1.5 items per CU; 64 cut that dKV kernel 2.1 -> 1.65 ms, and the
+// extra partial sums cost little once the reduction streamed them in groups).
+constexpr int64_t kItemPositions = 64;
 
 // State of query tile qt (positions qt*bq .. +bq-1) against keys [k0, k0+bk)
 // of `kind`, from the per-position intervals `rw` ([S][4]).
@@ -323,8 +324,7 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     const int64_t nkv = nkvr + nkvc;
     // Query tiles per item; at most 64 so that the key-stationary kernels can
     // hold an item's whole list in one register across the wave.
-    const int64_t chunk =
-        std::min<int64_t>(64, std::max<int64_t>(1, (kvb >= 64 ? kItemPositions : kItemPositions / 2) / bq));
+    const int64_t chunk = std::min<int64_t>(64, std::max<int64_t>(1, kItemPositions / bq));
     const int64_t nchunk = ceil_div(nqt, chunk);
     p->kvtile.assign((size_t)B * nkv * 2, 0);
     int64_t part_off = 0;
@@ -368,6 +368,8 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
           it.e0 = (int32_t)p->kvent.size();
           p->kvent.insert(p->kvent.end(), list.begin() + s0, list.begin() + s1);
           it.e1 = (int32_t)p->kvent.size();
+          // A tile's items take consecutive partial blocks (the reduction
+          // kernel relies on it).
           it.part_off = part_off;
           part_off += kvb * D;
           p->kvitem.push_back(it);
