@@ -149,6 +149,9 @@ class Plan:
 
     def __init__(self, handle: int):
         self._h = ctypes.c_void_p(handle)
+        # Held by the object so that a plan collected at interpreter exit, after
+        # the module's globals are cleared, can still be released.
+        self._destroy = _lib.hca_plan_destroy
         self.device_buffer = None  # keeps the uploaded torch buffer alive
 
     @property
@@ -157,9 +160,10 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            _lib.hca_plan_destroy(h)
-            self._h = ctypes.c_void_p(0)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
+            h.value = None
 
 
 def _i32(a: Optional[Sequence[int]]):

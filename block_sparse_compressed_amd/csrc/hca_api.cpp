@@ -31,6 +31,7 @@ Dims make_dims(const hca_plan *plan) {
   d.S_pad = in.nkt_raw * in.bk_raw;
   d.Sc_pad = in.nkt_comp * in.bk_comp;
   d.n_items = (int32_t)plan->kvorder.size();  // launch slots (items + padding)
+  d.n_items_full = plan->n_order_full;
   d.kv_bk = plan->kv_bk;
   d.nkv_raw = plan->nkv_raw;
   d.nkv_comp = plan->nkv_comp;

@@ -674,13 +674,13 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *p) {
 }
 
 
-template <int NW>
+template <int NW, int HALF>
 __global__ void __launch_bounds__(NW * 64, 1)
     hca_bwd_dkv512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                           const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
                           const float *__restrict__ lse, const float *__restrict__ delta,
                           const bf16raw *__restrict__ dout, float scale_log2, float scale,
-                          float *__restrict__ part) {
+                          float *__restrict__ part, int slot0) {
   constexpr int D = 512, KS = D / 32;
   constexpr int KEYS = 128, STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = KEYS * STEP * 2;
   static_assert(NW == 4, "4 waves: 32 score keys and one column quarter each");
@@ -693,35 +693,14 @@ __global__ void __launch_bounds__(NW * 64, 1)
   // below runs on the scalar unit.
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
-  const int item = p.kvorder[blockIdx.x];
+  const int item = p.kvorder[slot0 + blockIdx.x];
   if (item < 0) return;  // padding slot of the launch order
   const KvItem it = p.kvitem[item];
   const int b = it.b;
   const bool comp = it.kind != 0;
   const int nk = comp ? d.Sc : d.S;
   const int k0 = it.kt * KEYS;   // first key of the item
-  const int kw = k0 + 32 * wave;  // first of this wave's score keys
   const bf16raw *src = comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D;
-
-  // K fragments of this wave's 32 keys, B[k = d][n = key] of S = Q K^T.
-  // (Unconditional loads of a clamped key, zeroed past the end, so that all
-  // 32 loads are in flight together.)
-  bf16x8 kf[2][KS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key = kw + 16 * kb + j;
-    const bf16raw *krow = src + (size_t)min(key, nk - 1) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(krow + 32 * ks + 8 * g);
-      kf[kb][ks] = as_bf16x8(key < nk ? v : make_uint4(0, 0, 0, 0));
-    }
-  }
-  floatx4 acc[8][8];  // [16-key block][16-column block of this wave's quarter]
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-    for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int nq = it.e1 - it.e0;
   // A query tile is bq positions x H heads (bq a power of two, bq * H a
@@ -802,12 +781,45 @@ __global__ void __launch_bounds__(NW * 64, 1)
       tr_off[dl] = (8 * g + u) * 1024 + (((2 * dl + c0) ^ (u + 4 * g)) << 4) + ((j & 1) << 3) +
                    256 * wave;
   }
-  // Exchange tiles (P and dS, [8 key blocks][1 KiB]) in fragment order: block
-  // kb holds keys 16 kb + j, rows 8 g .. 8 g + 7 at byte 16 l of lane
-  // l = 16 g + j, both as the score phase produces them and as the gradient
-  // reads them as B operands, so writes and reads are flat.
-  const int xw0 = 16 * lane + 2048 * wave;  // this wave's keys 32 wave + 16 kb + j
+  // Exchange tiles (P and dS, up to 8 key blocks of 1 KiB) in fragment order:
+  // block kb holds keys 16 kb + j of the item's active keys, rows 8 g .. 8 g + 7
+  // at byte 16 l of lane l = 16 g + j, both as the score phase produces them
+  // and as the gradient reads them as B operands, so writes and reads are flat.
   const int xr0 = 16 * lane;
+
+  // HALF = 0: the item runs over all 128 keys of its tile.  HALF = 1 (a
+  // launch of its own, so its register allocation stays apart): items of
+  // which no row sees one 64-key half of the tile (the planner marks them:
+  // the first and last items of a sliding-window tile) run over the other
+  // half only; each wave scores 16 keys, the gradient covers 4 key blocks,
+  // and the idle half's partial is written as zeros.
+  {
+  constexpr int KPW = HALF ? 1 : 2;  // 16-key score blocks per wave
+  constexpr int NKB = 4 * KPW;       // active 16-key blocks of the item
+  const int hh = HALF ? (it.halves == 2 ? 1 : 0) : 0;  // active half
+  const int kbase = k0 + 64 * hh;
+  const int kw = kbase + 16 * KPW * wave;  // first of this wave's score keys
+  const int xw0 = 16 * lane + 1024 * KPW * wave;
+
+  // K fragments of this wave's score keys, B[k = d][n = key] of S = Q K^T.
+  // (Unconditional loads of a clamped key, zeroed past the end, so that all
+  // the loads are in flight together.)
+  bf16x8 kf[KPW][KS];
+#pragma unroll
+  for (int kb = 0; kb < KPW; ++kb) {
+    const int key = kw + 16 * kb + j;
+    const bf16raw *krow = src + (size_t)min(key, nk - 1) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(krow + 32 * ks + 8 * g);
+      kf[kb][ks] = as_bf16x8(key < nk ? v : make_uint4(0, 0, 0, 0));
+    }
+  }
+  floatx4 acc[NKB][8];  // [active 16-key block][16-column block of this wave's quarter]
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if (nsteps > 0) {
     stage(0);
@@ -842,11 +854,11 @@ __global__ void __launch_bounds__(NW * 64, 1)
 
     // Scores: operand fragments are read PF k-steps ahead of their MFMAs.
     constexpr int PF = 1;
-    floatx4 sv[2][2], pv[2][2];  // [row block][key block]
+    floatx4 sv[2][KPW], pv[2][KPW];  // [row block][key block]
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sv[rb][kb] = pv[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < KPW; ++kb) sv[rb][kb] = pv[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
     {
       bf16x8 fq[2][KS], fo[2][KS];
       auto qk_at = [&](int ks) { return qk_off[ks & 3] + 256 * (ks >> 2); };
@@ -866,7 +878,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < KPW; ++kb) {
             sv[rb][kb] = mfma16x16x32(fq[rb][ks], kf[kb][ks], sv[rb][kb]);
             pv[rb][kb] = mfma16x16x32(fo[rb][ks], kf[kb][ks], pv[rb][kb]);
           }
@@ -876,7 +888,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * KPW, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -887,7 +899,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 #pragma unroll
       for (int r = 0; r < 8; ++r) ri[r] = ri_s[slot][8 * g + r];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KPW; ++kb) {
         const int key = kw + 16 * kb + j;
         float pr[8], ds[8];
 #pragma unroll
@@ -915,7 +927,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     // key block ahead).
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
-      bf16x8 tq[4], to[4], xp[8], xd[8];
+      bf16x8 tq[4], to[4], xp[NKB], xd[NKB];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         tq[c] = tr_frag(qb + tr_off[4 * ps + c]);
@@ -924,8 +936,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
       xd[0] = lds_frag(xs + XBYTES + xr0);
       xp[0] = lds_frag(xs + xr0);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        if (kb + 1 < 8) {
+      for (int kb = 0; kb < NKB; ++kb) {
+        if (kb + 1 < NKB) {
           xd[kb + 1] = lds_frag(xs + XBYTES + xr0 + 1024 * (kb + 1));
           xp[kb + 1] = lds_frag(xs + xr0 + 1024 * (kb + 1));
         }
@@ -938,8 +950,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 16 + 2, 0);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        if (kb + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int kb = 0; kb < NKB; ++kb) {
+        if (kb + 1 < NKB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -950,19 +962,23 @@ __global__ void __launch_bounds__(NW * 64, 1)
     __syncthreads();
   }
 
-  // Partial [128 keys][512] of this item: this wave's 128 columns of every key.
+  // Partial [128 keys][512] of this item: this wave's 128 columns of every key
+  // (zeros for the idle half of a half item).
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
     float *out = part + it.part_off + (size_t)(16 * kb + j) * D + 128 * wave;
+    const bool act = HALF ? (kb >> 2) == hh : true;
+    const int ka = HALF ? (kb & 3) : kb;  // active block of key block kb
 #pragma unroll
     for (int dl = 0; dl < 8; ++dl) {
       float4 w;
-      w.x = acc[kb][dl][0];
-      w.y = acc[kb][dl][1];
-      w.z = acc[kb][dl][2];
-      w.w = acc[kb][dl][3];
+      w.x = act ? acc[ka][dl][0] : 0.f;
+      w.y = act ? acc[ka][dl][1] : 0.f;
+      w.z = act ? acc[ka][dl][2] : 0.f;
+      w.w = act ? acc[ka][dl][3] : 0.f;
       *reinterpret_cast<float4 *>(out + 16 * dl + 4 * g) = w;
     }
+  }
   }
 }
 
@@ -1073,9 +1089,16 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
   };
   switch (d.D) {
     case 512:
-      hipLaunchKernelGGL(hca_bwd_dkv512_kernel<4>, dim3(d.n_items), dim3(256), 0, s, d, p,
-                         (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc, lse, delta,
-                         (const bf16raw *)dout, sl2, scale, part);
+      // Full-tile items, then the half-tile items (see the kernel).
+      if (d.n_items_full > 0)
+        hipLaunchKernelGGL((hca_bwd_dkv512_kernel<4, 0>), dim3(d.n_items_full), dim3(256), 0, s,
+                           d, p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc,
+                           lse, delta, (const bf16raw *)dout, sl2, scale, part, 0);
+      if (d.n_items > d.n_items_full)
+        hipLaunchKernelGGL((hca_bwd_dkv512_kernel<4, 1>), dim3(d.n_items - d.n_items_full),
+                           dim3(256), 0, s, d, p, (const bf16raw *)q, (const bf16raw *)kv,
+                           (const bf16raw *)kvc, lse, delta, (const bf16raw *)dout, sl2, scale,
+                           part, d.n_items_full);
       break;
     case 128: go(hca_bwd_dkv_kernel<128>); break;
     case 64: go(hca_bwd_dkv_kernel<64>); break;

@@ -22,7 +22,10 @@ constexpr uint32_t kEntIdx = (1u << 30) - 1;
 // row `b`; the item's float32 partial gradient [kv_bk][D] is written at
 // `part_off` floats into the partial area of the backward workspace.
 struct KvItem {
-  int32_t b, kind, kt, e0, e1, pad;
+  int32_t b, kind, kt, e0, e1;
+  // 128-key items: bit 0 / bit 1 set when some row of the item sees a key of
+  // the lower / upper 64 (3 for other key-tile widths).
+  int32_t halves;
   int64_t part_off;
 };
 static_assert(sizeof(KvItem) == 32, "KvItem layout");
@@ -56,7 +59,8 @@ struct Dims {
   int32_t B, S, H, D, r, W, Sc;
   int32_t bq, bk_raw, bk_comp, nqt, nkt_raw, nkt_comp;
   int32_t S_pad, Sc_pad;  // nkt_raw * bk_raw, nkt_comp * bk_comp
-  int32_t n_items;  // launch slots of the key-stationary backward
+  int32_t n_items;       // launch slots of the key-stationary backward (both launches)
+  int32_t n_items_full;  // slots of its first launch (items over all keys of their tile)
   int32_t kv_bk, nkv_raw, nkv_comp;  // key tiles of the key-stationary backward
 };
 
@@ -107,7 +111,8 @@ struct hca_plan {
   std::vector<uint32_t> qent;
   std::vector<int32_t> qorder;
   std::vector<hca::KvItem> kvitem;
-  std::vector<int32_t> kvorder;
+  std::vector<int32_t> kvorder;  // launch slots: full-tile items, then half-tile items
+  int32_t n_order_full = 0;
   std::vector<uint32_t> kvent;
   std::vector<int32_t> kvtile;
   int32_t kv_bk = 32, nkv_raw = 0, nkv_comp = 0;  // key-stationary backward tiling

@@ -368,6 +368,23 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
           it.e0 = (int32_t)p->kvent.size();
           p->kvent.insert(p->kvent.end(), list.begin() + s0, list.begin() + s1);
           it.e1 = (int32_t)p->kvent.size();
+          it.halves = 3;
+          if (kvb == 128) {
+            // Which 64-key halves of the tile any row of the item sees, from
+            // the same per-position intervals as the tile states.
+            it.halves = 0;
+            const int64_t kmid = std::min<int64_t>(k0 + 64, nk), kend = std::min<int64_t>(k0 + kvb, nk);
+            for (size_t e = s0; e < s1; ++e) {
+              const int64_t qt = list[e] & kEntIdx;
+              for (int64_t i = qt * bq; i < std::min<int64_t>(S, qt * bq + bq); ++i) {
+                const int64_t lo = kind ? rw[i * 4 + 1] : rw[i * 4];
+                const int64_t hi = kind ? rw[i * 4 + 2] : i + 1;
+                if (std::max(lo, k0) < std::min(hi, kmid)) it.halves |= 1;
+                if (std::max(lo, kmid) < std::min(hi, kend)) it.halves |= 2;
+              }
+            }
+            if (it.halves == 0) it.halves = 3;  // (a listed tile always has a visible key)
+          }
           // A tile's items take consecutive partial blocks (the reduction
           // kernel relies on it).
           it.part_off = part_off;
@@ -390,36 +407,54 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     // on one XCD, where its L2 serves the repeated reads.  Groups go, heaviest
     // first, to the least-loaded XCD; slots past the end of a short XCD queue
     // hold -1 (no work).
+    // Half-tile items run in a second launch of their own; with few items per
+    // CU its tail costs more than the halved work saves (S = 16384: dKV 1.57
+    // -> 1.71 ms), so below 8 items per CU (256 CUs on MI355X) every item
+    // runs over its whole tile.
+    constexpr size_t kHalfItemsMin = 8 * 256;
+    if (p->kvitem.size() < kHalfItemsMin)
+      for (KvItem &it : p->kvitem) it.halves = 3;
+
+    // Two launches share the order array: items over all keys of their tile
+    // first, then the half-tile items (their own kernel instantiation).
     {
       constexpr int kXcd = 8;
       const int64_t ngroup = (int64_t)B * nchunk;
-      std::vector<int64_t> gwork(ngroup, 0);
-      std::vector<std::vector<int32_t>> gitems(ngroup);
-      for (size_t i = 0; i < p->kvitem.size(); ++i) {
-        gwork[item_group[i]] += p->kvitem[i].e1 - p->kvitem[i].e0;
-        gitems[item_group[i]].push_back((int32_t)i);
-      }
-      std::vector<int64_t> gorder;
-      for (int64_t gi = 0; gi < ngroup; ++gi)
-        if (!gitems[gi].empty()) gorder.push_back(gi);
-      std::stable_sort(gorder.begin(), gorder.end(),
-                       [&](int64_t x, int64_t y) { return gwork[x] > gwork[y]; });
-      std::vector<std::vector<int32_t>> queue(kXcd);
-      std::vector<int64_t> load(kXcd, 0);
-      for (int64_t gi : gorder) {
-        std::vector<int32_t> &its = gitems[gi];
-        std::stable_sort(its.begin(), its.end(), [&](int32_t x, int32_t y) {
-          return (p->kvitem[x].e1 - p->kvitem[x].e0) > (p->kvitem[y].e1 - p->kvitem[y].e0);
-        });
-        const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-        queue[x].insert(queue[x].end(), its.begin(), its.end());
-        load[x] += gwork[gi];
-      }
-      size_t qmax = 0;
-      for (const auto &qq : queue) qmax = std::max(qmax, qq.size());
-      p->kvorder.assign(qmax * kXcd, -1);
-      for (int x = 0; x < kXcd; ++x)
-        for (size_t k = 0; k < queue[x].size(); ++k) p->kvorder[k * kXcd + x] = queue[x][k];
+      auto build_order = [&](bool half) {
+        std::vector<int64_t> gwork(ngroup, 0);
+        std::vector<std::vector<int32_t>> gitems(ngroup);
+        for (size_t i = 0; i < p->kvitem.size(); ++i) {
+          if ((p->kvitem[i].halves != 3) != half) continue;
+          gwork[item_group[i]] += p->kvitem[i].e1 - p->kvitem[i].e0;
+          gitems[item_group[i]].push_back((int32_t)i);
+        }
+        std::vector<int64_t> gorder;
+        for (int64_t gi = 0; gi < ngroup; ++gi)
+          if (!gitems[gi].empty()) gorder.push_back(gi);
+        std::stable_sort(gorder.begin(), gorder.end(),
+                         [&](int64_t x, int64_t y) { return gwork[x] > gwork[y]; });
+        std::vector<std::vector<int32_t>> queue(kXcd);
+        std::vector<int64_t> load(kXcd, 0);
+        for (int64_t gi : gorder) {
+          std::vector<int32_t> &its = gitems[gi];
+          std::stable_sort(its.begin(), its.end(), [&](int32_t x, int32_t y) {
+            return (p->kvitem[x].e1 - p->kvitem[x].e0) > (p->kvitem[y].e1 - p->kvitem[y].e0);
+          });
+          const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+          queue[x].insert(queue[x].end(), its.begin(), its.end());
+          load[x] += gwork[gi];
+        }
+        size_t qmax = 0;
+        for (const auto &qq : queue) qmax = std::max(qmax, qq.size());
+        std::vector<int32_t> order(qmax * kXcd, -1);
+        for (int x = 0; x < kXcd; ++x)
+          for (size_t k = 0; k < queue[x].size(); ++k) order[k * kXcd + x] = queue[x][k];
+        return order;
+      };
+      p->kvorder = build_order(false);
+      p->n_order_full = (int32_t)p->kvorder.size();
+      const std::vector<int32_t> half_order = build_order(true);
+      p->kvorder.insert(p->kvorder.end(), half_order.begin(), half_order.end());
     }
 
     // ---- device image ----------------------------------------------------- //
