@@ -208,8 +208,13 @@ def sample_rows(wl, lengths, rng, n=96):
 
 def sample_keys(wl, lengths):
     """A few raw keys and the last complete compressed entry of a few documents
-    (entries whose visible rows are few, so the oracle sums them quickly)."""
-    kinds, idx = [0, 0, 0], [0, wl.S // 2 + 3, wl.S - 1]
+    (entries whose visible rows are few, so the oracle sums them quickly).  The
+    raw keys sit in both 64-key halves of the 128-key tile at k0 (the multiple
+    of 128 at or below S / 2): k0 + 3 is seen by the lower-half item of its
+    tile, k0 + 100 and k0 + 127 by its upper-half item, which the large
+    workloads run as half-tile items."""
+    k0 = wl.S // 2 // 128 * 128
+    kinds, idx = [0] * 5, [0, k0 + 3, k0 + 100, k0 + 127, wl.S - 1]
     ends = [wl.S] if lengths is None else list(np.cumsum(lengths[0]))
     starts = [0] if lengths is None else list(np.cumsum([0] + lengths[0][:-1]))
     for a, e in list(zip(starts, ends))[-3:]:
