@@ -142,8 +142,15 @@ def cpu_baseline(wl, target_s):
             break
         Sp *= 2
     Sp, dt, flops = best
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh
+                              if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model, "kind": "oracle",
             "sample": "first %d positions of %s (1 document, all %d heads), full forward + "
                       "backward in fp64, %.1f s" % (Sp, wl.name, wl.H, dt)}
 
