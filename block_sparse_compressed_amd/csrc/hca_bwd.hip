@@ -485,9 +485,26 @@ __global__ void __launch_bounds__(NW * 64, 1)
   });
 }
 
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// Transposed A operand of an MFMA from two ds_read_b64_tr_b16 reads: the
+// second read is `four_rows` bytes after the first (four rows further down a
+// row-major LDS tile).
+__device__ __forceinline__ bf16x8 tr_frag_rows(const char *p, int four_rows) {
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(p));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(p + four_rows));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // ---------------------------------------------------------------------------
 // 2. dKV, key-stationary.  4 waves: wave & 1 selects 16 of the tile's 32 keys,
-//    wave >> 1 selects one 32-row half of each 64-row step.
+//    wave >> 1 selects one 32-row half of each 64-row step.  Staged rows are
+//    unpadded with their 16-byte chunks XOR-swizzled (chunk c of row r at
+//    slot c ^ rsw(r)), so the score-phase fragment reads touch distinct bank
+//    groups and the gradient's transposed operands come from two
+//    ds_read_b64_tr_b16 reads each (sixteen 2-byte reads before).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256, 1)
@@ -499,9 +516,11 @@ __global__ void __launch_bounds__(256, 1)
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
   constexpr int STEP = 64;           // query rows staged per step
-  constexpr int QROW = D + 8;        // padded LDS row (bf16)
-  constexpr int RCH = STEP * D / 8;  // 16-B chunks per staged tensor
+  constexpr int QROW = D;            // LDS row (bf16), chunks swizzled
+  constexpr int NCH = D / 8;         // 16-B chunks per row
+  constexpr int RCH = STEP * NCH;    // 16-B chunks per staged tensor
   static_assert(STEP * QROW * 2 >= 2 * D * 16 * 4, "reduction scratch fits in q_lds");
+  auto rsw = [](int r) { return ((r & 3) | (((r >> 3) & 3) << 2)) & (NCH - 1); };
   __shared__ __attribute__((aligned(16))) bf16raw q_lds[STEP * QROW];
   __shared__ __attribute__((aligned(16))) bf16raw o_lds[STEP * QROW];  // dO rows
   __shared__ float lse_lds[STEP], dl_lds[STEP];
@@ -550,8 +569,8 @@ __global__ void __launch_bounds__(256, 1)
           qv = *reinterpret_cast<const uint4 *>(q + row * D + col * 8);
           dv = *reinterpret_cast<const uint4 *>(dout + row * D + col * 8);
         }
-        *reinterpret_cast<uint4 *>(q_lds + r * QROW + col * 8) = qv;
-        *reinterpret_cast<uint4 *>(o_lds + r * QROW + col * 8) = dv;
+        *reinterpret_cast<uint4 *>(q_lds + r * QROW + (col ^ rsw(r)) * 8) = qv;
+        *reinterpret_cast<uint4 *>(o_lds + r * QROW + (col ^ rsw(r)) * 8) = dv;
       }
       if (tid < STEP) {
         const int rho = base + tid;
@@ -579,8 +598,9 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const int arow = wr + r0 + 4 * rb;
-          const bf16x8 aq = as_bf16x8(lds_load16(q_lds + arow * QROW + 32 * ks + 8 * g));
-          const bf16x8 ad = as_bf16x8(lds_load16(o_lds + arow * QROW + 32 * ks + 8 * g));
+          const int slot = ((4 * ks + g) ^ rsw(arow)) * 8;
+          const bf16x8 aq = as_bf16x8(lds_load16(q_lds + arow * QROW + slot));
+          const bf16x8 ad = as_bf16x8(lds_load16(o_lds + arow * QROW + slot));
           s[rb] = mfma16x16x32(aq, kf[ks], s[rb]);
           t[rb] = mfma16x16x32(ad, kf[ks], t[rb]);
         }
@@ -602,18 +622,22 @@ __global__ void __launch_bounds__(256, 1)
           dsv[4 * rb + v] = pr * (t[rb][v] - dl_lds[rr]) * scale;
         }
       const bf16x8 pb = pack8(pv), dsb = pack8(dsv);
-      // dKV^T[d][key] += Q^T[d][rows] dS[rows][key] + dO^T[d][rows] P[rows][key]
+      // dKV^T[d][key] += Q^T[d][rows] dS[rows][key] + dO^T[d][rows] P[rows][key].
+      // Transposed A operand of column block db (d-row j, rows 8 g .. 8 g + 7
+      // of this wave's half): lane reads 8 bytes of row wr + 8 g + (j >> 2),
+      // logical chunk 2 db + ((j & 3) >> 1), half j & 1, and the same 4 rows
+      // further down; the two transpose reads leave lane j with column j.
+      {
+        const int tr_row = wr + 8 * g + (j >> 2);  // rows tr_row + 4 share its swizzle
+        const int c0 = (j & 3) >> 1, hb = (j & 1) * 8;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        bf16x8 aq, ad;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int rr = wr + 8 * g + u;
-          aq[u] = __builtin_bit_cast(__bf16, q_lds[rr * QROW + 16 * db + j]);
-          ad[u] = __builtin_bit_cast(__bf16, o_lds[rr * QROW + 16 * db + j]);
+        for (int db = 0; db < DB; ++db) {
+          const int off = tr_row * QROW * 2 + (((2 * db + c0) ^ rsw(tr_row)) << 4) + hb;
+          const bf16x8 aq = tr_frag_rows(reinterpret_cast<const char *>(q_lds) + off, 4 * QROW * 2);
+          const bf16x8 ad = tr_frag_rows(reinterpret_cast<const char *>(o_lds) + off, 4 * QROW * 2);
+          acc[db] = mfma16x16x32(aq, dsb, acc[db]);
+          acc[db] = mfma16x16x32(ad, pb, acc[db]);
         }
-        acc[db] = mfma16x16x32(aq, dsb, acc[db]);
-        acc[db] = mfma16x16x32(ad, pb, acc[db]);
       }
     }
   }
@@ -661,17 +685,9 @@ __global__ void __launch_bounds__(256, 1)
 //     128 keys per item give each 64 KiB row copy 2 x 256 MFMAs per wave of
 //     work, long enough to hide the copy of the next step behind it.
 // ---------------------------------------------------------------------------
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-
 // Transposed A operand (d-row j of a 16-wide column block, rows 8g..8g+7 of
 // the step) from a swizzled row-major [rows][512] tile: two transpose reads.
-__device__ __forceinline__ bf16x8 tr_frag(const char *p) {
-  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4 *)(p));
-  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4 *)(p + 4096));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
+__device__ __forceinline__ bf16x8 tr_frag(const char *p) { return tr_frag_rows(p, 4096); }
 
 
 template <int NW, int HALF>
