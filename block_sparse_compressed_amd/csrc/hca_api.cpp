@@ -180,15 +180,11 @@ extern "C" hca_status hca_attn_fwd(const hca_plan *plan, const void *q, const vo
   }
   uint8_t *w = static_cast<uint8_t *>(ws);
   void *kvt = w + plan->ws.kvt, *kvct = w + plan->ws.kvct;
-  err = timed(K_TRANSPOSE, hip_stream,
-              [&] { return launch_transpose_kv(kv, kvt, d.B, d.S, d.S_pad, d.D, hip_stream); });
+  err = timed(K_TRANSPOSE, hip_stream, [&] {
+    return launch_transpose_kv(kv, kvt, d.S, d.S_pad, d.Sc > 0 ? kv_comp : nullptr, kvct, d.Sc,
+                               d.Sc_pad, d.B, d.D, hip_stream);
+  });
   if (err) return hip_fail("hca_attn_fwd (transpose)", err);
-  if (d.Sc > 0) {
-    err = timed(K_TRANSPOSE, hip_stream, [&] {
-      return launch_transpose_kv(kv_comp, kvct, d.B, d.Sc, d.Sc_pad, d.D, hip_stream);
-    });
-    if (err) return hip_fail("hca_attn_fwd (transpose)", err);
-  }
   err = timed(K_FWD, hip_stream, [&] {
     return launch_fwd_bf16(d, p, q, kv, kv_comp ? kv_comp : kv, kvt, kvct, scale, o, lse,
                            hip_stream);
@@ -235,15 +231,11 @@ extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const vo
   void *kvt = w + plan->ws.kvt, *kvct = w + plan->ws.kvct;
   float *part = reinterpret_cast<float *>(w + plan->ws.part);
   const void *kvc = kv_comp ? kv_comp : kv;
-  err = timed(K_TRANSPOSE, hip_stream,
-              [&] { return launch_transpose_kv(kv, kvt, d.B, d.S, d.S_pad, d.D, hip_stream); });
+  err = timed(K_TRANSPOSE, hip_stream, [&] {
+    return launch_transpose_kv(kv, kvt, d.S, d.S_pad, d.Sc > 0 ? kv_comp : nullptr, kvct, d.Sc,
+                               d.Sc_pad, d.B, d.D, hip_stream);
+  });
   if (err) return hip_fail("hca_attn_bwd (transpose)", err);
-  if (d.Sc > 0) {
-    err = timed(K_TRANSPOSE, hip_stream, [&] {
-      return launch_transpose_kv(kv_comp, kvct, d.B, d.Sc, d.Sc_pad, d.D, hip_stream);
-    });
-    if (err) return hip_fail("hca_attn_bwd (transpose)", err);
-  }
   err = timed(K_BWD_DQ, hip_stream, [&] {
     return launch_bwd_dq_bf16(d, p, q, kv, kvc, kvt, kvct, o, lse, dout, scale, dq, delta,
                               hip_stream);

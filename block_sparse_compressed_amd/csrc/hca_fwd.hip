@@ -569,16 +569,29 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
   }
 }
 
+// One key tensor and its workspace copy (raw kv or compressed kv): N keys,
+// N_pad after padding to whole tiles.
+struct KvCopy {
+  const bf16raw *src;
+  bf16raw *dst;
+  int N, N_pad;
+};
+
 // Tile-major transpose: dst[b][t / 32][d][t % 32] = src[b][t][d] for t < N, 0 for
 // N <= t < N_pad (N_pad a multiple of 32).  Each 32-key tile's transpose is one
-// contiguous D x 32 block, so a kernel stages it with contiguous copies.
-__global__ void __launch_bounds__(256) hca_transpose_kernel(const bf16raw *__restrict__ src,
-                                                            bf16raw *__restrict__ dst, int N,
-                                                            int N_pad, int D) {
+// contiguous D x 32 block, so a kernel stages it with contiguous copies.  One
+// launch covers the raw keys (blockIdx.x < ceil(raw.N_pad / 64)), then the
+// compressed ones.
+__global__ void __launch_bounds__(256) hca_transpose_kernel(KvCopy raw, KvCopy cmp, int D) {
   __shared__ bf16raw tile[64][66];
-  const int b = blockIdx.z, t0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
-  const bf16raw *s = src + (size_t)b * N * D;
-  bf16raw *o = dst + (size_t)b * D * N_pad;
+  const int nraw = (raw.N_pad + 63) / 64;
+  const bool second = (int)blockIdx.x >= nraw;
+  const KvCopy k = second ? cmp : raw;
+  const int N = k.N, N_pad = k.N_pad;
+  const int b = blockIdx.z, t0 = (second ? blockIdx.x - nraw : blockIdx.x) * 64,
+            d0 = blockIdx.y * 64;
+  const bf16raw *s = k.src + (size_t)b * N * D;
+  bf16raw *o = k.dst + (size_t)b * D * N_pad;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int tt = i / 64, dd = i % 64, t = t0 + tt, dx = d0 + dd;
     tile[tt][dd] = (t < N && dx < D) ? s[(size_t)t * D + dx] : (bf16raw)0;
@@ -594,15 +607,19 @@ __global__ void __launch_bounds__(256) hca_transpose_kernel(const bf16raw *__res
 // 32 t + 31, zero past N) in MFMA fragment order, then its transpose in
 // fragment order (block and lane layout as the D = 512 kernels read them).
 // One workgroup per tile: the tile goes through LDS once, both orders are
-// written as contiguous 16-byte pieces.
-__global__ void __launch_bounds__(256) hca_image512_kernel(const bf16raw *__restrict__ src,
-                                                           bf16raw *__restrict__ dst, int N,
-                                                           int N_pad) {
+// written as contiguous 16-byte pieces.  One launch covers the raw tiles
+// (blockIdx.x < raw.N_pad / 32) and then the compressed ones.
+__global__ void __launch_bounds__(256) hca_image512_kernel(KvCopy raw, KvCopy cmp) {
   constexpr int D = 512, PITCH = D + 8;
   __shared__ __attribute__((aligned(16))) bf16raw tile[32 * PITCH];
-  const int b = blockIdx.y, t = blockIdx.x;
-  const bf16raw *s = src + (size_t)b * N * D;
-  uint4 *out = reinterpret_cast<uint4 *>(dst + ((size_t)b * N_pad + (size_t)t * 32) * 2 * D);
+  const int nraw = raw.N_pad / 32;
+  const bool second = (int)blockIdx.x >= nraw;
+  const KvCopy k = second ? cmp : raw;
+  const int b = blockIdx.y, t = second ? blockIdx.x - nraw : blockIdx.x;
+  const int N = k.N;
+  const bf16raw *s = k.src + (size_t)b * N * D;
+  uint4 *out =
+      reinterpret_cast<uint4 *>(k.dst + ((size_t)b * k.N_pad + (size_t)t * 32) * 2 * D);
   for (int c = threadIdx.x; c < 32 * D / 8; c += 256) {
     const int key = c / (D / 8), col = (c % (D / 8)) * 8, gk = t * 32 + key;
     *reinterpret_cast<uint4 *>(tile + key * PITCH + col) =
@@ -632,18 +649,22 @@ __global__ void __launch_bounds__(256) hca_image512_kernel(const bf16raw *__rest
   }
 }
 
-int launch_transpose_kv(const void *src, void *dst, int B, int N, int N_pad, int D,
-                        void *stream) {
-  if (N_pad == 0) return hipSuccess;
+int launch_transpose_kv(const void *kv, void *kvt, int N, int N_pad, const void *kvc,
+                        void *kvct, int Nc, int Nc_pad, int B, int D, void *stream) {
+  const KvCopy raw{(const bf16raw *)kv, (bf16raw *)kvt, N, N_pad};
+  const KvCopy cmp{(const bf16raw *)kvc, (bf16raw *)kvct, Nc, kvc ? Nc_pad : 0};
+  hipStream_t s = (hipStream_t)stream;
   if (D == 512) {
-    if (N_pad % 32) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(hca_image512_kernel, dim3(N_pad / 32, B), dim3(256), 0,
-                       (hipStream_t)stream, (const bf16raw *)src, (bf16raw *)dst, N, N_pad);
+    if (raw.N_pad % 32 || cmp.N_pad % 32) return (int)hipErrorInvalidValue;
+    const int tiles = raw.N_pad / 32 + cmp.N_pad / 32;
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(hca_image512_kernel, dim3(tiles, B), dim3(256), 0, s, raw, cmp);
     return (int)hipGetLastError();
   }
-  dim3 grid((N_pad + 63) / 64, (D + 63) / 64, B);
-  hipLaunchKernelGGL(hca_transpose_kernel, grid, dim3(256), 0, (hipStream_t)stream,
-                     (const bf16raw *)src, (bf16raw *)dst, N, N_pad, D);
+  const int blocks = (raw.N_pad + 63) / 64 + (cmp.N_pad + 63) / 64;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(hca_transpose_kernel, dim3(blocks, (D + 63) / 64, B), dim3(256), 0, s, raw,
+                     cmp, D);
   return (int)hipGetLastError();
 }
 

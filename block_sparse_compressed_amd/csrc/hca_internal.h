@@ -76,8 +76,8 @@ struct DevPlan {
 };
 
 // Launchers (defined in the .hip files).  Each returns a hipError_t as int.
-int launch_transpose_kv(const void *src, void *dst, int B, int N, int N_pad, int D,
-                        void *stream);
+int launch_transpose_kv(const void *kv, void *kvt, int N, int N_pad, const void *kvc,
+                        void *kvct, int Nc, int Nc_pad, int B, int D, void *stream);
 int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
                     const void *kvc, const void *kvt, const void *kvct, float scale, void *o,
                     float *lse, void *stream);
