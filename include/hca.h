@@ -198,17 +198,19 @@ hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const void *kv, con
                         void *dkv, void *dkv_comp, void *ws, uint64_t ws_bytes, void *hip_stream);
 
 /*
- * Kernel timing (instrumentation).  While enabled, every kernel the library
- * launches is bracketed by a pair of HIP events recorded on that launch's
- * stream.  hca_timing_read waits for the recorded events, writes per-kernel
- * totals (up to `capacity` entries, *count = number of kernels with launches)
- * and clears them.  Not thread-safe against concurrent hca_attn_* calls on
+ * Kernel timing (instrumentation).  While enabled, each kernel family's work
+ * in a call (one launch, or two where the work is split: the key-stationary
+ * backward's full-tile and half-tile items, the reduction's raw and
+ * compressed tiles) is bracketed by a pair of HIP events recorded on the
+ * call's stream.  hca_timing_read waits for the recorded events, writes
+ * per-family totals (up to `capacity` entries, *count = number of families
+ * timed) and clears them.  Not thread-safe against concurrent hca_attn_* calls on
  * other threads while enabled.  Errors: HCA_ERR_INVALID_ARG on NULL output
  * pointers, HCA_ERR_HIP if an event cannot be created or read.
  */
 typedef struct hca_kernel_time {
   char name[32];    /* kernel family, e.g. "fwd", "bwd_dq", "bwd_dkv" */
-  int64_t launches; /* number of timed launches since the last read */
+  int64_t launches; /* number of timed regions (calls) since the last read */
   double total_ms;  /* summed event-to-event duration */
 } hca_kernel_time;
 
