@@ -215,6 +215,14 @@ def sample_keys(wl, lengths):
     workloads run as half-tile items."""
     k0 = wl.S // 2 // 128 * 128
     kinds, idx = [0] * 5, [0, k0 + 3, k0 + 100, k0 + 127, wl.S - 1]
+    # S = 65536 (one document, where the dKV kernel runs half-tile items): the
+    # last entry of the lower half of the last 128-entry compressed tile.  The
+    # first rows that see it see none of the tile's upper half, so part of its
+    # gradient comes from half-tile items.  (The oracle recomputes every row
+    # that sees it, ~0.5 M rows, so it is checked on this workload only.)
+    if wl.S == 65536 and lengths is None:
+        kinds.append(1)
+        idx.append(wl.Sc - 65)
     ends = [wl.S] if lengths is None else list(np.cumsum(lengths[0]))
     starts = [0] if lengths is None else list(np.cumsum([0] + lengths[0][:-1]))
     for a, e in list(zip(starts, ends))[-3:]:
