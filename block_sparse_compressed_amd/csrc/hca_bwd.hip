@@ -14,10 +14,12 @@
 //     prologue from O and dO, and dQ is accumulated in registers and written
 //     once -- no atomics (the page on the static mask compiles the backward with
 //     an on-chip dQ reduction; here the whole dQ row stays on chip).
-//  2. key-stationary dKV: a workgroup owns one 32-key tile (raw or compressed)
-//     and walks the query tiles that see it, recomputing S and dP with the
-//     tile's K fragments held in VGPRs; long compressed-entry lists are split
-//     into several work items.  Each item writes a float32 partial.
+//  2. key-stationary dKV: a workgroup owns one work item -- a key tile (raw
+//     or compressed; 128 keys at D = 512, 32 otherwise) and the query tiles
+//     of one 64-position chunk that see it -- recomputing S and dP with the
+//     tile's K fragments held in VGPRs.  At D = 512, items whose rows see only
+//     one 64-key half of their tile run as a second launch over that half.
+//     Each item writes a float32 partial.
 //  3. a fixed-order reduction of the partials into dKV and dKV_comp, so the
 //     result is bitwise reproducible.
 #include <climits>
@@ -809,7 +811,6 @@ __global__ void __launch_bounds__(NW * 64, 1)
   // the first and last items of a sliding-window tile) run over the other
   // half only; each wave scores 16 keys, the gradient covers 4 key blocks,
   // and the idle half's partial is written as zeros.
-  {
   constexpr int KPW = HALF ? 1 : 2;  // 16-key score blocks per wave
   constexpr int NKB = 4 * KPW;       // active 16-key blocks of the item
   const int hh = HALF ? (it.halves == 2 ? 1 : 0) : 0;  // active half
@@ -994,7 +995,6 @@ __global__ void __launch_bounds__(NW * 64, 1)
       w.w = act ? acc[ka][dl][3] : 0.f;
       *reinterpret_cast<float4 *>(out + 16 * dl + 4 * g) = w;
     }
-  }
   }
 }
 

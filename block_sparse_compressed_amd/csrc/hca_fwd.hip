@@ -279,8 +279,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
 // NW = 8: 128 rows, one workgroup per CU, K and K^T double-buffered and one
 // tile apart (4 x 32 KiB), one barrier per tile, the S^T MFMAs of tile t+1
 // issued before the softmax and PV of tile t.
-// Tiles go global -> LDS directly (no VGPR staging), in swizzled layouts that
-// make every operand read conflict-free.
+// Tiles go global -> LDS directly (no VGPR staging) from the tile images, in
+// MFMA fragment order, so every operand read is a flat ds_read_b128.
 // ---------------------------------------------------------------------------
 // Lazy rescaling: a row's reference max m_run only moves when the tile max
 // exceeds it by more than kLazy (log2 units), so P = 2^(x - m_run) stays below
