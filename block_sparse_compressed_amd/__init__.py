@@ -30,7 +30,8 @@ HCA_TILE_EMPTY, HCA_TILE_PARTIAL, HCA_TILE_FULL = 0, 1, 2
 # Declared in include/hca.h; the ABI test checks the header and this list agree.
 EXPORTS = (
     "hca_block_mask_build", "hca_plan_get_info", "hca_plan_export_tiles",
-    "hca_plan_export_rows", "hca_plan_upload", "hca_plan_destroy", "hca_attn_fwd",
+    "hca_plan_export_rows", "hca_plan_export_items", "hca_plan_upload", "hca_plan_destroy",
+    "hca_attn_fwd",
     "hca_attn_bwd", "hca_timing_enable", "hca_timing_read", "hca_status_string",
     "hca_last_error",
 )
@@ -88,6 +89,8 @@ def _load_library():
     lib.hca_plan_export_tiles.restype = ctypes.c_int
     lib.hca_plan_export_rows.argtypes = [vp, vp]
     lib.hca_plan_export_rows.restype = ctypes.c_int
+    lib.hca_plan_export_items.argtypes = [vp, vp, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+    lib.hca_plan_export_items.restype = ctypes.c_int
     lib.hca_plan_upload.argtypes = [vp, vp, u64, vp]
     lib.hca_plan_upload.restype = ctypes.c_int
     lib.hca_plan_destroy.argtypes = [vp]
@@ -209,6 +212,17 @@ def hca_plan_export_rows(plan: Plan) -> np.ndarray:
     rows = np.empty((i.B, i.S, 3), dtype=np.int32)
     _check(_lib.hca_plan_export_rows(plan.handle, rows.ctypes.data))
     return rows
+
+
+def hca_plan_export_items(plan: Plan) -> np.ndarray:
+    """Key-stationary work items [n, 8] int64: batch row, kind, first key, keys per
+    item, first and last listed query tile, halves, partial-block offset."""
+    n = ctypes.c_int64(0)
+    _check(_lib.hca_plan_export_items(plan.handle, None, 0, ctypes.byref(n)))
+    items = np.empty((n.value, 8), dtype=np.int64)
+    _check(_lib.hca_plan_export_items(plan.handle, items.ctypes.data if items.size else None,
+                                      n.value, ctypes.byref(n)))
+    return items
 
 
 def _stream(stream):

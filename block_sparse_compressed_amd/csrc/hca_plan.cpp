@@ -554,4 +554,28 @@ extern "C" hca_status hca_plan_export_rows(const hca_plan *plan, int32_t *rows) 
   return HCA_OK;
 }
 
+extern "C" hca_status hca_plan_export_items(const hca_plan *plan, int64_t *items,
+                                            int64_t capacity, int64_t *count) {
+  if (!plan || !count || capacity < 0) {
+    set_error("hca_plan_export_items: NULL plan or count, or negative capacity");
+    return HCA_ERR_INVALID_ARG;
+  }
+  const int64_t n = (int64_t)plan->kvitem.size();
+  *count = n;
+  if (!items) return HCA_OK;
+  for (int64_t i = 0; i < std::min(n, capacity); ++i) {
+    const KvItem &it = plan->kvitem[i];
+    int64_t *o = items + i * 8;
+    o[0] = it.b;
+    o[1] = it.kind;
+    o[2] = (int64_t)it.kt * plan->kv_bk;
+    o[3] = plan->kv_bk;
+    o[4] = it.e1 > it.e0 ? (int64_t)(plan->kvent[it.e0] & kEntIdx) : -1;
+    o[5] = it.e1 > it.e0 ? (int64_t)(plan->kvent[it.e1 - 1] & kEntIdx) : -1;
+    o[6] = it.halves;
+    o[7] = it.part_off;
+  }
+  return HCA_OK;
+}
+
 extern "C" void hca_plan_destroy(hca_plan *plan) { delete plan; }

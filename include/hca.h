@@ -152,6 +152,20 @@ hca_status hca_plan_export_tiles(const hca_plan *plan, uint8_t *raw_states,
 hca_status hca_plan_export_rows(const hca_plan *plan, int32_t *rows);
 
 /*
+ * Key-stationary work items of the backward, for inspection.  *count
+ * receives the number of items; when `items` is not NULL, min(*count,
+ * capacity) rows of 8 int64 are written: batch row, kind (0 raw, 1
+ * compressed), first key, keys per item, first and last listed query tile,
+ * halves (bit 0 / bit 1 set when some row of the item sees a key of the lower
+ * / upper half of the item's keys; 3 whenever the item runs over all of them)
+ * and the element offset of the item's float32 partial block.  The items of
+ * one key tile are consecutive and own consecutive partial blocks.  Errors:
+ * HCA_ERR_INVALID_ARG on a NULL plan or count, or a negative capacity.
+ */
+hca_status hca_plan_export_items(const hca_plan *plan, int64_t *items, int64_t capacity,
+                                 int64_t *count);
+
+/*
  * Copies the plan's device image (schedule lists and per-position
  * intervals, info.device_bytes bytes) into the caller's device buffer with an
  * asynchronous copy on `hip_stream`, and records the buffer in the plan.  The

@@ -162,3 +162,74 @@ def test_schedule_is_consistent():
     assert info.device_bytes > 0 and info.ws_bwd_bytes > info.ws_fwd_bytes > 0
     # no device buffer is O(S^2): the plan image is linear in S
     assert info.device_bytes < 64 * wl.B * wl.S + 16 * (info.tiles_raw + info.tiles_comp) + 8192
+
+
+# --------------------------------------------------------------------------- #
+# key-stationary work items: visible halves and partial blocks
+# --------------------------------------------------------------------------- #
+
+def closed_form_intervals(S, r, W, lengths_row):
+    """Visible raw keys [lo, i] and entries [clo, chi) per position, written from
+    the definitions (contiguous documents, STRICT entries)."""
+    start = np.zeros(S, np.int64)
+    pos = 0
+    for L in (lengths_row or [S]):
+        start[pos:pos + L] = pos
+        pos += L
+    i = np.arange(S, dtype=np.int64)
+    lo = np.maximum(i - W + 1, start)
+    chi = (i + 1) // r
+    clo = np.minimum(-(-start // r), chi)
+    return lo, i + 1, clo, chi  # raw [lo, hi), comp [clo, chi)
+
+
+@pytest.mark.parametrize("lengths", [None, [[15000, 25000]]], ids=["one_doc", "two_docs"])
+def test_items_halves_and_partial_blocks(lengths):
+    """At S = 40000, H = 64, D = 512 the key-stationary backward has more than
+    2048 work items of 128 keys, so the planner marks items that see only one
+    64-key half of their tile.  Every item's mark must equal the halves that
+    its query tiles see, and the items of a key tile must own consecutive
+    partial blocks (the reduction relies on it)."""
+    S, H, D, r, W = 40000, 64, 512, 128, 128
+    plan, prob = build_both(1, S, H, D, r, W, lengths, hca.HCA_COMPSEG_STRICT)
+    info = hca.hca_plan_get_info(plan)
+    items = hca.hca_plan_export_items(plan)
+    assert len(items) >= 2048 and (items[:, 3] == 128).all()
+    lo, hi, clo, chi = closed_form_intervals(S, r, W, lengths[0] if lengths else None)
+    n_half = 0
+    for b, kind, k0, nk, qa, qz, halves, _ in items:
+        p = np.arange(qa * info.bq, min(S, (qz + 1) * info.bq))
+        a, z = (clo[p], chi[p]) if kind else (lo[p], hi[p])
+        nkeys = info.S_c if kind else S
+        mid, end = min(k0 + nk // 2, nkeys), min(k0 + nk, nkeys)
+        want = int((np.maximum(a, k0) < np.minimum(z, mid)).any()) | \
+            (int((np.maximum(a, mid) < np.minimum(z, end)).any()) << 1)
+        assert want != 0
+        assert halves == (3 if want == 3 else want), (kind, k0, qa, qz, halves, want)
+        n_half += halves != 3
+    assert n_half > 0  # first and last items of sliding-window tiles
+    # spot-check marked items against the oracle's element predicate
+    rng = np.random.default_rng(0)
+    half_items = items[items[:, 6] != 3]
+    for row in half_items[rng.choice(len(half_items), size=12, replace=False)]:
+        b, kind, k0, nk, qa, qz, halves, _ = (int(x) for x in row)
+        idle = range(k0 + nk // 2, k0 + nk) if halves == 1 else range(k0, k0 + nk // 2)
+        vis = oracle.vis_comp if kind else oracle.vis_raw
+        nkeys = info.S_c if kind else S
+        for i in range(qa * info.bq, min(S, (qz + 1) * info.bq)):
+            assert not any(vis(prob, b, i, t) for t in idle if t < nkeys)
+    # consecutive partial blocks per key tile
+    blk = 128 * D
+    for g0 in range(1, len(items)):
+        prev, cur = items[g0 - 1], items[g0]
+        if tuple(prev[:3]) == tuple(cur[:3]):
+            assert cur[7] == prev[7] + blk
+    assert len({tuple(x) for x in items[:, [0, 1, 2]]}) == \
+        sum(1 for g0 in range(len(items)) if g0 == 0 or tuple(items[g0 - 1, :3]) != tuple(items[g0, :3]))
+
+
+def test_items_small_problem_runs_whole_tiles():
+    """Below 8 items per CU every item runs over all keys of its tile."""
+    plan, _ = build_both(1, 16384, 64, 512, 128, 128, None, hca.HCA_COMPSEG_STRICT)
+    items = hca.hca_plan_export_items(plan)
+    assert 0 < len(items) < 2048 and (items[:, 6] == 3).all()
