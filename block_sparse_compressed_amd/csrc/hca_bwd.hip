@@ -294,197 +294,236 @@ __global__ void __launch_bounds__(NW * 64, 1)
   // two neighbouring tiles run back to back on one XCD.
   const int nslices = d.bq * d.H / M;
   const int lbq = __builtin_ctz(d.bq);
-  const int u = xcd_remap(blockIdx.x, d.B * d.nqt * nslices, 2 * nslices);
-  const int li = u / nslices, sl = u - li * nslices;
-  const int item = p.qorder[li];
-  const int b = item / d.nqt, qt = item - b * d.nqt;
-
-  const int rho = sl * M + wave * 16 + j;
-  const int pos = qt * d.bq + (rho & (d.bq - 1)), hh = rho >> lbq;
-  const bool valid = pos < d.S;
-  const size_t row = ((size_t)b * d.H + hh) * d.S + pos;
-  // Padded rows (pos >= S) read a real row and are zeroed / masked below:
-  // every prologue load is unconditional, so none of them waits for another.
-  const size_t rowc = ((size_t)b * d.H + hh) * d.S + min(pos, d.S - 1);
-  int rlo = INT_MAX, clo = 0, chi = 0;
-  float lse2 = -INFINITY;
-  bf16x8 qf[KS], dof[KS];
-  float dl;
-
-  // The list entries are needed for the first tile copies: load them first
-  // and wait for them once, before any copy is in flight.
-  const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
-  const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
-  __builtin_amdgcn_s_waitcnt(0);
-  auto entry = [&](int t) -> uint32_t {
-    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
-                  : uniform_load(p.qent, e_begin + t);
-  };
-  // K and K^T tiles come from the tile images (kvt, kvct) that the image
-  // kernel wrote at the start of the call.
-  const rsrc_t r_img =
-      make_rsrc(kvt + (size_t)b * 2 * D * d.S_pad, (uint32_t)d.S_pad * D * 4);
-  const rsrc_t r_imgc =
-      make_rsrc(kvct + (size_t)b * 2 * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 4);
-  auto stage_k = [&](int t) {  // K of list entry t
-    if (t >= nent) return;
-    const uint32_t ent = entry(t);
-    stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 0,
-                     kbase + (t & 1) * kTileBytes512, wave, lane);
-  };
-  auto stage_t = [&](int t) {  // K^T of list entry t
-    if (t >= nent) return;
-    const uint32_t ent = entry(t);
-    stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 1,
-                     tbase + (t & 1) * kTileBytes512, wave, lane);
-  };
-
+  const int nunits = d.B * d.nqt * nslices;
   // Operand reads are flat: lane l reads bytes 16 l .. 16 l + 15 of a block.
   const int frag_off = 16 * lane;
 
-  // S^T and dP^T of tile t (shared K A-operands): [0] keys 0-15, [1] keys 16-31.
-  // Operand fragments are read PF k-steps ahead of their MFMAs.
-  auto sdp = [&](int t, floatx4 (&s)[2], floatx4 (&dp)[2]) {
-    constexpr int PF = 3;
-    const char *kb = kbase + (t & 1) * kTileBytes512;
-    s[0] = s[1] = dp[0] = dp[1] = floatx4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 a0[KS], a1[KS];
-    auto at = [&](int ks) { return kb + 2048 * ks + frag_off; };
-#pragma unroll
-    for (int ks = 0; ks < PF; ++ks) {
-      a0[ks] = lds_frag(at(ks));
-      a1[ks] = lds_frag(at(ks) + 1024);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) {
-        a0[ks + PF] = lds_frag(at(ks + PF));
-        a1[ks + PF] = lds_frag(at(ks + PF) + 1024);
-      }
-      s[0] = mfma16x16x32(a0[ks], qf[ks], s[0]);
-      s[1] = mfma16x16x32(a1[ks], qf[ks], s[1]);
-      dp[0] = mfma16x16x32(a0[ks], dof[ks], dp[0]);
-      dp[1] = mfma16x16x32(a1[ks], dof[ks], dp[1]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < PF; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    }
+  // Persistent: workgroup w takes units w, w + G, w + 2G, ... (G = grid size, a
+  // multiple of 8, so all of them run on w's XCD), each one slice of M rows of
+  // a query tile.  While a unit works on its last key tile its Q and dO rows
+  // are dead, so the next unit's list entries and rows are loaded then.
+  int sl = 0, item = 0, e_begin = 0, nent = 0;
+  uint32_t ent_lane = 0u;
+  int4 rw;
+  float lv;
+  uint4 qv[KS], dv[KS], ov[KS];
+  auto locate = [&](int v, int &sl_, int &item_) {
+    const int u = xcd_remap(v, nunits, 2 * nslices);
+    const int li = u / nslices;
+    sl_ = u - li * nslices;
+    item_ = p.qorder[li];
   };
-
-  floatx4 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // First tile copies go out before the row loads, so the two latencies overlap.
-  stage_k(0);
-  stage_k(1);
-  stage_t(0);
-  {
-    const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + min(pos, d.S - 1)];
-    const float lv = lse[rowc];
-    uint4 qv[KS], dv[KS], ov[KS];
+  // Issues the loads of a unit's list entries and rows (entries first); no wait.
+  // Padded rows (pos >= S) read a real row and are zeroed / masked later, so
+  // every load is unconditional.
+  auto fetch = [&](int sl_, int item_) {
+    e_begin = p.qptr[item_];
+    nent = p.qptr[item_ + 1] - e_begin;
+    ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
+    const int b_ = item_ / d.nqt, qt_ = item_ - b_ * d.nqt;
+    const int rho = sl_ * M + wave * 16 + j;
+    const int pos_ = min(qt_ * d.bq + (rho & (d.bq - 1)), d.S - 1), hh_ = rho >> lbq;
+    const size_t rowc = ((size_t)b_ * d.H + hh_) * d.S + pos_;
+    rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b_ * d.S + pos_];
+    lv = lse[rowc];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qv[ks] = *reinterpret_cast<const uint4 *>(q + rowc * D + 32 * ks + 8 * g);
       dv[ks] = *reinterpret_cast<const uint4 *>(dout + rowc * D + 32 * ks + 8 * g);
       ov[ks] = *reinterpret_cast<const uint4 *>(o + rowc * D + 32 * ks + 8 * g);
     }
+  };
+
+  int v = blockIdx.x;
+  locate(v, sl, item);
+  fetch(sl, item);
+  for (;;) {
+    const int b = item / d.nqt, qt = item - b * d.nqt;
+    const int rho = sl * M + wave * 16 + j;
+    const int pos = qt * d.bq + (rho & (d.bq - 1)), hh = rho >> lbq;
+    const bool valid = pos < d.S;
+    const size_t row = ((size_t)b * d.H + hh) * d.S + pos;
+    const int vn = v + (int)gridDim.x;
+    const bool more = vn < nunits;
+    // Past the last unit the current one is fetched again (unused), so the
+    // row registers are always reloaded and never kept live across a unit.
+    int sl_n = sl, item_n = item;
+    if (more) locate(vn, sl_n, item_n);
+
+    auto entry = [&](int t) -> uint32_t {
+      return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
+                    : uniform_load(p.qent, e_begin + t);
+    };
+    // K and K^T tiles come from the tile images (kvt, kvct) that the image
+    // kernel wrote at the start of the call.
+    const rsrc_t r_img =
+        make_rsrc(kvt + (size_t)b * 2 * D * d.S_pad, (uint32_t)d.S_pad * D * 4);
+    const rsrc_t r_imgc =
+        make_rsrc(kvct + (size_t)b * 2 * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 4);
+    auto stage_k = [&](int t) {  // K of list entry t
+      if (t >= nent) return;
+      const uint32_t ent = entry(t);
+      stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 0,
+                       kbase + (t & 1) * kTileBytes512, wave, lane);
+    };
+    auto stage_t = [&](int t) {  // K^T of list entry t
+      if (t >= nent) return;
+      const uint32_t ent = entry(t);
+      stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 1,
+                       tbase + (t & 1) * kTileBytes512, wave, lane);
+    };
+
+    // S^T and dP^T of tile t (shared K A-operands): [0] keys 0-15, [1] keys 16-31.
+    // Operand fragments are read PF k-steps ahead of their MFMAs.
+    auto sdp = [&](int t, floatx4 (&s)[2], floatx4 (&dp)[2]) {
+      constexpr int PF = 3;
+      const char *kb = kbase + (t & 1) * kTileBytes512;
+      s[0] = s[1] = dp[0] = dp[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 a0[KS], a1[KS];
+      auto at = [&](int ks) { return kb + 2048 * ks + frag_off; };
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) {
+        a0[ks] = lds_frag(at(ks));
+        a1[ks] = lds_frag(at(ks) + 1024);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) {
+          a0[ks + PF] = lds_frag(at(ks + PF));
+          a1[ks + PF] = lds_frag(at(ks + PF) + 1024);
+        }
+        s[0] = mfma16x16x32(a0[ks], as_bf16x8(qv[ks]), s[0]);
+        s[1] = mfma16x16x32(a1[ks], as_bf16x8(qv[ks]), s[1]);
+        dp[0] = mfma16x16x32(a0[ks], as_bf16x8(dv[ks]), dp[0]);
+        dp[1] = mfma16x16x32(a1[ks], as_bf16x8(dv[ks]), dp[1]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+    };
+
+    // The first tile copies need only the list entries (loaded before the rows).
+    stage_k(0);
+    stage_k(1);
+    stage_t(0);
+    wait_all_loads();
     // A padded row keeps the clamped row's data: its key interval is empty
     // (and a tile holding it is never FULL), so its P and dS are zero, and its
     // dQ and delta are never stored.
     float part = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = as_bf16x8(qv[ks]);
-      dof[ks] = as_bf16x8(dv[ks]);
-      part += dot8(dv[ks], ov[ks]);
-    }
-    dl = group_sum(part);
-    rlo = valid ? rw.x : INT_MAX;
-    clo = valid ? rw.y : 0;
-    chi = valid ? rw.z : 0;
-    lse2 = valid ? lv * kLog2e : -INFINITY;
+    for (int ks = 0; ks < KS; ++ks) part += dot8(dv[ks], ov[ks]);
+    const float dl = group_sum(part);
+    const int rlo = valid ? rw.x : INT_MAX;
+    const int clo = valid ? rw.y : 0;
+    const int chi = valid ? rw.z : 0;
+    const float lse2 = valid ? lv * kLog2e : -INFINITY;
     if (valid && g == 0) delta[row] = dl;
-  }
-  wait_all_loads();
-  __syncthreads();
-  floatx4 sc[2], pc[2];
-  if (nent > 0) sdp(0, sc, pc);
-  __syncthreads();
-  stage_k(2);
-  stage_t(1);
-
-  // List entries are read only right after the barrier (where a wait for a
-  // scalar load costs nothing): ent holds the entry of the current tile.
-  uint32_t ent = nent > 0 ? entry(0) : 0u;
-  for (int it = 0; it < nent; ++it) {
-    floatx4 sn[2], pn[2];
-    if (it + 1 < nent) sdp(it + 1, sn, pn);
-
-    const bool comp = ent & kEntComp;
-    const int k0 = (int)(ent & kEntIdx) * kBK;
-    float x[8];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      x[v] = sc[0][v] * scale_log2 - lse2;
-      x[4 + v] = sc[1][v] * scale_log2 - lse2;
-    }
-    if (!(ent & kEntFull)) {
-      const int lo = (comp ? clo : rlo) - (k0 + 8 * g);
-      const int hi = (comp ? chi : pos + 1) - (k0 + 8 * g);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      x[v] = fast_exp2(x[v]) * (pc[0][v] - dl);
-      x[4 + v] = fast_exp2(x[4 + v]) * (pc[1][v] - dl);
-    }
-    const bf16x8 dsb = pack8(x);
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      // dQ^T += K^T dS^T: fragments read PV column blocks ahead.
-      constexpr int PV = 8;
-      const char *tb = tbase + (it & 1) * kTileBytes512 + frag_off;
-      bf16x8 kt[DB];
-#pragma unroll
-      for (int db = 0; db < PV; ++db) kt[db] = lds_frag(tb + db * 1024);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        if (db + PV < DB) kt[db + PV] = lds_frag(tb + (db + PV) * 1024);
-        acc[db] = mfma16x16x32(kt[db], dsb, acc[db]);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, PV, 0);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        if (db + PV < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    sc[0] = sn[0];
-    sc[1] = sn[1];
-    pc[0] = pn[0];
-    pc[1] = pn[1];
-    wait_all_loads();
     __syncthreads();
-    if (it + 1 < nent) ent = entry(it + 1);
-    stage_k(it + 3);
-    stage_t(it + 2);
-  }
 
-  // The tile buffers are free (the loop ended on a barrier with no copy in
-  // flight): each wave stages its 16 rows of dQ there and stores whole rows.
-  store_rows512(acc, scale, smem + wave * 16384, lane, [&](int r) -> bf16raw * {
-    const int rr = sl * M + wave * 16 + r;
-    const int pr = qt * d.bq + (rr & (d.bq - 1)), hr = rr >> lbq;
-    return pr < d.S ? dq + (((size_t)b * d.H + hr) * d.S + pr) * D : nullptr;
-  });
+    floatx4 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 sc[2], pc[2];
+    if (nent > 0) sdp(0, sc, pc);
+    __syncthreads();
+    stage_k(2);
+    stage_t(1);
+
+    // dS of tile it from its scores, then dQ^T += K^T dS^T.
+    auto grad = [&](int it, uint32_t ent) {
+      const bool comp = ent & kEntComp;
+      const int k0 = (int)(ent & kEntIdx) * kBK;
+      float x[8];
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        x[v4] = sc[0][v4] * scale_log2 - lse2;
+        x[4 + v4] = sc[1][v4] * scale_log2 - lse2;
+      }
+      if (!(ent & kEntFull)) {
+        const int lo = (comp ? clo : rlo) - (k0 + 8 * g);
+        const int hi = (comp ? chi : pos + 1) - (k0 + 8 * g);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
+      }
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        x[v4] = fast_exp2(x[v4]) * (pc[0][v4] - dl);
+        x[4 + v4] = fast_exp2(x[4 + v4]) * (pc[1][v4] - dl);
+      }
+      const bf16x8 dsb = pack8(x);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        // Fragments read PV column blocks ahead.
+        constexpr int PV = 8;
+        const char *tb = tbase + (it & 1) * kTileBytes512 + frag_off;
+        bf16x8 kt[DB];
+#pragma unroll
+        for (int db = 0; db < PV; ++db) kt[db] = lds_frag(tb + db * 1024);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          if (db + PV < DB) kt[db + PV] = lds_frag(tb + (db + PV) * 1024);
+          acc[db] = mfma16x16x32(kt[db], dsb, acc[db]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, PV, 0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          if (db + PV < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // List entries are read only right after the barrier (where a wait for a
+    // scalar load costs nothing): ent holds the entry of the current tile.
+    uint32_t ent = nent > 0 ? entry(0) : 0u;
+    const int last = nent - 1;
+    for (int it = 0; it < last; ++it) {
+      floatx4 sn[2], pn[2];
+      sdp(it + 1, sn, pn);
+      grad(it, ent);
+      sc[0] = sn[0];
+      sc[1] = sn[1];
+      pc[0] = pn[0];
+      pc[1] = pn[1];
+      wait_all_loads();
+      __syncthreads();
+      ent = entry(it + 1);
+      stage_k(it + 3);
+      stage_t(it + 2);
+    }
+    // The next unit's entries and rows load under the last tile and the store.
+    fetch(sl_n, item_n);
+    if (last >= 0) grad(last, ent);
+
+    // No copy is in flight and no wave reads the K buffers any more (the last
+    // tile reads only its K^T buffer): each wave stages its 16 rows of dQ there
+    // and stores whole rows.
+    // The store's LDS addresses depend on the lane only; an opaque copy of the
+    // lane keeps the compiler from hoisting all 32 of them out of the unit loop
+    // (they would be spilled, and every reload waits for the rows in flight).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    store_rows512(acc, scale, smem + wave * 16384, ln, [&](int r) -> bf16raw * {
+      const int rr = sl * M + wave * 16 + r;
+      const int pr = qt * d.bq + (rr & (d.bq - 1)), hr = rr >> lbq;
+      return pr < d.S ? dq + (((size_t)b * d.H + hr) * d.S + pr) * D : nullptr;
+    });
+    if (!more) {
+      wait_all_loads();
+      break;
+    }
+    // Every wave's staged rows are read before the next unit's copies land.
+    lds_barrier();
+    v = vn;
+    sl = sl_n;
+    item = item_n;
+  }
 }
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -1070,23 +1109,45 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Compute units of the current device rounded down to a multiple of 8 (the
+// XCD count), cached per device; 0 if the device cannot be queried.
+static int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n >= 8 ? n / 8 * 8 : 8;
+  }
+  return cached[dev];
+}
+
 int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
                        const void *kvc, const void *kvt, const void *kvct, const void *o,
                        const float *lse, const void *dout, float scale, void *dq, float *delta,
                        void *stream) {
   hipStream_t s = (hipStream_t)stream;
   const float sl2 = scale * kLog2e;
-  auto go = [&](auto kernel, int nw, int m) {
-    const dim3 grid(d.B * d.nqt * (d.bq * d.H / m));
-    hipLaunchKernelGGL(kernel, grid, dim3(nw * 64), 0, s, d, p, (const bf16raw *)q,
+  auto go = [&](auto kernel, int nw, int groups) {
+    hipLaunchKernelGGL(kernel, dim3(groups), dim3(nw * 64), 0, s, d, p, (const bf16raw *)q,
                        (const bf16raw *)kv, (const bf16raw *)kvc, (const bf16raw *)kvt,
                        (const bf16raw *)kvct, (const bf16raw *)o, lse, (const bf16raw *)dout, sl2,
                        scale, (bf16raw *)dq, delta);
   };
   switch (d.D) {
-    case 512: go(hca_bwd_dq512_kernel<4>, 4, 64); break;
-    case 128: go(hca_bwd_dq_kernel<128, 8, 1>, 8, 128); break;
-    case 64: go(hca_bwd_dq_kernel<64, 8, 1>, 8, 128); break;
+    case 512: {
+      // Persistent: one workgroup per compute unit (each takes 128 KiB of
+      // LDS), a multiple of 8 of them so every workgroup stays on one XCD.
+      const int units = d.B * d.nqt * (d.bq * d.H / 64);
+      const int cus = compute_units();
+      if (cus <= 0) return (int)hipErrorInvalidDevice;
+      go(hca_bwd_dq512_kernel<4>, 4, units < cus ? units : cus);
+      break;
+    }
+    case 128: go(hca_bwd_dq_kernel<128, 8, 1>, 8, d.B * d.nqt * (d.bq * d.H / 128)); break;
+    case 64: go(hca_bwd_dq_kernel<64, 8, 1>, 8, d.B * d.nqt * (d.bq * d.H / 128)); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
