@@ -314,23 +314,28 @@ __global__ void __launch_bounds__(NW * 64, 1)
     item_ = p.qorder[li];
   };
   // Issues the loads of a unit's list entries and rows (entries first); no wait.
-  // Padded rows (pos >= S) read a real row and are zeroed / masked later, so
-  // every load is unconditional.
+  // A wave's 16 rows are 16 consecutive positions of one head (bq >= 16), so
+  // each tensor is addressed from one wave-uniform row base plus a small
+  // per-lane offset.  Padded rows (pos >= S) read row S - 1 and are zeroed /
+  // masked later, so every load is unconditional.
   auto fetch = [&](int sl_, int item_) {
     e_begin = p.qptr[item_];
     nent = p.qptr[item_ + 1] - e_begin;
     ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
     const int b_ = item_ / d.nqt, qt_ = item_ - b_ * d.nqt;
-    const int rho = sl_ * M + wave * 16 + j;
-    const int pos_ = min(qt_ * d.bq + (rho & (d.bq - 1)), d.S - 1), hh_ = rho >> lbq;
-    const size_t rowc = ((size_t)b_ * d.H + hh_) * d.S + pos_;
-    rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b_ * d.S + pos_];
-    lv = lse[rowc];
+    const int rho0 = sl_ * M + wave * 16;
+    const int pos0 = qt_ * d.bq + (rho0 & (d.bq - 1)), hh_ = rho0 >> lbq;
+    const int jr = min(j, d.S - 1 - pos0);  // this lane's row within the wave
+    const size_t r0 = ((size_t)b_ * d.H + hh_) * d.S + pos0;
+    rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b_ * d.S + pos0 + jr];
+    lv = lse[r0 + jr];
+    const bf16raw *qb = q + r0 * D, *db_ = dout + r0 * D, *ob = o + r0 * D;
+    const int loff = jr * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qv[ks] = *reinterpret_cast<const uint4 *>(q + rowc * D + 32 * ks + 8 * g);
-      dv[ks] = *reinterpret_cast<const uint4 *>(dout + rowc * D + 32 * ks + 8 * g);
-      ov[ks] = *reinterpret_cast<const uint4 *>(o + rowc * D + 32 * ks + 8 * g);
+      qv[ks] = *reinterpret_cast<const uint4 *>(qb + loff + 32 * ks);
+      dv[ks] = *reinterpret_cast<const uint4 *>(db_ + loff + 32 * ks);
+      ov[ks] = *reinterpret_cast<const uint4 *>(ob + loff + 32 * ks);
     }
   };
 
@@ -483,7 +488,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     // scalar load costs nothing): ent holds the entry of the current tile.
     uint32_t ent = nent > 0 ? entry(0) : 0u;
     const int last = nent - 1;
-    for (int it = 0; it < last; ++it) {
+    for (int it = 0; it + 1 < last; ++it) {
       floatx4 sn[2], pn[2];
       sdp(it + 1, sn, pn);
       grad(it, ent);
@@ -497,8 +502,30 @@ __global__ void __launch_bounds__(NW * 64, 1)
       stage_k(it + 3);
       stage_t(it + 2);
     }
-    // The next unit's entries and rows load under the last tile and the store.
+    // Once the last tile's scores are taken this unit's Q and dO rows are
+    // dead: the next unit's entries and rows load from there on, under the
+    // last two tiles and the store (one fetch site, so the loaded registers
+    // need no copies that would wait for them).
+    floatx4 sn[2], pn[2];
+    uint32_t ent_last = 0u;
+    if (last >= 1) {
+      ent_last = entry(last);  // before the fetch replaces the entries
+      sdp(last, sn, pn);
+    }
     fetch(sl_n, item_n);
+    if (last >= 1) {
+      grad(last - 1, ent);
+      sc[0] = sn[0];
+      sc[1] = sn[1];
+      pc[0] = pn[0];
+      pc[1] = pn[1];
+      // The last K^T copy was issued before the fetch; loads complete in
+      // issue order, so leaving the 48 row loads (issued last) outstanding
+      // still waits for it.  The barrier orders LDS only.
+      asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+      lds_barrier();
+      ent = ent_last;
+    }
     if (last >= 0) grad(last, ent);
 
     // No copy is in flight and no wave reads the K buffers any more (the last
