@@ -307,20 +307,23 @@ __global__ void __launch_bounds__(NW * 64, 1)
   int4 rw;
   float lv;
   uint4 qv[KS], dv[KS], ov[KS];
-  auto locate = [&](int v, int &sl_, int &item_) {
+  // Unit v's slice, query tile and list extent, from scalar loads.
+  auto locate = [&](int v, int &sl_, int &item_, int &e_begin_, int &nent_) {
     const int u = xcd_remap(v, nunits, 2 * nslices);
     const int li = u / nslices;
     sl_ = u - li * nslices;
-    item_ = p.qorder[li];
+    item_ = (int)uniform_load((const uint32_t *)p.qorder, li);
+    e_begin_ = (int)uniform_load((const uint32_t *)p.qptr, item_);
+    nent_ = (int)uniform_load((const uint32_t *)p.qptr, item_ + 1) - e_begin_;
   };
   // Issues the loads of a unit's list entries and rows (entries first); no wait.
   // A wave's 16 rows are 16 consecutive positions of one head (bq >= 16), so
   // each tensor is addressed from one wave-uniform row base plus a small
   // per-lane offset.  Padded rows (pos >= S) read row S - 1 and are zeroed /
   // masked later, so every load is unconditional.
-  auto fetch = [&](int sl_, int item_) {
-    e_begin = p.qptr[item_];
-    nent = p.qptr[item_ + 1] - e_begin;
+  auto fetch = [&](int sl_, int item_, int e_begin_, int nent_) {
+    e_begin = e_begin_;
+    nent = nent_;
     ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
     const int b_ = item_ / d.nqt, qt_ = item_ - b_ * d.nqt;
     const int rho0 = sl_ * M + wave * 16;
@@ -340,8 +343,11 @@ __global__ void __launch_bounds__(NW * 64, 1)
   };
 
   int v = blockIdx.x;
-  locate(v, sl, item);
-  fetch(sl, item);
+  {
+    int e0, n0;
+    locate(v, sl, item, e0, n0);
+    fetch(sl, item, e0, n0);
+  }
   for (;;) {
     const int b = item / d.nqt, qt = item - b * d.nqt;
     const int rho = sl * M + wave * 16 + j;
@@ -350,10 +356,6 @@ __global__ void __launch_bounds__(NW * 64, 1)
     const size_t row = ((size_t)b * d.H + hh) * d.S + pos;
     const int vn = v + (int)gridDim.x;
     const bool more = vn < nunits;
-    // Past the last unit the current one is fetched again (unused), so the
-    // row registers are always reloaded and never kept live across a unit.
-    int sl_n = sl, item_n = item;
-    if (more) locate(vn, sl_n, item_n);
 
     auto entry = [&](int t) -> uint32_t {
       return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
@@ -415,6 +417,10 @@ __global__ void __launch_bounds__(NW * 64, 1)
     stage_k(0);
     stage_k(1);
     stage_t(0);
+    // Past the last unit the current one is fetched again (unused), so the
+    // row registers are always reloaded and never kept live across a unit.
+    int sl_n = sl, item_n = item, e_begin_n = e_begin, nent_n = nent;
+    if (more) locate(vn, sl_n, item_n, e_begin_n, nent_n);
     wait_all_loads();
     // A padded row keeps the clamped row's data: its key interval is empty
     // (and a tile holding it is never FULL), so its P and dS are zero, and its
@@ -512,7 +518,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
       ent_last = entry(last);  // before the fetch replaces the entries
       sdp(last, sn, pn);
     }
-    fetch(sl_n, item_n);
+    fetch(sl_n, item_n, e_begin_n, nent_n);
     if (last >= 1) {
       grad(last - 1, ent);
       sc[0] = sn[0];
