@@ -167,6 +167,19 @@ def test_rows_without_keys_give_zero_and_neg_inf():
     check_full(case, (o, lse, dq, dkv, dkvc))
 
 
+def test_query_tile_without_keys_d512():
+    """D = 512, compressed keys only with r = 32: positions 0-30 see nothing, so
+    the first 16-position query tile has an empty list while the other 37 do
+    not; 608 row slices of 64 rows, more than one per compute unit, so
+    workgroups that handle the empty tile go on to later ones."""
+    case = Case(1, 600, 64, 512, 32, 0, "bf16", seed=6)
+    o, lse, dq, dkv, dkvc = case.run()
+    assert torch.isneginf(lse[0, :, :31]).all()
+    assert (o[0, :, :31] == 0).all() and (dq[0, :, :31] == 0).all()
+    assert (dkv == 0).all()
+    check_full(case, (o, lse, dq, dkv, dkvc))
+
+
 def test_tiny_fp32_workload_every_element():
     wl = WORKLOADS[1]
     case = Case(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, wl.dtype, doc_lengths(wl), seed=wl.seed)
