@@ -10,8 +10,8 @@
 //
 // Three kernels, all driven by the host-built block table:
 //  1. query-stationary dQ: same tiling and key-tile walk as the forward; the
-//     row's Q and dO fragments stay in VGPRs, delta is computed in the
-//     prologue from O and dO, and dQ is accumulated in registers and written
+//     row's Q and dO fragments stay in VGPRs, delta is computed from O and dO
+//     before the tile walk, and dQ is accumulated in registers and written
 //     once -- no atomics (the page on the static mask compiles the backward with
 //     an on-chip dQ reduction; here the whole dQ row stays on chip).
 //  2. key-stationary dKV: a workgroup owns one work item -- a key tile (raw
@@ -22,6 +22,7 @@
 //     Each item writes a float32 partial.
 //  3. a fixed-order reduction of the partials into dKV and dKV_comp, so the
 //     result is bitwise reproducible.
+#include <atomic>
 #include <climits>
 
 #include "hca_device.h"
@@ -266,11 +267,13 @@ __global__ void __launch_bounds__(NW * 64, 1)
 
 // ---------------------------------------------------------------------------
 // 1b. dQ (+ delta) at D = 512: NW waves x 16 rows, one wave per SIMD (Q, dO
-//     and the dQ accumulator take ~260 registers).  Same staging as the
-//     forward: K and K^T tiles double-buffered in LDS one tile apart, filled
-//     by buffer-to-LDS loads in conflict-free swizzled layouts, one barrier per
-//     tile.  The S^T and dP^T products of tile t+1 share their K A-operands and
-//     are issued before dS and the dQ product of tile t, so VALU work overlaps
+//     and the dQ accumulator take ~260 registers), persistent: one workgroup
+//     per compute unit walks 64-row slices, loading the next slice's list
+//     entries and rows under its current slice's last two tiles.  K and K^T
+//     tiles double-buffered in LDS one tile apart, copied from the tile images
+//     by buffer-to-LDS loads in MFMA fragment order, one barrier per tile.
+//     The S^T and dP^T products of tile t+1 share their K A-operands and are
+//     issued before dS and the dQ product of tile t, so VALU work overlaps
 //     matrix-core work.
 // ---------------------------------------------------------------------------
 template <int NW>
@@ -1143,18 +1146,20 @@ __global__ void __launch_bounds__(256)
 }
 
 // Compute units of the current device rounded down to a multiple of 8 (the
-// XCD count), cached per device; 0 if the device cannot be queried.
+// XCD count), cached per device (threads that race store the same value); 0
+// if the device cannot be queried.
 static int compute_units() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    cached[dev] = n >= 8 ? n / 8 * 8 : 8;
+    n = n >= 8 ? n / 8 * 8 : 8;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
