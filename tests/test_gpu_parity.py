@@ -132,6 +132,8 @@ SMALL = [
     (1, 150, 4, 512, 32, 64, "bf16", "random", 0),
     # more 64-row slices (1104) than CUs: persistent dQ workgroups walk several
     (1, 1100, 64, 512, 16, 64, "bf16", [[300, 800]], 0),
+    # two batch entries at D = 512 (608 slices), packed documents
+    (2, 600, 32, 512, 16, 48, "bf16", "random", 0),
 ]
 
 
