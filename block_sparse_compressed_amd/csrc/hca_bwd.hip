@@ -331,7 +331,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
     const int b_ = item_ / d.nqt, qt_ = item_ - b_ * d.nqt;
     const int rho0 = sl_ * M + wave * 16;
     const int pos0 = qt_ * d.bq + (rho0 & (d.bq - 1)), hh_ = rho0 >> lbq;
-    const int jr = min(j, d.S - 1 - pos0);  // this lane's row within the wave
+    // this lane's row relative to pos0, clamped to row S - 1 (negative when
+    // the whole 16-row block lies past S, as in the last tile when bq = 32)
+    const int jr = min(j, d.S - 1 - pos0);
     const size_t r0 = ((size_t)b_ * d.H + hh_) * d.S + pos0;
     rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b_ * d.S + pos0 + jr];
     lv = lse[r0 + jr];

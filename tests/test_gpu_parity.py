@@ -130,6 +130,8 @@ SMALL = [
     (1, 250, 8, 512, 16, 40, "bf16", None, 0),
     (1, 100, 128, 512, 8, 30, "bf16", [[40, 60]], 1),
     (1, 150, 4, 512, 32, 64, "bf16", "random", 0),
+    # 32 x 4 tiles with S = 130: the last tile's second 16-position block is all padding
+    (1, 130, 4, 512, 32, 64, "bf16", None, 0),
     # more 64-row slices (1104) than CUs: persistent dQ workgroups walk several
     (1, 1100, 64, 512, 16, 64, "bf16", [[300, 800]], 0),
     # two batch entries at D = 512 (608 slices), packed documents
