@@ -23,7 +23,7 @@ import os
 import sys
 import time
 
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector ALU, published
 PEAK_HBM_GBS = 8000.0
 

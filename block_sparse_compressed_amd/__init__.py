@@ -52,7 +52,8 @@ class HcaUnsupported(HcaError, NotImplementedError):
 
 
 class _TileCfg(ctypes.Structure):
-    _fields_ = [("bq", ctypes.c_int32), ("bk_raw", ctypes.c_int32), ("bk_comp", ctypes.c_int32)]
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "bq", "bk_raw", "bk_comp", "half_items_min", "comp_item_chunks")]
 
 
 class _PlanInfo(ctypes.Structure):
@@ -60,7 +61,9 @@ class _PlanInfo(ctypes.Structure):
         "B", "S", "H", "D", "r", "W", "S_c", "dtype", "comp_mode", "bq", "bk_raw", "bk_comp",
         "nqt", "nkt_raw", "nkt_comp", "kernel_ok")] + [(n, ctypes.c_int64) for n in (
         "tiles_raw", "tiles_comp", "full_raw", "full_comp", "pairs_raw", "pairs_comp")] + [
-        (n, ctypes.c_uint64) for n in ("device_bytes", "ws_fwd_bytes", "ws_bwd_bytes")]
+        (n, ctypes.c_uint64) for n in ("device_bytes", "ws_fwd_bytes", "ws_bwd_bytes")] + [
+        (n, ctypes.c_int64) for n in ("items", "items_half", "part_blocks")] + [
+        (n, ctypes.c_int32) for n in ("comp_item_chunks", "reserved_")]
 
 
 class _KernelTime(ctypes.Structure):
@@ -145,6 +148,7 @@ class PlanInfo:
     tiles_raw: int; tiles_comp: int; full_raw: int; full_comp: int
     pairs_raw: int; pairs_comp: int
     device_bytes: int; ws_fwd_bytes: int; ws_bwd_bytes: int
+    items: int; items_half: int; part_blocks: int; comp_item_chunks: int; reserved_: int
 
 
 class Plan:
@@ -177,10 +181,12 @@ def _i32(a: Optional[Sequence[int]]):
 
 def hca_block_mask_build(B, S, r, W, S_c, seg_starts=None, seg_counts=None, H=1, D=64,
                          dtype=HCA_BF16, mode=HCA_COMPSEG_STRICT, tiles=None) -> Plan:
+    """tiles: None or (bq, bk_raw, bk_comp[, half_items_min[, comp_item_chunks]]),
+    0 = library choice (see hca_tile_cfg in include/hca.h)."""
     starts, counts = _i32(seg_starts), _i32(seg_counts)
     cfg = None
     if tiles is not None:
-        cfg = _TileCfg(*tiles)
+        cfg = _TileCfg(*(tuple(tiles) + (0,) * (5 - len(tiles))))
     out = ctypes.c_void_p()
     _check(_lib.hca_block_mask_build(
         B, S, r, W, S_c,
@@ -336,10 +342,11 @@ class HcaAttention:
         self.device = torch.device(device)
         buf = torch.empty(max(1, self.info.device_bytes), dtype=torch.uint8, device=self.device)
         hca_plan_upload(self.plan, buf)
-        self.ws_fwd = torch.empty(max(16, self.info.ws_fwd_bytes), dtype=torch.uint8,
-                                  device=self.device)
-        self.ws_bwd = torch.empty(max(16, self.info.ws_bwd_bytes), dtype=torch.uint8,
-                                  device=self.device)
+        # One workspace serves both passes: the backward's layout starts with the
+        # forward's (ws_bwd_bytes >= ws_fwd_bytes), and the calls run in turn on
+        # one stream.
+        self.ws = torch.empty(max(16, self.info.ws_bwd_bytes, self.info.ws_fwd_bytes),
+                              dtype=torch.uint8, device=self.device)
 
     def new_outputs(self):
         import torch
@@ -363,11 +370,11 @@ class HcaAttention:
         if o is None:
             o, lse = self.new_outputs()
         hca_attn_fwd(self.plan, q, kv, kv_comp if self.S_c > 0 else None, scale, o, lse,
-                     self.ws_fwd, stream)
+                     self.ws, stream)
         return o, lse
 
     def backward(self, q, kv, kv_comp, o, lse, dout, scale, grads=None, stream=None):
         dq, dkv, dkvc = grads if grads is not None else self.new_grads()
         hca_attn_bwd(self.plan, q, kv, kv_comp if self.S_c > 0 else None, o, lse, dout, scale,
-                     dq, dkv, dkvc if self.S_c > 0 else None, self.ws_bwd, stream)
+                     dq, dkv, dkvc if self.S_c > 0 else None, self.ws, stream)
         return dq, dkv, dkvc

@@ -67,8 +67,7 @@ hca_status check_common(const char *fn, const hca_plan *plan, float scale, void 
                         uint64_t ws_bytes, uint64_t ws_needed) {
   if (!plan) return fail(HCA_ERR_INVALID_ARG, std::string(fn) + ": plan is NULL");
   if (!plan->info.kernel_ok)
-    return fail(HCA_ERR_UNSUPPORTED,
-                std::string(fn) + ": no GPU kernel for this dtype / head dim / heads / tile shape");
+    return fail(HCA_ERR_UNSUPPORTED, std::string(fn) + ": " + plan->unsupported);
   if (!(std::isfinite(scale) && scale > 0.f))
     return fail(HCA_ERR_INVALID_ARG, std::string(fn) + ": scale must be finite and > 0");
   if (ws_bytes < ws_needed)

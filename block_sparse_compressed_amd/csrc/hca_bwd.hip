@@ -324,6 +324,10 @@ __global__ void __launch_bounds__(NW * 64, 1)
   // each tensor is addressed from one wave-uniform row base plus a small
   // per-lane offset.  Padded rows (pos >= S) read row S - 1 and are zeroed /
   // masked later, so every load is unconditional.
+  // fetch() ends with these vector-memory loads (Q, dO and O row fragments);
+  // the wait in the last tile below counts on them being the last ones issued.
+  constexpr int kRowLoads = 3 * KS;
+  static_assert(kRowLoads <= 63, "the vmcnt field holds at most 63 outstanding loads");
   auto fetch = [&](int sl_, int item_, int e_begin_, int nent_) {
     e_begin = e_begin_;
     nent = nent_;
@@ -524,16 +528,21 @@ __global__ void __launch_bounds__(NW * 64, 1)
       sdp(last, sn, pn);
     }
     fetch(sl_n, item_n, e_begin_n, nent_n);
+    // Nothing is scheduled across this point, so every load of fetch() is
+    // issued before the wait below.
+    __builtin_amdgcn_sched_barrier(0);
     if (last >= 1) {
       grad(last - 1, ent);
       sc[0] = sn[0];
       sc[1] = sn[1];
       pc[0] = pn[0];
       pc[1] = pn[1];
-      // The last K^T copy was issued before the fetch; loads complete in
-      // issue order, so leaving the 48 row loads (issued last) outstanding
-      // still waits for it.  The barrier orders LDS only.
-      asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+      // The last K^T copy was issued before the fetch, and fetch() issues at
+      // least kRowLoads vector-memory loads after it (its list, row-interval
+      // and LSE loads, then the row fragments).  Loads complete in issue
+      // order, so leaving kRowLoads outstanding still waits for the copy while
+      // the row loads stay in flight.  The barrier orders LDS only.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kRowLoads) : "memory");
       lds_barrier();
       ent = ent_last;
     }
@@ -804,10 +813,12 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const int lbq = __builtin_ctz(d.bq);
   const int SPQ = d.bq * d.H / STEP, lspq = __builtin_ctz(SPQ);
   const int nsteps = nq * SPQ;
-  // An item lists at most 64 query tiles: lane e holds entry e.
+  // Lane e holds list entry e; the entries past the first 64 (long
+  // compressed-tile items) are read through the scalar cache.
   const uint32_t ent_lane = lane < nq ? p.kvent[it.e0 + lane] : 0u;
   auto entry = [&](int e) -> uint32_t {
-    return (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, e);
+    return e < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, e)
+                  : uniform_load(p.kvent, it.e0 + e);
   };
   const size_t bat = (size_t)b * d.H * d.S * D;
   // Byte offset of this lane's 16-byte chunk in a staged row: row r = 8 wave + i
@@ -1056,12 +1067,15 @@ __global__ void __launch_bounds__(NW * 64, 1)
     __syncthreads();
   }
 
-  // Partial [128 keys][512] of this item: this wave's 128 columns of every key
-  // (zeros for the idle half of a half item).
+  // Partial [128 keys][512] of this item: this wave's 128 columns of every key.
+  // A half item writes zeros for its idle half, unless another half item of
+  // the tile shares the block and writes that half itself.
+  const bool shared = HALF && it.shared;
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
     float *out = part + it.part_off + (size_t)(16 * kb + j) * D + 128 * wave;
     const bool act = HALF ? (kb >> 2) == hh : true;
+    if (shared && !act) continue;
     const int ka = HALF ? (kb & 3) : kb;  // active block of key block kb
 #pragma unroll
     for (int dl = 0; dl < 8; ++dl) {
@@ -1080,11 +1094,12 @@ __global__ void __launch_bounds__(NW * 64, 1)
 // ---------------------------------------------------------------------------
 // One launch for the raw key tiles, one for the compressed ones; a workgroup
 // takes one (key tile, chunk of the tile's [kv_bk][D] block).  Thread (g, c)
-// sums the float4 column c of the tile's items i = g, g + G, g + 2 G, ... in
-// increasing order (eight loads in flight), and the G group sums are added in
-// group order.  The grouping is fixed, so the result is bitwise reproducible.
-// Raw tiles have a few items each (G = 1, 1024-element chunks); a compressed
-// tile has hundreds, streamed by G = 8 groups over 128-element chunks.
+// sums the float4 column c of the tile's partial blocks i = g, g + G, g + 2 G,
+// ... in increasing order (eight loads in flight), and the G group sums are
+// added in group order.  The grouping is fixed, so the result is bitwise
+// reproducible.  Raw tiles have a few blocks each (G = 1, 1024-element
+// chunks); a compressed tile has tens to hundreds, streamed by G = 8 groups
+// over 128-element chunks.
 template <int G>
 __global__ void __launch_bounds__(256)
     hca_dkv_reduce_kernel(Dims d, DevPlan p, const float *__restrict__ part, int dtype,
@@ -1098,6 +1113,7 @@ __global__ void __launch_bounds__(256)
   const int b = tile / ntl, kt = tile - b * ntl;
   const int t = comp ? d.nkv_raw + kt : kt;
   const int nk = comp ? d.Sc : d.S;
+  // The tile's partial blocks: n consecutive [kv_bk][D] blocks from block `first`.
   const int first = p.kvtile[2 * (b * nkt + t)], n = p.kvtile[2 * (b * nkt + t) + 1];
   const int D = d.D;
   const int g = threadIdx.x / C, c = threadIdx.x % C;
@@ -1111,10 +1127,9 @@ __global__ void __launch_bounds__(256)
     a.w += v.w;
   };
   if (n > g) {
-    // The planner gives a tile's items consecutive partial blocks, so item i of
-    // the tile sits i blocks after the first (no per-item table load).
+    // Block i of the tile sits i blocks after the first (no per-item table load).
     const size_t blk = (size_t)d.kv_bk * D;
-    const float *src = part + p.kvitem[first].part_off + e;
+    const float *src = part + (size_t)first * blk + e;
     int i = g;
     for (; i + 7 * G < n; i += 8 * G) {
       float4 v[8];

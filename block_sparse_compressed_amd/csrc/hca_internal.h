@@ -20,12 +20,18 @@ constexpr uint32_t kEntIdx = (1u << 30) - 1;
 // Key-tile work item for the key-stationary backward kernel: the query tiles
 // kv_ent[e0, e1) that see key tile `kt` (kv_bk keys) of kind `kind` in batch
 // row `b`; the item's float32 partial gradient [kv_bk][D] is written at
-// `part_off` floats into the partial area of the backward workspace.
+// `part_off` floats into the partial area of the backward workspace.  An item
+// that runs over one 64-key half of its tile (halves 1 or 2) writes that half
+// of its block only when `shared` is set (another half item of the same tile
+// writes the other half of the same block), and the whole block otherwise
+// (zeros for the idle half).
 struct KvItem {
   int32_t b, kind, kt, e0, e1;
   // 128-key items: bit 0 / bit 1 set when some row of the item sees a key of
-  // the lower / upper 64 (3 for other key-tile widths).
-  int32_t halves;
+  // the lower / upper 64 (3 for other key-tile widths, and whenever the
+  // item runs over all keys of its tile).
+  int16_t halves;
+  int16_t shared;
   int64_t part_off;
 };
 static_assert(sizeof(KvItem) == 32, "KvItem layout");
@@ -39,7 +45,7 @@ struct DevLayout {
   uint64_t kvitem = 0;   // KvItem [n_items] (tile-major)
   uint64_t kvorder = 0;  // int32 [n_items]: launch slot -> item, -1 = none
   uint64_t kvent = 0;    // uint32 [n_kvent]: bit 30 FULL, bits 0..29 query tile
-  uint64_t kvtile = 0;   // int32 [B][nkv_raw + nkv_comp][2]: first item, item count
+  uint64_t kvtile = 0;   // int32 [B][nkv_raw + nkv_comp][2]: first partial block, block count
   uint64_t total = 0;
 };
 
@@ -96,8 +102,10 @@ int launch_bwd_f32(const Dims &d, const DevPlan &p, const float *q, const float 
                    const float *kvc, const float *o, const float *lse, const float *dout,
                    float scale, float *dq, float *dkv, float *dkvc, float *delta, void *stream);
 
-// Tile shapes the GPU kernels are built for.
-bool kernel_supports(int dtype, int D, int H, int bq, int bk_raw, int bk_comp);
+// Tile shapes the GPU kernels are built for ("" = supported, else the reason).
+std::string kernel_supports(int dtype, int D, int H, int bq, int bk_raw, int bk_comp);
+// Sizes the kernels' 32-bit offsets can address ("" = fine, else the reason).
+std::string kernel_sizes_ok(int dtype, int D, int64_t S_pad, int64_t Sc_pad);
 void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp);
 
 void set_error(const std::string &msg);
@@ -118,6 +126,7 @@ struct hca_plan {
   int32_t kv_bk = 32, nkv_raw = 0, nkv_comp = 0;  // key-stationary backward tiling
   hca::DevLayout lay;
   hca::WsLayout ws;
+  std::string unsupported;     // why kernel_ok is 0 ("" when it is 1)
   std::vector<uint8_t> image;  // the device image, built once
   void *dev = nullptr;         // caller's device buffer after upload
 };

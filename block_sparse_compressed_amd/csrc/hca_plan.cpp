@@ -40,6 +40,20 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // extra partial sums cost little once the reduction streamed them in groups).
 constexpr int64_t kItemPositions = 64;
 
+// Items of a compressed key tile span a run of chunks (its rows can number
+// up to S x H, so one item per chunk would make the partial gradients grow
+// as S^2 / r): by default a run is sized so that one item is at most a
+// quarter of an even share of the whole backward over kCuTarget compute
+// units, which keeps the launch balanced and the number of compressed-tile
+// partials near 4 kCuTarget for any S.
+constexpr int64_t kCuTarget = 256;
+
+// Half-tile items (128-key tiles whose item sees one 64-key half) run in a
+// second launch of their own; with few items per CU its tail costs more than
+// the halved work saves (S = 16384: dKV 1.57 -> 1.71 ms), so below 8 items
+// per CU every item runs over its whole tile.
+constexpr int64_t kHalfItemsMin = 8 * kCuTarget;
+
 // State of query tile qt (positions qt*bq .. +bq-1) against keys [k0, k0+bk)
 // of `kind`, from the per-position intervals `rw` ([S][4]).
 int classify_tile(const int32_t *rw, int64_t S, int64_t qt, int bq, int kind, int64_t k0,
@@ -74,19 +88,37 @@ void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp) 
   *bk_comp = 32;
 }
 
-bool kernel_supports(int dtype, int D, int H, int bq, int bk_raw, int bk_comp) {
+std::string kernel_supports(int dtype, int D, int H, int bq, int bk_raw, int bk_comp) {
   if (dtype == HCA_BF16) {
-    if (bk_raw != 32 || bk_comp != 32) return false;
-    if (D == 64 || D == 128) return (int64_t)bq * H == 128;
-    // D = 512: bq >= 16 and bq * H >= 128, both powers of two.
+    if (bk_raw != 32 || bk_comp != 32) return "bfloat16 kernels need 32-key tiles";
     const int64_t rows = (int64_t)bq * H;
+    if (D == 64 || D == 128)
+      return rows == 128 ? "" : "head dim 64/128 kernels need bq * H == 128";
+    // D = 512: bq >= 16 and bq * H >= 128, both powers of two.
     if (D == 512)
       return bq >= 16 && (bq & (bq - 1)) == 0 && rows >= 128 && (rows & (rows - 1)) == 0 &&
-             rows <= 1 << 20;
-    return false;
+                     rows <= 1 << 20
+                 ? ""
+                 : "head dim 512 kernels need bq >= 16 and bq * H >= 128, both powers of two";
+    return "no bfloat16 kernel for this head dim (64, 128 and 512 are built)";
   }
   // float32 path: vector kernels, any tile shape.
-  return D % 64 == 0 && D >= 64 && D <= 512;
+  return D % 64 == 0 && D >= 64 && D <= 512 ? ""
+                                           : "float32 kernels need a head dim in 64..512, "
+                                             "a multiple of 64";
+}
+
+// The D = 512 kernels address a key tensor's tile images (4 D bytes per key:
+// K and K^T in bfloat16) with 32-bit buffer offsets; the D = 64 / 128 and
+// float32 kernels index with 64-bit offsets.
+std::string kernel_sizes_ok(int dtype, int D, int64_t S_pad, int64_t Sc_pad) {
+  if (dtype == HCA_BF16 && D == 512) {
+    const int64_t lim = (int64_t)1 << 31;
+    if (S_pad * D * 4 >= lim || Sc_pad * D * 4 >= lim)
+      return "sequence too long for the head dim 512 kernels' 32-bit tile-image offsets "
+             "(padded keys x 2048 bytes must stay below 2^31)";
+  }
+  return "";
 }
 
 }  // namespace hca
@@ -162,14 +194,20 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
   }
   int bq, bkr, bkc;
   default_tiles(dtype, D, H, &bq, &bkr, &bkc);
+  int64_t half_min = kHalfItemsMin;
+  int64_t comp_chunks_cfg = 0;
   if (tiles) {
-    if (tiles->bq < 0 || tiles->bk_raw < 0 || tiles->bk_comp < 0) {
-      set_error("hca_block_mask_build: tile sizes must be >= 0");
+    if (tiles->bq < 0 || tiles->bk_raw < 0 || tiles->bk_comp < 0 ||
+        tiles->comp_item_chunks < 0) {
+      set_error("hca_block_mask_build: tile sizes and comp_item_chunks must be >= 0");
       return HCA_ERR_INVALID_ARG;
     }
     if (tiles->bq) bq = tiles->bq;
     if (tiles->bk_raw) bkr = tiles->bk_raw;
     if (tiles->bk_comp) bkc = tiles->bk_comp;
+    if (tiles->half_items_min > 0) half_min = tiles->half_items_min;
+    if (tiles->half_items_min < 0) half_min = INT64_MAX;
+    comp_chunks_cfg = tiles->comp_item_chunks;
   }
   // Work-list entries pack tile indices into 30 bits.
   if (ceil_div(S, bq) >= (1 << 29) || ceil_div(S, bkr) >= (1 << 29)) {
@@ -191,7 +229,10 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     in.dtype = dtype; in.comp_mode = mode;
     in.bq = bq; in.bk_raw = bkr; in.bk_comp = bkc;
     in.nqt = (int32_t)nqt; in.nkt_raw = (int32_t)nktr; in.nkt_comp = (int32_t)nktc;
-    in.kernel_ok = kernel_supports(dtype, D, H, bq, bkr, bkc) ? 1 : 0;
+    p->unsupported = kernel_supports(dtype, D, H, bq, bkr, bkc);
+    if (p->unsupported.empty())
+      p->unsupported = kernel_sizes_ok(dtype, D, nktr * bkr, nktc * bkc);
+    in.kernel_ok = p->unsupported.empty() ? 1 : 0;
     p->kv_bk = kv_tile_keys(dtype, D);
 
     // ---- per-position visible intervals --------------------------------- //
@@ -322,14 +363,10 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     const int64_t kvb = p->kv_bk;
     const int64_t nkvr = ceil_div(S, kvb), nkvc = ceil_div(S_c, kvb);
     const int64_t nkv = nkvr + nkvc;
-    // Query tiles per item; at most 64 so that the key-stationary kernels can
-    // hold an item's whole list in one register across the wave.
-    const int64_t chunk = std::min<int64_t>(64, std::max<int64_t>(1, kItemPositions / bq));
-    const int64_t nchunk = ceil_div(nqt, chunk);
-    p->kvtile.assign((size_t)B * nkv * 2, 0);
-    int64_t part_off = 0;
-    std::vector<int64_t> item_group;  // (b, chunk) of each item
-    std::vector<uint32_t> list;
+    // Query tiles per 64-position chunk.
+    const int64_t chunk = std::max<int64_t>(1, kItemPositions / bq);
+    std::vector<std::vector<uint32_t>> lists((size_t)B * nkv);
+    int64_t total_entries = 0;
     for (int b = 0; b < B; ++b) {
       const int32_t *rw = &p->rows[((size_t)b * S) * 4];
       for (int64_t t = 0; t < nkv; ++t) {
@@ -346,21 +383,42 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
           p0 = (k0 + 1) * r - 1;
           p1 = S - 1;
         }
-        list.clear();
+        std::vector<uint32_t> &list = lists[(size_t)b * nkv + t];
         for (int64_t qt = p0 >= 0 && p0 <= p1 ? p0 / bq : 0; p0 <= p1 && qt <= p1 / bq; ++qt) {
           const int st = classify_tile(rw, S, qt, bq, kind, k0, kvb, nk);
           if (st != HCA_TILE_EMPTY)
             list.push_back((uint32_t)qt | (st == HCA_TILE_FULL ? kEntFull : 0u));
         }
-        p->kvtile[((size_t)b * nkv + t) * 2] = (int32_t)p->kvitem.size();
-        int32_t n = 0;
-        // Items break at multiples of `chunk` query tiles, the same grid for
-        // every key tile, so the items of different key tiles over one chunk
-        // stream exactly the same query rows.
+        total_entries += (int64_t)list.size();
+      }
+    }
+    // Chunks per compressed-tile item (raw tiles: one chunk per item; their
+    // keys are seen by at most W + kv_bk - 1 positions).
+    int64_t cchunks = comp_chunks_cfg;
+    if (cchunks == 0) {
+      const int64_t cap = total_entries / (4 * kCuTarget);  // query tiles per item at most
+      cchunks = std::max<int64_t>(1, cap / chunk);
+    }
+    const int64_t ngrid = ceil_div(ceil_div(nqt, chunk), cchunks);  // item groups per row
+    p->kvtile.assign((size_t)B * nkv * 2, 0);
+    std::vector<int64_t> item_group;  // (b, run of cchunks chunks) of each item
+    std::vector<int64_t> item_tile;   // b * nkv + t of each item
+    for (int b = 0; b < B; ++b) {
+      const int32_t *rw = &p->rows[((size_t)b * S) * 4];
+      for (int64_t t = 0; t < nkv; ++t) {
+        const int kind = t < nkvr ? 0 : 1;
+        const int64_t kt = kind ? t - nkvr : t;
+        const int64_t k0 = kt * kvb;
+        const int64_t nk = kind ? S_c : S;
+        const std::vector<uint32_t> &list = lists[(size_t)b * nkv + t];
+        const int64_t run = kind ? chunk * cchunks : chunk;  // query tiles per item at most
+        // Items break at multiples of `run` query tiles, the same grid for
+        // every key tile of a kind, so the items of different key tiles over
+        // one stretch of positions stream exactly the same query rows.
         for (size_t s0 = 0; s0 < list.size();) {
-          const int64_t ck = (int64_t)(list[s0] & kEntIdx) / chunk;
+          const int64_t ck = (int64_t)(list[s0] & kEntIdx) / run;
           size_t s1 = s0 + 1;
-          while (s1 < list.size() && (int64_t)(list[s1] & kEntIdx) / chunk == ck) ++s1;
+          while (s1 < list.size() && (int64_t)(list[s1] & kEntIdx) / run == ck) ++s1;
           KvItem it{};
           it.b = b;
           it.kind = kind;
@@ -385,41 +443,80 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
             }
             if (it.halves == 0) it.halves = 3;  // (a listed tile always has a visible key)
           }
-          // A tile's items take consecutive partial blocks (the reduction
-          // kernel relies on it).
-          it.part_off = part_off;
-          part_off += kvb * D;
           p->kvitem.push_back(it);
-          item_group.push_back((int64_t)b * nchunk + ck);
-          ++n;
+          const int64_t first_chunk = (int64_t)(list[s0] & kEntIdx) / chunk;
+          item_group.push_back((int64_t)b * ngrid + first_chunk / cchunks);
+          item_tile.push_back((int64_t)b * nkv + t);
           s0 = s1;
         }
-        p->kvtile[((size_t)b * nkv + t) * 2 + 1] = n;
       }
     }
     if (p->kvent.size() >= (size_t)INT32_MAX) throw std::bad_alloc();
     p->nkv_raw = (int32_t)nkvr;
     p->nkv_comp = (int32_t)nkvc;
+    in.comp_item_chunks = (int32_t)cchunks;
 
-    // Launch order.  Workgroup i of a launch goes to XCD i % kXcd, and each
-    // XCD runs its share in order.  The items of one chunk (its group) read
-    // the same query rows at about the same pace, so a group is kept together
-    // on one XCD, where its L2 serves the repeated reads.  Groups go, heaviest
-    // first, to the least-loaded XCD; slots past the end of a short XCD queue
-    // hold -1 (no work).
-    // Half-tile items run in a second launch of their own; with few items per
-    // CU its tail costs more than the halved work saves (S = 16384: dKV 1.57
-    // -> 1.71 ms), so below 8 items per CU (256 CUs on MI355X) every item
-    // runs over its whole tile.
-    constexpr size_t kHalfItemsMin = 8 * 256;
-    if (p->kvitem.size() < kHalfItemsMin)
+    // With few items, every item runs over its whole tile (see kHalfItemsMin).
+    if ((int64_t)p->kvitem.size() < half_min)
       for (KvItem &it : p->kvitem) it.halves = 3;
 
+    // Partial blocks.  A key tile's items own consecutive [kv_bk][D] float32
+    // blocks (the reduction sums them in block order).  Items over the whole
+    // tile take a block each; an item over the lower half and one over the
+    // upper half of the same tile share a block, each writing its half; a
+    // half item left without a partner writes its whole block, zeros in the
+    // idle half.
+    int64_t nblocks = 0;
+    {
+      size_t i0 = 0;
+      while (i0 < p->kvitem.size()) {
+        size_t i1 = i0 + 1;
+        while (i1 < p->kvitem.size() && item_tile[i1] == item_tile[i0]) ++i1;
+        const int64_t tile = item_tile[i0];
+        const int64_t first = nblocks;
+        std::vector<size_t> lows, highs;
+        for (size_t i = i0; i < i1; ++i) {
+          KvItem &it = p->kvitem[i];
+          it.shared = 0;
+          if (it.halves == 1) lows.push_back(i);
+          else if (it.halves == 2) highs.push_back(i);
+          else it.part_off = nblocks++ * kvb * D;
+        }
+        const size_t npair = std::min(lows.size(), highs.size());
+        for (size_t k = 0; k < std::max(lows.size(), highs.size()); ++k) {
+          const int64_t off = nblocks++ * kvb * D;
+          if (k < lows.size()) {
+            p->kvitem[lows[k]].part_off = off;
+            p->kvitem[lows[k]].shared = k < npair;
+          }
+          if (k < highs.size()) {
+            p->kvitem[highs[k]].part_off = off;
+            p->kvitem[highs[k]].shared = k < npair;
+          }
+        }
+        p->kvtile[tile * 2] = (int32_t)first;
+        p->kvtile[tile * 2 + 1] = (int32_t)(nblocks - first);
+        i0 = i1;
+      }
+    }
+    if (nblocks >= INT32_MAX) throw std::bad_alloc();
+    int64_t nhalf = 0;
+    for (const KvItem &it : p->kvitem) nhalf += it.halves != 3;
+    in.items = (int64_t)p->kvitem.size();
+    in.items_half = nhalf;
+    in.part_blocks = nblocks;
+
+    // Launch order.  Workgroup i of a launch goes to XCD i % kXcd, and each
+    // XCD runs its share in order.  The items of one group (one stretch of
+    // positions) read the same query rows at about the same pace, so a group
+    // is kept together on one XCD, where its L2 serves the repeated reads.
+    // Groups go, heaviest first, to the least-loaded XCD; slots past the end
+    // of a short XCD queue hold -1 (no work).
     // Two launches share the order array: items over all keys of their tile
     // first, then the half-tile items (their own kernel instantiation).
     {
       constexpr int kXcd = 8;
-      const int64_t ngroup = (int64_t)B * nchunk;
+      const int64_t ngroup = (int64_t)B * ngrid;
       auto build_order = [&](bool half) {
         std::vector<int64_t> gwork(ngroup, 0);
         std::vector<std::vector<int32_t>> gitems(ngroup);
@@ -496,7 +593,7 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     }
     w.fwd_total = dtype == HCA_BF16 ? off : 0;
     w.delta = place((uint64_t)B * H * S * 4);
-    w.part = place((uint64_t)std::max<int64_t>(1, part_off) * 4);
+    w.part = place((uint64_t)std::max<int64_t>(1, nblocks * kvb * D) * 4);
     w.bwd_total = off;
     in.ws_fwd_bytes = w.fwd_total;
     in.ws_bwd_bytes = w.bwd_total;
@@ -572,7 +669,7 @@ extern "C" hca_status hca_plan_export_items(const hca_plan *plan, int64_t *items
     o[3] = plan->kv_bk;
     o[4] = it.e1 > it.e0 ? (int64_t)(plan->kvent[it.e0] & kEntIdx) : -1;
     o[5] = it.e1 > it.e0 ? (int64_t)(plan->kvent[it.e1 - 1] & kEntIdx) : -1;
-    o[6] = it.halves;
+    o[6] = it.halves | (it.shared ? 4 : 0);
     o[7] = it.part_off;
   }
   return HCA_OK;

@@ -77,11 +77,25 @@ enum { HCA_TILE_EMPTY = 0, HCA_TILE_PARTIAL = 1, HCA_TILE_FULL = 2 };
  * choice for (D, H, dtype).  Any positive shape is accepted by the planner;
  * the GPU entry points run only the shapes their kernels are built for
  * (hca_plan_info.kernel_ok).
+ *
+ * Two further fields shape the work items of the key-stationary backward
+ * (they change the schedule, never the result beyond float summation order):
+ *   half_items_min    with 128-key items (head dim 512, bfloat16): an item whose
+ *                     rows see only one 64-key half of its key tile runs over
+ *                     that half alone once the plan has at least this many
+ *                     items; 0 = library choice (2048), < 0 = never.
+ *   comp_item_chunks  64-position chunks of query rows per work item of a
+ *                     compressed key tile; 0 = library choice (sized so that
+ *                     one item is at most a quarter of an even share of the
+ *                     work over 256 compute units, which also bounds the
+ *                     number of partial gradients independently of S).
  */
 typedef struct hca_tile_cfg {
   int32_t bq;
   int32_t bk_raw;
   int32_t bk_comp;
+  int32_t half_items_min;
+  int32_t comp_item_chunks;
 } hca_tile_cfg;
 
 typedef struct hca_plan hca_plan; /* opaque, host-owned */
@@ -94,14 +108,24 @@ typedef struct hca_plan_info {
   int32_t nqt;       /* ceil(S / bq) query tiles per batch row */
   int32_t nkt_raw;   /* ceil(S / bk_raw) */
   int32_t nkt_comp;  /* ceil(S_c / bk_comp) */
-  int32_t kernel_ok; /* 1: hca_attn_fwd / hca_attn_bwd run this plan */
+  int32_t kernel_ok; /* 1: hca_attn_fwd / hca_attn_bwd run this plan: a kernel exists for
+                        the dtype, head dim, heads and tile shape, and the sizes fit the
+                        kernels' 32-bit offsets (head dim 512, bfloat16: each key tensor
+                        padded to 32-key tiles times 4 D bytes below 2^31) */
   int64_t tiles_raw, tiles_comp;   /* non-empty tiles, summed over the batch */
   int64_t full_raw, full_comp;     /* of which FULL */
   int64_t pairs_raw, pairs_comp;   /* visible (query position, key) pairs, summed over the
                                       batch; multiply by H for (query row, key) pairs */
   uint64_t device_bytes;           /* size of the plan's device image */
   uint64_t ws_fwd_bytes;           /* workspace hca_attn_fwd needs */
-  uint64_t ws_bwd_bytes;           /* workspace hca_attn_bwd needs */
+  uint64_t ws_bwd_bytes;           /* workspace hca_attn_bwd needs (>= ws_fwd_bytes; the
+                                      backward's layout starts with the forward's, so one
+                                      buffer of ws_bwd_bytes serves both calls in turn) */
+  int64_t items;                   /* work items of the key-stationary backward */
+  int64_t items_half;              /* of which run over one 64-key half of their tile */
+  int64_t part_blocks;             /* float32 partial-gradient blocks (kv_bk x D each) */
+  int32_t comp_item_chunks;        /* 64-position chunks per compressed-tile item */
+  int32_t reserved_;
 } hca_plan_info;
 
 /*
@@ -157,9 +181,11 @@ hca_status hca_plan_export_rows(const hca_plan *plan, int32_t *rows);
  * capacity) rows of 8 int64 are written: batch row, kind (0 raw, 1
  * compressed), first key, keys per item, first and last listed query tile,
  * halves (bit 0 / bit 1 set when some row of the item sees a key of the lower
- * / upper half of the item's keys; 3 whenever the item runs over all of them)
- * and the element offset of the item's float32 partial block.  The items of
- * one key tile are consecutive and own consecutive partial blocks.  Errors:
+ * / upper half of the item's keys; 3 whenever the item runs over all of them;
+ * bit 2 set when a lower-half and an upper-half item of the tile share one
+ * partial block, each writing its half) and the element offset of the item's
+ * float32 partial block.  The items of one key tile are consecutive and
+ * their partial blocks are consecutive.  Errors:
  * HCA_ERR_INVALID_ARG on a NULL plan or count, or a negative capacity.
  */
 hca_status hca_plan_export_items(const hca_plan *plan, int64_t *items, int64_t capacity,

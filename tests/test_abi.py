@@ -46,7 +46,7 @@ def build_raw(B=1, S=64, r=8, W=4, Sc=None, starts=None, counts=None, H=4, D=64,
     out = ctypes.c_void_p()
     st = np.asarray(starts, np.int32) if starts is not None else None
     ct = np.asarray(counts, np.int32) if counts is not None else None
-    cfg = hca._TileCfg(*tiles) if tiles is not None else None
+    cfg = hca._TileCfg(*(tuple(tiles) + (0,) * (5 - len(tiles)))) if tiles is not None else None
     s = lib.hca_block_mask_build(B, S, r, W, (S // r if r > 0 else 0) if Sc is None else Sc,
                                  st.ctypes.data if st is not None else None,
                                  ct.ctypes.data if ct is not None else None, H, D, dtype, mode,
@@ -157,6 +157,25 @@ def test_unsupported_configurations(kw):
     assert hca.hca_plan_get_info(plan).kernel_ok == 0
     assert lib.hca_attn_fwd(*fwd_args(plan)) == hca.HCA_ERR_UNSUPPORTED
     assert lib.hca_attn_bwd(*bwd_args(plan)) == hca.HCA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("S,H,ok", [(1048544, 8, 1), (1048545, 8, 0), (2097184, 1, 0)])
+def test_sizes_past_32bit_image_offsets_unsupported(S, H, ok):
+    """Head dim 512 kernels address the tile images with 32-bit offsets: a plan
+    whose padded keys x 2048 bytes reach 2^31 is marked unsupported and both
+    passes return HCA_ERR_UNSUPPORTED (with the reason) instead of computing
+    on wrapped offsets."""
+    plan = hca.hca_block_mask_build(1, S, 128, 128, S // 128, H=H, D=512, dtype=hca.HCA_BF16)
+    assert hca.hca_plan_get_info(plan).kernel_ok == ok
+    if not ok:
+        assert lib.hca_attn_fwd(*fwd_args(plan)) == hca.HCA_ERR_UNSUPPORTED
+        assert "32-bit" in lib.hca_last_error().decode()
+        assert lib.hca_attn_bwd(*bwd_args(plan)) == hca.HCA_ERR_UNSUPPORTED
+
+
+def test_negative_comp_item_chunks_rejected():
+    s, out = build_raw(tiles=(0, 0, 0, 0, -1))
+    assert s == hca.HCA_ERR_INVALID_ARG and out.value is None
 
 
 def test_upload_checks(plan):

@@ -9,7 +9,9 @@ Bounds: max |gpu - oracle| / max |oracle| <= 2e-2 for bfloat16 and <= 1e-4 for
 float32 on every output; -inf log-sum-exp entries must coincide.
 """
 
+import json
 import math
+import os
 import sys
 
 import numpy as np
@@ -29,6 +31,15 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}
 def say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def record(case, errs):
+    """Appends the measured max relative errors of a case to the file named by
+    HCA_PARITY_LOG (one JSON object per line), when that variable is set."""
+    path = os.environ.get("HCA_PARITY_LOG")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps({"case": case, **{k: float(v) for k, v in errs.items()}}) + "\n")
 
 
 def rel_err(got, want):
@@ -57,17 +68,19 @@ def as_np(t):
 
 class Case:
     def __init__(self, B, S, H, D, r, W, dtype="bf16", lengths=None, mode=0, seed=0,
-                 value_scale=1.0, stream=None):
+                 value_scale=1.0, tiles=None, name=None):
         self.B, self.S, self.H, self.D, self.r, self.W = B, S, H, D, r, W
         self.Sc = S // r
         self.dtype, self.lengths, self.mode = dtype, lengths, mode
         self.scale = 1.0 / math.sqrt(D)
+        self.name = name or f"B{B}_S{S}_H{H}_D{D}_r{r}_W{W}_{dtype}_m{mode}" + (
+            "" if tiles is None else "_t" + "x".join(map(str, tiles)))
         say(f"case B={B} S={S} H={H} D={D} r={r} W={W} {dtype} mode={mode} seed={seed} "
-            f"docs={'none' if lengths is None else sum(len(x) for x in lengths)}")
+            f"docs={'none' if lengths is None else sum(len(x) for x in lengths)} tiles={tiles}")
         self.q, self.kv, self.kvc, self.dout = draw(B, S, H, D, self.Sc, dtype, seed,
                                                     value_scale, device="cuda")
         starts, counts = starts_csr(lengths, B)
-        self.att = hca.HcaAttention(B, S, H, D, r, W, dtype, starts, counts, mode)
+        self.att = hca.HcaAttention(B, S, H, D, r, W, dtype, starts, counts, mode, tiles)
         assert self.att.info.kernel_ok == 1
 
     def run(self, stream=None, poison=True):
@@ -92,6 +105,13 @@ class Case:
         return [to_host_bits(t) for t in (self.q, self.kv, self.kvc, self.dout)]
 
 
+def lse_err(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    fin = np.isfinite(want)
+    return rel_err(got[fin], want[fin]) if fin.any() else 0.0
+
+
 def check_full(case, outs=None):
     o, lse, dq, dkv, dkvc = outs if outs is not None else case.run()
     ref = oracle.full(case.problem(), *case.host())
@@ -100,7 +120,9 @@ def check_full(case, outs=None):
                 dkv=rel_err(as_np(dkv), ref["dkv"]))
     if case.Sc:
         errs["dkvc"] = rel_err(as_np(dkvc), ref["dkvc"])
+    errs["lse"] = lse_err(as_np(lse), ref["lse"])
     say(f"  errors {errs}")
+    record(case.name + " (every element)", errs)
     compare_lse(as_np(lse), ref["lse"], tol)
     for k, v in errs.items():
         assert v <= tol, (k, v)
@@ -157,6 +179,38 @@ def test_long_key_lists_every_element():
     check_full(Case(1, 2048, 16, 512, 8, 64, "bf16", [[700, 1348]], seed=11, value_scale=2.0))
 
 
+def test_key_lists_past_64_tiles_d512():
+    """r = 2 gives 2048 compressed entries (64 tiles of 32), so the last query
+    tiles list more than 64 key tiles: the forward and the persistent dQ read
+    the list entries past the 64 held in lanes from memory.  Half-tile dKV
+    items are forced on (threshold one item) and the compressed-tile items run
+    20 chunks long (80 listed query tiles), so the dKV kernel also reads
+    entries past 64."""
+    case = Case(1, 4096, 8, 512, 2, 128, "bf16", seed=21, tiles=(0, 0, 0, 1, 20))
+    info = case.att.info
+    assert info.items_half > 0 and info.comp_item_chunks == 20
+    items = hca.hca_plan_export_items(case.att.plan)
+    assert (items[:, 5] - items[:, 4]).max() + 1 > 64
+    raw, comp = hca.hca_plan_export_tiles(case.att.plan)
+    assert ((raw > 0).sum(-1) + (comp > 0).sum(-1)).max() > 64
+    check_full(case)
+
+
+@pytest.mark.parametrize("lengths", [None, [[700, 836]]], ids=["one_doc", "two_docs"])
+def test_half_tile_dkv_items_every_element(lengths):
+    """The half-tile dKV instantiation (items whose rows see one 64-key half of
+    a 128-key tile, in a launch of their own; lower- and upper-half items of a
+    tile share a partial block) normally runs only at S >= 65536.  The plan
+    knob turns it on at a size the oracle checks element by element, with a
+    document boundary in the second case."""
+    case = Case(1, 1536, 8, 512, 16, 128, "bf16", lengths, seed=22, tiles=(0, 0, 0, 1, 0))
+    info = case.att.info
+    items = hca.hca_plan_export_items(case.att.plan)
+    assert info.items_half > 0 and (items[:, 6] & 4).any()
+    assert ((items[:, 6] & 3) == 1).any() and ((items[:, 6] & 3) == 2).any()
+    check_full(case)
+
+
 def test_single_position():
     check_full(Case(1, 1, 64, 512, 1, 1, "bf16", seed=3))
     check_full(Case(1, 1, 16, 128, 4, 0, "bf16", seed=4))  # the only row sees nothing
@@ -196,6 +250,12 @@ def test_packed_bf16_workload_every_element():
     check_full(case)
 
 
+def bitwise_equal(a, b):
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
 def test_deterministic_and_stream():
     case = Case(2, 1000, 16, 128, 16, 64, "bf16", [[300, 700], [1000]], seed=7)
     a = case.run()
@@ -203,9 +263,27 @@ def test_deterministic_and_stream():
     with torch.cuda.stream(s):
         b = case.run(stream=s)
     s.synchronize()
-    for x, y in zip(a, b):
-        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
-                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+    bitwise_equal(a, b)
+
+
+def test_mid_workload_every_element_deterministic():
+    """The mid-length workload (S = 16384, H = 64, D = 512) compared with the
+    oracle on every element of O, LSE, dQ, dKV and dKV_comp, outputs
+    NaN-poisoned first; and run a second time on a non-default stream, where
+    every output must match the first run bit for bit (fixed-order
+    reductions, persistent dQ and the grouped dKV reduction included)."""
+    wl = WORKLOADS[3]
+    case = Case(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, wl.dtype, doc_lengths(wl), seed=wl.seed,
+                value_scale=wl.value_scale, name=wl.name)
+    a = case.run()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = case.run(stream=s)
+    s.synchronize()
+    bitwise_equal(a, b)
+    del b
+    say("  bitwise equal across runs and streams; oracle over every element")
+    check_full(case, a)
 
 
 # --------------------------------------------------------------------------- #
@@ -250,36 +328,81 @@ def sample_keys(wl, lengths):
     return np.array(kinds, np.int32), np.array(idx, np.int32)
 
 
-@pytest.mark.parametrize("wid", [3, 4, 5])
+def raw_key_tiles(wl, lengths):
+    """First keys of the 128-key raw tiles compared in full: the first, one in
+    the middle, the last (holding key S - 1), and one that straddles a
+    document start where there are documents (else one more in the middle)."""
+    last = (wl.S - 1) // 128 * 128
+    tiles = [0, wl.S // 2 // 128 * 128, last]
+    if lengths is not None:
+        starts = np.cumsum([0] + lengths[0][:-1])
+        a = int(starts[len(starts) // 2])
+        tiles.append(a // 128 * 128 if a % 128 else max(0, a - 64) // 128 * 128)
+    else:
+        tiles.append(wl.S // 4 // 128 * 128)
+    return sorted(set(tiles))
+
+
+def window_rows(wl, k0):
+    """Flat row indices (all heads) of the positions that can see a raw key of
+    [k0, k0 + 128): positions k0 .. k0 + 127 + W - 1."""
+    pos = np.arange(k0, min(wl.S, k0 + 128 + wl.W - 1), dtype=np.int64)
+    return (np.arange(wl.H, dtype=np.int64)[:, None] * wl.S + pos[None, :]).reshape(-1)
+
+
+@pytest.mark.parametrize("wid", [4, 5])
 def test_workload_full_size_sampled(wid):
+    """Full-size workloads in the benchmark's launch configuration, outputs
+    NaN-poisoned: every output element must be written; sampled rows, two
+    whole 16-position query tiles over all heads, every raw key of four
+    128-key tiles (first, middle, last, and one at a document start) and the
+    last compressed entry of a few documents are compared with the oracle."""
     wl = WORKLOADS[wid]
     lengths = doc_lengths(wl)
     case = Case(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, wl.dtype, lengths, seed=wl.seed,
-                value_scale=wl.value_scale)
-    o, lse, dq, dkv, dkvc = case.run(poison=False)
+                value_scale=wl.value_scale, name=wl.name)
+    o, lse, dq, dkv, dkvc = case.run(poison=True)
+    for t in (o, dq, dkv, dkvc):
+        assert not torch.isnan(t).any()
     say("  GPU pass done; copying inputs to host")
     prob = case.problem()
     host = case.host()
     rng = np.random.default_rng(wid)
     rows = sample_rows(wl, lengths, rng)
+    # two whole query tiles of 16 positions, all heads: the first and one at 3/4
+    for qt in (0, (3 * wl.S // 4) // 16):
+        pos = np.arange(qt * 16, min(wl.S, qt * 16 + 16), dtype=np.int64)
+        rows = np.concatenate([rows, (np.arange(wl.H)[:, None] * wl.S + pos[None, :]).ravel()])
+    rows = np.unique(rows)
     ro, rlse, _, rdq = oracle.rows(prob, *host, row_index=rows)
     flat = lambda t: t.reshape(-1, wl.D) if t.dim() == 4 else t.reshape(-1)
     idx = torch.as_tensor(rows, device="cuda")
-    go = as_np(flat(o)[idx])
-    glse = as_np(flat(lse)[idx])
-    gdq = as_np(flat(dq)[idx])
-    e = dict(o=rel_err(go, ro), dq=rel_err(gdq, rdq))
-    compare_lse(glse, rlse, TOL["bf16"])
-    say(f"  sampled rows: {len(rows)} errors {e}")
-    kinds, kidx = sample_keys(wl, lengths)
-    rk = oracle.keys(prob, *host, kinds, np.zeros_like(kinds), kidx)
-    gk = np.stack([as_np((dkvc if k else dkv)[0, i]) for k, i in zip(kinds, kidx)])
-    e["dkv_keys"] = rel_err(gk, rk)
-    say(f"  sampled keys {list(zip(kinds.tolist(), kidx.tolist()))} errors {e}")
+    e = dict(o=rel_err(as_np(flat(o)[idx]), ro), dq=rel_err(as_np(flat(dq)[idx]), rdq),
+             lse=lse_err(as_np(flat(lse)[idx]), rlse))
+    compare_lse(as_np(flat(lse)[idx]), rlse, TOL["bf16"])
+    say(f"  rows: {len(rows)} errors {e}")
+    # every raw key of the chosen 128-key tiles, from the rows that see them
+    tiles = raw_key_tiles(wl, lengths)
+    krows = np.unique(np.concatenate([window_rows(wl, k0) for k0 in tiles]))
+    _, klse, kdelta, _ = oracle.rows(prob, *host, row_index=krows)
+    lse_all = np.full(wl.B * wl.H * wl.S, np.nan)
+    delta_all = np.full(wl.B * wl.H * wl.S, np.nan)
+    lse_all[krows], delta_all[krows] = klse, kdelta
+    kidx = np.concatenate([np.arange(k0, min(wl.S, k0 + 128)) for k0 in tiles]).astype(np.int32)
+    kinds = np.zeros_like(kidx)
+    rk = oracle.keys(prob, *host, kinds, np.zeros_like(kinds), kidx, lse_all, delta_all)
+    e["dkv_tiles"] = rel_err(as_np(dkv[0][torch.as_tensor(kidx, device="cuda").long()]), rk)
+    say(f"  raw key tiles {tiles} ({len(kidx)} keys, {len(krows)} rows) errors {e}")
+    # compressed entries: the last complete one of a few documents (and, in the
+    # one-document workload, one whose gradient partly comes from half-tile items)
+    ckinds, cidx = sample_keys(wl, lengths)
+    sel = ckinds == 1
+    rc = oracle.keys(prob, *host, ckinds[sel], np.zeros_like(ckinds[sel]), cidx[sel])
+    e["dkvc_entries"] = rel_err(np.stack([as_np(dkvc[0, i]) for i in cidx[sel]]), rc)
+    say(f"  compressed entries {cidx[sel].tolist()} errors {e}")
+    record(wl.name + " (sampled)", e)
     for k, v in e.items():
         assert v <= TOL["bf16"], (k, v)
-    for t in (o, dq, dkv, dkvc):
-        assert not torch.isnan(t).any()
 
 
 def intervals(S, r, W, lengths_row, mode=0):

@@ -185,19 +185,21 @@ def closed_form_intervals(S, r, W, lengths_row):
 
 @pytest.mark.parametrize("lengths", [None, [[15000, 25000]]], ids=["one_doc", "two_docs"])
 def test_items_halves_and_partial_blocks(lengths):
-    """At S = 40000, H = 64, D = 512 the key-stationary backward has more than
-    2048 work items of 128 keys, so the planner marks items that see only one
-    64-key half of their tile.  Every item's mark must equal the halves that
-    its query tiles see, and the items of a key tile must own consecutive
-    partial blocks (the reduction relies on it)."""
+    """At S = 40000, H = 64, D = 512 with half-tile marking on (the knob sets
+    the threshold to one item), the planner marks 128-key items that see only
+    one 64-key half of their tile.  Every item's mark must equal the halves
+    that its query tiles see, and the items of a key tile must own
+    consecutive partial blocks (the reduction relies on it)."""
     S, H, D, r, W = 40000, 64, 512, 128, 128
-    plan, prob = build_both(1, S, H, D, r, W, lengths, hca.HCA_COMPSEG_STRICT)
+    plan, prob = build_both(1, S, H, D, r, W, lengths, hca.HCA_COMPSEG_STRICT,
+                            tiles=(0, 0, 0, 1, 0))
     info = hca.hca_plan_get_info(plan)
     items = hca.hca_plan_export_items(plan)
-    assert len(items) >= 2048 and (items[:, 3] == 128).all()
+    assert len(items) >= 1000 and (items[:, 3] == 128).all()
     lo, hi, clo, chi = closed_form_intervals(S, r, W, lengths[0] if lengths else None)
     n_half = 0
-    for b, kind, k0, nk, qa, qz, halves, _ in items:
+    for b, kind, k0, nk, qa, qz, hmark, _ in items:
+        halves = hmark & 3
         p = np.arange(qa * info.bq, min(S, (qz + 1) * info.bq))
         a, z = (clo[p], chi[p]) if kind else (lo[p], hi[p])
         nkeys = info.S_c if kind else S
@@ -210,22 +212,44 @@ def test_items_halves_and_partial_blocks(lengths):
     assert n_half > 0  # first and last items of sliding-window tiles
     # spot-check marked items against the oracle's element predicate
     rng = np.random.default_rng(0)
-    half_items = items[items[:, 6] != 3]
+    half_items = items[(items[:, 6] & 3) != 3]
     for row in half_items[rng.choice(len(half_items), size=12, replace=False)]:
         b, kind, k0, nk, qa, qz, halves, _ = (int(x) for x in row)
+        halves &= 3
         idle = range(k0 + nk // 2, k0 + nk) if halves == 1 else range(k0, k0 + nk // 2)
         vis = oracle.vis_comp if kind else oracle.vis_raw
         nkeys = info.S_c if kind else S
         for i in range(qa * info.bq, min(S, (qz + 1) * info.bq)):
             assert not any(vis(prob, b, i, t) for t in idle if t < nkeys)
-    # consecutive partial blocks per key tile
-    blk = 128 * D
-    for g0 in range(1, len(items)):
-        prev, cur = items[g0 - 1], items[g0]
-        if tuple(prev[:3]) == tuple(cur[:3]):
-            assert cur[7] == prev[7] + blk
-    assert len({tuple(x) for x in items[:, [0, 1, 2]]}) == \
-        sum(1 for g0 in range(len(items)) if g0 == 0 or tuple(items[g0 - 1, :3]) != tuple(items[g0, :3]))
+    check_partial_blocks(items, D, info)
+
+
+def check_partial_blocks(items, D, info):
+    """Each key tile's items are consecutive and own consecutive partial blocks
+    (the reduction sums a tile's blocks by position); a block is owned by one
+    item, or shared by exactly one lower-half and one upper-half item of the
+    tile, both marked shared; the tiles' block ranges tile [0, part_blocks)."""
+    blk = items[0, 3] * D
+    tiles = {}
+    for row in items:
+        key = (int(row[0]), int(row[1]), int(row[2]))
+        assert not tiles or key in tiles or key > max(tiles), "items of a tile are consecutive"
+        tiles.setdefault(key, []).append(row)
+    covered = []
+    for key, rows in tiles.items():
+        offs = {}
+        for row in rows:
+            assert row[7] % blk == 0
+            offs.setdefault(int(row[7]) // blk, []).append(int(row[6]))
+        ids = sorted(offs)
+        assert ids == list(range(ids[0], ids[0] + len(ids))), key
+        covered += ids
+        for owners in offs.values():
+            if len(owners) == 1:
+                assert owners[0] & 4 == 0
+            else:
+                assert sorted(owners) == [1 | 4, 2 | 4], owners
+    assert sorted(covered) == list(range(info.part_blocks))
 
 
 def test_items_small_problem_runs_whole_tiles():
@@ -233,3 +257,72 @@ def test_items_small_problem_runs_whole_tiles():
     plan, _ = build_both(1, 16384, 64, 512, 128, 128, None, hca.HCA_COMPSEG_STRICT)
     items = hca.hca_plan_export_items(plan)
     assert 0 < len(items) < 2048 and (items[:, 6] == 3).all()
+    info = hca.hca_plan_get_info(plan)
+    assert info.items == len(items) and info.items_half == 0
+    assert info.part_blocks == len(items)
+
+
+def test_half_items_knob():
+    """half_items_min = 1 marks half-tile items on a small problem (so the GPU
+    tests can run that kernel at sizes the oracle checks element by element);
+    half_items_min < 0 never marks them."""
+    S, H, D, r, W = 1536, 8, 512, 16, 128
+    plan, prob = build_both(1, S, H, D, r, W, None, hca.HCA_COMPSEG_STRICT,
+                            tiles=(0, 0, 0, 1, 0))
+    info = hca.hca_plan_get_info(plan)
+    items = hca.hca_plan_export_items(plan)
+    half = (items[:, 6] & 3) != 3
+    assert info.items_half == int(half.sum()) > 0
+    assert ((items[:, 6] & 3) == 1).any() and ((items[:, 6] & 3) == 2).any()
+    assert (items[:, 6] & 4).any()  # some lower/upper pairs share a block
+    check_partial_blocks(items, D, info)
+    assert info.part_blocks < len(items)
+    # every marked item's idle half is invisible to all of its rows
+    for row in items[half]:
+        b, kind, k0, nk, qa, qz, halves, _ = (int(x) for x in row)
+        idle = range(k0 + 64, k0 + 128) if halves & 3 == 1 else range(k0, k0 + 64)
+        vis = oracle.vis_comp if kind else oracle.vis_raw
+        nkeys = info.S_c if kind else S
+        for i in range(qa * info.bq, min(S, (qz + 1) * info.bq)):
+            assert not any(vis(prob, b, i, t) for t in idle if t < nkeys)
+    plan2, _ = build_both(1, S, H, D, r, W, None, hca.HCA_COMPSEG_STRICT,
+                          tiles=(0, 0, 0, -1, 0))
+    assert hca.hca_plan_get_info(plan2).items_half == 0
+    assert (hca.hca_plan_export_items(plan2)[:, 6] == 3).all()
+
+
+@pytest.mark.parametrize("chunks", [1, 3, 20])
+def test_compressed_item_chunks_knob(chunks):
+    """comp_item_chunks sets the 64-position chunks per compressed-tile item:
+    the items of a compressed tile cover its list in runs on one global grid of
+    `chunks` chunks; raw-tile items stay one chunk long."""
+    S, H, D, r, W = 6000, 8, 512, 4, 64
+    plan, _ = build_both(1, S, H, D, r, W, [[2500, 3500]], hca.HCA_COMPSEG_STRICT,
+                         tiles=(0, 0, 0, 0, chunks))
+    info = hca.hca_plan_get_info(plan)
+    assert info.comp_item_chunks == chunks
+    items = hca.hca_plan_export_items(plan)
+    per_chunk = 64 // info.bq
+    for b, kind, k0, nk, qa, qz, _, _ in items:
+        run = per_chunk * (chunks if kind else 1)
+        assert qa // run == qz // run, (kind, qa, qz)
+    comp = items[items[:, 1] == 1]
+    longest = int((comp[:, 5] - comp[:, 4]).max()) + 1
+    assert longest <= per_chunk * chunks
+    if chunks == 20:
+        assert longest > 64  # lists past 64 entries (read beyond the lane-held part)
+    check_partial_blocks(items, D, info)
+
+
+def test_workspace_grows_linearly():
+    """The backward workspace is O(S): compressed-tile items are bounded in
+    number, so doubling S at most about doubles it (it grew as S^2 / r when
+    every 64-position chunk of a compressed tile's rows was an item)."""
+    ws = {}
+    for S in (131072, 262144):
+        p = hca.hca_block_mask_build(1, S, 128, 128, S // 128, None, None, 64, 512,
+                                     hca.HCA_BF16)
+        ws[S] = hca.hca_plan_get_info(p).ws_bwd_bytes
+    assert ws[262144] <= 2.05 * ws[131072]
+    p = hca.hca_block_mask_build(1, 65536, 128, 128, 512, None, None, 64, 512, hca.HCA_BF16)
+    assert hca.hca_plan_get_info(p).ws_bwd_bytes < 0.75 * 2**30
