@@ -90,6 +90,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--comp-item-chunks", type=int, default=0,
+                    help="64-position chunks per compressed-tile work item of the key-"
+                         "stationary backward (0 = library choice)")
+    ap.add_argument("--half-items-min", type=int, default=0,
+                    help="item count from which half-tile items are used (0 = library "
+                         "choice, -1 = never)")
     ap.add_argument("--source-hashes", action="store_true",
                     help="print the source hash of each kernel and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -186,7 +192,11 @@ def main():
 
     q, kv, kvc, dout = draw_workload(wl, device=dev)
     torch.cuda.reset_peak_memory_stats()
-    att = hca.HcaAttention(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, wl.dtype, starts, counts)
+    tiles = None
+    if args.comp_item_chunks or args.half_items_min:
+        tiles = (0, 0, 0, args.half_items_min, args.comp_item_chunks)
+    att = hca.HcaAttention(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, wl.dtype, starts, counts,
+                           tiles=tiles)
     info = att.info
     scale = 1.0 / math.sqrt(wl.D)
     o, lse = att.new_outputs()
@@ -295,6 +305,10 @@ def main():
         "visible_pairs": P,
         "plan_build_ms": round(plan_ms, 2),
         "peak_mem_gib": round(peak_mem, 3),
+        "ws_bytes": max(info.ws_fwd_bytes, info.ws_bwd_bytes),
+        "bwd_items": {"items": info.items, "half": info.items_half,
+                      "partial_blocks": info.part_blocks,
+                      "comp_item_chunks": info.comp_item_chunks},
         "wall_s": round(wall, 3),
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
         "roofline": roofline,

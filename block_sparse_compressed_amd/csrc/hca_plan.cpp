@@ -40,12 +40,17 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // extra partial sums cost little once the reduction streamed them in groups).
 constexpr int64_t kItemPositions = 64;
 
-// Items of a compressed key tile span a run of chunks (its rows can number
-// up to S x H, so one item per chunk would make the partial gradients grow
-// as S^2 / r): by default a run is sized so that one item is at most a
-// quarter of an even share of the whole backward over kCuTarget compute
-// units, which keeps the launch balanced and the number of compressed-tile
-// partials near 4 kCuTarget for any S.
+// Items of a compressed key tile span a run of chunks: its rows can number up
+// to S x H, so one item per chunk would make the partial gradients grow as
+// S^2 / r.  Runs are kept as short as possible, though: items of different
+// key tiles over the same chunk stream the same rows, and when a compressed
+// tile's item covers several chunks it reads them long after the raw tiles'
+// items over the same chunks did, so the rows come from HBM twice (S = 65536:
+// dKV 9.0 ms with one-chunk runs, 10.3 with two, 10.5 with four).  By
+// default the run doubles from one chunk only until the compressed tiles'
+// partial blocks fit in twice the raw tiles' (which grow as S), with a floor
+// of 4 kCuTarget blocks: the workspace stays O(S) and shorter problems keep
+// one-chunk items.
 constexpr int64_t kCuTarget = 256;
 
 // Half-tile items (128-key tiles whose item sees one 64-key half) run in a
@@ -394,11 +399,24 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     }
     // Chunks per compressed-tile item (raw tiles: one chunk per item; their
     // keys are seen by at most W + kv_bk - 1 positions).
+    auto count_items = [&](int kind, int64_t run) {  // items of `kind` with runs of `run` qts
+      int64_t n = 0;
+      for (int b = 0; b < B; ++b)
+        for (int64_t t = kind ? nkvr : 0; t < (kind ? nkv : nkvr); ++t) {
+          const std::vector<uint32_t> &list = lists[(size_t)b * nkv + t];
+          for (size_t e = 0; e < list.size(); ++e)
+            if (e == 0 || (list[e] & kEntIdx) / run != (list[e - 1] & kEntIdx) / run) ++n;
+        }
+      return n;
+    };
     int64_t cchunks = comp_chunks_cfg;
     if (cchunks == 0) {
-      const int64_t cap = total_entries / (4 * kCuTarget);  // query tiles per item at most
-      cchunks = std::max<int64_t>(1, cap / chunk);
+      const int64_t budget = std::max<int64_t>(2 * count_items(0, chunk), 4 * kCuTarget);
+      cchunks = 1;
+      while (cchunks < ceil_div(nqt, chunk) && count_items(1, chunk * cchunks) > budget)
+        cchunks *= 2;
     }
+    (void)total_entries;
     const int64_t ngrid = ceil_div(ceil_div(nqt, chunk), cchunks);  // item groups per row
     p->kvtile.assign((size_t)B * nkv * 2, 0);
     std::vector<int64_t> item_group;  // (b, run of cchunks chunks) of each item

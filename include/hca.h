@@ -85,10 +85,10 @@ enum { HCA_TILE_EMPTY = 0, HCA_TILE_PARTIAL = 1, HCA_TILE_FULL = 2 };
  *                     that half alone once the plan has at least this many
  *                     items; 0 = library choice (2048), < 0 = never.
  *   comp_item_chunks  64-position chunks of query rows per work item of a
- *                     compressed key tile; 0 = library choice (sized so that
- *                     one item is at most a quarter of an even share of the
- *                     work over 256 compute units, which also bounds the
- *                     number of partial gradients independently of S).
+ *                     compressed key tile; 0 = library choice (one chunk,
+ *                     doubled only while the compressed tiles' partial
+ *                     gradients would exceed twice the raw tiles', so the
+ *                     backward workspace stays O(S)).
  */
 typedef struct hca_tile_cfg {
   int32_t bq;
