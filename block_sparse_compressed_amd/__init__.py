@@ -31,7 +31,7 @@ HCA_TILE_EMPTY, HCA_TILE_PARTIAL, HCA_TILE_FULL = 0, 1, 2
 EXPORTS = (
     "hca_block_mask_build", "hca_plan_get_info", "hca_plan_export_tiles",
     "hca_plan_export_rows", "hca_plan_export_items", "hca_plan_upload", "hca_plan_destroy",
-    "hca_attn_fwd",
+    "hca_attn_fwd", "hca_attn_fwd_noalloc",
     "hca_attn_bwd", "hca_timing_enable", "hca_timing_read", "hca_status_string",
     "hca_last_error",
 )
@@ -100,6 +100,8 @@ def _load_library():
     lib.hca_plan_destroy.restype = None
     lib.hca_attn_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, u64, vp]
     lib.hca_attn_fwd.restype = ctypes.c_int
+    lib.hca_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    lib.hca_attn_fwd_noalloc.restype = ctypes.c_int
     lib.hca_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                  u64, vp]
     lib.hca_attn_bwd.restype = ctypes.c_int
@@ -288,6 +290,28 @@ def hca_attn_fwd(plan: Plan, q, kv, kv_comp, scale, o, lse, ws, stream=None):
     _expect(lse, "lse", (i.B, i.H, i.S), torch.float32)
     _check(_lib.hca_attn_fwd(plan.handle, _ptr(q), _ptr(kv), _ptr(kv_comp), float(scale),
                              _ptr(o), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+# Scratch the library holds per device for hca_attn_fwd_noalloc (include/hca.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def hca_attn_fwd_noalloc(plan: Plan, q, kv, kv_comp, scale, o, lse, stream=None):
+    """Forward with the library's own scratch as workspace (no workspace argument,
+    no device allocation in the call); plans with ws_fwd_bytes above
+    NOALLOC_SCRATCH_BYTES are refused."""
+    import torch
+
+    i = hca_plan_get_info(plan)
+    et = _elem_dtype(i)
+    _expect(q, "q", (i.B, i.H, i.S, i.D), et)
+    _expect(kv, "kv", (i.B, i.S, i.D), et)
+    if i.S_c > 0:
+        _expect(kv_comp, "kv_comp", (i.B, i.S_c, i.D), et)
+    _expect(o, "o", (i.B, i.H, i.S, i.D), et)
+    _expect(lse, "lse", (i.B, i.H, i.S), torch.float32)
+    _check(_lib.hca_attn_fwd_noalloc(plan.handle, _ptr(q), _ptr(kv), _ptr(kv_comp), float(scale),
+                                     _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def hca_attn_bwd(plan: Plan, q, kv, kv_comp, o, lse, dout, scale, dq, dkv, dkv_comp, ws,

@@ -93,10 +93,11 @@ bool g_timing = false;
 std::vector<TimingRec> g_recs;
 
 // Runs `launch` (which enqueues one library kernel on `stream`), bracketed by
-// events when timing is enabled.
+// events when timing is enabled and `allowed` (the allocation-free entry
+// point never creates events).
 template <class F>
-int timed(int kid, void *stream, F launch) {
-  if (!g_timing) return launch();
+int timed(int kid, void *stream, F launch, bool allowed = true) {
+  if (!g_timing || !allowed) return launch();
   hipEvent_t a = nullptr, b = nullptr;
   if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return launch();
   hipEventRecord(a, (hipStream_t)stream);
@@ -152,20 +153,24 @@ extern "C" hca_status hca_plan_upload(hca_plan *plan, void *dev_buf, uint64_t by
   return HCA_OK;
 }
 
-extern "C" hca_status hca_attn_fwd(const hca_plan *plan, const void *q, const void *kv,
-                                   const void *kv_comp, float scale, void *o, float *lse,
-                                   void *ws, uint64_t ws_bytes, void *hip_stream) {
-  const char *fn = "hca_attn_fwd";
-  if (hca_status s = check_common(fn, plan, scale, ws, ws_bytes, plan ? plan->ws.fwd_total : 0))
-    return s;
+namespace {
+
+// Checks of the forward's pointer arguments (after check_common).
+hca_status check_fwd_ptrs(const char *fn, const hca_plan *plan, const void *q, const void *kv,
+                          const void *kv_comp, const void *o, const float *lse) {
   if (hca_status s = check_ptr(fn, "q", q)) return s;
   if (hca_status s = check_ptr(fn, "kv", kv)) return s;
   if (plan->info.S_c > 0)
     if (hca_status s = check_ptr(fn, "kv_comp", kv_comp)) return s;
   if (hca_status s = check_ptr(fn, "o", o)) return s;
   if (hca_status s = check_ptr(fn, "lse", lse)) return s;
-  if (!plan->dev) return fail(HCA_ERR_STATE, std::string(fn) + ": plan was not uploaded");
+  return HCA_OK;
+}
 
+// The forward's kernel sequence on a checked plan and workspace.
+hca_status run_fwd(const char *fn, const hca_plan *plan, const void *q, const void *kv,
+                   const void *kv_comp, float scale, void *o, float *lse, void *ws,
+                   void *hip_stream, bool timing = true) {
   const Dims d = make_dims(plan);
   const DevPlan p = make_devplan(plan);
   int err;
@@ -173,8 +178,8 @@ extern "C" hca_status hca_attn_fwd(const hca_plan *plan, const void *q, const vo
     err = timed(K_FWD_F32, hip_stream, [&] {
       return launch_fwd_f32(d, p, (const float *)q, (const float *)kv, (const float *)kv_comp,
                             scale, (float *)o, lse, hip_stream);
-    });
-    if (err) return hip_fail("hca_attn_fwd (float32 kernel)", err);
+    }, timing);
+    if (err) return hip_fail((std::string(fn) + " (float32 kernel)").c_str(), err);
     return HCA_OK;
   }
   uint8_t *w = static_cast<uint8_t *>(ws);
@@ -182,14 +187,56 @@ extern "C" hca_status hca_attn_fwd(const hca_plan *plan, const void *q, const vo
   err = timed(K_TRANSPOSE, hip_stream, [&] {
     return launch_transpose_kv(kv, kvt, d.S, d.S_pad, d.Sc > 0 ? kv_comp : nullptr, kvct, d.Sc,
                                d.Sc_pad, d.B, d.D, hip_stream);
-  });
-  if (err) return hip_fail("hca_attn_fwd (transpose)", err);
+  }, timing);
+  if (err) return hip_fail((std::string(fn) + " (transpose)").c_str(), err);
   err = timed(K_FWD, hip_stream, [&] {
     return launch_fwd_bf16(d, p, q, kv, kv_comp ? kv_comp : kv, kvt, kvct, scale, o, lse,
                            hip_stream);
-  });
-  if (err) return hip_fail("hca_attn_fwd (forward kernel)", err);
+  }, timing);
+  if (err) return hip_fail((std::string(fn) + " (forward kernel)").c_str(), err);
   return HCA_OK;
+}
+
+}  // namespace
+
+extern "C" hca_status hca_attn_fwd(const hca_plan *plan, const void *q, const void *kv,
+                                   const void *kv_comp, float scale, void *o, float *lse,
+                                   void *ws, uint64_t ws_bytes, void *hip_stream) {
+  const char *fn = "hca_attn_fwd";
+  if (hca_status s = check_common(fn, plan, scale, ws, ws_bytes, plan ? plan->ws.fwd_total : 0))
+    return s;
+  if (hca_status s = check_fwd_ptrs(fn, plan, q, kv, kv_comp, o, lse)) return s;
+  if (!plan->dev) return fail(HCA_ERR_STATE, std::string(fn) + ": plan was not uploaded");
+  return run_fwd(fn, plan, q, kv, kv_comp, scale, o, lse, ws, hip_stream);
+}
+
+extern "C" hca_status hca_attn_fwd_noalloc(const hca_plan *plan, const void *q, const void *kv,
+                                           const void *kv_comp, float scale, void *o,
+                                           float *lse, void *hip_stream) {
+  const char *fn = "hca_attn_fwd_noalloc";
+  if (!plan) return fail(HCA_ERR_INVALID_ARG, std::string(fn) + ": plan is NULL");
+  if (!plan->info.kernel_ok)
+    return fail(HCA_ERR_UNSUPPORTED, std::string(fn) + ": " + plan->unsupported);
+  if (plan->ws.fwd_total > kNoAllocScratchBytes)
+    return fail(HCA_ERR_WORKSPACE,
+                std::string(fn) + ": the forward needs " + std::to_string(plan->ws.fwd_total) +
+                    " bytes of workspace; the library's scratch holds " +
+                    std::to_string(kNoAllocScratchBytes) + " (use hca_attn_fwd)");
+  // The scratch stands in for the workspace: its size is the limit checked
+  // above, its address is known only after the checks that precede any HIP call.
+  static char placeholder alignas(16);
+  if (hca_status s = check_common(fn, plan, scale, &placeholder, kNoAllocScratchBytes,
+                                  plan->ws.fwd_total))
+    return s;
+  if (hca_status s = check_fwd_ptrs(fn, plan, q, kv, kv_comp, o, lse)) return s;
+  if (!plan->dev) return fail(HCA_ERR_STATE, std::string(fn) + ": plan was not uploaded");
+  void *ws = nullptr;
+  if (plan->ws.fwd_total > 0) {
+    int err = 0;
+    ws = noalloc_scratch(&err);
+    if (!ws) return hip_fail("hca_attn_fwd_noalloc (scratch address)", err);
+  }
+  return run_fwd(fn, plan, q, kv, kv_comp, scale, o, lse, ws, hip_stream, false);
 }
 
 extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const void *kv,

@@ -16,6 +16,7 @@
 // consecutive keys, which is exactly the B operand layout the PV product
 // needs, so P never goes through LDS.
 #include <climits>
+#include <mutex>
 
 #include "hca_device.h"
 #include "hca_internal.h"
@@ -693,6 +694,39 @@ int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+// Library-held scratch of the allocation-free forward (hca_attn_fwd_noalloc):
+// the tile images of the call's kv and kv_comp.  Each device the library runs
+// on holds one copy until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol, never a device address: kernels receive the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, resolved once per device
+// (nullptr and *err set if the device or the symbol cannot be queried).
+void *noalloc_scratch(int *err) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    *err = e != hipSuccess ? (int)e : (int)hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  *err = 0;
+  return addr[dev];
 }
 
 }  // namespace hca

@@ -102,6 +102,11 @@ int launch_bwd_f32(const Dims &d, const DevPlan &p, const float *q, const float 
                    const float *kvc, const float *o, const float *lse, const float *dout,
                    float scale, float *dq, float *dkv, float *dkvc, float *delta, void *stream);
 
+// Scratch of the allocation-free forward: a file-scope device array in
+// hca_fwd.hip of this many bytes (the limit hca.h states).
+constexpr uint64_t kNoAllocScratchBytes = HCA_NOALLOC_SCRATCH_BYTES;
+void *noalloc_scratch(int *err);
+
 // Tile shapes the GPU kernels are built for ("" = supported, else the reason).
 std::string kernel_supports(int dtype, int D, int H, int bq, int bk_raw, int bk_comp);
 // Sizes the kernels' 32-bit offsets can address ("" = fine, else the reason).

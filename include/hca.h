@@ -221,6 +221,28 @@ hca_status hca_attn_fwd(const hca_plan *plan, const void *q, const void *kv, con
                         void *hip_stream);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory and
+ * cannot hand over a workspace either: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same operation, checks,
+ * kernels and results as hca_attn_fwd (bit for bit), but its workspace is a
+ * scratch array the library holds in device memory: HCA_NOALLOC_SCRATCH_BYTES
+ * per device, resolved once per device on the first call there (the calling
+ * thread's current device must be the stream's).  The call makes no device
+ * allocation and no allocating library call.  Every byte the kernels read from
+ * the scratch is written earlier in the same call, so no clearing is needed.
+ * All calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race and must not be
+ * issued; calls in sequence on one stream are fine.
+ * Errors: as hca_attn_fwd, plus HCA_ERR_WORKSPACE (before any HIP call) when
+ * the plan's ws_fwd_bytes exceeds HCA_NOALLOC_SCRATCH_BYTES, and HCA_ERR_HIP
+ * when the device or the scratch address cannot be queried.
+ */
+#define HCA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+hca_status hca_attn_fwd_noalloc(const hca_plan *plan, const void *q, const void *kv,
+                                const void *kv_comp, float scale, void *o, float *lse,
+                                void *hip_stream);
+
+/*
  * Backward pass: dq, dkv (raw) and dkv_comp (compressed), all in the plan
  * dtype, given the forward's o and lse and the loss gradient dout.
  *   dq[b,h,i]  = scale * sum_k dS_k kv_k

@@ -178,6 +178,27 @@ def test_negative_comp_item_chunks_rejected():
     assert s == hca.HCA_ERR_INVALID_ARG and out.value is None
 
 
+def test_fwd_noalloc_error_paths(plan):
+    """The allocation-free forward checks its arguments like hca_attn_fwd, and
+    refuses a plan whose forward workspace exceeds the library's scratch, all
+    before any HIP call."""
+    f = lib.hca_attn_fwd_noalloc
+    args = lambda **o: fwd_args(plan, **o)[:7] + (None,)
+    assert f(*args()) == hca.HCA_ERR_STATE
+    assert f(*args(q=None)) == hca.HCA_ERR_INVALID_ARG
+    assert f(*args(lse=FAKE + 4)) == hca.HCA_ERR_INVALID_ARG
+    assert f(*args(scale=0.0)) == hca.HCA_ERR_INVALID_ARG
+    assert f(None, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE, None) == \
+        hca.HCA_ERR_INVALID_ARG
+    # S = 40000 at D = 512: 80 MiB of tile images, past the 64 MiB scratch
+    big = hca.hca_block_mask_build(1, 40000, 128, 128, 312, H=8, D=512, dtype=hca.HCA_BF16)
+    assert hca.hca_plan_get_info(big).ws_fwd_bytes > hca.NOALLOC_SCRATCH_BYTES
+    assert f(*(fwd_args(big)[:7] + (None,))) == hca.HCA_ERR_WORKSPACE
+    assert "scratch" in lib.hca_last_error().decode()
+    unsup = hca.hca_block_mask_build(1, 64, 8, 4, 8, H=3, D=64, dtype=hca.HCA_BF16)
+    assert f(*(fwd_args(unsup)[:7] + (None,))) == hca.HCA_ERR_UNSUPPORTED
+
+
 def test_upload_checks(plan):
     info = hca.hca_plan_get_info(plan)
     assert lib.hca_plan_upload(plan.handle, None, info.device_bytes, None) == \
