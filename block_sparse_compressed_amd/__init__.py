@@ -29,7 +29,8 @@ HCA_TILE_EMPTY, HCA_TILE_PARTIAL, HCA_TILE_FULL = 0, 1, 2
 
 # Declared in include/hca.h; the ABI test checks the header and this list agree.
 EXPORTS = (
-    "hca_block_mask_build", "hca_plan_get_info", "hca_plan_export_tiles",
+    "hca_block_mask_build", "hca_block_mask_build_gqa", "hca_plan_get_info",
+    "hca_plan_export_tiles",
     "hca_plan_export_rows", "hca_plan_export_items", "hca_plan_upload", "hca_plan_destroy",
     "hca_attn_fwd", "hca_attn_fwd_noalloc",
     "hca_attn_bwd", "hca_timing_enable", "hca_timing_read", "hca_status_string",
@@ -63,7 +64,7 @@ class _PlanInfo(ctypes.Structure):
         "tiles_raw", "tiles_comp", "full_raw", "full_comp", "pairs_raw", "pairs_comp")] + [
         (n, ctypes.c_uint64) for n in ("device_bytes", "ws_fwd_bytes", "ws_bwd_bytes")] + [
         (n, ctypes.c_int64) for n in ("items", "items_half", "part_blocks")] + [
-        (n, ctypes.c_int32) for n in ("comp_item_chunks", "reserved_")]
+        (n, ctypes.c_int32) for n in ("comp_item_chunks", "kv_heads")]
 
 
 class _KernelTime(ctypes.Structure):
@@ -86,6 +87,9 @@ def _load_library():
     lib.hca_block_mask_build.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32,
                                          vp, ctypes.POINTER(vp)]
     lib.hca_block_mask_build.restype = ctypes.c_int
+    lib.hca_block_mask_build_gqa.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i32, i32,
+                                             i32, i32, vp, ctypes.POINTER(vp)]
+    lib.hca_block_mask_build_gqa.restype = ctypes.c_int
     lib.hca_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
     lib.hca_plan_get_info.restype = ctypes.c_int
     lib.hca_plan_export_tiles.argtypes = [vp, vp, vp]
@@ -150,7 +154,7 @@ class PlanInfo:
     tiles_raw: int; tiles_comp: int; full_raw: int; full_comp: int
     pairs_raw: int; pairs_comp: int
     device_bytes: int; ws_fwd_bytes: int; ws_bwd_bytes: int
-    items: int; items_half: int; part_blocks: int; comp_item_chunks: int; reserved_: int
+    items: int; items_half: int; part_blocks: int; comp_item_chunks: int; kv_heads: int
 
 
 class Plan:
@@ -181,17 +185,35 @@ def _i32(a: Optional[Sequence[int]]):
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
+def _cfg(tiles):
+    if tiles is None:
+        return None
+    return _TileCfg(*(tuple(tiles) + (0,) * (5 - len(tiles))))
+
+
 def hca_block_mask_build(B, S, r, W, S_c, seg_starts=None, seg_counts=None, H=1, D=64,
                          dtype=HCA_BF16, mode=HCA_COMPSEG_STRICT, tiles=None) -> Plan:
     """tiles: None or (bq, bk_raw, bk_comp[, half_items_min[, comp_item_chunks]]),
     0 = library choice (see hca_tile_cfg in include/hca.h)."""
     starts, counts = _i32(seg_starts), _i32(seg_counts)
-    cfg = None
-    if tiles is not None:
-        cfg = _TileCfg(*(tuple(tiles) + (0,) * (5 - len(tiles))))
+    cfg = _cfg(tiles)
     out = ctypes.c_void_p()
     _check(_lib.hca_block_mask_build(
         B, S, r, W, S_c,
+        starts.ctypes.data if starts is not None else None,
+        counts.ctypes.data if counts is not None else None,
+        H, D, dtype, mode, ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out)))
+    return Plan(out.value)
+
+
+def hca_block_mask_build_gqa(B, kv_heads, S, r, W, S_c, seg_starts=None, seg_counts=None, H=1,
+                             D=64, dtype=HCA_BF16, mode=HCA_COMPSEG_STRICT, tiles=None) -> Plan:
+    """Plan with kv_heads key/value heads (query head h uses kv head h // (H // kv_heads))."""
+    starts, counts = _i32(seg_starts), _i32(seg_counts)
+    cfg = _cfg(tiles)
+    out = ctypes.c_void_p()
+    _check(_lib.hca_block_mask_build_gqa(
+        B, kv_heads, S, r, W, S_c,
         starts.ctypes.data if starts is not None else None,
         counts.ctypes.data if counts is not None else None,
         H, D, dtype, mode, ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out)))
@@ -205,19 +227,21 @@ def hca_plan_get_info(plan: Plan) -> PlanInfo:
 
 
 def hca_plan_export_tiles(plan: Plan):
-    """Returns (raw [B, nqt, nkt_raw], comp [B, nqt, nkt_comp]) uint8 tables."""
+    """Returns (raw [B * kv_heads, nqt, nkt_raw], comp [B * kv_heads, nqt, nkt_comp])
+    uint8 tables."""
     i = hca_plan_get_info(plan)
-    raw = np.empty((i.B, i.nqt, i.nkt_raw), dtype=np.uint8)
-    comp = np.empty((i.B, i.nqt, i.nkt_comp), dtype=np.uint8)
+    nb = i.B * i.kv_heads
+    raw = np.empty((nb, i.nqt, i.nkt_raw), dtype=np.uint8)
+    comp = np.empty((nb, i.nqt, i.nkt_comp), dtype=np.uint8)
     _check(_lib.hca_plan_export_tiles(plan.handle, raw.ctypes.data if raw.size else None,
                                       comp.ctypes.data if comp.size else None))
     return raw, comp
 
 
 def hca_plan_export_rows(plan: Plan) -> np.ndarray:
-    """Per-position intervals [B, S, 3] int32: raw_lo, comp_lo, comp_hi."""
+    """Per-position intervals [B * kv_heads, S, 3] int32: raw_lo, comp_lo, comp_hi."""
     i = hca_plan_get_info(plan)
-    rows = np.empty((i.B, i.S, 3), dtype=np.int32)
+    rows = np.empty((i.B * i.kv_heads, i.S, 3), dtype=np.int32)
     _check(_lib.hca_plan_export_rows(plan.handle, rows.ctypes.data))
     return rows
 
@@ -271,6 +295,13 @@ def _expect(t, name, shape, dtype):
                                                                    tuple(t.shape), t.dtype))
 
 
+def _kv_shape(info, n):
+    """Shape of kv / dkv (n = S) or kv_comp / dkv_comp (n = S_c)."""
+    if info.kv_heads == 1:
+        return (info.B, n, info.D)
+    return (info.B, info.kv_heads, n, info.D)
+
+
 def _elem_dtype(info):
     import torch
 
@@ -283,9 +314,9 @@ def hca_attn_fwd(plan: Plan, q, kv, kv_comp, scale, o, lse, ws, stream=None):
     i = hca_plan_get_info(plan)
     et = _elem_dtype(i)
     _expect(q, "q", (i.B, i.H, i.S, i.D), et)
-    _expect(kv, "kv", (i.B, i.S, i.D), et)
+    _expect(kv, "kv", _kv_shape(i, i.S), et)
     if i.S_c > 0:
-        _expect(kv_comp, "kv_comp", (i.B, i.S_c, i.D), et)
+        _expect(kv_comp, "kv_comp", _kv_shape(i, i.S_c), et)
     _expect(o, "o", (i.B, i.H, i.S, i.D), et)
     _expect(lse, "lse", (i.B, i.H, i.S), torch.float32)
     _check(_lib.hca_attn_fwd(plan.handle, _ptr(q), _ptr(kv), _ptr(kv_comp), float(scale),
@@ -305,9 +336,9 @@ def hca_attn_fwd_noalloc(plan: Plan, q, kv, kv_comp, scale, o, lse, stream=None)
     i = hca_plan_get_info(plan)
     et = _elem_dtype(i)
     _expect(q, "q", (i.B, i.H, i.S, i.D), et)
-    _expect(kv, "kv", (i.B, i.S, i.D), et)
+    _expect(kv, "kv", _kv_shape(i, i.S), et)
     if i.S_c > 0:
-        _expect(kv_comp, "kv_comp", (i.B, i.S_c, i.D), et)
+        _expect(kv_comp, "kv_comp", _kv_shape(i, i.S_c), et)
     _expect(o, "o", (i.B, i.H, i.S, i.D), et)
     _expect(lse, "lse", (i.B, i.H, i.S), torch.float32)
     _check(_lib.hca_attn_fwd_noalloc(plan.handle, _ptr(q), _ptr(kv), _ptr(kv_comp), float(scale),
@@ -323,10 +354,10 @@ def hca_attn_bwd(plan: Plan, q, kv, kv_comp, o, lse, dout, scale, dq, dkv, dkv_c
     for t, n in ((q, "q"), (o, "o"), (dout, "dout"), (dq, "dq")):
         _expect(t, n, (i.B, i.H, i.S, i.D), et)
     for t, n in ((kv, "kv"), (dkv, "dkv")):
-        _expect(t, n, (i.B, i.S, i.D), et)
+        _expect(t, n, _kv_shape(i, i.S), et)
     if i.S_c > 0:
-        _expect(kv_comp, "kv_comp", (i.B, i.S_c, i.D), et)
-        _expect(dkv_comp, "dkv_comp", (i.B, i.S_c, i.D), et)
+        _expect(kv_comp, "kv_comp", _kv_shape(i, i.S_c), et)
+        _expect(dkv_comp, "dkv_comp", _kv_shape(i, i.S_c), et)
     _expect(lse, "lse", (i.B, i.H, i.S), torch.float32)
     _check(_lib.hca_attn_bwd(plan.handle, _ptr(q), _ptr(kv), _ptr(kv_comp), _ptr(o), _ptr(lse),
                              _ptr(dout), float(scale), _ptr(dq), _ptr(dkv), _ptr(dkv_comp),
@@ -353,15 +384,20 @@ class HcaAttention:
     """
 
     def __init__(self, B, S, H, D, r, W, dtype="bf16", seg_starts=None, seg_counts=None,
-                 mode=HCA_COMPSEG_STRICT, tiles=None, device="cuda"):
+                 mode=HCA_COMPSEG_STRICT, tiles=None, device="cuda", kv_heads=1):
         import torch
 
         self.B, self.S, self.H, self.D, self.r, self.W = B, S, H, D, r, W
         self.S_c = S // r
+        self.kv_heads = kv_heads
         self.dtype = HCA_BF16 if dtype == "bf16" else HCA_F32
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.plan = hca_block_mask_build(B, S, r, W, self.S_c, seg_starts, seg_counts, H, D,
-                                         self.dtype, mode, tiles)
+        if kv_heads == 1:
+            self.plan = hca_block_mask_build(B, S, r, W, self.S_c, seg_starts, seg_counts, H, D,
+                                             self.dtype, mode, tiles)
+        else:
+            self.plan = hca_block_mask_build_gqa(B, kv_heads, S, r, W, self.S_c, seg_starts,
+                                                 seg_counts, H, D, self.dtype, mode, tiles)
         self.info = hca_plan_get_info(self.plan)
         self.device = torch.device(device)
         buf = torch.empty(max(1, self.info.device_bytes), dtype=torch.uint8, device=self.device)
@@ -385,8 +421,9 @@ class HcaAttention:
 
         dq = torch.empty((self.B, self.H, self.S, self.D), dtype=self.torch_dtype,
                          device=self.device)
-        dkv = torch.empty((self.B, self.S, self.D), dtype=self.torch_dtype, device=self.device)
-        dkvc = torch.empty((self.B, self.S_c, self.D), dtype=self.torch_dtype,
+        dkv = torch.empty(_kv_shape(self.info, self.S), dtype=self.torch_dtype,
+                          device=self.device)
+        dkvc = torch.empty(_kv_shape(self.info, self.S_c), dtype=self.torch_dtype,
                            device=self.device)
         return dq, dkv, dkvc
 

@@ -25,13 +25,14 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 Dims make_dims(const hca_plan *plan) {
   const hca_plan_info &in = plan->info;
   Dims d{};
-  d.B = in.B; d.S = in.S; d.H = in.H; d.D = in.D; d.r = in.r; d.W = in.W; d.Sc = in.S_c;
+  // B x kv_heads MQA problems of H / kv_heads heads each (see hca_block_mask_build_gqa)
+  d.B = plan->rows_b; d.S = in.S; d.H = in.H / in.kv_heads; d.D = in.D; d.r = in.r;
+  d.W = in.W; d.Sc = in.S_c;
   d.bq = in.bq; d.bk_raw = in.bk_raw; d.bk_comp = in.bk_comp;
   d.nqt = in.nqt; d.nkt_raw = in.nkt_raw; d.nkt_comp = in.nkt_comp;
   d.S_pad = in.nkt_raw * in.bk_raw;
   d.Sc_pad = in.nkt_comp * in.bk_comp;
   d.n_items = (int32_t)plan->kvorder.size();  // launch slots (items + padding)
-  d.n_items_full = plan->n_order_full;
   d.kv_bk = plan->kv_bk;
   d.nkv_raw = plan->nkv_raw;
   d.nkv_comp = plan->nkv_comp;

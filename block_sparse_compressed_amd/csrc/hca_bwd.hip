@@ -16,13 +16,14 @@
 //     an on-chip dQ reduction; here the whole dQ row stays on chip).
 //  2. key-stationary dKV: a workgroup owns one work item -- a key tile (raw
 //     or compressed; 128 keys at D = 512, 32 otherwise) and the query tiles
-//     of one 64-position chunk that see it -- recomputing S and dP with the
-//     tile's K fragments held in VGPRs.  At D = 512, items whose rows see only
-//     one 64-key half of their tile run as a second launch over that half.
-//     Each item writes a float32 partial.
+//     of a run of 64-position chunks that see it -- recomputing S and dP with
+//     the tile's K fragments held in VGPRs.  At D = 512, items whose rows see
+//     only one 64-key half of their tile run over that half.  Each item
+//     writes a float32 partial.
 //  3. a fixed-order reduction of the partials into dKV and dKV_comp, so the
 //     result is bitwise reproducible.
 #include <atomic>
+#include <type_traits>
 #include <climits>
 
 #include "hca_device.h"
@@ -755,96 +756,84 @@ __global__ void __launch_bounds__(256, 1)
   }
 }
 
-// ---------------------------------------------------------------------------
-// 2b. dKV at D = 512, key-stationary.  A work item is a 128-key tile and a run
-//     of query tiles that see it.  Query rows stream through LDS in 32-row
-//     steps (Q and dO, 64 KiB, double-buffered, direct global->LDS copies,
-//     swizzled rows).  Each step has two phases:
-//       scores    wave w forms S = Q K^T and dP = dO K^T for all 32 rows and
-//                 its 32 keys (K fragments of those keys held in VGPRs); then
-//                 P = 2^(S log2e scale - LSE log2e), dS = scale P (dP - delta),
-//                 stored as bf16 in exchange tiles in LDS (fragment order);
-//       gradient  wave w accumulates dKV^T[d][key] += Q^T dS + dO^T P over the
-//                 step's rows for its quarter of the columns, d in
-//                 [128 w, 128 w + 128), and all 128 keys: A operands are
-//                 ds_read_b64_tr_b16 reads of the row-major Q / dO tiles, B
-//                 operands come from the exchange tile, and the fp32 sums
-//                 (256 per lane) stay in accumulation registers for the item.
-//     128 keys per item give each 64 KiB row copy 2 x 256 MFMAs per wave of
-//     work, long enough to hide the copy of the next step behind it.
-// ---------------------------------------------------------------------------
 // Transposed A operand (d-row j of a 16-wide column block, rows 8g..8g+7 of
-// the step) from a swizzled row-major [rows][512] tile: two transpose reads.
+// a step) from a swizzled row-major [rows][512] tile: two transpose reads.
 __device__ __forceinline__ bf16x8 tr_frag(const char *p) { return tr_frag_rows(p, 4096); }
 
-
-template <int NW, int HALF>
-__global__ void __launch_bounds__(NW * 64, 1)
-    hca_bwd_dkv512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
-                          const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
-                          const float *__restrict__ lse, const float *__restrict__ delta,
-                          const bf16raw *__restrict__ dout, float scale_log2, float scale,
-                          float *__restrict__ part, int slot0) {
-  constexpr int D = 512, KS = D / 32;
-  constexpr int KEYS = 128, STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = KEYS * STEP * 2;
-  static_assert(NW == 4, "4 waves: 32 score keys and one column quarter each");
+// ---------------------------------------------------------------------------
+// 2b. dKV at D = 512, key-stationary, eight waves (two per SIMD).  A work
+//     item is a 128-key tile and the query tiles of one chunk of positions
+//     that see it.  Query rows stream through LDS in 32-row steps (Q and dO,
+//     64 KiB, double-buffered, direct global->LDS copies, rows stored with
+//     their 16-byte chunks XOR-swizzled).  Each step has two phases:
+//       scores    S = Q K^T and dP = dO K^T for the wave's keys (K fragments
+//                 held in VGPRs); P = 2^(S log2e scale - LSE log2e), dS =
+//                 scale P (dP - delta), stored as bf16 in exchange tiles in
+//                 LDS in MFMA fragment order;
+//       gradient  dKV^T[d][key] += Q^T dS + dO^T P over the step's rows, A
+//                 operands from ds_read_b64_tr_b16 reads of the row tiles,
+//                 B operands from the exchange tiles.
+//     Wave w holds the K fragments of 16 keys (64
+//     registers) and accumulates dKV^T for 64 columns, d in [64 w, 64 w + 64),
+//     over all 128 keys (128 accumulation registers), so each wave needs at
+//     most 256 registers and a SIMD runs two waves.  (A four-wave version,
+//     32 score keys and 256 accumulators per wave, one wave per SIMD, ran
+//     8.9 ms at S = 65536 against 8.6 for this one.)  Items over all keys of their tile and items over one 64-key half
+//     run in the same launch (a wave-uniform branch per item), so both kinds
+//     stream the rows of one chunk together through the L2.
+//       full item  wave w scores keys 16 w .. 16 w + 15 of the tile for the
+//                  step's 32 rows; the gradient covers key blocks 0..7.
+//       half item  wave w scores keys 16 (w & 3) .. of the active half for
+//                  row block w >> 2 (16 rows); the gradient covers the half's
+//                  four key blocks.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(512, 1)
+    hca_bwd_dkv512x8_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                            const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
+                            const float *__restrict__ lse, const float *__restrict__ delta,
+                            const bf16raw *__restrict__ dout, float scale_log2, float scale,
+                            float *__restrict__ part) {
+  constexpr int D = 512, KS = D / 32, NW = 8;
+  constexpr int STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = 128 * STEP * 2;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * STEP_BYTES];  // [buf][Q | dO]
   __shared__ __attribute__((aligned(16))) char xs[2 * XBYTES];             // [P | dS]
-  // Row table per step slot: lse log2e, delta, first and one-past-last key.
-  __shared__ float4 ri_s[2][STEP];
+  __shared__ float4 ri_s[2][STEP];  // per step row: lse log2e, delta, key interval
 
-  // The wave index is made visibly wave-uniform so that the row bookkeeping
-  // below runs on the scalar unit.
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
-  const int item = p.kvorder[slot0 + blockIdx.x];
+  const int item = p.kvorder[blockIdx.x];
   if (item < 0) return;  // padding slot of the launch order
   const KvItem it = p.kvitem[item];
   const int b = it.b;
   const bool comp = it.kind != 0;
   const int nk = comp ? d.Sc : d.S;
-  const int k0 = it.kt * KEYS;   // first key of the item
+  const int k0 = it.kt * 128;
   const bf16raw *src = comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D;
-
   const int nq = it.e1 - it.e0;
-  // A query tile is bq positions x H heads (bq a power of two, bq * H a
-  // multiple of 128), rows ordered position-fastest: row rho is position
-  // qt * bq + (rho & (bq - 1)), head rho >> lbq.  SPQ steps of 32 rows each.
   const int lbq = __builtin_ctz(d.bq);
   const int SPQ = d.bq * d.H / STEP, lspq = __builtin_ctz(SPQ);
   const int nsteps = nq * SPQ;
-  // Lane e holds list entry e; the entries past the first 64 (long
-  // compressed-tile items) are read through the scalar cache.
   const uint32_t ent_lane = lane < nq ? p.kvent[it.e0 + lane] : 0u;
   auto entry = [&](int e) -> uint32_t {
     return e < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, e)
                   : uniform_load(p.kvent, it.e0 + e);
   };
   const size_t bat = (size_t)b * d.H * d.S * D;
-  // Byte offset of this lane's 16-byte chunk in a staged row: row r = 8 wave + i
-  // is stored with swizzle (i & 3) | (wave << 2).
-  uint32_t lane_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lane_off[i] = (uint32_t)((lane ^ (i | (wave << 2))) << 4);
-  // Step s covers rows u*32 .. u*32+31 of query tile entry e = s / SPQ.
-  auto stage = [&](int s) {
+  // Wave w stages rows 4 w .. 4 w + 3 of each step; row r's chunk c sits at
+  // slot c ^ sw(r), sw(r) = (r & 3) | ((r >> 3) << 2).
+  const uint32_t lane_sw = (uint32_t)(lane ^ ((wave >> 1) << 2));
+  auto copy_row = [&](int s, uint32_t qb_lds, int k) {  // row k >> 1 of this wave, Q or dO
     const int e = s >> lspq, u = s & (SPQ - 1);
     const int qt = (int)(entry(e) & kEntIdx);
-    const uint32_t qb = lds_addr(smem + (s & 1) * 2 * STEP_BYTES);
-#pragma unroll
-    for (int i = 0; i < STEP / NW; ++i) {
-      const int r = wave * (STEP / NW) + i;
-      const int rho = u * STEP + r;
-      const int pos = min(qt * d.bq + (rho & (d.bq - 1)), d.S - 1), h = rho >> lbq;
-      const size_t rowoff = bat + ((size_t)h * d.S + pos) * D;  // wave-uniform
-      dma16(q + rowoff, lane_off[i & 3], qb + r * 1024);
-      dma16(dout + rowoff, lane_off[i & 3], qb + STEP_BYTES + r * 1024);
-    }
+    const int i = k >> 1, r = 4 * wave + i, rho = u * STEP + r;
+    const int pos = min(qt * d.bq + (rho & (d.bq - 1)), d.S - 1), h = rho >> lbq;
+    const size_t rowoff = bat + ((size_t)h * d.S + pos) * D;  // wave-uniform
+    const uint32_t voff = (lane_sw ^ (uint32_t)i) << 4;
+    if (k & 1)
+      dma16(dout + rowoff, voff, qb_lds + STEP_BYTES + r * 1024);
+    else
+      dma16(q + rowoff, voff, qb_lds + r * 1024);
   };
-  // Row table of the next step (lse log2e, delta, key interval), loaded by
-  // every wave while the current step computes and written to LDS by wave 0
-  // at its end.  The loads are unconditional (clamped position) and their
-  // values are not touched until then, so no wait for them lands mid-step.
   int4 nrw = make_int4(0, 0, 0, 0);
   float nl = 0.f, nd = 0.f;
   int npos = 0;
@@ -870,221 +859,188 @@ __global__ void __launch_bounds__(NW * 64, 1)
       ri_s[slot][lane] = w;
     }
   };
-
-  // Score-phase A operands: row i of row block rb maps to step row
-  // 8 (i >> 2) + 4 rb + (i & 3), so lane (g, j) ends up holding rows
-  // 8 g .. 8 g + 7 of key j of each 16-key block (4 rb + v for block rb).
-  int qk_off[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n)
-    qk_off[n] = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (4 * (n ^ (j >> 2)) + (g ^ (j & 3)));
-  // Transpose-read offsets for the column blocks 8 wave + dl of this quarter.
-  int tr_off[8];
-  {
-    const int u = j >> 2, c0 = (j & 3) >> 1;
-#pragma unroll
-    for (int dl = 0; dl < 8; ++dl)
-      tr_off[dl] = (8 * g + u) * 1024 + (((2 * dl + c0) ^ (u + 4 * g)) << 4) + ((j & 1) << 3) +
-                   256 * wave;
-  }
-  // Exchange tiles (P and dS, up to 8 key blocks of 1 KiB) in fragment order:
-  // block kb holds keys 16 kb + j of the item's active keys, rows 8 g .. 8 g + 7
-  // at byte 16 l of lane l = 16 g + j, both as the score phase produces them
-  // and as the gradient reads them as B operands, so writes and reads are flat.
+  // Score A operands: lane j reads step row 8 (j >> 2) + (j & 3) (+ 4 for row
+  // block 1), chunk 4 ks + g, so lane (g, j) ends up with rows 8 g + 4 rb + v
+  // (v = 0..3) of key j of its 16-key block.
+  const int qk_base = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (g ^ (j & 3));
+  // Transposed A operands of the gradient, column block 4 wave + dl: d-row j,
+  // rows 8 g .. 8 g + 7 (two transpose reads, rows 8 g + (j >> 2) and + 4).
+  const int tr_sw = (8 * (wave & 1) + ((j & 3) >> 1)) ^ ((j >> 2) + 4 * g);
+  const int tr_base = (8 * g + (j >> 2)) * 1024 + 256 * (wave >> 1) + ((j & 1) << 3);
   const int xr0 = 16 * lane;
 
-  // HALF = 0: the item runs over all 128 keys of its tile.  HALF = 1 (a
-  // launch of its own, so its register allocation stays apart): items of
-  // which no row sees one 64-key half of the tile (the planner marks them:
-  // the first and last items of a sliding-window tile) run over the other
-  // half only; each wave scores 16 keys, the gradient covers 4 key blocks,
-  // and the idle half's partial is written as zeros.
-  constexpr int KPW = HALF ? 1 : 2;  // 16-key score blocks per wave
-  constexpr int NKB = 4 * KPW;       // active 16-key blocks of the item
-  const int hh = HALF ? (it.halves == 2 ? 1 : 0) : 0;  // active half
-  const int kbase = k0 + 64 * hh;
-  const int kw = kbase + 16 * KPW * wave;  // first of this wave's score keys
-  const int xw0 = 16 * lane + 1024 * KPW * wave;
-
-  // K fragments of this wave's score keys, B[k = d][n = key] of S = Q K^T.
-  // (Unconditional loads of a clamped key, zeroed past the end, so that all
-  // the loads are in flight together.)
-  bf16x8 kf[KPW][KS];
-#pragma unroll
-  for (int kb = 0; kb < KPW; ++kb) {
-    const int key = kw + 16 * kb + j;
+  const bool half = it.halves != 3;
+  const int hh = it.halves == 2 ? 1 : 0;  // active half of a half item
+  // This wave's 16 score keys.
+  const int skey = half ? k0 + 64 * hh + 16 * (wave & 3) : k0 + 16 * wave;
+  bf16x8 kf[KS];
+  {
+    const int key = skey + j;
     const bf16raw *krow = src + (size_t)min(key, nk - 1) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint4 v = *reinterpret_cast<const uint4 *>(krow + 32 * ks + 8 * g);
-      kf[kb][ks] = as_bf16x8(key < nk ? v : make_uint4(0, 0, 0, 0));
+      kf[ks] = as_bf16x8(key < nk ? v : make_uint4(0, 0, 0, 0));
     }
   }
-  floatx4 acc[NKB][8];  // [active 16-key block][16-column block of this wave's quarter]
+  floatx4 acc[8][4];  // [key block][column block of this wave]
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
+  for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int dl = 0; dl < 4; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if (nsteps > 0) {
-    stage(0);
+    const uint32_t qb0 = lds_addr(smem);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) copy_row(0, qb0, k);
     rowinfo(0);
     put_rowinfo(0);
   }
   wait_all_loads();
   __syncthreads();
 
-  for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) rowinfo(s + 1);
-    // Rows of the next step (on the last step: this step's rows again, into
-    // the idle buffer), copied one instruction per score k-step below so the
-    // wave never stalls issuing a burst of 16 copies.
-    const int sn = min(s + 1, nsteps - 1);
-    const int qt_n = (int)(entry(sn >> lspq) & kEntIdx), u_n = sn & (SPQ - 1);
-    const uint32_t qb_n = lds_addr(smem + ((s + 1) & 1) * 2 * STEP_BYTES);
-    auto copy_one = [&](int ks) {  // row ks >> 1 of this wave's 8, Q (even) or dO (odd)
-      const int i = ks >> 1, r = wave * (STEP / NW) + i, rho = u_n * STEP + r;
-      const int pos = min(qt_n * d.bq + (rho & (d.bq - 1)), d.S - 1), h = rho >> lbq;
-      const size_t rowoff = bat + ((size_t)h * d.S + pos) * D;  // wave-uniform
-      if (ks & 1)
-        dma16(dout + rowoff, lane_off[i & 3], qb_n + STEP_BYTES + r * 1024);
-      else
-        dma16(q + rowoff, lane_off[i & 3], qb_n + r * 1024);
-    };
-    const int slot = s & 1;
-    const bool full = entry(s >> lspq) & kEntFull;
-    const char *qb = smem + slot * 2 * STEP_BYTES;
-    const char *ob = qb + STEP_BYTES;
-    __builtin_amdgcn_sched_barrier(0);
+  // One step of `HALF` kind: scores, P / dS to the exchange tiles, gradient.
+  auto steps = [&](auto half_tag) {
+    constexpr int HALF = decltype(half_tag)::value;
+    constexpr int NRB = HALF ? 1 : 2;  // row blocks scored by this wave
+    constexpr int NKB = HALF ? 4 : 8;  // key blocks of the gradient
+    const int rb0 = HALF ? (wave >> 2) : 0;
+    const int xblk = HALF ? (wave & 3) : wave;  // exchange block this wave writes
+    for (int s = 0; s < nsteps; ++s) {
+      const int sn = min(s + 1, nsteps - 1);
+      const uint32_t qb_n = lds_addr(smem + ((s + 1) & 1) * 2 * STEP_BYTES);
+      const int slot = s & 1;
+      const bool full = entry(s >> lspq) & kEntFull;
+      // Per-step opaque copies of the lane offsets: left visible, the
+      // compiler hoists every derived address out of the step loop and has
+      // to spill them.
+      int qkb = qk_base, trb = tr_base, xr = xr0;
+      asm volatile("" : "+v"(qkb), "+v"(trb), "+v"(xr));
+      const char *qb = smem + slot * 2 * STEP_BYTES;
+      const char *ob = qb + STEP_BYTES;
+      __builtin_amdgcn_sched_barrier(0);
 
-    // Scores: operand fragments are read PF k-steps ahead of their MFMAs.
-    constexpr int PF = 1;
-    floatx4 sv[2][KPW], pv[2][KPW];  // [row block][key block]
+      // Scores, one row block after the other: fragments of k-step ks + 1 are
+      // read while the MFMAs of ks run (group barriers keep the compiler from
+      // hoisting every read).  The next step's rows are copied during the
+      // first row block, one instruction per two k-steps.
+      floatx4 sv[NRB], pv[NRB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < NRB; ++rb) {
+        sv[rb] = pv[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int rbo = 4096 * (rb0 + rb);
+        bf16x8 fq[KS], fo[KS];
+        auto fetch = [&](int ks) {
+          const int off = qkb + 64 * ((ks & 3) ^ (j >> 2)) + 256 * (ks >> 2) + rbo;
+          fq[ks] = lds_frag(qb + off);
+          fo[ks] = lds_frag(ob + off);
+        };
+        fetch(0);
 #pragma unroll
-      for (int kb = 0; kb < KPW; ++kb) sv[rb][kb] = pv[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    {
-      bf16x8 fq[2][KS], fo[2][KS];
-      auto qk_at = [&](int ks) { return qk_off[ks & 3] + 256 * (ks >> 2); };
-      auto fetch = [&](int ks) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          fq[rb][ks] = lds_frag(qb + qk_at(ks) + 4096 * rb);
-          fo[rb][ks] = lds_frag(ob + qk_at(ks) + 4096 * rb);
+        for (int ks = 0; ks < KS; ++ks) {
+          if (rb == 0 && (ks & 1) == 0) copy_row(sn, qb_n, ks >> 1);
+          if (ks + 1 < KS) fetch(ks + 1);
+          sv[rb] = mfma16x16x32(fq[ks], kf[ks], sv[rb]);
+          pv[rb] = mfma16x16x32(fo[ks], kf[ks], pv[rb]);
         }
-      };
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int ks = 0; ks < PF; ++ks) fetch(ks);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        copy_one(ks);
-        if (ks + PF < KS) fetch(ks + PF);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int kb = 0; kb < KPW; ++kb) {
-            sv[rb][kb] = mfma16x16x32(fq[rb][ks], kf[kb][ks], sv[rb][kb]);
-            pv[rb][kb] = mfma16x16x32(fo[rb][ks], kf[kb][ks], pv[rb][kb]);
-          }
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int ks = 0; ks < PF; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * KPW, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
 
-    // P and dS of rows 8 g .. 8 g + 7 for this wave's keys -> exchange tile.
-    {
-      float4 ri[8];
+      // P and dS of rows 8 g + 4 rb + v (v = 0..3) for key skey + j: bytes
+      // 8 rb .. 8 rb + 7 of this lane's 16 in the exchange block.
+      {
+        const int key = skey + j;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) ri[r] = ri_s[slot][8 * g + r];
-#pragma unroll
-      for (int kb = 0; kb < KPW; ++kb) {
-        const int key = kw + 16 * kb + j;
-        float pr[8], ds[8];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < NRB; ++rb) {
+          bf16x4 pp, dd;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float4 rr = ri[4 * rb + v];
-            // Branch-free: exp2 always, then a select (a branch per value would
-            // cost more than the exp2 it skips).
+            const float4 rr = ri_s[slot][8 * g + 4 * (rb0 + rb) + v];
             const bool vis =
                 full | ((key >= __float_as_int(rr.z)) & (key < __float_as_int(rr.w)));
-            const float ex = fast_exp2(sv[rb][kb][v] * scale_log2 - rr.x);
+            const float ex = fast_exp2(sv[rb][v] * scale_log2 - rr.x);
             const float e = vis ? ex : 0.f;
-            pr[4 * rb + v] = e;
-            ds[4 * rb + v] = e * (pv[rb][kb][v] - rr.y) * scale;
+            pp[v] = (__bf16)e;
+            dd[v] = (__bf16)(e * (pv[rb][v] - rr.y) * scale);
           }
-        *reinterpret_cast<bf16x8 *>(xs + xw0 + 1024 * kb) = pack8(pr);
-        *reinterpret_cast<bf16x8 *>(xs + XBYTES + xw0 + 1024 * kb) = pack8(ds);
-      }
-    }
-    lds_barrier();  // exchange tile complete; the next step's copies stay in flight
-
-    // Gradient, in two passes of four column blocks: the pass's transpose-read
-    // fragments are held, the exchange fragments stream through (read one
-    // key block ahead).
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      bf16x8 tq[4], to[4], xp[NKB], xd[NKB];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        tq[c] = tr_frag(qb + tr_off[4 * ps + c]);
-        to[c] = tr_frag(ob + tr_off[4 * ps + c]);
-      }
-      xd[0] = lds_frag(xs + XBYTES + xr0);
-      xp[0] = lds_frag(xs + xr0);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        if (kb + 1 < NKB) {
-          xd[kb + 1] = lds_frag(xs + XBYTES + xr0 + 1024 * (kb + 1));
-          xp[kb + 1] = lds_frag(xs + xr0 + 1024 * (kb + 1));
+          const int xo = xr + 8 * (rb0 + rb) + 1024 * xblk;
+          *reinterpret_cast<bf16x4 *>(xs + xo) = pp;
+          *reinterpret_cast<bf16x4 *>(xs + XBYTES + xo) = dd;
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[kb][4 * ps + c] = mfma16x16x32(tq[c], xd[kb], acc[kb][4 * ps + c]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[kb][4 * ps + c] = mfma16x16x32(to[c], xp[kb], acc[kb][4 * ps + c]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 16 + 2, 0);
+      lds_barrier();  // exchange tiles complete; the next step's copies stay in flight
+      // Next step's row table, loaded under the gradient and stored after it.
+      if (s + 1 < nsteps) rowinfo(s + 1);
+
+      // Gradient, two passes of two column blocks: the pass's transposed row
+      // fragments are held while the exchange fragments stream through.
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        if (kb + 1 < NKB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      for (int ps = 0; ps < 2; ++ps) {
+        bf16x8 tq[2], to[2], xd[NKB], xp[NKB];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int to_ = trb + ((tr_sw ^ (2 * (2 * ps + c))) << 4);
+          tq[c] = tr_frag(qb + to_);
+          to[c] = tr_frag(ob + to_);
+        }
+        xd[0] = lds_frag(xs + XBYTES + xr);
+        xp[0] = lds_frag(xs + xr);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          if (kb + 1 < NKB) {
+            xd[kb + 1] = lds_frag(xs + XBYTES + xr + 1024 * (kb + 1));
+            xp[kb + 1] = lds_frag(xs + xr + 1024 * (kb + 1));
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            acc[kb][2 * ps + c] = mfma16x16x32(tq[c], xd[kb], acc[kb][2 * ps + c]);
+            acc[kb][2 * ps + c] = mfma16x16x32(to[c], xp[kb], acc[kb][2 * ps + c]);
+          }
+        }
+        // 8 transpose reads and the first exchange pair, then per key block
+        // the next pair and four MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2, 0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          if (kb + 1 < NKB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < nsteps) put_rowinfo((s + 1) & 1);
+      wait_all_loads();
+      __syncthreads();
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < nsteps) put_rowinfo((s + 1) & 1);
-    wait_all_loads();
-    __syncthreads();
-  }
+  };
+  if (half)
+    steps(std::integral_constant<int, 1>{});
+  else
+    steps(std::integral_constant<int, 0>{});
 
-  // Partial [128 keys][512] of this item: this wave's 128 columns of every key.
-  // A half item writes zeros for its idle half, unless another half item of
-  // the tile shares the block and writes that half itself.
-  const bool shared = HALF && it.shared;
+  // Partial [128 keys][512] of this item: this wave's 64 columns of every key.
+  // A half item's accumulators 0..3 hold its active half; it writes zeros for
+  // the idle half unless another half item of the tile shares the block.
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
-    float *out = part + it.part_off + (size_t)(16 * kb + j) * D + 128 * wave;
-    const bool act = HALF ? (kb >> 2) == hh : true;
-    if (shared && !act) continue;
-    const int ka = HALF ? (kb & 3) : kb;  // active block of key block kb
+    const bool act = !half || (kb >> 2) == hh;
+    if (half && it.shared && !act) continue;
+    const int ka = half ? (kb & 3) : kb;
+    float *out = part + it.part_off + (size_t)(16 * kb + j) * D + 64 * wave + 4 * g;
 #pragma unroll
-    for (int dl = 0; dl < 8; ++dl) {
+    for (int dl = 0; dl < 4; ++dl) {
       float4 w;
       w.x = act ? acc[ka][dl][0] : 0.f;
       w.y = act ? acc[ka][dl][1] : 0.f;
       w.z = act ? acc[ka][dl][2] : 0.f;
       w.w = act ? acc[ka][dl][3] : 0.f;
-      *reinterpret_cast<float4 *>(out + 16 * dl + 4 * g) = w;
+      *reinterpret_cast<float4 *>(out + 16 * dl) = w;
     }
   }
 }
@@ -1221,16 +1177,10 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
   };
   switch (d.D) {
     case 512:
-      // Full-tile items, then the half-tile items (see the kernel).
-      if (d.n_items_full > 0)
-        hipLaunchKernelGGL((hca_bwd_dkv512_kernel<4, 0>), dim3(d.n_items_full), dim3(256), 0, s,
-                           d, p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc,
-                           lse, delta, (const bf16raw *)dout, sl2, scale, part, 0);
-      if (d.n_items > d.n_items_full)
-        hipLaunchKernelGGL((hca_bwd_dkv512_kernel<4, 1>), dim3(d.n_items - d.n_items_full),
-                           dim3(256), 0, s, d, p, (const bf16raw *)q, (const bf16raw *)kv,
-                           (const bf16raw *)kvc, lse, delta, (const bf16raw *)dout, sl2, scale,
-                           part, d.n_items_full);
+      // Every item (over all keys of its tile or over one half) in one launch.
+      hipLaunchKernelGGL(hca_bwd_dkv512x8_kernel, dim3(d.n_items), dim3(512), 0, s, d, p,
+                         (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc, lse,
+                         delta, (const bf16raw *)dout, sl2, scale, part);
       break;
     case 128: go(hca_bwd_dkv_kernel<128>); break;
     case 64: go(hca_bwd_dkv_kernel<64>); break;

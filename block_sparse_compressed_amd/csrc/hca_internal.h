@@ -65,8 +65,7 @@ struct Dims {
   int32_t B, S, H, D, r, W, Sc;
   int32_t bq, bk_raw, bk_comp, nqt, nkt_raw, nkt_comp;
   int32_t S_pad, Sc_pad;  // nkt_raw * bk_raw, nkt_comp * bk_comp
-  int32_t n_items;       // launch slots of the key-stationary backward (both launches)
-  int32_t n_items_full;  // slots of its first launch (items over all keys of their tile)
+  int32_t n_items;       // launch slots of the key-stationary backward
   int32_t kv_bk, nkv_raw, nkv_comp;  // key tiles of the key-stationary backward
 };
 
@@ -124,11 +123,11 @@ struct hca_plan {
   std::vector<uint32_t> qent;
   std::vector<int32_t> qorder;
   std::vector<hca::KvItem> kvitem;
-  std::vector<int32_t> kvorder;  // launch slots: full-tile items, then half-tile items
-  int32_t n_order_full = 0;
+  std::vector<int32_t> kvorder;  // launch slots (-1 = none)
   std::vector<uint32_t> kvent;
   std::vector<int32_t> kvtile;
   int32_t kv_bk = 32, nkv_raw = 0, nkv_comp = 0;  // key-stationary backward tiling
+  int32_t rows_b = 0;  // rows of the plan's tables: batch rows x kv heads
   hca::DevLayout lay;
   hca::WsLayout ws;
   std::string unsupported;     // why kernel_ok is 0 ("" when it is 1)

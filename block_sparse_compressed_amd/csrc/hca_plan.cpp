@@ -53,11 +53,10 @@ constexpr int64_t kItemPositions = 64;
 // one-chunk items.
 constexpr int64_t kCuTarget = 256;
 
-// Half-tile items (128-key tiles whose item sees one 64-key half) run in a
-// second launch of their own; with few items per CU its tail costs more than
-// the halved work saves (S = 16384: dKV 1.57 -> 1.71 ms), so below 8 items
-// per CU every item runs over its whole tile.
-constexpr int64_t kHalfItemsMin = 8 * kCuTarget;
+// Half-tile items (128-key tiles whose item sees one 64-key half) share the
+// key-stationary launch with the items over whole tiles, so by default they
+// are used at any size.
+constexpr int64_t kHalfItemsMin = 1;
 
 // State of query tile qt (positions qt*bq .. +bq-1) against keys [k0, k0+bk)
 // of `kind`, from the per-position intervals `rw` ([S][4]).
@@ -130,43 +129,56 @@ std::string kernel_sizes_ok(int dtype, int D, int64_t S_pad, int64_t Sc_pad) {
 
 using namespace hca;
 
-extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int32_t W,
-                                           int32_t S_c, const int32_t *seg_starts,
-                                           const int32_t *seg_counts, int32_t H, int32_t D,
-                                           hca_dtype dtype, hca_compseg_mode mode,
-                                           const hca_tile_cfg *tiles, hca_plan **out) {
+// Builds the plan of B batch rows x G kv heads.  Query head h uses kv head
+// h / (H / G), so each (batch row, kv head) pair with its H / G query heads is
+// one MQA problem with the same documents, and their tensors are contiguous
+// slices of q [B][H][S][D] and kv [B][G][S][D]: the plan holds B * G such
+// rows of H / G heads, and the kernels run them unchanged.
+static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, int32_t r,
+                             int32_t W, int32_t S_c, const int32_t *seg_starts,
+                             const int32_t *seg_counts, int32_t H, int32_t D, hca_dtype dtype,
+                             hca_compseg_mode mode, const hca_tile_cfg *tiles, hca_plan **out) {
+  const std::string F(fn);
   if (!out) {
-    set_error("hca_block_mask_build: out is NULL");
+    set_error(F + ": out is NULL");
     return HCA_ERR_INVALID_ARG;
   }
   *out = nullptr;
   if (B < 1 || S < 1 || H < 1 || D < 1) {
-    set_error("hca_block_mask_build: B, S, H and D must all be >= 1");
+    set_error(F + ": B, S, H and D must all be >= 1");
+    return HCA_ERR_INVALID_ARG;
+  }
+  if (G < 1 || H % G != 0) {
+    set_error(F + ": kv_heads must be >= 1 and divide H");
+    return HCA_ERR_INVALID_ARG;
+  }
+  if ((int64_t)B * G > (1 << 20)) {
+    set_error(F + ": B x kv_heads must be at most 2^20");
     return HCA_ERR_INVALID_ARG;
   }
   if (r < 1) {
-    set_error("hca_block_mask_build: compression ratio r must be >= 1");
+    set_error(F + ": compression ratio r must be >= 1");
     return HCA_ERR_INVALID_ARG;
   }
   if (W < 0) {
-    set_error("hca_block_mask_build: window W must be >= 0");
+    set_error(F + ": window W must be >= 0");
     return HCA_ERR_INVALID_ARG;
   }
   if (S_c != S / r) {
-    set_error("hca_block_mask_build: S_c must equal floor(S / r) = " + std::to_string(S / r) +
+    set_error(F + ": S_c must equal floor(S / r) = " + std::to_string(S / r) +
               ", got " + std::to_string(S_c));
     return HCA_ERR_INVALID_ARG;
   }
   if (dtype != HCA_F32 && dtype != HCA_BF16) {
-    set_error("hca_block_mask_build: unknown dtype");
+    set_error(F + ": unknown dtype");
     return HCA_ERR_INVALID_ARG;
   }
   if (mode != HCA_COMPSEG_STRICT && mode != HCA_COMPSEG_LAST) {
-    set_error("hca_block_mask_build: unknown compressed-segment mode");
+    set_error(F + ": unknown compressed-segment mode");
     return HCA_ERR_INVALID_ARG;
   }
   if ((seg_starts == nullptr) != (seg_counts == nullptr)) {
-    set_error("hca_block_mask_build: seg_starts and seg_counts must both be NULL or both set");
+    set_error(F + ": seg_starts and seg_counts must both be NULL or both set");
     return HCA_ERR_INVALID_ARG;
   }
   // Document lists: per row strictly increasing, first 0, all < S.
@@ -174,7 +186,7 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
   if (seg_counts) {
     for (int b = 0; b < B; ++b) {
       if (seg_counts[b] < 1 || seg_counts[b] > S) {
-        set_error("hca_block_mask_build: seg_counts[" + std::to_string(b) +
+        set_error(F + ": seg_counts[" + std::to_string(b) +
                   "] must be in [1, S]");
         return HCA_ERR_INVALID_ARG;
       }
@@ -184,18 +196,38 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
       const int32_t *st = seg_starts + seg_off[b];
       int64_t n = seg_off[b + 1] - seg_off[b];
       if (st[0] != 0) {
-        set_error("hca_block_mask_build: first document start of row " + std::to_string(b) +
+        set_error(F + ": first document start of row " + std::to_string(b) +
                   " must be 0");
         return HCA_ERR_INVALID_ARG;
       }
       for (int64_t j = 1; j < n; ++j) {
         if (st[j] <= st[j - 1] || st[j] >= S) {
-          set_error("hca_block_mask_build: document starts of row " + std::to_string(b) +
+          set_error(F + ": document starts of row " + std::to_string(b) +
                     " must be strictly increasing and < S");
           return HCA_ERR_INVALID_ARG;
         }
       }
     }
+  }
+  // B * G rows of H / G heads from here on; the documents of batch row b are
+  // repeated for each of its kv heads (internal row b * G + g).
+  const int32_t B_caller = B, H_caller = H;
+  std::vector<int32_t> starts_rep, counts_rep;
+  if (G > 1) {
+    if (seg_counts) {
+      for (int b = 0; b < B; ++b)
+        for (int g = 0; g < G; ++g) {
+          starts_rep.insert(starts_rep.end(), seg_starts + seg_off[b], seg_starts + seg_off[b + 1]);
+          counts_rep.push_back(seg_counts[b]);
+        }
+      seg_starts = starts_rep.data();
+      seg_counts = counts_rep.data();
+    }
+    B *= G;
+    H /= G;
+    seg_off.assign(B + 1, 0);
+    if (seg_counts)
+      for (int b = 0; b < B; ++b) seg_off[b + 1] = seg_off[b] + seg_counts[b];
   }
   int bq, bkr, bkc;
   default_tiles(dtype, D, H, &bq, &bkr, &bkc);
@@ -204,7 +236,7 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
   if (tiles) {
     if (tiles->bq < 0 || tiles->bk_raw < 0 || tiles->bk_comp < 0 ||
         tiles->comp_item_chunks < 0) {
-      set_error("hca_block_mask_build: tile sizes and comp_item_chunks must be >= 0");
+      set_error(F + ": tile sizes and comp_item_chunks must be >= 0");
       return HCA_ERR_INVALID_ARG;
     }
     if (tiles->bq) bq = tiles->bq;
@@ -216,13 +248,13 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
   }
   // Work-list entries pack tile indices into 30 bits.
   if (ceil_div(S, bq) >= (1 << 29) || ceil_div(S, bkr) >= (1 << 29)) {
-    set_error("hca_block_mask_build: too many tiles");
+    set_error(F + ": too many tiles");
     return HCA_ERR_INVALID_ARG;
   }
 
   hca_plan *p = new (std::nothrow) hca_plan();
   if (!p) {
-    set_error("hca_block_mask_build: out of host memory");
+    set_error(F + ": out of host memory");
     return HCA_ERR_NOMEM;
   }
   try {
@@ -230,7 +262,9 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     const int64_t nktr = ceil_div(S, bkr);
     const int64_t nktc = ceil_div(S_c, bkc);
     hca_plan_info &in = p->info;
-    in.B = B; in.S = S; in.H = H; in.D = D; in.r = r; in.W = W; in.S_c = S_c;
+    in.B = B_caller; in.S = S; in.H = H_caller; in.D = D; in.r = r; in.W = W; in.S_c = S_c;
+    in.kv_heads = G;
+    p->rows_b = B;
     in.dtype = dtype; in.comp_mode = mode;
     in.bq = bq; in.bk_raw = bkr; in.bk_comp = bkc;
     in.nqt = (int32_t)nqt; in.nkt_raw = (int32_t)nktr; in.nkt_comp = (int32_t)nktc;
@@ -259,8 +293,9 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
         pairs_comp += chi - clo;
       }
     }
-    in.pairs_raw = pairs_raw;
-    in.pairs_comp = pairs_comp;
+    // Every kv head's rows see the same pattern: pairs per caller batch row.
+    in.pairs_raw = pairs_raw / G;
+    in.pairs_comp = pairs_comp / G;
 
     // ---- query-tile schedule (CSR) ---------------------------------------- //
     p->qptr.assign((size_t)B * nqt + 1, 0);
@@ -530,16 +565,13 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     // is kept together on one XCD, where its L2 serves the repeated reads.
     // Groups go, heaviest first, to the least-loaded XCD; slots past the end
     // of a short XCD queue hold -1 (no work).
-    // Two launches share the order array: items over all keys of their tile
-    // first, then the half-tile items (their own kernel instantiation).
     {
       constexpr int kXcd = 8;
       const int64_t ngroup = (int64_t)B * ngrid;
-      auto build_order = [&](bool half) {
+      auto build_order = [&]() {
         std::vector<int64_t> gwork(ngroup, 0);
         std::vector<std::vector<int32_t>> gitems(ngroup);
         for (size_t i = 0; i < p->kvitem.size(); ++i) {
-          if ((p->kvitem[i].halves != 3) != half) continue;
           gwork[item_group[i]] += p->kvitem[i].e1 - p->kvitem[i].e0;
           gitems[item_group[i]].push_back((int32_t)i);
         }
@@ -566,10 +598,7 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
           for (size_t k = 0; k < queue[x].size(); ++k) order[k * kXcd + x] = queue[x][k];
         return order;
       };
-      p->kvorder = build_order(false);
-      p->n_order_full = (int32_t)p->kvorder.size();
-      const std::vector<int32_t> half_order = build_order(true);
-      p->kvorder.insert(p->kvorder.end(), half_order.begin(), half_order.end());
+      p->kvorder = build_order();
     }
 
     // ---- device image ----------------------------------------------------- //
@@ -617,11 +646,30 @@ extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int3
     in.ws_bwd_bytes = w.bwd_total;
   } catch (const std::bad_alloc &) {
     delete p;
-    set_error("hca_block_mask_build: out of host memory");
+    set_error(F + ": out of host memory");
     return HCA_ERR_NOMEM;
   }
   *out = p;
   return HCA_OK;
+}
+
+extern "C" hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int32_t W,
+                                           int32_t S_c, const int32_t *seg_starts,
+                                           const int32_t *seg_counts, int32_t H, int32_t D,
+                                           hca_dtype dtype, hca_compseg_mode mode,
+                                           const hca_tile_cfg *tiles, hca_plan **out) {
+  return build_plan("hca_block_mask_build", B, 1, S, r, W, S_c, seg_starts, seg_counts, H, D,
+                    dtype, mode, tiles, out);
+}
+
+extern "C" hca_status hca_block_mask_build_gqa(int32_t B, int32_t kv_heads, int32_t S,
+                                               int32_t r, int32_t W, int32_t S_c,
+                                               const int32_t *seg_starts,
+                                               const int32_t *seg_counts, int32_t H, int32_t D,
+                                               hca_dtype dtype, hca_compseg_mode mode,
+                                               const hca_tile_cfg *tiles, hca_plan **out) {
+  return build_plan("hca_block_mask_build_gqa", B, kv_heads, S, r, W, S_c, seg_starts,
+                    seg_counts, H, D, dtype, mode, tiles, out);
 }
 
 extern "C" hca_status hca_plan_get_info(const hca_plan *plan, hca_plan_info *out) {
@@ -641,9 +689,10 @@ extern "C" hca_status hca_plan_export_tiles(const hca_plan *plan, uint8_t *raw_s
   }
   const hca_plan_info &in = plan->info;
   const size_t nqt = in.nqt, nktr = in.nkt_raw, nktc = in.nkt_comp;
-  if (raw_states) std::memset(raw_states, HCA_TILE_EMPTY, (size_t)in.B * nqt * nktr);
-  if (comp_states) std::memset(comp_states, HCA_TILE_EMPTY, (size_t)in.B * nqt * nktc);
-  for (int b = 0; b < in.B; ++b)
+  const int nb = plan->rows_b;  // batch rows x kv heads
+  if (raw_states) std::memset(raw_states, HCA_TILE_EMPTY, (size_t)nb * nqt * nktr);
+  if (comp_states) std::memset(comp_states, HCA_TILE_EMPTY, (size_t)nb * nqt * nktc);
+  for (int b = 0; b < nb; ++b)
     for (size_t qt = 0; qt < nqt; ++qt)
       for (int32_t e = plan->qptr[b * nqt + qt]; e < plan->qptr[b * nqt + qt + 1]; ++e) {
         uint32_t v = plan->qent[e];
@@ -663,7 +712,7 @@ extern "C" hca_status hca_plan_export_rows(const hca_plan *plan, int32_t *rows) 
     set_error("hca_plan_export_rows: NULL argument");
     return HCA_ERR_INVALID_ARG;
   }
-  const size_t n = (size_t)plan->info.B * plan->info.S;
+  const size_t n = (size_t)plan->rows_b * plan->info.S;
   for (size_t j = 0; j < n; ++j)
     for (int c = 0; c < 3; ++c) rows[j * 3 + c] = plan->rows[j * 4 + c];
   return HCA_OK;

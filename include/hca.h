@@ -83,7 +83,7 @@ enum { HCA_TILE_EMPTY = 0, HCA_TILE_PARTIAL = 1, HCA_TILE_FULL = 2 };
  *   half_items_min    with 128-key items (head dim 512, bfloat16): an item whose
  *                     rows see only one 64-key half of its key tile runs over
  *                     that half alone once the plan has at least this many
- *                     items; 0 = library choice (2048), < 0 = never.
+ *                     items; 0 = library choice (1: always), < 0 = never.
  *   comp_item_chunks  64-position chunks of query rows per work item of a
  *                     compressed key tile; 0 = library choice (one chunk,
  *                     doubled only while the compressed tiles' partial
@@ -125,7 +125,7 @@ typedef struct hca_plan_info {
   int64_t items_half;              /* of which run over one 64-key half of their tile */
   int64_t part_blocks;             /* float32 partial-gradient blocks (kv_bk x D each) */
   int32_t comp_item_chunks;        /* 64-position chunks per compressed-tile item */
-  int32_t reserved_;
+  int32_t kv_heads;                /* key/value heads G (1: MQA); see hca_block_mask_build_gqa */
 } hca_plan_info;
 
 /*
@@ -154,6 +154,27 @@ hca_status hca_block_mask_build(int32_t B, int32_t S, int32_t r, int32_t W, int3
                                 const int32_t *seg_starts, const int32_t *seg_counts,
                                 int32_t H, int32_t D, hca_dtype dtype, hca_compseg_mode mode,
                                 const hca_tile_cfg *tiles, hca_plan **out);
+
+/*
+ * Grouped-query variant: kv_heads = G key/value heads (G divides H), query
+ * head h attending to key/value head h / (H / G).  The pages dispatch the MQA
+ * kernel only when the layer has a single key/value head ("Add HCA Static
+ * Compilation for Splash Attention [Deepseek v4]", Description), so layers
+ * with several are served here: each (batch row, key/value head) with its
+ * H / G query heads is one MQA problem of the kind above, with the batch
+ * row's documents.  Layouts: q, o, dout, dq [B][H][S][D] (unchanged);
+ * kv, dkv [B][G][S][D]; kv_comp, dkv_comp [B][G][S_c][D]; lse [B][H][S].
+ * The plan's tables (hca_plan_export_tiles / _rows / _items) then have
+ * B * G rows, row b * G + g for batch row b and key/value head g, and
+ * tiles_*, full_* count over them; pairs_* stay per batch row.  G = 1 is
+ * hca_block_mask_build.  Errors: as hca_block_mask_build, and
+ * HCA_ERR_INVALID_ARG when G < 1, G does not divide H or B * G > 2^20.
+ */
+hca_status hca_block_mask_build_gqa(int32_t B, int32_t kv_heads, int32_t S, int32_t r,
+                                    int32_t W, int32_t S_c, const int32_t *seg_starts,
+                                    const int32_t *seg_counts, int32_t H, int32_t D,
+                                    hca_dtype dtype, hca_compseg_mode mode,
+                                    const hca_tile_cfg *tiles, hca_plan **out);
 
 /* Fills *out with the plan's sizes and counts.  HCA_ERR_INVALID_ARG on NULL. */
 hca_status hca_plan_get_info(const hca_plan *plan, hca_plan_info *out);

@@ -252,14 +252,16 @@ def check_partial_blocks(items, D, info):
     assert sorted(covered) == list(range(info.part_blocks))
 
 
-def test_items_small_problem_runs_whole_tiles():
-    """Below 8 items per CU every item runs over all keys of its tile."""
+def test_items_half_tiles_marked_at_any_size():
+    """The one-launch key-stationary kernel runs half-tile items beside the
+    full ones, so the planner marks them at any size (S = 16384 here), and
+    lower/upper pairs share partial blocks."""
     plan, _ = build_both(1, 16384, 64, 512, 128, 128, None, hca.HCA_COMPSEG_STRICT)
     items = hca.hca_plan_export_items(plan)
-    assert 0 < len(items) < 2048 and (items[:, 6] == 3).all()
     info = hca.hca_plan_get_info(plan)
-    assert info.items == len(items) and info.items_half == 0
-    assert info.part_blocks == len(items)
+    assert info.items == len(items) and info.items_half > 0
+    assert info.part_blocks < len(items)
+    check_partial_blocks(items, 512, info)
 
 
 def test_half_items_knob():
