@@ -115,8 +115,9 @@ def segment_ids(lengths: Optional[List[List[int]]], B: int, S: int) -> np.ndarra
     return seg
 
 
-def draw(B, S, H, D, Sc, dtype="bf16", seed=0, value_scale=1.0, device="cpu"):
-    """Draws q [B,H,S,D], kv [B,S,D], kv_comp [B,Sc,D], dout [B,H,S,D] (torch)."""
+def draw(B, S, H, D, Sc, dtype="bf16", seed=0, value_scale=1.0, device="cpu", kv_heads=1):
+    """Draws q [B,H,S,D], kv [B,S,D], kv_comp [B,Sc,D], dout [B,H,S,D] (torch); with
+    kv_heads = G > 1, kv [B,G,S,D] and kv_comp [B,G,Sc,D]."""
     import torch
 
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
@@ -130,8 +131,9 @@ def draw(B, S, H, D, Sc, dtype="bf16", seed=0, value_scale=1.0, device="cpu"):
         return t.to(tdt)
 
     q = one((B, H, S, D), value_scale)
-    kv = one((B, S, D), value_scale)
-    kvc = one((B, Sc, D), value_scale)
+    g = () if kv_heads == 1 else (kv_heads,)
+    kv = one((B,) + g + (S, D), value_scale)
+    kvc = one((B,) + g + (Sc, D), value_scale)
     dout = one((B, H, S, D), 1.0)
     return q, kv, kvc, dout
 

@@ -218,6 +218,39 @@ def full(prob, q, kv, kvc, dout):
     )
 
 
+def full_gqa(prob, kv_heads, q, kv, kvc, dout):
+    """Every output with several key/value heads: query head h attends to
+    key/value head h // (H // kv_heads).  Each key/value head with its group of
+    query heads is an independent single-head (MQA) problem with the same
+    documents, so this is the MQA oracle run once per group: prob.H is the total
+    number of query heads; kv [B, G, S, D], kvc [B, G, Sc, D] (G = kv_heads).
+
+    The pages dispatch the single-KV-head kernel only when there is one KV head
+    ("Add HCA Static Compilation for Splash Attention [Deepseek v4]",
+    Description); a layer with several key/value heads groups its query heads
+    over them (grouped-query attention).  Returns the dict of full() with dkv
+    [B, G, S, D] and dkvc [B, G, Sc, D].
+    """
+    G = kv_heads
+    B, S, H, D, Sc = prob.B, prob.S, prob.H, prob.D, prob.Sc
+    assert H % G == 0 and kv.shape == (B, G, S, D)
+    Hg = H // G
+    sub = Problem(B, S, Hg, D, prob.r, prob.W, Sc, prob.scale, prob.seg, prob.comp_mode,
+                  prob.in_dtype)
+    out = {k: [] for k in ("o", "lse", "delta", "dq", "dkv", "dkvc")}
+    for g in range(G):
+        hs = slice(g * Hg, (g + 1) * Hg)
+        kvc_g = kvc[:, g] if Sc > 0 else None
+        r = full(sub, np.ascontiguousarray(q[:, hs]), np.ascontiguousarray(kv[:, g]),
+                 None if kvc_g is None else np.ascontiguousarray(kvc_g),
+                 np.ascontiguousarray(dout[:, hs]))
+        for k in out:
+            out[k].append(r[k])
+    return dict(o=np.concatenate(out["o"], 1), lse=np.concatenate(out["lse"], 1),
+                delta=np.concatenate(out["delta"], 1), dq=np.concatenate(out["dq"], 1),
+                dkv=np.stack(out["dkv"], 1), dkvc=np.stack(out["dkvc"], 1))
+
+
 def tile_states(prob, kind, bq, bk):
     """Brute-force tile table [B, ceil(S/bq), ceil(N/bk)] uint8 (0/1/2)."""
     lib = _load()

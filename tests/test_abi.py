@@ -199,6 +199,33 @@ def test_fwd_noalloc_error_paths(plan):
     assert f(*(fwd_args(unsup)[:7] + (None,))) == hca.HCA_ERR_UNSUPPORTED
 
 
+def test_gqa_build_checks_and_tables():
+    """hca_block_mask_build_gqa: kv_heads must divide H; the plan's tables hold
+    one MQA problem per (batch row, kv head) with the batch row's documents,
+    identical to the single-head plan of the same documents; pair counts stay
+    per batch row."""
+    out = ctypes.c_void_p()
+    for G, H in ((0, 8), (3, 8), (-1, 8)):
+        assert lib.hca_block_mask_build_gqa(1, G, 64, 8, 4, 8, None, None, H, 64, hca.HCA_BF16, 0,
+                                            None, ctypes.byref(out)) == hca.HCA_ERR_INVALID_ARG
+    starts, counts = [0, 40, 0, 10, 70], [2, 3]
+    one = hca.hca_block_mask_build(2, 100, 8, 20, 12, starts, counts, H=16, D=512)
+    gqa = hca.hca_block_mask_build_gqa(2, 4, 100, 8, 20, 12, starts, counts, H=64, D=512)
+    i1, ig = hca.hca_plan_get_info(one), hca.hca_plan_get_info(gqa)
+    assert ig.kv_heads == 4 and i1.kv_heads == 1 and ig.kernel_ok == 1
+    assert (ig.pairs_raw, ig.pairs_comp) == (i1.pairs_raw, i1.pairs_comp)
+    assert ig.tiles_raw == 4 * i1.tiles_raw and ig.items == 4 * i1.items
+    r1, c1 = hca.hca_plan_export_tiles(one)
+    rg, cg = hca.hca_plan_export_tiles(gqa)
+    np.testing.assert_array_equal(rg, np.repeat(r1, 4, axis=0))
+    np.testing.assert_array_equal(cg, np.repeat(c1, 4, axis=0))
+    np.testing.assert_array_equal(hca.hca_plan_export_rows(gqa),
+                                  np.repeat(hca.hca_plan_export_rows(one), 4, axis=0))
+    # kernel support follows the heads per kv head (D = 64: bq x H / G = 128)
+    p = hca.hca_block_mask_build_gqa(1, 2, 64, 8, 4, 8, H=6, D=64)
+    assert hca.hca_plan_get_info(p).kernel_ok == 0
+
+
 def test_upload_checks(plan):
     info = hca.hca_plan_get_info(plan)
     assert lib.hca_plan_upload(plan.handle, None, info.device_bytes, None) == \

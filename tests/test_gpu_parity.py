@@ -68,7 +68,7 @@ def as_np(t):
 
 class Case:
     def __init__(self, B, S, H, D, r, W, dtype="bf16", lengths=None, mode=0, seed=0,
-                 value_scale=1.0, tiles=None, name=None):
+                 value_scale=1.0, tiles=None, name=None, kv_heads=1):
         self.B, self.S, self.H, self.D, self.r, self.W = B, S, H, D, r, W
         self.Sc = S // r
         self.dtype, self.lengths, self.mode = dtype, lengths, mode
@@ -78,9 +78,11 @@ class Case:
         say(f"case B={B} S={S} H={H} D={D} r={r} W={W} {dtype} mode={mode} seed={seed} "
             f"docs={'none' if lengths is None else sum(len(x) for x in lengths)} tiles={tiles}")
         self.q, self.kv, self.kvc, self.dout = draw(B, S, H, D, self.Sc, dtype, seed,
-                                                    value_scale, device="cuda")
+                                                    value_scale, device="cuda",
+                                                    kv_heads=kv_heads)
         starts, counts = starts_csr(lengths, B)
-        self.att = hca.HcaAttention(B, S, H, D, r, W, dtype, starts, counts, mode, tiles)
+        self.att = hca.HcaAttention(B, S, H, D, r, W, dtype, starts, counts, mode, tiles,
+                                    kv_heads=kv_heads)
         assert self.att.info.kernel_ok == 1
 
     def run(self, stream=None, poison=True):
@@ -209,6 +211,46 @@ def test_half_tile_dkv_items_every_element(lengths):
     assert info.items_half > 0 and (items[:, 6] & 4).any()
     assert ((items[:, 6] & 3) == 1).any() and ((items[:, 6] & 3) == 2).any()
     check_full(case)
+
+
+def check_full_gqa(case, G, outs):
+    o, lse, dq, dkv, dkvc = outs
+    ref = oracle.full_gqa(case.problem(), G, *case.host())
+    tol = TOL[case.dtype]
+    errs = dict(o=rel_err(as_np(o), ref["o"]), dq=rel_err(as_np(dq), ref["dq"]),
+                dkv=rel_err(as_np(dkv), ref["dkv"]), lse=lse_err(as_np(lse), ref["lse"]))
+    if case.Sc:
+        errs["dkvc"] = rel_err(as_np(dkvc), ref["dkvc"])
+    say(f"  errors {errs}")
+    record(case.name + f"_G{G} (every element)", errs)
+    compare_lse(as_np(lse), ref["lse"], tol)
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    for t in (o, dq, dkv) + ((dkvc,) if case.Sc else ()):
+        assert not torch.isnan(t).any()
+
+
+GQA = [
+    # B, G, S, H, D, r, W, dtype, lengths
+    (2, 2, 700, 16, 512, 16, 64, "bf16", "random"),
+    (1, 4, 515, 64, 128, 8, 48, "bf16", None),
+    (1, 8, 300, 64, 512, 32, 128, "bf16", [[120, 180]]),
+    (1, 2, 200, 4, 64, 8, 30, "f32", None),
+]
+
+
+@pytest.mark.parametrize("spec", GQA, ids=lambda s: "B%d_G%d_S%d_H%d_D%d_%s" % (
+    s[0], s[1], s[2], s[3], s[4], s[7]))
+def test_grouped_kv_heads_every_element(spec):
+    """Several key/value heads (query head h on kv head h // (H / G)), through
+    hca_block_mask_build_gqa, against the oracle's grouped form."""
+    B, G, S, H, D, r, W, dtype, lengths = spec
+    if lengths == "random":
+        rng = np.random.default_rng(S)
+        lengths = [random_lengths(rng, S, 1, S // 2) for _ in range(B)]
+    case = Case(B, S, H, D, r, W, dtype, lengths, seed=S + G, kv_heads=G)
+    assert case.att.info.kv_heads == G and tuple(case.kv.shape) == (B, G, S, D)
+    check_full_gqa(case, G, case.run())
 
 
 def test_single_position():

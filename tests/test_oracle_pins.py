@@ -10,6 +10,8 @@ Pins used (none re-types the oracle's own arithmetic):
     W = 1 (single visible key), duplicated keys (LSE shifts by ln 2);
   * the backward against fp64 central finite differences of sum(O * dO);
   * the identity delta_i = <dO_i, O_i>;
+  * several key/value heads: the grouped form reduces to causal attention over
+    each group's head (torch SDPA with repeat_interleave, fp64, autograd);
   * visible-pair counts against their closed forms.
 """
 
@@ -170,6 +172,50 @@ def test_compressed_path_reduces_to_causal(B, S, H, D, lengths, mode):
     np.testing.assert_allclose(got["dq"], dq, atol=1e-11, rtol=1e-9)
     np.testing.assert_allclose(got["dkvc"], dkv, atol=1e-11, rtol=1e-9)
     assert np.all(got["dkv"] == 0.0)
+
+
+def causal_reference_grouped(q, kv, scale, dout):
+    """Causal attention of query heads q [H, S, D] over key/value heads kv [G, S, D],
+    head h reading kv[h // (H // G)] (torch repeat_interleave), in fp64 with
+    autograd: O, LSE, dQ, dKV [G, S, D]."""
+    H, G = q.shape[0], kv.shape[0]
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(kv, requires_grad=True)
+    kk = kt.repeat_interleave(H // G, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kk, kk, is_causal=True, scale=scale)
+    o.backward(torch.tensor(dout))
+    logits = (qt.detach() @ kk.detach().transpose(1, 2)) * scale
+    causal = torch.ones(q.shape[1], q.shape[1], dtype=torch.bool).tril()
+    lse = torch.logsumexp(logits.masked_fill(~causal, -math.inf), dim=-1)
+    return o.detach().numpy(), lse.numpy(), qt.grad.numpy(), kt.grad.numpy()
+
+
+@pytest.mark.parametrize("path", ["raw", "compressed"])
+@pytest.mark.parametrize("H,G", [(4, 2), (6, 3), (4, 4)])
+def test_grouped_kv_heads_reduce_to_causal(H, G, path):
+    """Several key/value heads: with W >= S and no entries (raw path), or r = 1,
+    W = 0 and kv_comp = kv (compressed path), every query head reduces to
+    causal attention over its group's key/value head, which torch computes with
+    repeat_interleave; a wrong head-to-group map (h % G) or a gradient summed
+    over the wrong heads fails."""
+    rng = np.random.default_rng(14 + H + G)
+    B, S, D = 2, 17, 8
+    q, kv, dout = rnd(rng, B, H, S, D), rnd(rng, B, G, S, D), rnd(rng, B, H, S, D)
+    if path == "raw":
+        p = make_problem(B, S, H, D, r=S + 1, W=S)
+        got = oracle.full_gqa(p, G, q, kv, np.zeros((B, G, 0, D)), dout)
+        key = "dkv"
+    else:
+        p = make_problem(B, S, H, D, r=1, W=0)
+        got = oracle.full_gqa(p, G, q, kv, kv.copy(), dout)
+        key = "dkvc"
+        assert np.all(got["dkv"] == 0.0)
+    for b in range(B):
+        o, lse, dq, dkv = causal_reference_grouped(q[b], kv[b], p.scale, dout[b])
+        np.testing.assert_allclose(got["o"][b], o, atol=1e-12, rtol=1e-10)
+        np.testing.assert_allclose(got["lse"][b], lse, atol=1e-12, rtol=1e-10)
+        np.testing.assert_allclose(got["dq"][b], dq, atol=1e-11, rtol=1e-9)
+        np.testing.assert_allclose(got[key][b], dkv, atol=1e-11, rtol=1e-9)
 
 
 def test_duplicated_keys_shift_lse_by_ln2():
