@@ -35,6 +35,7 @@ _LIB_PATH = os.path.join(_HERE, "libhca_oracle.so")
 
 STRICT = 0
 LAST = 1
+MASK = 2  # compressed visibility from a given dense mask [B, S, Sc]
 EMPTY, PARTIAL, FULL = 0, 1, 2
 
 
@@ -58,7 +59,7 @@ class _Problem(ctypes.Structure):
         ("D", ctypes.c_int32), ("r", ctypes.c_int32), ("W", ctypes.c_int32),
         ("Sc", ctypes.c_int32), ("comp_mode", ctypes.c_int32),
         ("in_dtype", ctypes.c_int32), ("pad_", ctypes.c_int32),
-        ("scale", ctypes.c_double), ("seg", ctypes.c_void_p),
+        ("scale", ctypes.c_double), ("seg", ctypes.c_void_p), ("comp_mask", ctypes.c_void_p),
     ]
 
 
@@ -102,11 +103,15 @@ class Problem:
     """Parameters of one HCA problem plus the per-token document ids."""
 
     def __init__(self, B, S, H, D, r, W, Sc, scale, seg=None, comp_mode=STRICT,
-                 in_dtype="f32"):
+                 in_dtype="f32", comp_mask=None):
         if seg is None:
             seg = np.zeros((B, S), dtype=np.int32)
         self.seg = np.ascontiguousarray(seg, dtype=np.int32)
         assert self.seg.shape == (B, S)
+        self.comp_mask = None
+        if comp_mode == MASK:
+            self.comp_mask = np.ascontiguousarray(comp_mask, dtype=np.uint8)
+            assert self.comp_mask.shape == (B, S, Sc)
         self.B, self.S, self.H, self.D = B, S, H, D
         self.r, self.W, self.Sc = r, W, Sc
         self.scale = float(scale)
@@ -114,11 +119,12 @@ class Problem:
         self.in_dtype = in_dtype
         self._c = _Problem(B, S, H, D, r, W, Sc, comp_mode,
                            {"f32": 0, "bf16": 1, "f64": 2}[in_dtype], 0, self.scale,
-                           self.seg.ctypes.data)
+                           self.seg.ctypes.data,
+                           None if self.comp_mask is None else self.comp_mask.ctypes.data)
 
     def with_dtype(self, in_dtype):
         return Problem(self.B, self.S, self.H, self.D, self.r, self.W, self.Sc,
-                       self.scale, self.seg, self.comp_mode, in_dtype)
+                       self.scale, self.seg, self.comp_mode, in_dtype, self.comp_mask)
 
     @property
     def c(self):
@@ -236,7 +242,7 @@ def full_gqa(prob, kv_heads, q, kv, kvc, dout):
     assert H % G == 0 and kv.shape == (B, G, S, D)
     Hg = H // G
     sub = Problem(B, S, Hg, D, prob.r, prob.W, Sc, prob.scale, prob.seg, prob.comp_mode,
-                  prob.in_dtype)
+                  prob.in_dtype, prob.comp_mask)
     out = {k: [] for k in ("o", "lse", "delta", "dq", "dkv", "dkvc")}
     for g in range(G):
         hs = slice(g * Hg, (g + 1) * Hg)
@@ -249,6 +255,17 @@ def full_gqa(prob, kv_heads, q, kv, kvc, dout):
     return dict(o=np.concatenate(out["o"], 1), lse=np.concatenate(out["lse"], 1),
                 delta=np.concatenate(out["delta"], 1), dq=np.concatenate(out["dq"], 1),
                 dkv=np.stack(out["dkv"], 1), dkvc=np.stack(out["dkvc"], 1))
+
+
+def topk_mask(B, S, Sc, idx):
+    """Dense compressed-key mask [B, S, Sc] uint8 of a per-query selection:
+    idx [B, S, K] int, entry idx[b, i, k] selected for query i (negative =
+    none; repeats select once)."""
+    idx = np.asarray(idx)
+    mask = np.zeros((B, S, Sc), np.uint8)
+    b, i, _ = np.nonzero(idx >= 0)
+    mask[b, i, idx[idx >= 0]] = 1
+    return mask
 
 
 def tile_states(prob, kind, bq, bk):

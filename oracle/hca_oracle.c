@@ -19,7 +19,9 @@
  *     to query i  iff  (c+1)*r <= i+1  and  segc(c) == seg(i)
  *   where segc(c) is the entry's document: in STRICT mode the document that
  *   holds the whole window (or none when the window straddles a boundary), in
- *   LAST mode the document of the window's last raw position.
+ *   LAST mode the document of the window's last raw position.  In MASK mode
+ *   a given dense mask decides every compressed pair instead (see
+ *   hco_vis_comp).
  *   Segment ids isolate packed documents ("document packing boundary
  *   isolation", same page, Description; the segment-equality mask in
  *   "DSV4: Route compressed and sliding train attention onto the splash
@@ -65,11 +67,12 @@
 
 typedef struct {
   int32_t B, S, H, D, r, W, Sc;
-  int32_t comp_mode; /* 0 = STRICT, 1 = LAST */
+  int32_t comp_mode; /* 0 = STRICT, 1 = LAST, 2 = MASK */
   int32_t in_dtype;  /* 0 = float32, 1 = bfloat16 bit patterns, 2 = float64 */
   int32_t pad_;
   double scale;
-  const int32_t *seg; /* [B][S] */
+  const int32_t *seg;        /* [B][S] */
+  const uint8_t *comp_mask;  /* [B][S][Sc], MASK mode only: nonzero = visible */
 } hco_problem;
 
 /* ---- element access ------------------------------------------------------ */
@@ -105,8 +108,17 @@ int hco_vis_raw(const hco_problem *p, int32_t b, int64_t i, int64_t t) {
   return seg_of(p, b, t) == seg_of(p, b, i);
 }
 
+/*
+ * MASK mode: the visibility of every (query, compressed entry) pair is given
+ * as a materialised dense mask, the form in which the dynamic path of "Add
+ * HCA Static Compilation for Splash Attention [Deepseek v4]" (Description)
+ * hands the compressed attention its pattern (a dense (B, 1, S, S_comp) mask
+ * in device memory), and in which a per-query selection of entries (a top-k
+ * over the compressed keys) is expressed.  The raw window keeps its rule.
+ */
 int hco_vis_comp(const hco_problem *p, int32_t b, int64_t i, int64_t c) {
   if (i < 0 || i >= p->S || c < 0 || c >= p->Sc) return 0;
+  if (p->comp_mode == 2) return p->comp_mask[((int64_t)b * p->S + i) * p->Sc + c] != 0;
   if ((c + 1) * (int64_t)p->r > i + 1) return 0;
   return comp_segment(p, b, (int32_t)c) == seg_of(p, b, i);
 }

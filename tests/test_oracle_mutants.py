@@ -50,6 +50,11 @@ MUTANTS = {
     "tile_rows_one_past": ("for (int64_t i = qt * bq; i < (qt + 1) * bq; ++i) {",
                            "for (int64_t i = qt * bq; i <= (qt + 1) * bq; ++i) {"),
     "tile_states_swapped": ("  return all ? 2 : 1;", "  return all ? 1 : 2;"),
+    "mask_transposed": ("p->comp_mask[((int64_t)b * p->S + i) * p->Sc + c] != 0;",
+                        "p->comp_mask[((int64_t)b * p->S + c) * p->Sc + i % p->Sc] != 0;"),
+    "mask_mode_keeps_completion": ("  if (p->comp_mode == 2) return p->comp_mask[",
+                                   "  if (p->comp_mode == 2 && (c + 1) * (int64_t)p->r <= i + 1)"
+                                   " return p->comp_mask["),
 }
 
 

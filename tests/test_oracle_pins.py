@@ -12,6 +12,9 @@ Pins used (none re-types the oracle's own arithmetic):
   * the identity delta_i = <dO_i, O_i>;
   * several key/value heads: the grouped form reduces to causal attention over
     each group's head (torch SDPA with repeat_interleave, fp64, autograd);
+  * compressed visibility from a given dense mask (random, or a top-k index
+    selection): attention with the explicit boolean mask over the
+    concatenated keys (torch, fp64, autograd);
   * visible-pair counts against their closed forms.
 """
 
@@ -216,6 +219,78 @@ def test_grouped_kv_heads_reduce_to_causal(H, G, path):
         np.testing.assert_allclose(got["lse"][b], lse, atol=1e-12, rtol=1e-10)
         np.testing.assert_allclose(got["dq"][b], dq, atol=1e-11, rtol=1e-9)
         np.testing.assert_allclose(got[key][b], dkv, atol=1e-11, rtol=1e-9)
+
+
+def explicit_mask_reference(q, kv, kvc, comp_mask, scale, dout):
+    """Attention of q [H, S, D] over the raw keys kv [S, D] under the causal mask
+    and the compressed keys kvc [Sc, D] under the given mask [S, Sc], as one
+    softmax over the concatenated key axis (torch, fp64, autograd)."""
+    S, Sc = kv.shape[0], kvc.shape[0]
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(kv, requires_grad=True)
+    ct = torch.tensor(kvc, requires_grad=True)
+    keys = torch.cat([kt, ct], 0)
+    allowed = torch.cat([torch.ones(S, S, dtype=torch.bool).tril(),
+                         torch.tensor(comp_mask, dtype=torch.bool)], 1)
+    logits = (qt @ keys.T) * scale
+    logits = logits.masked_fill(~allowed, -math.inf)
+    p = torch.softmax(logits, -1)
+    o = p @ keys
+    o.backward(torch.tensor(dout))
+    lse = torch.logsumexp(logits.detach(), -1)
+    return o.detach().numpy(), lse.numpy(), qt.grad.numpy(), kt.grad.numpy(), ct.grad.numpy()
+
+
+@pytest.mark.parametrize("kind", ["random", "topk"])
+def test_mask_mode_matches_explicit_mask_attention(kind):
+    """MASK mode (compressed visibility from a given dense mask): with a causal
+    raw window (W >= S) it must equal attention with the explicit boolean mask
+    [causal | given mask] over the concatenated keys; the mask is random, or
+    the one of a per-query top-k index selection (with padding and repeats)."""
+    rng = np.random.default_rng(21 if kind == "random" else 22)
+    B, S, H, D, Sc = 2, 19, 3, 8, 11
+    q, kv, kvc, dout = (rnd(rng, B, H, S, D), rnd(rng, B, S, D), rnd(rng, B, Sc, D),
+                        rnd(rng, B, H, S, D))
+    if kind == "random":
+        mask = (rng.random((B, S, Sc)) < 0.35).astype(np.uint8)
+    else:
+        idx = rng.integers(-2, Sc, size=(B, S, 4))  # negatives are padding
+        idx[:, :, 3] = idx[:, :, 0]                  # a repeated pick
+        mask = oracle.topk_mask(B, S, Sc, idx)
+        for b in range(B):
+            for i in range(S):
+                assert set(np.nonzero(mask[b, i])[0]) == {int(x) for x in idx[b, i] if x >= 0}
+    p = oracle.Problem(B, S, H, D, 1, S, Sc, 1.0 / math.sqrt(D), None, oracle.MASK, "f64",
+                       comp_mask=mask)
+    got = oracle.full(p, q, kv, kvc, dout)
+    for b in range(B):
+        o, lse, dq, dkv, dkvc = explicit_mask_reference(q[b], kv[b], kvc[b], mask[b], p.scale,
+                                                        dout[b])
+        np.testing.assert_allclose(got["o"][b], o, atol=1e-12, rtol=1e-10)
+        np.testing.assert_allclose(got["lse"][b], lse, atol=1e-12, rtol=1e-10)
+        np.testing.assert_allclose(got["dq"][b], dq, atol=1e-11, rtol=1e-9)
+        np.testing.assert_allclose(got["dkv"][b], dkv, atol=1e-11, rtol=1e-9)
+        np.testing.assert_allclose(got["dkvc"][b], dkvc, atol=1e-11, rtol=1e-9)
+
+
+def test_mask_mode_with_the_hca_pattern_matches_strict():
+    """The dense mask of the HCA pattern itself (completed windows of the
+    query's document) in MASK mode gives the STRICT results."""
+    rng = np.random.default_rng(23)
+    B, S, H, D, r, W = 1, 40, 2, 8, 4, 6
+    lengths = [[13, 27]]
+    q, kv, kvc, dout = (rnd(rng, B, H, S, D), rnd(rng, B, S, D), rnd(rng, B, S // r, D),
+                        rnd(rng, B, H, S, D))
+    strict = make_problem(B, S, H, D, r, W, lengths)
+    mask = np.zeros((B, S, S // r), np.uint8)
+    for i in range(S):
+        for c in range(S // r):
+            mask[0, i, c] = oracle.vis_comp(strict, 0, i, c)
+    masked = oracle.Problem(B, S, H, D, r, W, S // r, strict.scale, segment_ids(lengths, B, S),
+                            oracle.MASK, "f64", comp_mask=mask)
+    a, b = oracle.full(strict, q, kv, kvc, dout), oracle.full(masked, q, kv, kvc, dout)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
 
 
 def test_duplicated_keys_shift_lse_by_ln2():
