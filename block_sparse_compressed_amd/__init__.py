@@ -29,7 +29,8 @@ HCA_TILE_EMPTY, HCA_TILE_PARTIAL, HCA_TILE_FULL = 0, 1, 2
 
 # Declared in include/hca.h; the ABI test checks the header and this list agree.
 EXPORTS = (
-    "hca_block_mask_build", "hca_block_mask_build_gqa", "hca_plan_get_info",
+    "hca_block_mask_build", "hca_block_mask_build_gqa", "hca_block_mask_build_masked",
+    "hca_block_mask_build_topk", "hca_plan_get_info",
     "hca_plan_export_tiles",
     "hca_plan_export_rows", "hca_plan_export_items", "hca_plan_upload", "hca_plan_destroy",
     "hca_attn_fwd", "hca_attn_fwd_noalloc",
@@ -64,7 +65,8 @@ class _PlanInfo(ctypes.Structure):
         "tiles_raw", "tiles_comp", "full_raw", "full_comp", "pairs_raw", "pairs_comp")] + [
         (n, ctypes.c_uint64) for n in ("device_bytes", "ws_fwd_bytes", "ws_bwd_bytes")] + [
         (n, ctypes.c_int64) for n in ("items", "items_half", "part_blocks")] + [
-        (n, ctypes.c_int32) for n in ("comp_item_chunks", "kv_heads")]
+        (n, ctypes.c_int32) for n in ("comp_item_chunks", "kv_heads", "comp_masked",
+                                      "reserved_")]
 
 
 class _KernelTime(ctypes.Structure):
@@ -90,6 +92,12 @@ def _load_library():
     lib.hca_block_mask_build_gqa.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i32, i32,
                                              i32, i32, vp, ctypes.POINTER(vp)]
     lib.hca_block_mask_build_gqa.restype = ctypes.c_int
+    lib.hca_block_mask_build_masked.argtypes = [i32, i32, i32, i32, vp, vp, i32, i32, i32, vp,
+                                                vp, ctypes.POINTER(vp)]
+    lib.hca_block_mask_build_masked.restype = ctypes.c_int
+    lib.hca_block_mask_build_topk.argtypes = [i32, i32, i32, i32, vp, vp, i32, i32, i32, vp,
+                                              i32, vp, ctypes.POINTER(vp)]
+    lib.hca_block_mask_build_topk.restype = ctypes.c_int
     lib.hca_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
     lib.hca_plan_get_info.restype = ctypes.c_int
     lib.hca_plan_export_tiles.argtypes = [vp, vp, vp]
@@ -155,6 +163,7 @@ class PlanInfo:
     pairs_raw: int; pairs_comp: int
     device_bytes: int; ws_fwd_bytes: int; ws_bwd_bytes: int
     items: int; items_half: int; part_blocks: int; comp_item_chunks: int; kv_heads: int
+    comp_masked: int; reserved_: int
 
 
 class Plan:
@@ -217,6 +226,40 @@ def hca_block_mask_build_gqa(B, kv_heads, S, r, W, S_c, seg_starts=None, seg_cou
         starts.ctypes.data if starts is not None else None,
         counts.ctypes.data if counts is not None else None,
         H, D, dtype, mode, ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out)))
+    return Plan(out.value)
+
+
+def hca_block_mask_build_masked(B, S, W, S_c, comp_mask, seg_starts=None, seg_counts=None, H=1,
+                                D=512, dtype=HCA_BF16, tiles=None) -> Plan:
+    """Plan whose compressed-key visibility is the host mask comp_mask [B, S, S_c]
+    (nonzero = visible); the raw window keeps its rule."""
+    mask = np.ascontiguousarray(np.asarray(comp_mask) != 0, dtype=np.uint8)
+    if mask.shape != (B, S, S_c):
+        raise HcaInvalidArgument(HCA_ERR_INVALID_ARG, "comp_mask must be [B, S, S_c]")
+    starts, counts = _i32(seg_starts), _i32(seg_counts)
+    cfg = _cfg(tiles)
+    out = ctypes.c_void_p()
+    _check(_lib.hca_block_mask_build_masked(
+        B, S, W, S_c, starts.ctypes.data if starts is not None else None,
+        counts.ctypes.data if counts is not None else None, H, D, dtype, mask.ctypes.data,
+        ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out)))
+    return Plan(out.value)
+
+
+def hca_block_mask_build_topk(B, S, W, S_c, idx, seg_starts=None, seg_counts=None, H=1, D=512,
+                              dtype=HCA_BF16, tiles=None) -> Plan:
+    """Plan for attention over the per-query compressed entries idx [B, S, K]
+    (negative = none) plus the raw window."""
+    ix = np.ascontiguousarray(np.asarray(idx), dtype=np.int32)
+    if ix.ndim != 3 or ix.shape[:2] != (B, S):
+        raise HcaInvalidArgument(HCA_ERR_INVALID_ARG, "idx must be [B, S, K]")
+    starts, counts = _i32(seg_starts), _i32(seg_counts)
+    cfg = _cfg(tiles)
+    out = ctypes.c_void_p()
+    _check(_lib.hca_block_mask_build_topk(
+        B, S, W, S_c, starts.ctypes.data if starts is not None else None,
+        counts.ctypes.data if counts is not None else None, H, D, dtype, ix.ctypes.data,
+        ix.shape[2], ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out)))
     return Plan(out.value)
 
 
@@ -384,15 +427,19 @@ class HcaAttention:
     """
 
     def __init__(self, B, S, H, D, r, W, dtype="bf16", seg_starts=None, seg_counts=None,
-                 mode=HCA_COMPSEG_STRICT, tiles=None, device="cuda", kv_heads=1):
+                 mode=HCA_COMPSEG_STRICT, tiles=None, device="cuda", kv_heads=1, plan=None):
+        """plan: a plan built elsewhere (for instance hca_block_mask_build_masked);
+        r is then unused and S_c comes from the plan."""
         import torch
 
         self.B, self.S, self.H, self.D, self.r, self.W = B, S, H, D, r, W
-        self.S_c = S // r
+        self.S_c = S // r if plan is None else hca_plan_get_info(plan).S_c
         self.kv_heads = kv_heads
         self.dtype = HCA_BF16 if dtype == "bf16" else HCA_F32
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        if kv_heads == 1:
+        if plan is not None:
+            self.plan = plan
+        elif kv_heads == 1:
             self.plan = hca_block_mask_build(B, S, r, W, self.S_c, seg_starts, seg_counts, H, D,
                                              self.dtype, mode, tiles)
         else:

@@ -36,6 +36,7 @@ Dims make_dims(const hca_plan *plan) {
   d.kv_bk = plan->kv_bk;
   d.nkv_raw = plan->nkv_raw;
   d.nkv_comp = plan->nkv_comp;
+  d.cmask_ldw = plan->cmask_ldw;
   return d;
 }
 
@@ -51,6 +52,7 @@ DevPlan make_devplan(const hca_plan *plan) {
   p.kvorder = reinterpret_cast<const int32_t *>(base + L.kvorder);
   p.kvent = reinterpret_cast<const uint32_t *>(base + L.kvent);
   p.kvtile = reinterpret_cast<const int32_t *>(base + L.kvtile);
+  p.cmask = plan->cmask_ldw ? reinterpret_cast<const uint32_t *>(base + L.cmask) : nullptr;
   return p;
 }
 

@@ -277,7 +277,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
 //     issued before dS and the dQ product of tile t, so VALU work overlaps
 //     matrix-core work.
 // ---------------------------------------------------------------------------
-template <int NW>
+// MASKED: compressed visibility from the plan's mask bits (separate
+// instantiation, as for the forward).
+template <int NW, bool MASKED>
 __global__ void __launch_bounds__(NW * 64, 1)
     hca_bwd_dq512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                          const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
@@ -455,8 +457,17 @@ __global__ void __launch_bounds__(NW * 64, 1)
     stage_k(2);
     stage_t(1);
 
+    // Masked plans: the 32 visibility bits of this row for the compressed
+    // tile of entry `e`, loaded when the entry becomes current (0 otherwise).
+    auto mask_word = [&](uint32_t e) -> uint32_t {
+      if constexpr (MASKED) {
+        if ((e & kEntComp) && !(e & kEntFull) && valid)
+          return p.cmask[((size_t)b * d.S + pos) * d.cmask_ldw + (e & kEntIdx)];
+      }
+      return 0u;
+    };
     // dS of tile it from its scores, then dQ^T += K^T dS^T.
-    auto grad = [&](int it, uint32_t ent) {
+    auto grad = [&](int it, uint32_t ent, uint32_t mw) {
       const bool comp = ent & kEntComp;
       const int k0 = (int)(ent & kEntIdx) * kBK;
       float x[8];
@@ -466,10 +477,16 @@ __global__ void __launch_bounds__(NW * 64, 1)
         x[4 + v4] = sc[1][v4] * scale_log2 - lse2;
       }
       if (!(ent & kEntFull)) {
-        const int lo = (comp ? clo : rlo) - (k0 + 8 * g);
-        const int hi = (comp ? chi : pos + 1) - (k0 + 8 * g);
+        if (MASKED && comp) {
+          const uint32_t bits = mw >> (8 * g);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
+          for (int t = 0; t < 8; ++t) x[t] = ((bits >> t) & 1u) ? x[t] : -INFINITY;
+        } else {
+          const int lo = (comp ? clo : rlo) - (k0 + 8 * g);
+          const int hi = (comp ? chi : pos + 1) - (k0 + 8 * g);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
+        }
       }
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
@@ -503,11 +520,12 @@ __global__ void __launch_bounds__(NW * 64, 1)
     // List entries are read only right after the barrier (where a wait for a
     // scalar load costs nothing): ent holds the entry of the current tile.
     uint32_t ent = nent > 0 ? entry(0) : 0u;
+    uint32_t mw = mask_word(ent);
     const int last = nent - 1;
     for (int it = 0; it + 1 < last; ++it) {
       floatx4 sn[2], pn[2];
       sdp(it + 1, sn, pn);
-      grad(it, ent);
+      grad(it, ent, mw);
       sc[0] = sn[0];
       sc[1] = sn[1];
       pc[0] = pn[0];
@@ -515,6 +533,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
       wait_all_loads();
       __syncthreads();
       ent = entry(it + 1);
+      mw = mask_word(ent);
       stage_k(it + 3);
       stage_t(it + 2);
     }
@@ -523,9 +542,11 @@ __global__ void __launch_bounds__(NW * 64, 1)
     // last two tiles and the store (one fetch site, so the loaded registers
     // need no copies that would wait for them).
     floatx4 sn[2], pn[2];
-    uint32_t ent_last = 0u;
+    uint32_t ent_last = 0u, mw_last = 0u;
     if (last >= 1) {
       ent_last = entry(last);  // before the fetch replaces the entries
+      // (its mask word before the row loads too, so they stay the last ones issued)
+      mw_last = mask_word(ent_last);
       sdp(last, sn, pn);
     }
     fetch(sl_n, item_n, e_begin_n, nent_n);
@@ -533,7 +554,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     // issued before the wait below.
     __builtin_amdgcn_sched_barrier(0);
     if (last >= 1) {
-      grad(last - 1, ent);
+      grad(last - 1, ent, mw);
       sc[0] = sn[0];
       sc[1] = sn[1];
       pc[0] = pn[0];
@@ -546,8 +567,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
       asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kRowLoads) : "memory");
       lds_barrier();
       ent = ent_last;
+      mw = mw_last;
     }
-    if (last >= 0) grad(last, ent);
+    if (last >= 0) grad(last, ent, mw);
 
     // No copy is in flight and no wave reads the K buffers any more (the last
     // tile reads only its K^T buffer): each wave stages its 16 rows of dQ there
@@ -787,6 +809,10 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *p) { return tr_frag_rows(p
 //                  row block w >> 2 (16 rows); the gradient covers the half's
 //                  four key blocks.
 // ---------------------------------------------------------------------------
+// MASKED: compressed visibility from the plan's mask bits (separate
+// instantiation): each step row's 128 bits of the item's tile travel with the
+// row table.
+template <bool MASKED>
 __global__ void __launch_bounds__(512, 1)
     hca_bwd_dkv512x8_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                             const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
@@ -798,6 +824,9 @@ __global__ void __launch_bounds__(512, 1)
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * STEP_BYTES];  // [buf][Q | dO]
   __shared__ __attribute__((aligned(16))) char xs[2 * XBYTES];             // [P | dS]
   __shared__ float4 ri_s[2][STEP];  // per step row: lse log2e, delta, key interval
+  // Masked plans: per step slot, the 128 visibility bits of the item's tile
+  // for rows lane & 31 (lanes 32..63 copy the same rows again).
+  __shared__ __attribute__((aligned(16))) uint4 rm_s[MASKED ? 2 : 1][MASKED ? 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
@@ -847,6 +876,12 @@ __global__ void __launch_bounds__(512, 1)
     nrw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
     nl = lse[row];
     nd = delta[row];
+    // Masked: the row's 128 bits of the item's tile (words k0 / 32 .. + 3) go
+    // straight to LDS (no registers); waited for with the row copies.  A
+    // padded row reads its clamped row's bits; the softmax ignores them.
+    if (MASKED && comp && wave == 0)
+      dma16(p.cmask, (uint32_t)((((size_t)b * d.S + pc) * d.cmask_ldw + k0 / 32) * 4),
+            lds_addr(&rm_s[MASKED ? (s & 1) : 0][0]));
   };
   auto put_rowinfo = [&](int slot) {
     if (wave == 0 && lane < STEP) {
@@ -961,9 +996,20 @@ __global__ void __launch_bounds__(512, 1)
           bf16x4 pp, dd;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float4 rr = ri_s[slot][8 * g + 4 * (rb0 + rb) + v];
-            const bool vis =
-                full | ((key >= __float_as_int(rr.z)) & (key < __float_as_int(rr.w)));
+            const int row = 8 * g + 4 * (rb0 + rb) + v;
+            const float4 rr = ri_s[slot][row];
+            bool vis;
+            if (MASKED && comp) {
+              // the word of this lane's key (a padded row's interval start is
+              // INT_MAX: never visible)
+              const int kk = key - k0;
+              const uint32_t word =
+                  reinterpret_cast<const uint32_t *>(&rm_s[MASKED ? slot : 0][row])[kk >> 5];
+              vis = full | ((((word >> (kk & 31)) & 1u) != 0) &
+                            (__float_as_int(rr.z) != INT_MAX));
+            } else {
+              vis = full | ((key >= __float_as_int(rr.z)) & (key < __float_as_int(rr.w)));
+            }
             const float ex = fast_exp2(sv[rb][v] * scale_log2 - rr.x);
             const float e = vis ? ex : 0.f;
             pp[v] = (__bf16)e;
@@ -1154,7 +1200,10 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
       const int units = d.B * d.nqt * (d.bq * d.H / 64);
       const int cus = compute_units();
       if (cus <= 0) return (int)hipErrorInvalidDevice;
-      go(hca_bwd_dq512_kernel<4>, 4, units < cus ? units : cus);
+      if (d.cmask_ldw)
+        go(hca_bwd_dq512_kernel<4, true>, 4, units < cus ? units : cus);
+      else
+        go(hca_bwd_dq512_kernel<4, false>, 4, units < cus ? units : cus);
       break;
     }
     case 128: go(hca_bwd_dq_kernel<128, 8, 1>, 8, d.B * d.nqt * (d.bq * d.H / 128)); break;
@@ -1178,9 +1227,14 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
   switch (d.D) {
     case 512:
       // Every item (over all keys of its tile or over one half) in one launch.
-      hipLaunchKernelGGL(hca_bwd_dkv512x8_kernel, dim3(d.n_items), dim3(512), 0, s, d, p,
-                         (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc, lse,
-                         delta, (const bf16raw *)dout, sl2, scale, part);
+      if (d.cmask_ldw)
+        hipLaunchKernelGGL(hca_bwd_dkv512x8_kernel<true>, dim3(d.n_items), dim3(512), 0, s, d,
+                           p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc, lse,
+                           delta, (const bf16raw *)dout, sl2, scale, part);
+      else
+        hipLaunchKernelGGL(hca_bwd_dkv512x8_kernel<false>, dim3(d.n_items), dim3(512), 0, s, d,
+                           p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc, lse,
+                           delta, (const bf16raw *)dout, sl2, scale, part);
       break;
     case 128: go(hca_bwd_dkv_kernel<128>); break;
     case 64: go(hca_bwd_dkv_kernel<64>); break;

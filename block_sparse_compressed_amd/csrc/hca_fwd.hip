@@ -291,7 +291,10 @@ constexpr float kLazy = 8.f;
 // NW = 8: one workgroup per CU, K and K^T double-buffered (128 KiB of LDS).
 // NW = 4: two workgroups per CU, K and K^T single-buffered (64 KiB each), so
 // one workgroup's row loads, barriers and tile waits overlap the other's math.
-template <int NW, int MB>
+// MASKED: compressed visibility from the plan's mask bits (masked plans);
+// otherwise from the per-position intervals.  Separate instantiations, so the
+// interval kernel carries none of the mask code.
+template <int NW, int MB, bool MASKED>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
     hca_fwd512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                       const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
@@ -428,6 +431,20 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
         qf[mb][ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g));
     }
   };
+  // Masked plans (compressed visibility from a given mask): the 32 visibility
+  // bits of each row for the compressed tile of entry `ent`, loaded when the
+  // entry becomes current, one tile ahead of their use (0 otherwise).
+  uint32_t mword[MB];
+  auto load_mask = [&](uint32_t ent) {
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        mword[mb] = 0u;
+        if ((ent & kEntComp) && !(ent & kEntFull) && valid[mb])
+          mword[mb] = p.cmask[((size_t)b * d.S + pos[mb]) * d.cmask_ldw + (ent & kEntIdx)];
+      }
+    }
+  };
   // Online softmax of tile `it` (scores sc, list entry ent) and O^T += K^T P^T.
   auto soft_pv = [&](int it, const floatx4 (&sc)[MB][2], uint32_t ent) {
     const bool comp = ent & kEntComp;
@@ -442,11 +459,18 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
         x[4 + v] = sc[mb][1][v] * scale_log2;
       }
       if (!(ent & kEntFull)) {
-        // visible keys of this row: [lo, hi) relative to this lane's 8 keys
-        const int lo = (comp ? clo[mb] : rlo[mb]) - (k0 + 8 * g);
-        const int hi = (comp ? chi[mb] : pos[mb] + 1) - (k0 + 8 * g);
+        if (MASKED && comp) {
+          // this lane's 8 keys: bits 8 g .. 8 g + 7 of the row's tile word
+          const uint32_t bits = mword[mb] >> (8 * g);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
+          for (int t = 0; t < 8; ++t) x[t] = ((bits >> t) & 1u) ? x[t] : -INFINITY;
+        } else {
+          // visible keys of this row: [lo, hi) relative to this lane's 8 keys
+          const int lo = (comp ? clo[mb] : rlo[mb]) - (k0 + 8 * g);
+          const int hi = (comp ? chi[mb] : pos[mb] + 1) - (k0 + 8 * g);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
+        }
       }
       float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -508,6 +532,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     // List entries are read only right after the barrier (where a wait for a
     // scalar load costs nothing): ent holds the entry of the current tile.
     uint32_t ent = nent > 0 ? entry(0) : 0u;
+    load_mask(ent);
     for (int it = 0; it < nent; ++it) {
       floatx4 sn[MB][2];
       if (it + 1 < nent) qk(it + 1, sn);
@@ -519,7 +544,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
       }
       wait_all_loads();
       __syncthreads();
-      if (it + 1 < nent) ent = entry(it + 1);
+      if (it + 1 < nent) {
+        ent = entry(it + 1);
+        load_mask(ent);
+      }
       stage_k(it + 3);
       stage_t(it + 2);
     }
@@ -537,12 +565,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     __syncthreads();  // K buffer free
     stage_k(1);
     uint32_t ent = nent > 0 ? entry(0) : 0u;
+    load_mask(ent);
     for (int it = 0; it < nent; ++it) {
       soft_pv(it, sc, ent);
       wait_all_loads();  // K of tile it + 1
       __syncthreads();   // K^T buffer free, K of tile it + 1 visible
       if (it + 1 < nent) {
         ent = entry(it + 1);
+        load_mask(ent);
         stage_t(it + 1);
         qk(it + 1, sc);
         wait_all_loads();  // K^T of tile it + 1
@@ -684,9 +714,15 @@ int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *
     case 512: {
       constexpr int NW = HCA_FWD_NW, MB = HCA_FWD_MB;
       const dim3 g512(d.B * d.nqt * (d.bq * d.H / (NW * MB * 16)));
-      hipLaunchKernelGGL((hca_fwd512_kernel<NW, MB>), g512, dim3(NW * 64), 0, s, d, p,
-                         (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc,
-                         (const bf16raw *)kvt, (const bf16raw *)kvct, sl2, (bf16raw *)o, lse);
+      auto go512 = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, g512, dim3(NW * 64), 0, s, d, p, (const bf16raw *)q,
+                           (const bf16raw *)kv, (const bf16raw *)kvc, (const bf16raw *)kvt,
+                           (const bf16raw *)kvct, sl2, (bf16raw *)o, lse);
+      };
+      if (d.cmask_ldw)
+        go512(hca_fwd512_kernel<NW, MB, true>);
+      else
+        go512(hca_fwd512_kernel<NW, MB, false>);
       break;
     }
     case 128: args(hca_fwd_bf16_kernel<128, 8, 1>, 8); break;

@@ -46,6 +46,8 @@ struct DevLayout {
   uint64_t kvorder = 0;  // int32 [n_items]: launch slot -> item, -1 = none
   uint64_t kvent = 0;    // uint32 [n_kvent]: bit 30 FULL, bits 0..29 query tile
   uint64_t kvtile = 0;   // int32 [B][nkv_raw + nkv_comp][2]: first partial block, block count
+  uint64_t cmask = 0;    // uint32 [B][S][cmask_ldw]: compressed-key visibility bits (masked
+                         // plans only)
   uint64_t total = 0;
 };
 
@@ -67,6 +69,7 @@ struct Dims {
   int32_t S_pad, Sc_pad;  // nkt_raw * bk_raw, nkt_comp * bk_comp
   int32_t n_items;       // launch slots of the key-stationary backward
   int32_t kv_bk, nkv_raw, nkv_comp;  // key tiles of the key-stationary backward
+  int32_t cmask_ldw;  // words per position of the compressed-key mask; 0: interval rule
 };
 
 struct DevPlan {
@@ -78,6 +81,7 @@ struct DevPlan {
   const int32_t *kvorder;
   const uint32_t *kvent;
   const int32_t *kvtile;
+  const uint32_t *cmask;  // masked plans: visibility bits of compressed keys
 };
 
 // Launchers (defined in the .hip files).  Each returns a hipError_t as int.
@@ -128,6 +132,7 @@ struct hca_plan {
   std::vector<int32_t> kvtile;
   int32_t kv_bk = 32, nkv_raw = 0, nkv_comp = 0;  // key-stationary backward tiling
   int32_t rows_b = 0;  // rows of the plan's tables: batch rows x kv heads
+  int32_t cmask_ldw = 0;  // masked plans: words per position of the device mask
   hca::DevLayout lay;
   hca::WsLayout ws;
   std::string unsupported;     // why kernel_ok is 0 ("" when it is 1)

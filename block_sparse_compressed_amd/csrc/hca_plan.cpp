@@ -74,6 +74,22 @@ int classify_tile(const int32_t *rw, int64_t S, int64_t qt, int bq, int kind, in
   return any ? (all ? HCA_TILE_FULL : HCA_TILE_PARTIAL) : HCA_TILE_EMPTY;
 }
 
+// State of query tile qt against compressed entries [k0, k0 + bk) when their
+// visibility is a given dense mask `m` ([S][Sc] of one batch row).
+int classify_tile_mask(const uint8_t *m, int64_t S, int64_t Sc, int64_t qt, int bq, int64_t k0,
+                       int64_t bk) {
+  const int64_t i0 = qt * bq, i1 = std::min<int64_t>(S, i0 + bq);
+  const int64_t kend = std::min<int64_t>(k0 + bk, Sc);
+  bool any = false, all = i0 + bq <= S && k0 + bk <= Sc;
+  for (int64_t i = i0; i < i1; ++i)
+    for (int64_t c = k0; c < kend; ++c) {
+      const bool v = m[i * Sc + c] != 0;
+      any |= v;
+      all &= v;
+    }
+  return any ? (all ? HCA_TILE_FULL : HCA_TILE_PARTIAL) : HCA_TILE_EMPTY;
+}
+
 }  // namespace
 
 // Keys per work item of the key-stationary backward: 128 (4 waves x 32 keys)
@@ -134,10 +150,13 @@ using namespace hca;
 // one MQA problem with the same documents, and their tensors are contiguous
 // slices of q [B][H][S][D] and kv [B][G][S][D]: the plan holds B * G such
 // rows of H / G heads, and the kernels run them unchanged.
+// cmask: NULL, or a dense mask [B][S][S_c] that decides the visibility of
+// every compressed pair (G = 1); the raw window keeps its rule.
 static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, int32_t r,
                              int32_t W, int32_t S_c, const int32_t *seg_starts,
                              const int32_t *seg_counts, int32_t H, int32_t D, hca_dtype dtype,
-                             hca_compseg_mode mode, const hca_tile_cfg *tiles, hca_plan **out) {
+                             hca_compseg_mode mode, const hca_tile_cfg *tiles, hca_plan **out,
+                             const uint8_t *cmask = nullptr) {
   const std::string F(fn);
   if (!out) {
     set_error(F + ": out is NULL");
@@ -164,7 +183,7 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     set_error(F + ": window W must be >= 0");
     return HCA_ERR_INVALID_ARG;
   }
-  if (S_c != S / r) {
+  if (!cmask && S_c != S / r) {
     set_error(F + ": S_c must equal floor(S / r) = " + std::to_string(S / r) +
               ", got " + std::to_string(S_c));
     return HCA_ERR_INVALID_ARG;
@@ -271,6 +290,14 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     p->unsupported = kernel_supports(dtype, D, H, bq, bkr, bkc);
     if (p->unsupported.empty())
       p->unsupported = kernel_sizes_ok(dtype, D, nktr * bkr, nktc * bkc);
+    if (p->unsupported.empty() && cmask && !(dtype == HCA_BF16 && D == 512))
+      p->unsupported = "plans with a given compressed-key mask run on the head dim 512 "
+                       "bfloat16 kernels only";
+    // the key-stationary kernel addresses the mask bits with 32-bit byte offsets
+    if (p->unsupported.empty() && cmask &&
+        (int64_t)B * S * ceil_div(S_c, 128) * 16 >= ((int64_t)1 << 31))
+      p->unsupported = "compressed-key mask too large for 32-bit offsets";
+    in.comp_masked = cmask ? 1 : 0;
     in.kernel_ok = p->unsupported.empty() ? 1 : 0;
     p->kv_bk = kv_tile_keys(dtype, D);
 
@@ -287,10 +314,17 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
         int64_t chi = std::min<int64_t>((i + 1) / r, S_c);
         int64_t clo = mode == HCA_COMPSEG_STRICT ? ceil_div(a, r) : a / r;
         if (clo > chi) clo = chi;
+        if (cmask) {  // the mask decides; the interval spans every entry
+          clo = 0;
+          chi = S_c;
+          const uint8_t *mr = cmask + ((size_t)b * S + i) * S_c;
+          for (int64_t c = 0; c < S_c; ++c) pairs_comp += mr[c] != 0;
+        } else {
+          pairs_comp += chi - clo;
+        }
         int32_t *row = &p->rows[((size_t)b * S + i) * 4];
         row[0] = (int32_t)rlo; row[1] = (int32_t)clo; row[2] = (int32_t)chi; row[3] = 0;
         pairs_raw += std::max<int64_t>(0, i - rlo + 1);
-        pairs_comp += chi - clo;
       }
     }
     // Every kv head's rows see the same pattern: pairs per caller batch row.
@@ -331,6 +365,18 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
           }
         }
         // compressed entry tiles
+        if (cmask) {
+          const uint8_t *m = cmask + (size_t)b * S * S_c;
+          for (int64_t kt = 0; kt < nktc; ++kt) {
+            const int st = classify_tile_mask(m, S, S_c, qt, bq, kt * bkc, bkc);
+            if (st == HCA_TILE_EMPTY) continue;
+            p->qent.push_back((uint32_t)kt | kEntComp | (st == HCA_TILE_FULL ? kEntFull : 0u));
+            full_comp += st == HCA_TILE_FULL;
+            cost[(size_t)b * nqt + qt] += bkc;
+          }
+          p->qptr[(size_t)b * nqt + qt + 1] = (int32_t)p->qent.size();
+          continue;
+        }
         lo = INT64_MAX;
         hi = -1;
         for (int64_t i = i0; i < i1; ++i) {
@@ -420,12 +466,15 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
           p0 = k0;
           p1 = W > 0 ? std::min<int64_t>(S - 1, k0 + kvb - 1 + W - 1) : -1;
         } else {
-          p0 = (k0 + 1) * r - 1;
+          p0 = cmask ? 0 : (k0 + 1) * r - 1;
           p1 = S - 1;
         }
         std::vector<uint32_t> &list = lists[(size_t)b * nkv + t];
         for (int64_t qt = p0 >= 0 && p0 <= p1 ? p0 / bq : 0; p0 <= p1 && qt <= p1 / bq; ++qt) {
-          const int st = classify_tile(rw, S, qt, bq, kind, k0, kvb, nk);
+          const int st = kind && cmask
+                             ? classify_tile_mask(cmask + (size_t)b * S * S_c, S, S_c, qt, bq,
+                                                  k0, kvb)
+                             : classify_tile(rw, S, qt, bq, kind, k0, kvb, nk);
           if (st != HCA_TILE_EMPTY)
             list.push_back((uint32_t)qt | (st == HCA_TILE_FULL ? kEntFull : 0u));
         }
@@ -488,6 +537,12 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
             for (size_t e = s0; e < s1; ++e) {
               const int64_t qt = list[e] & kEntIdx;
               for (int64_t i = qt * bq; i < std::min<int64_t>(S, qt * bq + bq); ++i) {
+                if (kind && cmask) {
+                  const uint8_t *mr = cmask + ((size_t)b * S + i) * S_c;
+                  for (int64_t c = k0; c < kend; ++c)
+                    if (mr[c]) it.halves |= c < kmid ? 1 : 2;
+                  continue;
+                }
                 const int64_t lo = kind ? rw[i * 4 + 1] : rw[i * 4];
                 const int64_t hi = kind ? rw[i * 4 + 2] : i + 1;
                 if (std::max(lo, k0) < std::min(hi, kmid)) it.halves |= 1;
@@ -613,6 +668,12 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     L.kvorder = place(std::max<size_t>(1, p->kvorder.size()) * 4);
     L.kvent = place(std::max<size_t>(1, p->kvent.size()) * 4);
     L.kvtile = place(p->kvtile.size() * 4);
+    if (cmask) {
+      // The mask as bits: per (row, query position) ceil(S_c / 128) * 4 words,
+      // bit c % 32 of word c / 32 set when entry c is visible.
+      p->cmask_ldw = (int32_t)(ceil_div(S_c, 128) * 4);
+      L.cmask = place((uint64_t)B * S * p->cmask_ldw * 4);
+    }
     L.total = off;
     p->image.assign(L.total, 0);
     auto put = [&](uint64_t o, const void *src, size_t bytes) {
@@ -626,6 +687,15 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     put(L.kvorder, p->kvorder.data(), p->kvorder.size() * 4);
     put(L.kvent, p->kvent.data(), p->kvent.size() * 4);
     put(L.kvtile, p->kvtile.data(), p->kvtile.size() * 4);
+    if (cmask) {
+      uint32_t *words = reinterpret_cast<uint32_t *>(p->image.data() + L.cmask);
+      for (size_t row = 0; row < (size_t)B * S; ++row) {
+        const uint8_t *mr = cmask + row * S_c;
+        uint32_t *wr = words + row * p->cmask_ldw;
+        for (int64_t c = 0; c < S_c; ++c)
+          if (mr[c]) wr[c >> 5] |= 1u << (c & 31);
+      }
+    }
     in.device_bytes = L.total;
 
     // ---- workspaces ------------------------------------------------------- //
@@ -670,6 +740,52 @@ extern "C" hca_status hca_block_mask_build_gqa(int32_t B, int32_t kv_heads, int3
                                                const hca_tile_cfg *tiles, hca_plan **out) {
   return build_plan("hca_block_mask_build_gqa", B, kv_heads, S, r, W, S_c, seg_starts,
                     seg_counts, H, D, dtype, mode, tiles, out);
+}
+
+extern "C" hca_status hca_block_mask_build_masked(int32_t B, int32_t S, int32_t W, int32_t S_c,
+                                                  const int32_t *seg_starts,
+                                                  const int32_t *seg_counts, int32_t H,
+                                                  int32_t D, hca_dtype dtype,
+                                                  const uint8_t *comp_mask,
+                                                  const hca_tile_cfg *tiles, hca_plan **out) {
+  if (!comp_mask || S_c < 0) {
+    set_error("hca_block_mask_build_masked: comp_mask is NULL or S_c < 0");
+    if (out) *out = nullptr;
+    return HCA_ERR_INVALID_ARG;
+  }
+  // r only enters the compressed rule, which the mask replaces.
+  return build_plan("hca_block_mask_build_masked", B, 1, S, 1, W, S_c, seg_starts, seg_counts,
+                    H, D, dtype, HCA_COMPSEG_STRICT, tiles, out, comp_mask);
+}
+
+extern "C" hca_status hca_block_mask_build_topk(int32_t B, int32_t S, int32_t W, int32_t S_c,
+                                                const int32_t *seg_starts,
+                                                const int32_t *seg_counts, int32_t H, int32_t D,
+                                                hca_dtype dtype, const int32_t *idx, int32_t K,
+                                                const hca_tile_cfg *tiles, hca_plan **out) {
+  if (out) *out = nullptr;
+  if (!idx || K < 1 || S_c < 1 || B < 1 || S < 1) {
+    set_error("hca_block_mask_build_topk: idx is NULL, or K, S_c, B or S < 1");
+    return HCA_ERR_INVALID_ARG;
+  }
+  std::vector<uint8_t> mask;
+  try {
+    mask.assign((size_t)B * S * S_c, 0);
+  } catch (const std::bad_alloc &) {
+    set_error("hca_block_mask_build_topk: out of host memory");
+    return HCA_ERR_NOMEM;
+  }
+  for (size_t row = 0; row < (size_t)B * S; ++row)
+    for (int32_t k = 0; k < K; ++k) {
+      const int32_t c = idx[row * K + k];
+      if (c >= S_c) {
+        set_error("hca_block_mask_build_topk: index " + std::to_string(c) + " >= S_c");
+        return HCA_ERR_INVALID_ARG;
+      }
+      if (c >= 0) mask[row * S_c + c] = 1;
+    }
+  return build_plan("hca_block_mask_build_topk", B, 1, S, 1, W, S_c, seg_starts, seg_counts, H,
+                    D, dtype, HCA_COMPSEG_STRICT, tiles, out, mask.data());
 }
 
 extern "C" hca_status hca_plan_get_info(const hca_plan *plan, hca_plan_info *out) {

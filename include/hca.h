@@ -126,6 +126,9 @@ typedef struct hca_plan_info {
   int64_t part_blocks;             /* float32 partial-gradient blocks (kv_bk x D each) */
   int32_t comp_item_chunks;        /* 64-position chunks per compressed-tile item */
   int32_t kv_heads;                /* key/value heads G (1: MQA); see hca_block_mask_build_gqa */
+  int32_t comp_masked;             /* 1: compressed visibility from a given mask (see
+                                      hca_block_mask_build_masked) */
+  int32_t reserved_;
 } hca_plan_info;
 
 /*
@@ -175,6 +178,45 @@ hca_status hca_block_mask_build_gqa(int32_t B, int32_t kv_heads, int32_t S, int3
                                     const int32_t *seg_counts, int32_t H, int32_t D,
                                     hca_dtype dtype, hca_compseg_mode mode,
                                     const hca_tile_cfg *tiles, hca_plan **out);
+
+/*
+ * Plan whose compressed-key pattern is a given dense mask instead of the HCA
+ * rule: comp_mask is a host array [B][S][S_c], nonzero where query i may see
+ * compressed entry c (any pattern; S_c is free, r does not enter).  This is
+ * the form in which the dynamic path of "Add HCA Static Compilation for
+ * Splash Attention [Deepseek v4]" (Description) hands compressed attention
+ * its pattern -- a dense (B, 1, S, S_comp) mask -- kept here as the
+ * comparison with the analytic plan.  The raw window keeps its rule (window
+ * W, documents as in hca_block_mask_build).  The planner reads every mask
+ * element (O(B S S_c) host work, against O(B S) for the analytic plan),
+ * classifies tiles from it, and stores it in the plan's device image as bits
+ * (ceil(S_c / 128) * 16 bytes per position), which the kernels read for the
+ * compressed tiles that are PARTIAL; the caller's array is not kept.
+ * hca_attn_fwd / hca_attn_bwd then run unchanged (head dim 512 bfloat16
+ * kernels only; other head dims and float32 give kernel_ok = 0).
+ * Errors: as hca_block_mask_build, and HCA_ERR_INVALID_ARG on a NULL mask.
+ */
+hca_status hca_block_mask_build_masked(int32_t B, int32_t S, int32_t W, int32_t S_c,
+                                       const int32_t *seg_starts, const int32_t *seg_counts,
+                                       int32_t H, int32_t D, hca_dtype dtype,
+                                       const uint8_t *comp_mask, const hca_tile_cfg *tiles,
+                                       hca_plan **out);
+
+/*
+ * Plan for attention over a given per-query selection of compressed entries,
+ * the CSA form of the compressed path (a top-k indexer picks entries per
+ * query; "Add HCA Static Compilation for Splash Attention [Deepseek v4]",
+ * Description: CSA requires a top-k step): idx is a host array [B][S][K] of
+ * entry indices (negative = no entry, repeats count once), shared by all
+ * heads of a position, plus the raw window as above.  Same as
+ * hca_block_mask_build_masked with the mask of the selection.  Errors: as
+ * hca_block_mask_build_masked, and HCA_ERR_INVALID_ARG for K < 1 or an index
+ * >= S_c.
+ */
+hca_status hca_block_mask_build_topk(int32_t B, int32_t S, int32_t W, int32_t S_c,
+                                     const int32_t *seg_starts, const int32_t *seg_counts,
+                                     int32_t H, int32_t D, hca_dtype dtype, const int32_t *idx,
+                                     int32_t K, const hca_tile_cfg *tiles, hca_plan **out);
 
 /* Fills *out with the plan's sizes and counts.  HCA_ERR_INVALID_ARG on NULL. */
 hca_status hca_plan_get_info(const hca_plan *plan, hca_plan_info *out);
