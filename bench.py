@@ -96,6 +96,11 @@ def parse():
     ap.add_argument("--half-items-min", type=int, default=0,
                     help="item count from which half-tile items are used (0 = library "
                          "choice, -1 = never)")
+    ap.add_argument("--comp-pattern", default="rule", choices=("rule", "dense", "topk"),
+                    help="rule: the analytic plan; dense: the same pattern materialised as a "
+                         "dense compressed-key mask kept in device memory, planned from the "
+                         "mask (the dynamic-mask comparison); topk: the CSA form, per-query "
+                         "compressed-entry selections (workload csa_topk_bf16)")
     ap.add_argument("--source-hashes", action="store_true",
                     help="print the source hash of each kernel and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -175,28 +180,61 @@ def main():
         return
     import torch
 
-    import block_sparse_compressed_amd as hca
-    from hca_inputs import WORKLOADS, doc_lengths, draw_workload, starts_csr
+    import numpy as np
 
-    wl = {w.name: w for w in WORKLOADS.values()}[args.workload]
+    import block_sparse_compressed_amd as hca
+    from hca_inputs import (CSA_TOPK, CSA_TOPK_K, WORKLOADS, doc_lengths, draw_workload,
+                            starts_csr, topk_indices)
+
+    if args.comp_pattern == "topk":
+        args.workload = CSA_TOPK.name
+    wl = {w.name: w for w in list(WORKLOADS.values()) + [CSA_TOPK]}[args.workload]
+    if (wl is CSA_TOPK) != (args.comp_pattern == "topk"):
+        print("bench.py: workload %s goes with --comp-pattern %s" % (
+            wl.name, "topk" if wl is CSA_TOPK else "rule or dense"), file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lengths = doc_lengths(wl)
     starts, counts = starts_csr(lengths, wl.B)
-
-    t0 = time.perf_counter()
-    plan_probe = hca.hca_block_mask_build(wl.B, wl.S, wl.r, wl.W, wl.Sc, starts, counts, wl.H,
-                                          wl.D, hca.HCA_BF16 if wl.dtype == "bf16" else hca.HCA_F32)
-    plan_ms = (time.perf_counter() - t0) * 1e3
-    del plan_probe
-
-    q, kv, kvc, dout = draw_workload(wl, device=dev)
-    torch.cuda.reset_peak_memory_stats()
+    dt = hca.HCA_BF16 if wl.dtype == "bf16" else hca.HCA_F32
     tiles = None
     if args.comp_item_chunks or args.half_items_min:
         tiles = (0, 0, 0, args.half_items_min, args.comp_item_chunks)
+
+    # Plan build (host), timed once outside the step loop.  dense: the analytic
+    # plan's per-position intervals give the dense mask of the same pattern,
+    # which is then planned from the mask (every element read).
+    comp_mask = topk = None
+    if args.comp_pattern == "dense":
+        rows = hca.hca_plan_export_rows(hca.hca_block_mask_build(
+            wl.B, wl.S, wl.r, wl.W, wl.Sc, starts, counts, wl.H, wl.D, dt))
+        c = np.arange(wl.Sc, dtype=np.int32)[None, None, :]
+        comp_mask = ((c >= rows[:, :, 1:2]) & (c < rows[:, :, 2:3])).astype(np.uint8)
+    if args.comp_pattern == "topk":
+        topk = topk_indices(wl, CSA_TOPK_K)
+
+    def build_plan():
+        if comp_mask is not None:
+            return hca.hca_block_mask_build_masked(wl.B, wl.S, wl.W, wl.Sc, comp_mask, starts,
+                                                   counts, wl.H, wl.D, dt, tiles)
+        if topk is not None:
+            return hca.hca_block_mask_build_topk(wl.B, wl.S, wl.W, wl.Sc, topk, starts, counts,
+                                                 wl.H, wl.D, dt, tiles)
+        return hca.hca_block_mask_build(wl.B, wl.S, wl.r, wl.W, wl.Sc, starts, counts, wl.H,
+                                        wl.D, dt, hca.HCA_COMPSEG_STRICT, tiles)
+
+    t0 = time.perf_counter()
+    plan = build_plan()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+
+    q, kv, kvc, dout = draw_workload(wl, device=dev)
+    torch.cuda.reset_peak_memory_stats()
+    # dense: the materialised mask stays resident in device memory, as in a
+    # pipeline that hands the attention a dense mask each step.
+    mask_dev = torch.from_numpy(comp_mask).to(dev) if comp_mask is not None else None
     att = hca.HcaAttention(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, wl.dtype, starts, counts,
-                           tiles=tiles)
+                           tiles=tiles, plan=plan)
     info = att.info
     scale = 1.0 / math.sqrt(wl.D)
     o, lse = att.new_outputs()
@@ -297,6 +335,8 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "H": wl.H, "D": wl.D, "r": wl.r,
                    "W": wl.W, "S_c": wl.Sc,
                    "documents": 1 if lengths is None else sum(len(x) for x in lengths),
+                   "comp_pattern": args.comp_pattern,
+                   "topk": None if topk is None else int(topk.shape[2]),
                    "parallelism": "single GPU"},
         "tokens_per_s": round(wl.B * wl.S / (ms * 1e-3), 1),
         "fwd_ms": round(fwd_ms, 4),
@@ -304,6 +344,9 @@ def main():
         "fwd_tokens_per_s": round(wl.B * wl.S / (fwd_ms * 1e-3), 1),
         "visible_pairs": P,
         "plan_build_ms": round(plan_ms, 2),
+        "comp_pattern": args.comp_pattern,
+        "plan_device_bytes": info.device_bytes,
+        "comp_mask_bytes": 0 if mask_dev is None else mask_dev.numel(),
         "peak_mem_gib": round(peak_mem, 3),
         "ws_bytes": max(info.ws_fwd_bytes, info.ws_bwd_bytes),
         "bwd_items": {"items": info.items, "half": info.items_half,
@@ -319,7 +362,7 @@ def main():
                      for k in per_step if recorded_util(k, wl.name) or
                      recorded_traffic(k, wl.name)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.comp_pattern == "rule":
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -65,6 +65,33 @@ WORKLOADS = {
 }
 
 
+# The CSA form of the compressed path (compress ratio 4, a top-k selection of
+# compressed entries per query, shared by its heads), at the mid-length shape.
+# The pages give the ratio but not k; 512 entries per query is used.  The
+# selection is drawn here (seeded), not computed by an indexer.
+CSA_TOPK = Workload("csa_topk_bf16", 1, 16384, 64, 512, 4, 4096, 128, "bf16", seed=6)
+CSA_TOPK_K = 512
+
+
+def topk_indices(wl: Workload, K: int) -> np.ndarray:
+    """Per-query selections [B, S, K] int32 for the top-k workload: query i picks
+    min(K, n_i) distinct entries uniformly among the n_i = (i + 1) // r entries
+    whose windows end at or before it (-1 fills the rest), from
+    numpy.random.default_rng(seed)."""
+    rng = np.random.default_rng(wl.seed)
+    out = np.full((wl.B, wl.S, K), -1, np.int32)
+    for b in range(wl.B):
+        for i0 in range(0, wl.S, 1024):
+            i1 = min(wl.S, i0 + 1024)
+            done = (np.arange(i0, i1) + 1) // wl.r
+            key = rng.random((i1 - i0, wl.Sc))
+            key[np.arange(wl.Sc)[None, :] >= done[:, None]] = np.inf
+            pick = np.argpartition(key, min(K, wl.Sc) - 1, axis=1)[:, :K].astype(np.int32)
+            pick[np.take_along_axis(key, pick, 1) == np.inf] = -1
+            out[b, i0:i1, :pick.shape[1]] = pick
+    return out
+
+
 def doc_lengths(wl: Workload) -> Optional[List[List[int]]]:
     """Per batch row, the list of document lengths (None: one document)."""
     if wl.docs is None:

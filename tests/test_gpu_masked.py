@@ -119,3 +119,60 @@ def test_hca_pattern_as_mask_matches_analytic_plan_bitwise():
     for x, y in zip(a, m):
         bits = (lambda t: t.view(torch.int16)) if x.dtype == torch.bfloat16 else (lambda t: t)
         assert torch.equal(bits(x), bits(y))
+
+
+def test_csa_topk_workload_full_size_sampled():
+    """The CSA-form workload the benchmark times (S = 16384, H = 64, D = 512,
+    compress ratio 4, 512 selected entries per query, W = 128), NaN-poisoned
+    outputs all written; sampled rows and two whole query tiles of 16
+    positions over all heads, every raw key of one 128-key tile, and two
+    compressed entries compared with the oracle's MASK mode."""
+    from hca_inputs import CSA_TOPK, CSA_TOPK_K, draw_workload, topk_indices
+
+    wl = CSA_TOPK
+    idx = topk_indices(wl, CSA_TOPK_K)
+    plan = hca.hca_block_mask_build_topk(wl.B, wl.S, wl.W, wl.Sc, idx, H=wl.H, D=wl.D)
+    att = hca.HcaAttention(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, "bf16", plan=plan)
+    q, kv, kvc, dout = draw_workload(wl, device="cuda")
+    scale = 1.0 / math.sqrt(wl.D)
+    o, lse, dq, dkv, dkvc = run(att, q, kv, kvc, dout, scale)
+    for t in (o, dq, dkv, dkvc):
+        assert not torch.isnan(t).any()
+    say("  GPU pass done")
+    mask = oracle.topk_mask(wl.B, wl.S, wl.Sc, idx)
+    prob = oracle.Problem(wl.B, wl.S, wl.H, wl.D, wl.r, wl.W, wl.Sc, scale, None, oracle.MASK,
+                          "bf16", comp_mask=mask)
+    host = [to_host_bits(t) for t in (q, kv, kvc, dout)]
+    rng = np.random.default_rng(6)
+    rows = rng.integers(0, wl.H * wl.S, size=64)
+    for qt in (3, wl.S // 16 - 1):
+        pos = np.arange(qt * 16, qt * 16 + 16)
+        rows = np.concatenate([rows, (np.arange(wl.H)[:, None] * wl.S + pos[None, :]).ravel()])
+    rows = np.unique(rows)
+    ro, rlse, _, rdq = oracle.rows(prob, *host, row_index=rows)
+    flat = lambda t: t.reshape(-1, wl.D) if t.dim() == 4 else t.reshape(-1)
+    ix = torch.as_tensor(rows, device="cuda")
+    e = dict(o=rel_err(as_np(flat(o)[ix]), ro), dq=rel_err(as_np(flat(dq)[ix]), rdq),
+             lse=rel_err(as_np(flat(lse)[ix]), rlse))
+    # raw keys 8192 .. 8319: rows of positions 8192 .. 8446, all heads
+    k0 = 8192
+    pos = np.arange(k0, k0 + 128 + wl.W - 1)
+    krows = (np.arange(wl.H)[:, None] * wl.S + pos[None, :]).ravel()
+    _, klse, kdelta, _ = oracle.rows(prob, *host, row_index=krows)
+    lse_all = np.full(wl.H * wl.S, np.nan)
+    delta_all = np.full(wl.H * wl.S, np.nan)
+    lse_all[krows], delta_all[krows] = klse, kdelta
+    kidx = np.arange(k0, k0 + 128, dtype=np.int32)
+    rk = oracle.keys(prob, *host, np.zeros_like(kidx), np.zeros_like(kidx), kidx, lse_all,
+                     delta_all)
+    e["dkv_tile"] = rel_err(as_np(dkv[0, k0:k0 + 128]), rk)
+    # compressed entries selected by late queries only (one to a few hundred
+    # positions see them, so the oracle recomputes their rows quickly)
+    cidx = np.array([wl.Sc - 3, wl.Sc - 40, wl.Sc - 600], np.int32)
+    rc = oracle.keys(prob, *host, np.ones_like(cidx), np.zeros_like(cidx), cidx)
+    e["dkvc_entries"] = rel_err(np.stack([as_np(dkvc[0, c]) for c in cidx]), rc)
+    say(f"  csa_topk sampled errors {e}")
+    from test_gpu_parity import record
+    record("csa_topk_bf16 (sampled)", e)
+    for k, v in e.items():
+        assert v <= TOL, (k, v)
