@@ -96,6 +96,9 @@ def parse():
     ap.add_argument("--half-items-min", type=int, default=0,
                     help="item count from which half-tile items are used (0 = library "
                          "choice, -1 = never)")
+    ap.add_argument("--kv-keys", type=int, default=0,
+                    help="keys per key tile of the key-stationary backward (0 = library "
+                         "choice; 64 or 128 at head dim 512)")
     ap.add_argument("--comp-pattern", default="rule", choices=("rule", "dense", "topk"),
                     help="rule: the analytic plan; dense: the same pattern materialised as a "
                          "dense compressed-key mask kept in device memory, planned from the "
@@ -199,8 +202,8 @@ def main():
     starts, counts = starts_csr(lengths, wl.B)
     dt = hca.HCA_BF16 if wl.dtype == "bf16" else hca.HCA_F32
     tiles = None
-    if args.comp_item_chunks or args.half_items_min:
-        tiles = (0, 0, 0, args.half_items_min, args.comp_item_chunks)
+    if args.comp_item_chunks or args.half_items_min or args.kv_keys:
+        tiles = (0, 0, 0, args.half_items_min, args.comp_item_chunks, args.kv_keys)
 
     # Plan build (host), timed once outside the step loop.  dense: the analytic
     # plan's per-position intervals give the dense mask of the same pattern,
@@ -351,7 +354,7 @@ def main():
         "ws_bytes": max(info.ws_fwd_bytes, info.ws_bwd_bytes),
         "bwd_items": {"items": info.items, "half": info.items_half,
                       "partial_blocks": info.part_blocks,
-                      "comp_item_chunks": info.comp_item_chunks},
+                      "comp_item_chunks": info.comp_item_chunks, "kv_keys": info.kv_keys},
         "wall_s": round(wall, 3),
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
         "roofline": roofline,

@@ -55,7 +55,7 @@ class HcaUnsupported(HcaError, NotImplementedError):
 
 class _TileCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "bq", "bk_raw", "bk_comp", "half_items_min", "comp_item_chunks")]
+        "bq", "bk_raw", "bk_comp", "half_items_min", "comp_item_chunks", "kv_keys")]
 
 
 class _PlanInfo(ctypes.Structure):
@@ -66,7 +66,7 @@ class _PlanInfo(ctypes.Structure):
         (n, ctypes.c_uint64) for n in ("device_bytes", "ws_fwd_bytes", "ws_bwd_bytes")] + [
         (n, ctypes.c_int64) for n in ("items", "items_half", "part_blocks")] + [
         (n, ctypes.c_int32) for n in ("comp_item_chunks", "kv_heads", "comp_masked",
-                                      "reserved_")]
+                                      "kv_keys")]
 
 
 class _KernelTime(ctypes.Structure):
@@ -163,7 +163,7 @@ class PlanInfo:
     pairs_raw: int; pairs_comp: int
     device_bytes: int; ws_fwd_bytes: int; ws_bwd_bytes: int
     items: int; items_half: int; part_blocks: int; comp_item_chunks: int; kv_heads: int
-    comp_masked: int; reserved_: int
+    comp_masked: int; kv_keys: int
 
 
 class Plan:
@@ -197,12 +197,12 @@ def _i32(a: Optional[Sequence[int]]):
 def _cfg(tiles):
     if tiles is None:
         return None
-    return _TileCfg(*(tuple(tiles) + (0,) * (5 - len(tiles))))
+    return _TileCfg(*(tuple(tiles) + (0,) * (6 - len(tiles))))
 
 
 def hca_block_mask_build(B, S, r, W, S_c, seg_starts=None, seg_counts=None, H=1, D=64,
                          dtype=HCA_BF16, mode=HCA_COMPSEG_STRICT, tiles=None) -> Plan:
-    """tiles: None or (bq, bk_raw, bk_comp[, half_items_min[, comp_item_chunks]]),
+    """tiles: None or (bq, bk_raw, bk_comp[, half_items_min[, comp_item_chunks[, kv_keys]]]),
     0 = library choice (see hca_tile_cfg in include/hca.h)."""
     starts, counts = _i32(seg_starts), _i32(seg_counts)
     cfg = _cfg(tiles)

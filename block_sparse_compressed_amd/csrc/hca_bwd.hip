@@ -15,11 +15,11 @@
 //     once -- no atomics (the page on the static mask compiles the backward with
 //     an on-chip dQ reduction; here the whole dQ row stays on chip).
 //  2. key-stationary dKV: a workgroup owns one work item -- a key tile (raw
-//     or compressed; 128 keys at D = 512, 32 otherwise) and the query tiles
-//     of a run of 64-position chunks that see it -- recomputing S and dP with
-//     the tile's K fragments held in VGPRs.  At D = 512, items whose rows see
-//     only one 64-key half of their tile run over that half.  Each item
-//     writes a float32 partial.
+//     or compressed; 64 or 128 keys at D = 512, 32 otherwise) and the query
+//     tiles of a run of 64-position chunks that see it -- recomputing S and
+//     dP with the tile's K fragments held in VGPRs.  With 128-key tiles,
+//     items whose rows see only one 64-key half of their tile run over that
+//     half.  Each item writes a float32 partial.
 //  3. a fixed-order reduction of the partials into dKV and dKV_comp, so the
 //     result is bitwise reproducible.
 #include <atomic>
@@ -800,8 +800,10 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *p) { return tr_frag_rows(p
 //     over all 128 keys (128 accumulation registers), so each wave needs at
 //     most 256 registers and a SIMD runs two waves.  (A four-wave version,
 //     32 score keys and 256 accumulators per wave, one wave per SIMD, ran
-//     8.9 ms at S = 65536 against 8.6 for this one.)  Items over all keys of their tile and items over one 64-key half
-//     run in the same launch (a wave-uniform branch per item), so both kinds
+//     8.9 ms at S = 65536 against 8.6 for this one.)  Plans from a given
+//     mask use this kernel by default; plans from the rule use 2c.  Items over
+//     all keys of their tile and items over one 64-key half run in the same
+//     launch (a wave-uniform branch per item), so both kinds
 //     stream the rows of one chunk together through the L2.
 //       full item  wave w scores keys 16 w .. 16 w + 15 of the tile for the
 //                  step's 32 rows; the gradient covers key blocks 0..7.
@@ -1092,6 +1094,258 @@ __global__ void __launch_bounds__(512, 1)
 }
 
 // ---------------------------------------------------------------------------
+// 2c. dKV at D = 512, 64-key items, four waves, two workgroups per CU.  Each
+//     wave holds the K fragments of 16 keys (64 registers) and accumulates
+//     dKV^T for 128 columns, d in [128 w, 128 w + 128), over the item's 64
+//     keys (128 accumulation registers).  Rows are staged single-buffered
+//     (32-row steps, Q and dO, 64 KiB), so a workgroup needs 73 KiB of LDS
+//     and two of them, independent, share a CU: one's copies, barriers and
+//     softmax run under the other's MFMAs.  Every item runs over its whole
+//     tile (no half items).  At S = 65536 from the rule it took 8.53 ms per
+//     call against 8.78 for 2b (narrower tiles follow the window's edges
+//     more closely); on per-query top-k selections, whose tiles are nearly
+//     all non-empty at either width, 14.8 ms against 12.6 (each row streams
+//     through twice as many items), so plans from a mask keep 2b.
+// ---------------------------------------------------------------------------
+template <bool MASKED>
+__global__ void __launch_bounds__(256, 2)
+    hca_bwd_dkv512k64_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                             const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
+                             const float *__restrict__ lse, const float *__restrict__ delta,
+                             const bf16raw *__restrict__ dout, float scale_log2, float scale,
+                             float *__restrict__ part) {
+  constexpr int D = 512, KS = D / 32, KEYS = 64;
+  constexpr int STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = KEYS * STEP * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STEP_BYTES];  // [Q | dO]
+  __shared__ __attribute__((aligned(16))) char xs[2 * XBYTES];         // [P | dS]
+  __shared__ float4 ri_s[STEP];  // per step row: lse log2e, delta, key interval
+  // Masked plans: per step row (lanes 32..63 repeat rows 0..31) the four
+  // 32-bit words of the mask that hold the item's 64 entries.
+  __shared__ __attribute__((aligned(16))) uint4 rm_s[MASKED ? 64 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  const int item = p.kvorder[blockIdx.x];
+  if (item < 0) return;  // padding slot of the launch order
+  const KvItem it = p.kvitem[item];
+  const int b = it.b;
+  const bool comp = it.kind != 0;
+  const int nk = comp ? d.Sc : d.S;
+  const int k0 = it.kt * KEYS;
+  const bf16raw *src = comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D;
+  const int nq = it.e1 - it.e0;
+  const int lbq = __builtin_ctz(d.bq);
+  const int SPQ = d.bq * d.H / STEP, lspq = __builtin_ctz(SPQ);
+  const int nsteps = nq * SPQ;
+  const uint32_t ent_lane = lane < nq ? p.kvent[it.e0 + lane] : 0u;
+  auto entry = [&](int e) -> uint32_t {
+    return e < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, e)
+                  : uniform_load(p.kvent, it.e0 + e);
+  };
+  const size_t bat = (size_t)b * d.H * d.S * D;
+  const uint32_t qb_lds = lds_addr(smem);
+  // Wave w stages rows 8 w .. 8 w + 7 of each step; row r's chunk c sits at
+  // slot c ^ sw(r), sw(r) = (r & 3) | ((r >> 3) << 2).
+  const uint32_t lane_sw = (uint32_t)(lane ^ (wave << 2));
+  auto stage = [&](int s) {
+    const int e = s >> lspq, u = s & (SPQ - 1);
+    const int qt = (int)(entry(e) & kEntIdx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * wave + i, rho = u * STEP + r;
+      const int pos = min(qt * d.bq + (rho & (d.bq - 1)), d.S - 1), h = rho >> lbq;
+      const size_t rowoff = bat + ((size_t)h * d.S + pos) * D;  // wave-uniform
+      const uint32_t voff = (lane_sw ^ (uint32_t)(i & 3)) << 4;
+      dma16(q + rowoff, voff, qb_lds + r * 1024);
+      dma16(dout + rowoff, voff, qb_lds + STEP_BYTES + r * 1024);
+    }
+  };
+  int4 nrw = make_int4(0, 0, 0, 0);
+  float nl = 0.f, nd = 0.f;
+  int npos = 0;
+  auto rowinfo = [&](int s) {  // row (lane & 31) of step s, into registers
+    const int e = s >> lspq, u = s & (SPQ - 1);
+    const int qt = (int)(entry(e) & kEntIdx);
+    const int rho = u * STEP + (lane & (STEP - 1));
+    npos = qt * d.bq + (rho & (d.bq - 1));
+    const int h = rho >> lbq, pc = min(npos, d.S - 1);
+    const size_t row = ((size_t)b * d.H + h) * d.S + pc;
+    nrw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
+    nl = lse[row];
+    nd = delta[row];
+  };
+  // Row table of the step whose row information was loaded last, to LDS; in
+  // masked plans with the 16 bytes of mask that hold the item's 64 bits
+  // (words 4 (kt / 2) .., copied straight to LDS; a padded row's bits are
+  // ignored by the softmax).  Called only while no wave reads the tables.
+  auto put_rowinfo = [&]() {
+    if (MASKED && comp && wave == 0) {
+      const int pc = min(npos, d.S - 1);
+      dma16(p.cmask,
+            (uint32_t)((((size_t)b * d.S + pc) * d.cmask_ldw + 4 * (it.kt >> 1)) * 4),
+            lds_addr(&rm_s[0]));
+    }
+    if (wave == 0 && lane < STEP) {
+      const bool ok = npos < d.S;
+      float4 w;
+      w.x = ok ? nl * kLog2e : 0.f;
+      w.y = ok ? nd : 0.f;
+      w.z = __int_as_float(ok ? (comp ? nrw.y : nrw.x) : INT_MAX);
+      w.w = __int_as_float(ok ? (comp ? nrw.z : npos + 1) : 0);
+      ri_s[lane] = w;
+    }
+  };
+  const int qk_base = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (g ^ (j & 3));
+  // Transposed A operands of the gradient, column block 8 wave + dl: chunk
+  // 16 wave + 2 dl + c0 of rows 8 g + (j >> 2) (and + 4).
+  const int tr_sw = ((j & 3) >> 1) ^ ((j >> 2) + 4 * g);
+  const int tr_base = (8 * g + (j >> 2)) * 1024 + 256 * wave + ((j & 1) << 3);
+  const int xr0 = 16 * lane;
+  const int skey = k0 + 16 * wave;  // this wave's score keys skey .. skey + 15
+
+  bf16x8 kf[KS];
+  {
+    const int key = skey + j;
+    const bf16raw *krow = src + (size_t)min(key, nk - 1) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(krow + 32 * ks + 8 * g);
+      kf[ks] = as_bf16x8(key < nk ? v : make_uint4(0, 0, 0, 0));
+    }
+  }
+  floatx4 acc[4][8];  // [key block][column block of this wave]
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (nsteps > 0) {
+    stage(0);
+    rowinfo(0);
+    put_rowinfo();
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    wait_all_loads();
+    __syncthreads();  // rows, row table and mask bits of step s in LDS
+    const bool full = entry(s >> lspq) & kEntFull;
+    int qkb = qk_base, trb = tr_base, xr = xr0;
+    asm volatile("" : "+v"(qkb), "+v"(trb), "+v"(xr));
+    const char *qb = smem, *ob = smem + STEP_BYTES;
+    // Next step's row table loads go out now; stored after the gradient.
+    if (s + 1 < nsteps) rowinfo(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Scores, one 16-row block after the other.
+    floatx4 sv[2], pv[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      sv[rb] = pv[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 fq[KS], fo[KS];
+      auto fetch = [&](int ks) {
+        const int off = qkb + 64 * ((ks & 3) ^ (j >> 2)) + 256 * (ks >> 2) + 4096 * rb;
+        fq[ks] = lds_frag(qb + off);
+        fo[ks] = lds_frag(ob + off);
+      };
+      fetch(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) fetch(ks + 1);
+        sv[rb] = mfma16x16x32(fq[ks], kf[ks], sv[rb]);
+        pv[rb] = mfma16x16x32(fo[ks], kf[ks], pv[rb]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // P and dS of rows 8 g + 4 rb + v for key skey + j -> exchange block wave.
+    {
+      const int key = skey + j;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        bf16x4 pp, dd;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 8 * g + 4 * rb + v;
+          const float4 rr = ri_s[row];
+          bool vis;
+          if (MASKED && comp) {
+            const int kk = 64 * (it.kt & 1) + (key - k0);  // bit within the 16 bytes
+            const uint32_t word = reinterpret_cast<const uint32_t *>(&rm_s[row])[kk >> 5];
+            vis = full | ((((word >> (kk & 31)) & 1u) != 0) &
+                          (__float_as_int(rr.z) != INT_MAX));
+          } else {
+            vis = full | ((key >= __float_as_int(rr.z)) & (key < __float_as_int(rr.w)));
+          }
+          const float ex = fast_exp2(sv[rb][v] * scale_log2 - rr.x);
+          const float e = vis ? ex : 0.f;
+          pp[v] = (__bf16)e;
+          dd[v] = (__bf16)(e * (pv[rb][v] - rr.y) * scale);
+        }
+        const int xo = xr + 8 * rb + 1024 * wave;
+        *reinterpret_cast<bf16x4 *>(xs + xo) = pp;
+        *reinterpret_cast<bf16x4 *>(xs + XBYTES + xo) = dd;
+      }
+    }
+    lds_barrier();  // exchange tiles complete
+
+    // Gradient, two passes of four column blocks: the pass's transposed row
+    // fragments are held while the four exchange pairs stream through.
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      bf16x8 tq[4], to[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int to_ = trb + ((tr_sw ^ (2 * (4 * ps + c))) << 4);
+        tq[c] = tr_frag(qb + to_);
+        to[c] = tr_frag(ob + to_);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 xd = lds_frag(xs + XBYTES + xr + 1024 * kb);
+        const bf16x8 xp = lds_frag(xs + xr + 1024 * kb);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[kb][4 * ps + c] = mfma16x16x32(tq[c], xd, acc[kb][4 * ps + c]);
+          acc[kb][4 * ps + c] = mfma16x16x32(to[c], xp, acc[kb][4 * ps + c]);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16 + 2, 0);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();  // rows, exchange, row table and mask bits of step s no longer read
+    if (s + 1 < nsteps) {
+      stage(s + 1);
+      put_rowinfo();
+    }
+  }
+
+  // Partial [64 keys][512]: this wave's 128 columns of every key.
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    float *out = part + it.part_off + (size_t)(16 * kb + j) * D + 128 * wave + 4 * g;
+#pragma unroll
+    for (int dl = 0; dl < 8; ++dl) {
+      float4 w;
+      w.x = acc[kb][dl][0];
+      w.y = acc[kb][dl][1];
+      w.z = acc[kb][dl][2];
+      w.w = acc[kb][dl][3];
+      *reinterpret_cast<float4 *>(out + 16 * dl) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. Fixed-order sum of the partials of every key tile -> dKV / dKV_comp.
 // ---------------------------------------------------------------------------
 // One launch for the raw key tiles, one for the compressed ones; a workgroup
@@ -1226,6 +1480,17 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
   };
   switch (d.D) {
     case 512:
+      if (d.kv_bk == 64) {
+        if (d.cmask_ldw)
+          hipLaunchKernelGGL(hca_bwd_dkv512k64_kernel<true>, dim3(d.n_items), dim3(256), 0, s,
+                             d, p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc,
+                             lse, delta, (const bf16raw *)dout, sl2, scale, part);
+        else
+          hipLaunchKernelGGL(hca_bwd_dkv512k64_kernel<false>, dim3(d.n_items), dim3(256), 0, s,
+                             d, p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc,
+                             lse, delta, (const bf16raw *)dout, sl2, scale, part);
+        break;
+      }
       // Every item (over all keys of its tile or over one half) in one launch.
       if (d.cmask_ldw)
         hipLaunchKernelGGL(hca_bwd_dkv512x8_kernel<true>, dim3(d.n_items), dim3(512), 0, s, d,

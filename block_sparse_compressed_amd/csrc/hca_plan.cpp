@@ -92,9 +92,21 @@ int classify_tile_mask(const uint8_t *m, int64_t S, int64_t Sc, int64_t qt, int 
 
 }  // namespace
 
-// Keys per work item of the key-stationary backward: 128 (4 waves x 32 keys)
-// for the D = 512 bf16 kernel, otherwise the forward's 32-key tile.
-int kv_tile_keys(int dtype, int D) { return (dtype == HCA_BF16 && D == 512) ? 128 : 32; }
+// Keys per key tile of the key-stationary backward (a work item covers one
+// tile).  Head dim 512, bf16: 64 (four waves x 16 keys) for plans from the
+// rule, whose visible keys form intervals that narrower tiles follow more
+// closely; 128 (eight waves x 16 keys) for plans from a given mask, whose
+// scattered entries leave few tiles empty at either width, so wider tiles
+// stream each query row half as often.  Other kernels: the forward's 32-key
+// tile.  `want` (the tile configuration's kv_keys) overrides where the width
+// has a kernel; 0 if it has none.
+static int kv_tile_keys(int dtype, int D, bool masked, int want) {
+  if (dtype == HCA_BF16 && D == 512) {
+    if (want == 0) return masked ? 128 : 64;
+    return want == 64 || want == 128 ? want : 0;
+  }
+  return want == 0 || want == 32 ? 32 : 0;
+}
 
 void default_tiles(int dtype, int D, int H, int *bq, int *bk_raw, int *bk_comp) {
   if (dtype == HCA_BF16 && H >= 1 && H <= 128 && 128 % H == 0) {
@@ -252,6 +264,11 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
   default_tiles(dtype, D, H, &bq, &bkr, &bkc);
   int64_t half_min = kHalfItemsMin;
   int64_t comp_chunks_cfg = 0;
+  const int kv_keys = kv_tile_keys(dtype, D, cmask != nullptr, tiles ? tiles->kv_keys : 0);
+  if (kv_keys == 0) {
+    set_error(F + ": kv_keys must be 0, 64 or 128 at head dim 512 bfloat16, else 0 or 32");
+    return HCA_ERR_INVALID_ARG;
+  }
   if (tiles) {
     if (tiles->bq < 0 || tiles->bk_raw < 0 || tiles->bk_comp < 0 ||
         tiles->comp_item_chunks < 0) {
@@ -299,7 +316,8 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
       p->unsupported = "compressed-key mask too large for 32-bit offsets";
     in.comp_masked = cmask ? 1 : 0;
     in.kernel_ok = p->unsupported.empty() ? 1 : 0;
-    p->kv_bk = kv_tile_keys(dtype, D);
+    p->kv_bk = kv_keys;
+    in.kv_keys = kv_keys;
 
     // ---- per-position visible intervals --------------------------------- //
     p->rows.assign((size_t)B * S * 4, 0);

@@ -78,8 +78,13 @@ enum { HCA_TILE_EMPTY = 0, HCA_TILE_PARTIAL = 1, HCA_TILE_FULL = 2 };
  * the GPU entry points run only the shapes their kernels are built for
  * (hca_plan_info.kernel_ok).
  *
- * Two further fields shape the work items of the key-stationary backward
+ * Three further fields shape the work items of the key-stationary backward
  * (they change the schedule, never the result beyond float summation order):
+ *   kv_keys           keys per key tile of that backward; 0 = library choice.
+ *                     Head dim 512, bfloat16: 64 or 128 (library choice 64 for
+ *                     plans built from the rule, 128 for plans built from a
+ *                     given mask, whose scattered entries fill wider tiles);
+ *                     other kernels: 32.  Any other value is rejected.
  *   half_items_min    with 128-key items (head dim 512, bfloat16): an item whose
  *                     rows see only one 64-key half of its key tile runs over
  *                     that half alone once the plan has at least this many
@@ -96,6 +101,7 @@ typedef struct hca_tile_cfg {
   int32_t bk_comp;
   int32_t half_items_min;
   int32_t comp_item_chunks;
+  int32_t kv_keys;
 } hca_tile_cfg;
 
 typedef struct hca_plan hca_plan; /* opaque, host-owned */
@@ -128,7 +134,7 @@ typedef struct hca_plan_info {
   int32_t kv_heads;                /* key/value heads G (1: MQA); see hca_block_mask_build_gqa */
   int32_t comp_masked;             /* 1: compressed visibility from a given mask (see
                                       hca_block_mask_build_masked) */
-  int32_t reserved_;
+  int32_t kv_keys;                 /* keys per key tile of the key-stationary backward */
 } hca_plan_info;
 
 /*

@@ -70,15 +70,20 @@ def check_against_oracle(name, B, S, H, W, Sc, mask, lengths, plan, seed):
         assert not torch.isnan(t).any()
 
 
-@pytest.mark.parametrize("density", [0.05, 0.5])
-def test_random_mask_every_element(density):
+@pytest.mark.parametrize("density,kv_keys", [(0.05, 0), (0.5, 0), (0.05, 64)])
+def test_random_mask_every_element(density, kv_keys):
+    """Random masks over ragged documents; kv_keys = 64 runs the masked plan
+    through the 64-key key-stationary kernel instead of the 128-key one."""
     rng = np.random.default_rng(int(density * 1000))
     B, S, H, W, Sc = 1, 523, 64, 96, 150
     lengths = [random_lengths(rng, S, 60, 300)]
     mask = (rng.random((B, S, Sc)) < density).astype(np.uint8)
     starts, counts = starts_csr(lengths, B)
-    plan = hca.hca_block_mask_build_masked(B, S, W, Sc, mask, starts, counts, H=H, D=512)
-    check_against_oracle(f"masked_d{density}", B, S, H, W, Sc, mask, lengths, plan, seed=41)
+    plan = hca.hca_block_mask_build_masked(B, S, W, Sc, mask, starts, counts, H=H, D=512,
+                                           tiles=(0, 0, 0, 0, 0, kv_keys))
+    assert hca.hca_plan_get_info(plan).kv_keys == (kv_keys or 128)
+    check_against_oracle(f"masked_d{density}_k{kv_keys or 128}", B, S, H, W, Sc, mask, lengths,
+                         plan, seed=41)
 
 
 def test_topk_selection_every_element():
@@ -99,8 +104,12 @@ def test_topk_selection_every_element():
     check_against_oracle("topk_r4_k48", B, S, H, W, Sc, mask, None, plan, seed=42)
 
 
-def test_hca_pattern_as_mask_matches_analytic_plan_bitwise():
+@pytest.mark.parametrize("kv_keys", [64, 128])
+def test_hca_pattern_as_mask_matches_analytic_plan_bitwise(kv_keys):
+    """Both plans at the same key tile width, so the key-stationary items, and
+    with them the summation order, are the same."""
     B, S, H, r, W = 1, 2100, 64, 32, 128
+    tiles = (0, 0, 0, 0, 0, kv_keys)
     lengths = [[900, 1200]]
     starts, counts = starts_csr(lengths, B)
     strict = oracle.Problem(B, S, H, 512, r, W, S // r, 0.1, segment_ids(lengths, B, S))
@@ -111,9 +120,12 @@ def test_hca_pattern_as_mask_matches_analytic_plan_bitwise():
             mask[0, i, c] = oracle.vis_comp(strict, 0, i, c)
     scale = 1.0 / math.sqrt(512)
     q, kv, kvc, dout = draw(B, S, H, 512, Sc, "bf16", 43, device="cuda")
-    analytic = hca.HcaAttention(B, S, H, 512, r, W, "bf16", starts, counts)
+    analytic = hca.HcaAttention(B, S, H, 512, r, W, "bf16", plan=hca.hca_block_mask_build(
+        B, S, r, W, Sc, starts, counts, H, 512, hca.HCA_BF16, tiles=tiles))
     masked = hca.HcaAttention(B, S, H, 512, r, W, "bf16", plan=hca.hca_block_mask_build_masked(
-        B, S, W, Sc, mask, starts, counts, H=H, D=512))
+        B, S, W, Sc, mask, starts, counts, H=H, D=512, tiles=tiles))
+    ia, im = hca.hca_plan_export_items(analytic.plan), hca.hca_plan_export_items(masked.plan)
+    assert np.array_equal(ia, im) and analytic.info.kv_keys == kv_keys
     a = run(analytic, q, kv, kvc, dout, scale)
     m = run(masked, q, kv, kvc, dout, scale)
     for x, y in zip(a, m):

@@ -181,16 +181,18 @@ def test_long_key_lists_every_element():
     check_full(Case(1, 2048, 16, 512, 8, 64, "bf16", [[700, 1348]], seed=11, value_scale=2.0))
 
 
-def test_key_lists_past_64_tiles_d512():
+@pytest.mark.parametrize("kv_keys", [64, 128])
+def test_key_lists_past_64_tiles_d512(kv_keys):
     """r = 2 gives 2048 compressed entries (64 tiles of 32), so the last query
     tiles list more than 64 key tiles: the forward and the persistent dQ read
-    the list entries past the 64 held in lanes from memory.  Half-tile dKV
-    items are forced on (threshold one item) and the compressed-tile items run
-    20 chunks long (80 listed query tiles), so the dKV kernel also reads
-    entries past 64."""
-    case = Case(1, 4096, 8, 512, 2, 128, "bf16", seed=21, tiles=(0, 0, 0, 1, 20))
+    the list entries past the 64 held in lanes from memory.  The compressed-
+    tile items of the key-stationary backward run 20 chunks long (80 listed
+    query tiles), so its kernels (64- and 128-key, the latter with half-tile
+    items forced on) also read entries past 64."""
+    case = Case(1, 4096, 8, 512, 2, 128, "bf16", seed=21, tiles=(0, 0, 0, 1, 20, kv_keys))
     info = case.att.info
-    assert info.items_half > 0 and info.comp_item_chunks == 20
+    assert info.comp_item_chunks == 20 and info.kv_keys == kv_keys
+    assert (info.items_half > 0) == (kv_keys == 128)
     items = hca.hca_plan_export_items(case.att.plan)
     assert (items[:, 5] - items[:, 4]).max() + 1 > 64
     raw, comp = hca.hca_plan_export_tiles(case.att.plan)
@@ -200,12 +202,11 @@ def test_key_lists_past_64_tiles_d512():
 
 @pytest.mark.parametrize("lengths", [None, [[700, 836]]], ids=["one_doc", "two_docs"])
 def test_half_tile_dkv_items_every_element(lengths):
-    """The half-tile dKV instantiation (items whose rows see one 64-key half of
-    a 128-key tile, in a launch of their own; lower- and upper-half items of a
-    tile share a partial block) normally runs only at S >= 65536.  The plan
-    knob turns it on at a size the oracle checks element by element, with a
-    document boundary in the second case."""
-    case = Case(1, 1536, 8, 512, 16, 128, "bf16", lengths, seed=22, tiles=(0, 0, 0, 1, 0))
+    """Half-tile items of the 128-key key-stationary kernel (items whose rows
+    see one 64-key half of their tile run over that half; lower- and upper-half
+    items of a tile share a partial block), at a size the oracle checks
+    element by element, with a document boundary in the second case."""
+    case = Case(1, 1536, 8, 512, 16, 128, "bf16", lengths, seed=22, tiles=(0, 0, 0, 1, 0, 128))
     info = case.att.info
     items = hca.hca_plan_export_items(case.att.plan)
     assert info.items_half > 0 and (items[:, 6] & 4).any()

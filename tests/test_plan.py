@@ -185,14 +185,14 @@ def closed_form_intervals(S, r, W, lengths_row):
 
 @pytest.mark.parametrize("lengths", [None, [[15000, 25000]]], ids=["one_doc", "two_docs"])
 def test_items_halves_and_partial_blocks(lengths):
-    """At S = 40000, H = 64, D = 512 with half-tile marking on (the knob sets
-    the threshold to one item), the planner marks 128-key items that see only
+    """At S = 40000, H = 64, D = 512 with 128-key tiles and half-tile marking
+    on (the knob sets the threshold to one item), the planner marks items that see only
     one 64-key half of their tile.  Every item's mark must equal the halves
     that its query tiles see, and the items of a key tile must own
     consecutive partial blocks (the reduction relies on it)."""
     S, H, D, r, W = 40000, 64, 512, 128, 128
     plan, prob = build_both(1, S, H, D, r, W, lengths, hca.HCA_COMPSEG_STRICT,
-                            tiles=(0, 0, 0, 1, 0))
+                            tiles=(0, 0, 0, 1, 0, 128))
     info = hca.hca_plan_get_info(plan)
     items = hca.hca_plan_export_items(plan)
     assert len(items) >= 1000 and (items[:, 3] == 128).all()
@@ -253,10 +253,11 @@ def check_partial_blocks(items, D, info):
 
 
 def test_items_half_tiles_marked_at_any_size():
-    """The one-launch key-stationary kernel runs half-tile items beside the
-    full ones, so the planner marks them at any size (S = 16384 here), and
-    lower/upper pairs share partial blocks."""
-    plan, _ = build_both(1, 16384, 64, 512, 128, 128, None, hca.HCA_COMPSEG_STRICT)
+    """With 128-key tiles the one-launch key-stationary kernel runs half-tile
+    items beside the full ones, so the planner marks them at any size
+    (S = 16384 here), and lower/upper pairs share partial blocks."""
+    plan, _ = build_both(1, 16384, 64, 512, 128, 128, None, hca.HCA_COMPSEG_STRICT,
+                         tiles=(0, 0, 0, 0, 0, 128))
     items = hca.hca_plan_export_items(plan)
     info = hca.hca_plan_get_info(plan)
     assert info.items == len(items) and info.items_half > 0
@@ -265,12 +266,12 @@ def test_items_half_tiles_marked_at_any_size():
 
 
 def test_half_items_knob():
-    """half_items_min = 1 marks half-tile items on a small problem (so the GPU
+    """With 128-key tiles, half_items_min = 1 marks half-tile items on a small problem (so the GPU
     tests can run that kernel at sizes the oracle checks element by element);
     half_items_min < 0 never marks them."""
     S, H, D, r, W = 1536, 8, 512, 16, 128
     plan, prob = build_both(1, S, H, D, r, W, None, hca.HCA_COMPSEG_STRICT,
-                            tiles=(0, 0, 0, 1, 0))
+                            tiles=(0, 0, 0, 1, 0, 128))
     info = hca.hca_plan_get_info(plan)
     items = hca.hca_plan_export_items(plan)
     half = (items[:, 6] & 3) != 3
@@ -288,9 +289,49 @@ def test_half_items_knob():
         for i in range(qa * info.bq, min(S, (qz + 1) * info.bq)):
             assert not any(vis(prob, b, i, t) for t in idle if t < nkeys)
     plan2, _ = build_both(1, S, H, D, r, W, None, hca.HCA_COMPSEG_STRICT,
-                          tiles=(0, 0, 0, -1, 0))
+                          tiles=(0, 0, 0, -1, 0, 128))
     assert hca.hca_plan_get_info(plan2).items_half == 0
     assert (hca.hca_plan_export_items(plan2)[:, 6] == 3).all()
+
+
+def test_kv_keys_choice():
+    """Key tile width of the key-stationary backward: 64 keys for D = 512
+    plans from the rule, 128 for plans from a given mask, 32 at other head
+    dims; kv_keys overrides it where a kernel of that width exists.  64-key
+    items always run over their whole tile (no half marks), and their partial
+    blocks are 64 x D."""
+    S, H, r, W = 1536, 8, 16, 128
+    rule, prob = build_both(1, S, H, 512, r, W, None, hca.HCA_COMPSEG_STRICT)
+    info = hca.hca_plan_get_info(rule)
+    items = hca.hca_plan_export_items(rule)
+    assert info.kv_keys == 64 and (items[:, 3] == 64).all()
+    assert info.items_half == 0 and (items[:, 6] == 3).all()
+    assert info.part_blocks == len(items)
+    check_partial_blocks(items, 512, info)
+    # every visible key of the problem lies in some item's tile and query tiles
+    covered = set()
+    for b, kind, k0, nk, qa, qz, _, _ in items:
+        covered.add((int(kind), int(k0) // 64, int(qa), int(qz)))
+    for i in range(0, S, 97):
+        qt = i // info.bq
+        for t in range(S):
+            if oracle.vis_raw(prob, 0, i, t):
+                assert any(k == 0 and kt == t // 64 and qa <= qt <= qz
+                           for k, kt, qa, qz in covered), (i, t)
+    mask = np.zeros((1, S, S // r), np.uint8)
+    mask[0, :, ::3] = 1
+    masked = hca.hca_block_mask_build_masked(1, S, W, S // r, mask, None, None, H, 512,
+                                             hca.HCA_BF16)
+    assert hca.hca_plan_get_info(masked).kv_keys == 128
+    masked64 = hca.hca_block_mask_build_masked(1, S, W, S // r, mask, None, None, H, 512,
+                                               hca.HCA_BF16, tiles=(0, 0, 0, 0, 0, 64))
+    assert hca.hca_plan_get_info(masked64).kv_keys == 64
+    d128 = hca.hca_block_mask_build(1, S, r, W, S // r, None, None, H, 128, hca.HCA_BF16)
+    assert hca.hca_plan_get_info(d128).kv_keys == 32
+    for D, bad in ((512, 32), (512, 96), (512, 256), (128, 64), (64, 128)):
+        with pytest.raises(hca.HcaError, match="kv_keys"):
+            hca.hca_block_mask_build(1, S, r, W, S // r, None, None, H, D, hca.HCA_BF16,
+                                     tiles=(0, 0, 0, 0, 0, bad))
 
 
 @pytest.mark.parametrize("chunks", [1, 3, 20])
