@@ -3,8 +3,8 @@
 // A query tile is bq positions x all H heads (single KV head, so every head of
 // a position sees the same keys; the shared-KV einsum form of "[DeepSeek-V4]
 // Implement Compressed Attention Layers", review suggestions); a workgroup
-// owns the tile (D = 64 / 128: 128 rows) or a slice of it (D = 512: 64 rows of
-// a 16-position x 64-head tile).  It walks the tile's list of non-empty key
+// owns the tile (D = 64 / 128: 128 rows) or a slice of it (D = 512: 128 rows
+// of a 16-position x 64-head tile).  It walks the tile's list of non-empty key
 // tiles from the host-built block table (EMPTY tiles never appear; "Add HCA
 // Static Compilation for Splash Attention [Deepseek v4]", Description), stages
 // each 32-key tile of the shared K = V tensor in LDS once for all heads, and
@@ -14,7 +14,9 @@
 //   O^T += K^T P^T   (P rounded to bf16, K^T read from a transposed LDS copy)
 // Computing S transposed leaves each lane holding one query row and 8
 // consecutive keys, which is exactly the B operand layout the PV product
-// needs, so P never goes through LDS.
+// needs: at D = 64 / 128 P stays in registers; at D = 512 each wave's P
+// fragment goes through LDS once so that the PV product can be split over D
+// (see hca_fwd512s_kernel).
 #include <climits>
 #include <mutex>
 
@@ -26,17 +28,8 @@ namespace hca {
 
 constexpr int kBK = 32;  // keys per tile (raw and compressed)
 
-#ifndef HCA_FWD_NW
-#define HCA_FWD_NW 4  // waves of the D = 512 forward: 4 (two workgroups per CU) or 8
-#endif
-#ifndef HCA_FWD_MB
-#define HCA_FWD_MB 1  // 16-row blocks per wave of the D = 512 forward
-#endif
 #ifndef HCA_FWD_QK_PF
 #define HCA_FWD_QK_PF 3  // k-steps of K fragments in flight ahead of the S^T MFMAs
-#endif
-#ifndef HCA_FWD_PV_PF
-#define HCA_FWD_PV_PF 4  // column blocks of K^T fragments in flight ahead of the PV MFMAs
 #endif
 
 
@@ -268,53 +261,41 @@ __global__ void __launch_bounds__(NW * 64, 1)
   }
 }
 
-// ---------------------------------------------------------------------------
-// D = 512 forward: NW waves x 16 rows per workgroup (one wave = 16 consecutive
-// positions of one head).
-//
-// NW = 4 (the default): 64 rows, two workgroups per CU, K and K^T tiles
-// single-buffered (32 KiB each).  Per tile: softmax and O^T += K^T P^T of tile
-// t (K of tile t+1 arriving meanwhile), barrier, copy K^T of tile t+1 while
-// S^T = K Q^T of tile t+1 runs, barrier, copy K of tile t+2.  The second
-// workgroup on the CU fills this one's waits and its row loads.
-// NW = 8: 128 rows, one workgroup per CU, K and K^T double-buffered and one
-// tile apart (4 x 32 KiB), one barrier per tile, the S^T MFMAs of tile t+1
-// issued before the softmax and PV of tile t.
-// Tiles go global -> LDS directly (no VGPR staging) from the tile images, in
-// MFMA fragment order, so every operand read is a flat ds_read_b128.
-// ---------------------------------------------------------------------------
 // Lazy rescaling: a row's reference max m_run only moves when the tile max
 // exceeds it by more than kLazy (log2 units), so P = 2^(x - m_run) stays below
 // 2^kLazy and the O rescale (a wave-uniform branch) is rare.
 constexpr float kLazy = 8.f;
 
-// NW = 8: one workgroup per CU, K and K^T double-buffered (128 KiB of LDS).
-// NW = 4: two workgroups per CU, K and K^T single-buffered (64 KiB each), so
-// one workgroup's row loads, barriers and tile waits overlap the other's math.
-// MASKED: compressed visibility from the plan's mask bits (masked plans);
-// otherwise from the per-position intervals.  Separate instantiations, so the
-// interval kernel carries none of the mask code.
-template <int NW, int MB, bool MASKED>
-__global__ void __launch_bounds__(NW * 64, 8 / NW)
-    hca_fwd512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
-                      const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
-                      const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
-                      float scale_log2, bf16raw *__restrict__ o, float *__restrict__ lse) {
-  constexpr int D = 512, KS = D / 32, DB = D / 16;
-  constexpr int M = NW * MB * 16;  // rows per workgroup
-  // [K buffer 0][K buffer 1][K^T buffer 0][K^T buffer 1]
-  constexpr bool kSingle = NW == 4;
-  constexpr int kBufs = kSingle ? 1 : 2;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufs * kTileBytes512];
+// ---------------------------------------------------------------------------
+// D = 512 forward with the PV product split over the head dimension.
+// ---------------------------------------------------------------------------
+// Eight waves, 128 rows per workgroup (one workgroup per CU, two waves per
+// SIMD), K and K^T double-buffered (128 KiB).  The scores stay row-blocked:
+// wave w holds the Q fragments of rows 16 w .. 16 w + 15 and forms their S^T
+// and softmax.  The PV product is split over D instead: wave w accumulates
+// O^T for columns 64 w .. 64 w + 63 of all 128 rows, so each K^T fragment it
+// reads from LDS feeds eight MFMAs (one per row block) instead of one.  P goes
+// through LDS (one 1 KiB fragment per wave and tile, double-buffered), with
+// each row's lazy-rescale factor.  Per wave and tile the LDS reads fall from
+// 64 KiB (32 K and 32 K^T fragments) to 44 KiB (32 K, 4 K^T, 8 P fragments),
+// and one tile copy serves 128 rows instead of 64.
+template <bool MASKED>
+__global__ void __launch_bounds__(512, 1)
+    hca_fwd512s_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                       const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
+                       float scale_log2, bf16raw *__restrict__ o, float *__restrict__ lse) {
+  constexpr int D = 512, KS = D / 32, NW = 8, M = 128, RB = M / 16, CB = D / 16 / NW;
+  // [K 0][K 1][K^T 0][K^T 1]; after the tile walk, the output rows.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes512];
+  __shared__ __attribute__((aligned(1024))) char pbuf[2][RB * 1024];  // P fragments per row block
+  __shared__ float alpha_s[2][M];  // per row: O rescale factor of the tile
+  __shared__ int resc_s[2][RB];    // per row block: any row rescaled in the tile
+  __shared__ float inv_s[M];       // per row: 1 / l
   char *const kbase = smem;
-  char *const tbase = smem + kBufs * kTileBytes512;
+  char *const tbase = smem + 2 * kTileBytes512;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
-  // A query tile is bq positions x H heads, rows ordered position-fastest
-  // (row rho = position rho % bq, head rho / bq), cut into slices of M rows;
-  // one wave's 16 rows are 16 consecutive positions of one head.  The slices
-  // of two neighbouring tiles run back to back on one XCD.
   const int nslices = d.bq * d.H / M;
   const int lbq = __builtin_ctz(d.bq);
   const int u = xcd_remap(blockIdx.x, d.B * d.nqt * nslices, 2 * nslices);
@@ -322,61 +303,58 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
   const int item = p.qorder[li];
   const int b = item / d.nqt, qt = item - b * d.nqt;
 
-  int pos[MB], hh[MB], rlo[MB], clo[MB], chi[MB];
-  bool valid[MB];
-  bf16x8 qf[MB][KS];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int rho = sl * M + (wave * MB + mb) * 16 + j;
-    pos[mb] = qt * d.bq + (rho & (d.bq - 1));
-    hh[mb] = rho >> lbq;
-    valid[mb] = pos[mb] < d.S;
-    rlo[mb] = INT_MAX;
-    clo[mb] = chi[mb] = 0;
-  }
+  // This lane's score row: row 16 wave + j of the slice.
+  const int rho = sl * M + wave * 16 + j;
+  const int pos = qt * d.bq + (rho & (d.bq - 1)), hh = rho >> lbq;
+  const bool valid = pos < d.S;
 
   const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
-  // The tile's list, one entry per lane: entries are fetched with readlane,
-  // not with a dependent memory load per tile (lists longer than 64 fall back
-  // to memory for the tail).  They are needed for the first tile copies: load
-  // them first and wait for them once, before any copy is in flight.
   const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
   __builtin_amdgcn_s_waitcnt(0);
   auto entry = [&](int t) -> uint32_t {
     return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
                   : uniform_load(p.qent, e_begin + t);
   };
-  // K and K^T tiles come from the tile images (kvt, kvct) that the image
-  // kernel wrote at the start of the call.
   const rsrc_t r_img =
       make_rsrc(kvt + (size_t)b * 2 * D * d.S_pad, (uint32_t)d.S_pad * D * 4);
   const rsrc_t r_imgc =
       make_rsrc(kvct + (size_t)b * 2 * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 4);
-  auto stage_k = [&](int t) {  // K of list entry t
+  auto stage_k = [&](int t) {
     if (t >= nent) return;
     const uint32_t ent = entry(t);
     stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 0,
-                     kbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
+                     kbase + (t & 1) * kTileBytes512, wave, lane);
   };
-  auto stage_t = [&](int t) {  // K^T of list entry t
+  auto stage_t = [&](int t) {
     if (t >= nent) return;
     const uint32_t ent = entry(t);
     stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 1,
-                     tbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
+                     tbase + (t & 1) * kTileBytes512, wave, lane);
   };
-
-  // Operand reads are flat: lane l reads bytes 16 l .. 16 l + 15 of a block.
   const int frag_off = 16 * lane;
 
-  // S^T of tile t for every row block: two 16-key halves per block.
-  // Operand fragments are read QK_PF k-steps ahead of their MFMAs (the
-  // group barriers keep the compiler from collapsing the distance), so each
-  // MFMA finds its operand landed instead of waiting out an LDS round trip.
-  auto qk = [&](int t, floatx4 (&s)[MB][2]) {
-    constexpr int PF = HCA_FWD_QK_PF;
-    const char *kb = kbase + (t & (kBufs - 1)) * kTileBytes512 + frag_off;
+  // Q fragments and the row's key intervals (padded rows read the last row
+  // and get empty intervals).
+  bf16x8 qf[KS];
+  int rlo, clo, chi;
+  auto load_q = [&]() {
+    const int pc = min(pos, d.S - 1);
+    const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
+    rlo = valid ? rw.x : INT_MAX;
+    clo = valid ? rw.y : 0;
+    chi = valid ? rw.z : 0;
+    const bf16raw *qrow = q + (((size_t)b * d.H + hh) * d.S + pc) * D;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) s[mb][0] = s[mb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g));
+  };
+
+  // S^T of tile t for this wave's rows: two 16-key halves, K fragments read
+  // QK_PF k-steps ahead of their MFMAs.
+  auto qk = [&](int t, floatx4 (&s)[2]) {
+    constexpr int PF = HCA_FWD_QK_PF;
+    const char *kb = kbase + (t & 1) * kTileBytes512 + frag_off;
+    s[0] = s[1] = floatx4{0.f, 0.f, 0.f, 0.f};
     bf16x8 a0[KS], a1[KS];
 #pragma unroll
     for (int ks = 0; ks < PF; ++ks) {
@@ -389,214 +367,183 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
         a0[ks + PF] = lds_frag(kb + 2048 * (ks + PF));
         a1[ks + PF] = lds_frag(kb + 2048 * (ks + PF) + 1024);
       }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        s[mb][0] = mfma16x16x32(a0[ks], qf[mb][ks], s[mb][0]);
-        s[mb][1] = mfma16x16x32(a1[ks], qf[mb][ks], s[mb][1]);
-      }
+      s[0] = mfma16x16x32(a0[ks], qf[ks], s[0]);
+      s[1] = mfma16x16x32(a1[ks], qf[ks], s[1]);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * MB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   };
 
-  float m_run[MB], l_run[MB];
-  floatx4 oacc[MB][DB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    m_run[mb] = -INFINITY;
-    l_run[mb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[mb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // Query rows and their key intervals.  All loads are unconditional (a padded
-  // row, pos >= S, reads the last row): issued back to back, waited for once.
-  // A padded row's interval is empty and a tile holding it is never FULL, so
-  // it contributes nothing, and it is never stored.
-  auto load_q = [&]() {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int pc = min(pos[mb], d.S - 1);
-      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
-      rlo[mb] = valid[mb] ? rw.x : INT_MAX;
-      clo[mb] = valid[mb] ? rw.y : 0;
-      chi[mb] = valid[mb] ? rw.z : 0;
-      const bf16raw *qrow = q + (((size_t)b * d.H + hh[mb]) * d.S + pc) * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[mb][ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g));
-    }
-  };
-  // Masked plans (compressed visibility from a given mask): the 32 visibility
-  // bits of each row for the compressed tile of entry `ent`, loaded when the
-  // entry becomes current, one tile ahead of their use (0 otherwise).
-  uint32_t mword[MB];
-  auto load_mask = [&](uint32_t ent) {
+  // Masked plans: the row's 32 visibility bits for the compressed tile of
+  // entry `ent` (0 for raw, FULL and padded).
+  auto load_mask = [&](uint32_t ent) -> uint32_t {
     if constexpr (MASKED) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        mword[mb] = 0u;
-        if ((ent & kEntComp) && !(ent & kEntFull) && valid[mb])
-          mword[mb] = p.cmask[((size_t)b * d.S + pos[mb]) * d.cmask_ldw + (ent & kEntIdx)];
-      }
+      if ((ent & kEntComp) && !(ent & kEntFull) && valid)
+        return p.cmask[((size_t)b * d.S + pos) * d.cmask_ldw + (ent & kEntIdx)];
     }
+    return 0u;
   };
-  // Online softmax of tile `it` (scores sc, list entry ent) and O^T += K^T P^T.
-  auto soft_pv = [&](int it, const floatx4 (&sc)[MB][2], uint32_t ent) {
+
+  // Online softmax of tile t (owner of the rows): P to the exchange buffer
+  // t & 1, with the rows' rescale factors.
+  float m_run = -INFINITY, l_run = 0.f;
+  auto softmax = [&](int t, const floatx4 (&sc)[2], uint32_t ent, uint32_t mword) {
     const bool comp = ent & kEntComp;
     const int k0 = (int)(ent & kEntIdx) * kBK;
-    bf16x8 pb[MB];
+    float x[8];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float x[8];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        x[v] = sc[mb][0][v] * scale_log2;
-        x[4 + v] = sc[mb][1][v] * scale_log2;
-      }
-      if (!(ent & kEntFull)) {
-        if (MASKED && comp) {
-          // this lane's 8 keys: bits 8 g .. 8 g + 7 of the row's tile word
-          const uint32_t bits = mword[mb] >> (8 * g);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) x[t] = ((bits >> t) & 1u) ? x[t] : -INFINITY;
-        } else {
-          // visible keys of this row: [lo, hi) relative to this lane's 8 keys
-          const int lo = (comp ? clo[mb] : rlo[mb]) - (k0 + 8 * g);
-          const int hi = (comp ? chi[mb] : pos[mb] + 1) - (k0 + 8 * g);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
-        }
-      }
-      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mx = group_max(mx);
-      const bool up = mx > m_run[mb] + kLazy;
-      if (__builtin_amdgcn_ballot_w64(up)) {
-        const float m_new = up ? mx : m_run[mb];
-        const float alpha = fast_exp2(m_run[mb] - (m_new == -INFINITY ? 0.f : m_new));
-        l_run[mb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[mb][db] *= alpha;
-        m_run[mb] = m_new;
-      }
-      const float m_use = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        x[t] = fast_exp2(x[t] - m_use);
-        l_run[mb] += x[t];
-      }
-      pb[mb] = pack8(x);
+    for (int v = 0; v < 4; ++v) {
+      x[v] = sc[0][v] * scale_log2;
+      x[4 + v] = sc[1][v] * scale_log2;
     }
-    // K^T fragments read PV_PF column blocks ahead of their MFMAs.
-    constexpr int PV = HCA_FWD_PV_PF;
-    const char *tb = tbase + (it & (kBufs - 1)) * kTileBytes512 + frag_off;
-    bf16x8 kt[DB];
+    if (!(ent & kEntFull)) {
+      if (MASKED && comp) {
+        const uint32_t bits = mword >> (8 * g);
 #pragma unroll
-    for (int db = 0; db < PV; ++db) kt[db] = lds_frag(tb + db * 1024);
+        for (int i = 0; i < 8; ++i) x[i] = ((bits >> i) & 1u) ? x[i] : -INFINITY;
+      } else {
+        const int lo = (comp ? clo : rlo) - (k0 + 8 * g);
+        const int hi = (comp ? chi : pos + 1) - (k0 + 8 * g);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      if (db + PV < DB) kt[db + PV] = lds_frag(tb + (db + PV) * 1024);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oacc[mb][db] = mfma16x16x32(kt[db], pb[mb], oacc[mb][db]);
+        for (int i = 0; i < 8; ++i) x[i] = (i >= lo && i < hi) ? x[i] : -INFINITY;
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, PV, 0);
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = group_max(mx);
+    const bool up = mx > m_run + kLazy;
+    const bool any = __builtin_amdgcn_ballot_w64(up) != 0;
+    float alpha = 1.f;
+    if (any) {
+      const float m_new = up ? mx : m_run;
+      alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      if (db + PV < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
+    for (int i = 0; i < 8; ++i) {
+      x[i] = fast_exp2(x[i] - m_use);
+      l_run += x[i];
+    }
+    *reinterpret_cast<bf16x8 *>(pbuf[t & 1] + wave * 1024 + frag_off) = pack8(x);
+    if (g == 0) alpha_s[t & 1][wave * 16 + j] = alpha;
+    if (lane == 0) resc_s[t & 1][wave] = any ? 1 : 0;
+  };
+
+  // O^T[64 w .. 64 w + 63][all rows] += K^T P^T of tile t: the wave's four
+  // K^T fragments are held while the eight P fragments stream through.
+  floatx4 oacc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int c = 0; c < CB; ++c) oacc[rb][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto pv = [&](int t) {
+    const int bf = t & 1;
+    const int4 f0 = *reinterpret_cast<const int4 *>(&resc_s[bf][0]);
+    const int4 f1 = *reinterpret_cast<const int4 *>(&resc_s[bf][4]);
+    const int fl[RB] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (__builtin_amdgcn_readfirstlane(fl[rb])) {
+        const float a = alpha_s[bf][rb * 16 + j];
+#pragma unroll
+        for (int c = 0; c < CB; ++c) oacc[rb][c] *= a;
+      }
+    }
+    const char *tb = tbase + bf * kTileBytes512 + wave * CB * 1024 + frag_off;
+    const char *pb = pbuf[bf] + frag_off;
+    bf16x8 kt[CB], pf[RB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) kt[c] = lds_frag(tb + c * 1024);
+    pf[0] = lds_frag(pb);
+    pf[1] = lds_frag(pb + 1024);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (rb + 2 < RB) pf[rb + 2] = lds_frag(pb + (rb + 2) * 1024);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) oacc[rb][c] = mfma16x16x32(kt[c], pf[rb], oacc[rb][c]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, CB + 2, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (rb + 2 < RB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
     }
   };
 
-  if constexpr (!kSingle) {
-    // Double-buffered: K runs two tiles ahead, K^T one; S of tile t+1 is
-    // issued before the softmax and PV of tile t; one barrier per tile.
-    // First tile copies go out before the query-row loads, so the two
-    // latencies overlap.
-    stage_k(0);
-    stage_k(1);
-    stage_t(0);
-    load_q();
+  // K runs two tiles ahead, K^T one; the S^T of tile t + 1 is issued before
+  // the PV of tile t, its softmax after; one barrier per tile.
+  stage_k(0);
+  stage_k(1);
+  stage_t(0);
+  load_q();
+  wait_all_loads();
+  __syncthreads();
+  floatx4 sc[2];
+  if (nent > 0) {
+    const uint32_t e0 = entry(0);
+    const uint32_t mw = load_mask(e0);
+    qk(0, sc);
+    softmax(0, sc, e0, mw);
+  }
+  __syncthreads();  // P of tile 0 visible; K buffer 0 free
+  stage_k(2);
+  stage_t(1);
+  for (int it = 0; it < nent; ++it) {
+    const bool more = it + 1 < nent;
+    const uint32_t en = more ? entry(it + 1) : 0u;
+    const uint32_t mw = load_mask(en);
+    if (more) qk(it + 1, sc);
+    pv(it);
+    if (more) softmax(it + 1, sc, en, mw);
     wait_all_loads();
     __syncthreads();
-    floatx4 sc[MB][2];
-    if (nent > 0) qk(0, sc);
-    __syncthreads();
-    stage_k(2);
-    stage_t(1);
-
-    // List entries are read only right after the barrier (where a wait for a
-    // scalar load costs nothing): ent holds the entry of the current tile.
-    uint32_t ent = nent > 0 ? entry(0) : 0u;
-    load_mask(ent);
-    for (int it = 0; it < nent; ++it) {
-      floatx4 sn[MB][2];
-      if (it + 1 < nent) qk(it + 1, sn);
-      soft_pv(it, sc, ent);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        sc[mb][0] = sn[mb][0];
-        sc[mb][1] = sn[mb][1];
-      }
-      wait_all_loads();
-      __syncthreads();
-      if (it + 1 < nent) {
-        ent = entry(it + 1);
-        load_mask(ent);
-      }
-      stage_k(it + 3);
-      stage_t(it + 2);
-    }
-  } else {
-    // Single-buffered: the copy of K for tile t+1 overlaps the softmax and PV
-    // of tile t, the copy of K^T for tile t+1 overlaps S of tile t+1; two
-    // barriers per tile.  The second workgroup on the CU covers the rest.
-    stage_k(0);
-    stage_t(0);
-    load_q();
-    wait_all_loads();
-    __syncthreads();
-    floatx4 sc[MB][2];
-    if (nent > 0) qk(0, sc);
-    __syncthreads();  // K buffer free
-    stage_k(1);
-    uint32_t ent = nent > 0 ? entry(0) : 0u;
-    load_mask(ent);
-    for (int it = 0; it < nent; ++it) {
-      soft_pv(it, sc, ent);
-      wait_all_loads();  // K of tile it + 1
-      __syncthreads();   // K^T buffer free, K of tile it + 1 visible
-      if (it + 1 < nent) {
-        ent = entry(it + 1);
-        load_mask(ent);
-        stage_t(it + 1);
-        qk(it + 1, sc);
-        wait_all_loads();  // K^T of tile it + 1
-        __syncthreads();   // K buffer free, K^T of tile it + 1 visible
-        stage_k(it + 2);
-      }
-    }
+    stage_k(it + 3);
+    stage_t(it + 2);
   }
 
-  // The tile buffers are free (the loop ended on a barrier with no copy in
-  // flight): each 16-row block is staged there and stored as whole rows.
-  static_assert(NW * MB * 16384 <= 2 * kBufs * kTileBytes512, "row staging fits the tiles");
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const float l = group_sum(l_run[mb]);
+  // Row statistics: 1 / l to LDS for every wave, LSE by the owner.
+  {
+    const float l = group_sum(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    store_rows512(oacc[mb], inv, smem + (wave * MB + mb) * 16384, lane, [&](int r) -> bf16raw * {
-      const int rr = sl * M + (wave * MB + mb) * 16 + r;
-      const int pr = qt * d.bq + (rr & (d.bq - 1)), hr = rr >> lbq;
-      return pr < d.S ? o + (((size_t)b * d.H + hr) * d.S + pr) * D : nullptr;
-    });
-    if (valid[mb] && g == 0)
-      lse[((size_t)b * d.H + hh[mb]) * d.S + pos[mb]] =
-          l > 0.f ? (m_run[mb] + __log2f(l)) * kLn2 : -INFINITY;
+    if (g == 0) inv_s[wave * 16 + j] = inv;
+    if (valid && g == 0)
+      lse[((size_t)b * d.H + hh) * d.S + pos] =
+          l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();  // inv_s visible (the tile buffers are idle: no copy in flight)
+  // Normalised O as bf16 into the tile buffers, row r at r * 1024 with its
+  // 16-byte chunk c at (c ^ (r & 15)), then every wave stores 16 whole rows.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * 16 + j;
+    const float inv = inv_s[r];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      ushort4 w;
+      w.x = f2bf(oacc[rb][c][0] * inv);
+      w.y = f2bf(oacc[rb][c][1] * inv);
+      w.z = f2bf(oacc[rb][c][2] * inv);
+      w.w = f2bf(oacc[rb][c][3] * inv);
+      const int chunk = 8 * wave + 2 * c + (g >> 1);
+      *reinterpret_cast<ushort4 *>(smem + r * 1024 + ((chunk ^ j) << 4) + ((g & 1) << 3)) = w;
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int r = wave * 16 + i;
+    const int rr = sl * M + r;
+    const int pr = qt * d.bq + (rr & (d.bq - 1)), hr = rr >> lbq;
+    if (pr < d.S) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(smem + r * 1024 + ((lane ^ (r & 15)) << 4));
+      *reinterpret_cast<uint4 *>(o + (((size_t)b * d.H + hr) * d.S + pr) * D + 8 * lane) = v;
+    }
   }
 }
 
@@ -712,17 +659,16 @@ int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *
   };
   switch (d.D) {
     case 512: {
-      constexpr int NW = HCA_FWD_NW, MB = HCA_FWD_MB;
-      const dim3 g512(d.B * d.nqt * (d.bq * d.H / (NW * MB * 16)));
-      auto go512 = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, g512, dim3(NW * 64), 0, s, d, p, (const bf16raw *)q,
-                           (const bf16raw *)kv, (const bf16raw *)kvc, (const bf16raw *)kvt,
-                           (const bf16raw *)kvct, sl2, (bf16raw *)o, lse);
+      // 128 rows per workgroup (bq * H is a power of two >= 128).
+      const dim3 gs(d.B * d.nqt * (d.bq * d.H / 128));
+      auto gos = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, gs, dim3(512), 0, s, d, p, (const bf16raw *)q,
+                           (const bf16raw *)kvt, (const bf16raw *)kvct, sl2, (bf16raw *)o, lse);
       };
       if (d.cmask_ldw)
-        go512(hca_fwd512_kernel<NW, MB, true>);
+        gos(hca_fwd512s_kernel<true>);
       else
-        go512(hca_fwd512_kernel<NW, MB, false>);
+        gos(hca_fwd512s_kernel<false>);
       break;
     }
     case 128: args(hca_fwd_bf16_kernel<128, 8, 1>, 8); break;
