@@ -66,7 +66,7 @@ class _PlanInfo(ctypes.Structure):
         (n, ctypes.c_uint64) for n in ("device_bytes", "ws_fwd_bytes", "ws_bwd_bytes")] + [
         (n, ctypes.c_int64) for n in ("items", "items_half", "part_blocks")] + [
         (n, ctypes.c_int32) for n in ("comp_item_chunks", "kv_heads", "comp_masked",
-                                      "kv_keys")]
+                                      "kv_keys")] + [("ws_pds_bytes", ctypes.c_uint64)]
 
 
 class _KernelTime(ctypes.Structure):
@@ -163,7 +163,7 @@ class PlanInfo:
     pairs_raw: int; pairs_comp: int
     device_bytes: int; ws_fwd_bytes: int; ws_bwd_bytes: int
     items: int; items_half: int; part_blocks: int; comp_item_chunks: int; kv_heads: int
-    comp_masked: int; kv_keys: int
+    comp_masked: int; kv_keys: int; ws_pds_bytes: int
 
 
 class Plan:

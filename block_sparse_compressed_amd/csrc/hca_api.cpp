@@ -37,6 +37,7 @@ Dims make_dims(const hca_plan *plan) {
   d.nkv_raw = plan->nkv_raw;
   d.nkv_comp = plan->nkv_comp;
   d.cmask_ldw = plan->cmask_ldw;
+  d.pds_rows = plan->pds_rows;
   return d;
 }
 
@@ -53,6 +54,7 @@ DevPlan make_devplan(const hca_plan *plan) {
   p.kvent = reinterpret_cast<const uint32_t *>(base + L.kvent);
   p.kvtile = reinterpret_cast<const int32_t *>(base + L.kvtile);
   p.cmask = plan->cmask_ldw ? reinterpret_cast<const uint32_t *>(base + L.cmask) : nullptr;
+  p.kvpe = plan->pds_rows ? reinterpret_cast<const int32_t *>(base + L.kvpe) : nullptr;
   return p;
 }
 
@@ -279,6 +281,7 @@ extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const vo
   }
   void *kvt = w + plan->ws.kvt, *kvct = w + plan->ws.kvct;
   float *part = reinterpret_cast<float *>(w + plan->ws.part);
+  void *pds = plan->pds_rows ? w + plan->ws.pds : nullptr;
   const void *kvc = kv_comp ? kv_comp : kv;
   err = timed(K_TRANSPOSE, hip_stream, [&] {
     return launch_transpose_kv(kv, kvt, d.S, d.S_pad, d.Sc > 0 ? kv_comp : nullptr, kvct, d.Sc,
@@ -286,12 +289,13 @@ extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const vo
   });
   if (err) return hip_fail("hca_attn_bwd (transpose)", err);
   err = timed(K_BWD_DQ, hip_stream, [&] {
-    return launch_bwd_dq_bf16(d, p, q, kv, kvc, kvt, kvct, o, lse, dout, scale, dq, delta,
+    return launch_bwd_dq_bf16(d, p, q, kv, kvc, kvt, kvct, o, lse, dout, scale, dq, delta, pds,
                               hip_stream);
   });
   if (err) return hip_fail("hca_attn_bwd (dQ kernel)", err);
   err = timed(K_BWD_DKV, hip_stream, [&] {
-    return launch_bwd_dkv_bf16(d, p, q, kv, kvc, lse, delta, dout, scale, part, hip_stream);
+    return launch_bwd_dkv_bf16(d, p, q, kv, kvc, lse, delta, dout, scale, pds, part,
+                               hip_stream);
   });
   if (err) return hip_fail("hca_attn_bwd (dKV kernel)", err);
   err = timed(K_DKV_REDUCE, hip_stream, [&] {

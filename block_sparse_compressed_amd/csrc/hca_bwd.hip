@@ -278,15 +278,20 @@ __global__ void __launch_bounds__(NW * 64, 1)
 //     matrix-core work.
 // ---------------------------------------------------------------------------
 // MASKED: compressed visibility from the plan's mask bits (separate
-// instantiation, as for the forward).
-template <int NW, bool MASKED>
+// instantiation, as for the forward).  STORE: P and scale * dS of every tile
+// also go to the stored-P/dS area (bf16), for the key-stationary pass: list
+// entry e of a query tile owns the block pds + e * 2 R * 64 bytes (R = bq H
+// rows), P rows then dS rows, 64 bytes per row (32 keys), the 16-byte chunk
+// c of row rho at chunk position c ^ ((rho >> 3) & 3).
+template <int NW, bool MASKED, bool STORE>
 __global__ void __launch_bounds__(NW * 64, 1)
     hca_bwd_dq512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                          const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
                          const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
                          const bf16raw *__restrict__ o, const float *__restrict__ lse,
                          const bf16raw *__restrict__ dout, float scale_log2, float scale,
-                         bf16raw *__restrict__ dq, float *__restrict__ delta) {
+                         bf16raw *__restrict__ dq, float *__restrict__ delta,
+                         char *__restrict__ pds) {
   constexpr int D = 512, KS = D / 32, DB = D / 16;
   constexpr int M = NW * 16;
   __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes512];
@@ -363,6 +368,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
   for (;;) {
     const int b = item / d.nqt, qt = item - b * d.nqt;
     const int rho = sl * M + wave * 16 + j;
+    const int eb = e_begin;  // this unit's first list entry (fetch() moves e_begin on)
     const int pos = qt * d.bq + (rho & (d.bq - 1)), hh = rho >> lbq;
     const bool valid = pos < d.S;
     const size_t row = ((size_t)b * d.H + hh) * d.S + pos;
@@ -489,9 +495,23 @@ __global__ void __launch_bounds__(NW * 64, 1)
         }
       }
 #pragma unroll
+      for (int v4 = 0; v4 < 8; ++v4) x[v4] = fast_exp2(x[v4]);
+      if constexpr (STORE) {
+        float y[8];
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          y[v4] = x[v4] * (pc[0][v4] - dl) * scale;
+          y[4 + v4] = x[4 + v4] * (pc[1][v4] - dl) * scale;
+        }
+        char *blk = pds + (size_t)(eb + it) * (2 * (size_t)d.pds_rows * 64) +
+                    (size_t)rho * 64 + ((g ^ ((rho >> 3) & 3)) << 4);
+        *reinterpret_cast<bf16x8 *>(blk) = pack8(x);
+        *reinterpret_cast<bf16x8 *>(blk + (size_t)d.pds_rows * 64) = pack8(y);
+      }
+#pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        x[v4] = fast_exp2(x[v4]) * (pc[0][v4] - dl);
-        x[4 + v4] = fast_exp2(x[4 + v4]) * (pc[1][v4] - dl);
+        x[v4] = x[v4] * (pc[0][v4] - dl);
+        x[4 + v4] = x[4 + v4] * (pc[1][v4] - dl);
       }
       const bf16x8 dsb = pack8(x);
       __builtin_amdgcn_sched_barrier(0);
@@ -563,7 +583,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
       // least kRowLoads vector-memory loads after it (its list, row-interval
       // and LSE loads, then the row fragments).  Loads complete in issue
       // order, so leaving kRowLoads outstanding still waits for the copy while
-      // the row loads stay in flight.  The barrier orders LDS only.
+      // the row loads stay in flight (with STORE, the two stores of the tile
+      // above also count: they only make the wait stricter).  The barrier
+      // orders LDS only.
       asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kRowLoads) : "memory");
       lds_barrier();
       ent = ent_last;
@@ -1094,34 +1116,28 @@ __global__ void __launch_bounds__(512, 1)
 }
 
 // ---------------------------------------------------------------------------
-// 2c. dKV at D = 512, 64-key items, four waves, two workgroups per CU.  Each
-//     wave holds the K fragments of 16 keys (64 registers) and accumulates
-//     dKV^T for 128 columns, d in [128 w, 128 w + 128), over the item's 64
-//     keys (128 accumulation registers).  Rows are staged single-buffered
-//     (32-row steps, Q and dO, 64 KiB), so a workgroup needs 73 KiB of LDS
-//     and two of them, independent, share a CU: one's copies, barriers and
-//     softmax run under the other's MFMAs.  Every item runs over its whole
-//     tile (no half items).  At S = 65536 from the rule it took 8.53 ms per
-//     call against 8.78 for 2b (narrower tiles follow the window's edges
-//     more closely); on per-query top-k selections, whose tiles are nearly
-//     all non-empty at either width, 14.8 ms against 12.6 (each row streams
-//     through twice as many items), so plans from a mask keep 2b.
+// 2c. dKV at D = 512 from stored P and dS (64-key tiles).  The dQ pass has
+//     already formed P and scale * dS (bf16) of every listed (query tile,
+//     32-key tile) pair; this pass only accumulates dKV^T[d][key] += Q^T dS +
+//     dO^T P.  One workgroup of four waves per work item (a 64-key tile and
+//     the query tiles of a run of 64-position chunks that see it), two
+//     workgroups per CU.  Per 32-row step, Q and dO rows (64 KiB, chunks
+//     XOR-swizzled) and the P / dS rows of the tile's two 32-key halves
+//     (8 KiB, as stored) are copied straight to LDS, single-buffered (the
+//     other workgroup on the CU covers the copy).  Wave w accumulates columns
+//     d in [128 w, 128 w + 128) of all 64 keys (128 fp32 sums per lane); the A
+//     operands are transpose reads of the row tiles, the B operands transpose
+//     reads of the P / dS tiles.  A half that the query tile does not list is
+//     read as zeros (an empty buffer range).
 // ---------------------------------------------------------------------------
-template <bool MASKED>
 __global__ void __launch_bounds__(256, 2)
-    hca_bwd_dkv512k64_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
-                             const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
-                             const float *__restrict__ lse, const float *__restrict__ delta,
-                             const bf16raw *__restrict__ dout, float scale_log2, float scale,
-                             float *__restrict__ part) {
-  constexpr int D = 512, KS = D / 32, KEYS = 64;
-  constexpr int STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = KEYS * STEP * 2;
+    hca_bwd_dkv512s_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                           const bf16raw *__restrict__ dout, const char *__restrict__ pds,
+                           float *__restrict__ part) {
+  constexpr int D = 512, STEP = 32, STEP_BYTES = STEP * 1024;
+  constexpr int PT = STEP * 64;  // bytes of one stored half-tile step (32 rows x 32 keys)
   __shared__ __attribute__((aligned(1024))) char smem[2 * STEP_BYTES];  // [Q | dO]
-  __shared__ __attribute__((aligned(16))) char xs[2 * XBYTES];         // [P | dS]
-  __shared__ float4 ri_s[STEP];  // per step row: lse log2e, delta, key interval
-  // Masked plans: per step row (lanes 32..63 repeat rows 0..31) the four
-  // 32-bit words of the mask that hold the item's 64 entries.
-  __shared__ __attribute__((aligned(16))) uint4 rm_s[MASKED ? 64 : 1];
+  __shared__ __attribute__((aligned(1024))) char ps[4 * PT];           // [P lo|P hi|dS lo|dS hi]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
@@ -1129,27 +1145,20 @@ __global__ void __launch_bounds__(256, 2)
   if (item < 0) return;  // padding slot of the launch order
   const KvItem it = p.kvitem[item];
   const int b = it.b;
-  const bool comp = it.kind != 0;
-  const int nk = comp ? d.Sc : d.S;
-  const int k0 = it.kt * KEYS;
-  const bf16raw *src = comp ? kvc + (size_t)b * d.Sc * D : kv + (size_t)b * d.S * D;
   const int nq = it.e1 - it.e0;
   const int lbq = __builtin_ctz(d.bq);
   const int SPQ = d.bq * d.H / STEP, lspq = __builtin_ctz(SPQ);
   const int nsteps = nq * SPQ;
-  const uint32_t ent_lane = lane < nq ? p.kvent[it.e0 + lane] : 0u;
-  auto entry = [&](int e) -> uint32_t {
-    return e < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, e)
-                  : uniform_load(p.kvent, it.e0 + e);
-  };
+  const size_t blk_bytes = 2 * (size_t)d.pds_rows * 64;  // one list entry's P and dS
   const size_t bat = (size_t)b * d.H * d.S * D;
   const uint32_t qb_lds = lds_addr(smem);
-  // Wave w stages rows 8 w .. 8 w + 7 of each step; row r's chunk c sits at
-  // slot c ^ sw(r), sw(r) = (r & 3) | ((r >> 3) << 2).
+  // Wave w stages rows 8 w .. 8 w + 7 of Q and dO; row r's chunk c sits at slot
+  // c ^ sw(r), sw(r) = (r & 3) | ((r >> 3) << 2).  Wave w also copies stored
+  // block w (P lo, P hi, dS lo, dS hi): 2 KiB, two 1 KiB copies.
   const uint32_t lane_sw = (uint32_t)(lane ^ (wave << 2));
   auto stage = [&](int s) {
     const int e = s >> lspq, u = s & (SPQ - 1);
-    const int qt = (int)(entry(e) & kEntIdx);
+    const int qt = (int)(uniform_load(p.kvent, it.e0 + e) & kEntIdx);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * wave + i, rho = u * STEP + r;
@@ -1159,174 +1168,68 @@ __global__ void __launch_bounds__(256, 2)
       dma16(q + rowoff, voff, qb_lds + r * 1024);
       dma16(dout + rowoff, voff, qb_lds + STEP_BYTES + r * 1024);
     }
+    const int ent = (int)uniform_load((const uint32_t *)p.kvpe, 2 * (it.e0 + e) + (wave & 1));
+    // rows u * 32 .. u * 32 + 31 of the half's P (wave < 2) or dS (wave >= 2)
+    const char *src = pds + (ent >= 0 ? (size_t)ent * blk_bytes : 0) +
+                      (size_t)(wave >> 1) * d.pds_rows * 64 + (size_t)u * PT;
+    const rsrc_t r = make_rsrc(src, ent >= 0 ? PT : 0);
+    buf_load16(r, lds_addr(ps + wave * PT), 16 * lane);
+    buf_load16(r, lds_addr(ps + wave * PT + 1024), 1024 + 16 * lane);
   };
-  int4 nrw = make_int4(0, 0, 0, 0);
-  float nl = 0.f, nd = 0.f;
-  int npos = 0;
-  auto rowinfo = [&](int s) {  // row (lane & 31) of step s, into registers
-    const int e = s >> lspq, u = s & (SPQ - 1);
-    const int qt = (int)(entry(e) & kEntIdx);
-    const int rho = u * STEP + (lane & (STEP - 1));
-    npos = qt * d.bq + (rho & (d.bq - 1));
-    const int h = rho >> lbq, pc = min(npos, d.S - 1);
-    const size_t row = ((size_t)b * d.H + h) * d.S + pc;
-    nrw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
-    nl = lse[row];
-    nd = delta[row];
-  };
-  // Row table of the step whose row information was loaded last, to LDS; in
-  // masked plans with the 16 bytes of mask that hold the item's 64 bits
-  // (words 4 (kt / 2) .., copied straight to LDS; a padded row's bits are
-  // ignored by the softmax).  Called only while no wave reads the tables.
-  auto put_rowinfo = [&]() {
-    if (MASKED && comp && wave == 0) {
-      const int pc = min(npos, d.S - 1);
-      dma16(p.cmask,
-            (uint32_t)((((size_t)b * d.S + pc) * d.cmask_ldw + 4 * (it.kt >> 1)) * 4),
-            lds_addr(&rm_s[0]));
-    }
-    if (wave == 0 && lane < STEP) {
-      const bool ok = npos < d.S;
-      float4 w;
-      w.x = ok ? nl * kLog2e : 0.f;
-      w.y = ok ? nd : 0.f;
-      w.z = __int_as_float(ok ? (comp ? nrw.y : nrw.x) : INT_MAX);
-      w.w = __int_as_float(ok ? (comp ? nrw.z : npos + 1) : 0);
-      ri_s[lane] = w;
-    }
-  };
-  const int qk_base = (8 * (j >> 2) + (j & 3)) * 1024 + 16 * (g ^ (j & 3));
-  // Transposed A operands of the gradient, column block 8 wave + dl: chunk
-  // 16 wave + 2 dl + c0 of rows 8 g + (j >> 2) (and + 4).
+  // Transposed A operands of column block 8 wave + dl: chunk 16 wave + 2 dl +
+  // c0 of rows 8 g + (j >> 2) (and + 4) of the swizzled row tiles.
   const int tr_sw = ((j & 3) >> 1) ^ ((j >> 2) + 4 * g);
   const int tr_base = (8 * g + (j >> 2)) * 1024 + 256 * wave + ((j & 1) << 3);
-  const int xr0 = 16 * lane;
-  const int skey = k0 + 16 * wave;  // this wave's score keys skey .. skey + 15
+  // B operands of key block kb (keys 16 kb .. 16 kb + 15): rows 8 g + (j >> 2)
+  // (and + 4) of the stored half kb >> 1, keys 16 (kb & 1) + 4 (j & 3) .. + 3,
+  // i.e. chunk 2 (kb & 1) + ((j & 3) >> 1) at position chunk ^ g.
+  auto xfrag = [&](int tensor, int kb) {
+    const int chunk = 2 * (kb & 1) + ((j & 3) >> 1);
+    const int off = (2 * tensor + (kb >> 1)) * PT + (8 * g + (j >> 2)) * 64 +
+                    ((chunk ^ g) << 4) + ((j & 1) << 3);
+    return tr_frag_rows(ps + off, 256);
+  };
 
-  bf16x8 kf[KS];
-  {
-    const int key = skey + j;
-    const bf16raw *krow = src + (size_t)min(key, nk - 1) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(krow + 32 * ks + 8 * g);
-      kf[ks] = as_bf16x8(key < nk ? v : make_uint4(0, 0, 0, 0));
-    }
-  }
   floatx4 acc[4][8];  // [key block][column block of this wave]
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (nsteps > 0) {
-    stage(0);
-    rowinfo(0);
-    put_rowinfo();
-  }
+  if (nsteps > 0) stage(0);
   for (int s = 0; s < nsteps; ++s) {
     wait_all_loads();
-    __syncthreads();  // rows, row table and mask bits of step s in LDS
-    const bool full = entry(s >> lspq) & kEntFull;
-    int qkb = qk_base, trb = tr_base, xr = xr0;
-    asm volatile("" : "+v"(qkb), "+v"(trb), "+v"(xr));
+    __syncthreads();  // rows and P / dS of step s in LDS
+    int trb = tr_base;
+    asm volatile("" : "+v"(trb));
     const char *qb = smem, *ob = smem + STEP_BYTES;
-    // Next step's row table loads go out now; stored after the gradient.
-    if (s + 1 < nsteps) rowinfo(s + 1);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Scores, one 16-row block after the other.
-    floatx4 sv[2], pv[2];
+    bf16x8 xp[4], xd[4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      sv[rb] = pv[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 fq[KS], fo[KS];
-      auto fetch = [&](int ks) {
-        const int off = qkb + 64 * ((ks & 3) ^ (j >> 2)) + 256 * (ks >> 2) + 4096 * rb;
-        fq[ks] = lds_frag(qb + off);
-        fo[ks] = lds_frag(ob + off);
-      };
-      fetch(0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) fetch(ks + 1);
-        sv[rb] = mfma16x16x32(fq[ks], kf[ks], sv[rb]);
-        pv[rb] = mfma16x16x32(fo[ks], kf[ks], pv[rb]);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int kb = 0; kb < 4; ++kb) {
+      xp[kb] = xfrag(0, kb);
+      xd[kb] = xfrag(1, kb);
     }
-
-    // P and dS of rows 8 g + 4 rb + v for key skey + j -> exchange block wave.
-    {
-      const int key = skey + j;
+    // Two passes of four column blocks: the pass's transposed row fragments
+    // are held while the key blocks stream through.
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        bf16x4 pp, dd;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = 8 * g + 4 * rb + v;
-          const float4 rr = ri_s[row];
-          bool vis;
-          if (MASKED && comp) {
-            const int kk = 64 * (it.kt & 1) + (key - k0);  // bit within the 16 bytes
-            const uint32_t word = reinterpret_cast<const uint32_t *>(&rm_s[row])[kk >> 5];
-            vis = full | ((((word >> (kk & 31)) & 1u) != 0) &
-                          (__float_as_int(rr.z) != INT_MAX));
-          } else {
-            vis = full | ((key >= __float_as_int(rr.z)) & (key < __float_as_int(rr.w)));
-          }
-          const float ex = fast_exp2(sv[rb][v] * scale_log2 - rr.x);
-          const float e = vis ? ex : 0.f;
-          pp[v] = (__bf16)e;
-          dd[v] = (__bf16)(e * (pv[rb][v] - rr.y) * scale);
-        }
-        const int xo = xr + 8 * rb + 1024 * wave;
-        *reinterpret_cast<bf16x4 *>(xs + xo) = pp;
-        *reinterpret_cast<bf16x4 *>(xs + XBYTES + xo) = dd;
-      }
-    }
-    lds_barrier();  // exchange tiles complete
-
-    // Gradient, two passes of four column blocks: the pass's transposed row
-    // fragments are held while the four exchange pairs stream through.
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
+    for (int ps_ = 0; ps_ < 2; ++ps_) {
       bf16x8 tq[4], to[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int to_ = trb + ((tr_sw ^ (2 * (4 * ps + c))) << 4);
+        const int to_ = trb + ((tr_sw ^ (2 * (4 * ps_ + c))) << 4);
         tq[c] = tr_frag(qb + to_);
         to[c] = tr_frag(ob + to_);
       }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 xd = lds_frag(xs + XBYTES + xr + 1024 * kb);
-        const bf16x8 xp = lds_frag(xs + xr + 1024 * kb);
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          acc[kb][4 * ps + c] = mfma16x16x32(tq[c], xd, acc[kb][4 * ps + c]);
-          acc[kb][4 * ps + c] = mfma16x16x32(to[c], xp, acc[kb][4 * ps + c]);
+          acc[kb][4 * ps_ + c] = mfma16x16x32(tq[c], xd[kb], acc[kb][4 * ps_ + c]);
+          acc[kb][4 * ps_ + c] = mfma16x16x32(to[c], xp[kb], acc[kb][4 * ps_ + c]);
         }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 16 + 2, 0);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();  // rows, exchange, row table and mask bits of step s no longer read
-    if (s + 1 < nsteps) {
-      stage(s + 1);
-      put_rowinfo();
-    }
+    __syncthreads();  // step s no longer read
+    if (s + 1 < nsteps) stage(s + 1);
   }
 
   // Partial [64 keys][512]: this wave's 128 columns of every key.
@@ -1438,7 +1341,7 @@ static int compute_units() {
 int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
                        const void *kvc, const void *kvt, const void *kvct, const void *o,
                        const float *lse, const void *dout, float scale, void *dq, float *delta,
-                       void *stream) {
+                       void *pds, void *stream) {
   hipStream_t s = (hipStream_t)stream;
   const float sl2 = scale * kLog2e;
   auto go = [&](auto kernel, int nw, int groups) {
@@ -1447,6 +1350,12 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
                        (const bf16raw *)kvct, (const bf16raw *)o, lse, (const bf16raw *)dout, sl2,
                        scale, (bf16raw *)dq, delta);
   };
+  auto go512 = [&](auto kernel, int groups) {
+    hipLaunchKernelGGL(kernel, dim3(groups), dim3(256), 0, s, d, p, (const bf16raw *)q,
+                       (const bf16raw *)kv, (const bf16raw *)kvc, (const bf16raw *)kvt,
+                       (const bf16raw *)kvct, (const bf16raw *)o, lse, (const bf16raw *)dout, sl2,
+                       scale, (bf16raw *)dq, delta, (char *)pds);
+  };
   switch (d.D) {
     case 512: {
       // Persistent: one workgroup per compute unit (each takes 128 KiB of
@@ -1454,10 +1363,14 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
       const int units = d.B * d.nqt * (d.bq * d.H / 64);
       const int cus = compute_units();
       if (cus <= 0) return (int)hipErrorInvalidDevice;
+      const int grid = units < cus ? units : cus;
+      if (d.pds_rows && !pds) return (int)hipErrorInvalidValue;
       if (d.cmask_ldw)
-        go(hca_bwd_dq512_kernel<4, true>, 4, units < cus ? units : cus);
+        d.pds_rows ? go512(hca_bwd_dq512_kernel<4, true, true>, grid)
+                   : go512(hca_bwd_dq512_kernel<4, true, false>, grid);
       else
-        go(hca_bwd_dq512_kernel<4, false>, 4, units < cus ? units : cus);
+        d.pds_rows ? go512(hca_bwd_dq512_kernel<4, false, true>, grid)
+                   : go512(hca_bwd_dq512_kernel<4, false, false>, grid);
       break;
     }
     case 128: go(hca_bwd_dq_kernel<128, 8, 1>, 8, d.B * d.nqt * (d.bq * d.H / 128)); break;
@@ -1469,7 +1382,8 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
 
 int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
                         const void *kvc, const float *lse, const float *delta,
-                        const void *dout, float scale, float *part, void *stream) {
+                        const void *dout, float scale, const void *pds, float *part,
+                        void *stream) {
   if (d.n_items == 0) return hipSuccess;
   hipStream_t s = (hipStream_t)stream;
   const float sl2 = scale * kLog2e;
@@ -1480,17 +1394,14 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
   };
   switch (d.D) {
     case 512:
-      if (d.kv_bk == 64) {
-        if (d.cmask_ldw)
-          hipLaunchKernelGGL(hca_bwd_dkv512k64_kernel<true>, dim3(d.n_items), dim3(256), 0, s,
-                             d, p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc,
-                             lse, delta, (const bf16raw *)dout, sl2, scale, part);
-        else
-          hipLaunchKernelGGL(hca_bwd_dkv512k64_kernel<false>, dim3(d.n_items), dim3(256), 0, s,
-                             d, p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc,
-                             lse, delta, (const bf16raw *)dout, sl2, scale, part);
+      if (d.pds_rows) {
+        // 64-key tiles: P and dS were stored by the dQ pass.
+        if (d.kv_bk != 64 || !pds) return (int)hipErrorInvalidValue;
+        hipLaunchKernelGGL(hca_bwd_dkv512s_kernel, dim3(d.n_items), dim3(256), 0, s, d, p,
+                           (const bf16raw *)q, (const bf16raw *)dout, (const char *)pds, part);
         break;
       }
+      if (d.kv_bk != 128) return (int)hipErrorInvalidValue;
       // Every item (over all keys of its tile or over one half) in one launch.
       if (d.cmask_ldw)
         hipLaunchKernelGGL(hca_bwd_dkv512x8_kernel<true>, dim3(d.n_items), dim3(512), 0, s, d,

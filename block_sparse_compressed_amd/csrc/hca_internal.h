@@ -48,6 +48,9 @@ struct DevLayout {
   uint64_t kvtile = 0;   // int32 [B][nkv_raw + nkv_comp][2]: first partial block, block count
   uint64_t cmask = 0;    // uint32 [B][S][cmask_ldw]: compressed-key visibility bits (masked
                          // plans only)
+  uint64_t kvpe = 0;     // int32 [n_kvent][2]: stored-P/dS blocks of the two 32-key halves
+                         // of each key-tile entry (qent index, -1 = not listed; 64-key
+                         // tiles at D = 512 only)
   uint64_t total = 0;
 };
 
@@ -58,6 +61,9 @@ struct WsLayout {
   uint64_t kvct = 0;    // the same for compressed kv, Sc_pad entries
   uint64_t delta = 0;   // float32 [B][H][S] (backward)
   uint64_t part = 0;    // float32 partial key gradients (backward)
+  uint64_t pds = 0;     // bf16 P and dS per query-tile entry e: [e][P | dS][bq * H rows]
+                        // [32 keys], chunks swizzled (64-key tiles at D = 512 only)
+  uint64_t pds_bytes = 0;
   uint64_t fwd_total = 0;
   uint64_t bwd_total = 0;
 };
@@ -70,6 +76,7 @@ struct Dims {
   int32_t n_items;       // launch slots of the key-stationary backward
   int32_t kv_bk, nkv_raw, nkv_comp;  // key tiles of the key-stationary backward
   int32_t cmask_ldw;  // words per position of the compressed-key mask; 0: interval rule
+  int32_t pds_rows;   // rows per stored P/dS block (bq * H); 0: dKV recomputes S and dP
 };
 
 struct DevPlan {
@@ -82,6 +89,7 @@ struct DevPlan {
   const uint32_t *kvent;
   const int32_t *kvtile;
   const uint32_t *cmask;  // masked plans: visibility bits of compressed keys
+  const int32_t *kvpe;    // stored-P/dS plans: qent index of each kvent's two halves
 };
 
 // Launchers (defined in the .hip files).  Each returns a hipError_t as int.
@@ -93,10 +101,11 @@ int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *
 int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
                        const void *kvc, const void *kvt, const void *kvct, const void *o,
                        const float *lse, const void *dout, float scale, void *dq, float *delta,
-                       void *stream);
+                       void *pds, void *stream);
 int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
                         const void *kvc, const float *lse, const float *delta,
-                        const void *dout, float scale, float *part, void *stream);
+                        const void *dout, float scale, const void *pds, float *part,
+                        void *stream);
 int launch_dkv_reduce(const Dims &d, const DevPlan &p, const float *part, int dtype, void *dkv,
                       void *dkvc, void *stream);
 int launch_fwd_f32(const Dims &d, const DevPlan &p, const float *q, const float *kv,
@@ -130,9 +139,11 @@ struct hca_plan {
   std::vector<int32_t> kvorder;  // launch slots (-1 = none)
   std::vector<uint32_t> kvent;
   std::vector<int32_t> kvtile;
+  std::vector<int32_t> kvpe;  // stored-P/dS plans: [n_kvent][2]
   int32_t kv_bk = 32, nkv_raw = 0, nkv_comp = 0;  // key-stationary backward tiling
   int32_t rows_b = 0;  // rows of the plan's tables: batch rows x kv heads
   int32_t cmask_ldw = 0;  // masked plans: words per position of the device mask
+  int32_t pds_rows = 0;   // stored-P/dS plans: rows per stored block (bq * H)
   hca::DevLayout lay;
   hca::WsLayout ws;
   std::string unsupported;     // why kernel_ok is 0 ("" when it is 1)

@@ -674,6 +674,42 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
       p->kvorder = build_order();
     }
 
+    // ---- stored P and dS --------------------------------------------------- //
+    // With 64-key tiles at D = 512 the dQ pass stores P and dS (bf16) of every
+    // listed (query tile, 32-key tile) pair, and the key-stationary pass reads
+    // them instead of recomputing S and dP.  A 64-key tile's entry for query
+    // tile qt names the stored blocks of its two 32-key halves: their indices
+    // in qt's list (the qent CSR), -1 where qt does not list that half.
+    const bool stored = dtype == HCA_BF16 && D == 512 && kvb == 64;
+    if (stored) {
+      p->pds_rows = (int32_t)(bq * H);
+      p->kvpe.assign(p->kvent.size() * 2, -1);
+      std::vector<std::pair<uint64_t, int32_t>> keyed;  // (qt, kind, tile) -> qent index
+      for (int b = 0; b < B; ++b) {
+        keyed.clear();
+        for (int64_t qt = 0; qt < nqt; ++qt)
+          for (int32_t e = p->qptr[b * nqt + qt]; e < p->qptr[b * nqt + qt + 1]; ++e) {
+            const uint32_t ent = p->qent[e];
+            keyed.emplace_back(((uint64_t)qt << 32) | (ent & (kEntComp | kEntIdx)), e);
+          }
+        std::sort(keyed.begin(), keyed.end());
+        auto find = [&](int64_t qt, uint32_t kind, int64_t tile) -> int32_t {
+          const uint64_t key = ((uint64_t)qt << 32) | (kind ? kEntComp : 0u) | (uint32_t)tile;
+          auto at = std::lower_bound(keyed.begin(), keyed.end(),
+                                     std::make_pair(key, (int32_t)INT32_MIN));
+          return at != keyed.end() && at->first == key ? at->second : -1;
+        };
+        for (const KvItem &it : p->kvitem) {
+          if (it.b != b) continue;
+          for (int32_t e = it.e0; e < it.e1; ++e) {
+            const int64_t qt = p->kvent[e] & kEntIdx;
+            p->kvpe[2 * (size_t)e] = find(qt, it.kind, 2 * (int64_t)it.kt);
+            p->kvpe[2 * (size_t)e + 1] = find(qt, it.kind, 2 * (int64_t)it.kt + 1);
+          }
+        }
+      }
+    }
+
     // ---- device image ----------------------------------------------------- //
     DevLayout &L = p->lay;
     uint64_t off = 0;
@@ -692,6 +728,7 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
       p->cmask_ldw = (int32_t)(ceil_div(S_c, 128) * 4);
       L.cmask = place((uint64_t)B * S * p->cmask_ldw * 4);
     }
+    if (stored) L.kvpe = place(std::max<size_t>(1, p->kvpe.size()) * 4);
     L.total = off;
     p->image.assign(L.total, 0);
     auto put = [&](uint64_t o, const void *src, size_t bytes) {
@@ -705,6 +742,7 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     put(L.kvorder, p->kvorder.data(), p->kvorder.size() * 4);
     put(L.kvent, p->kvent.data(), p->kvent.size() * 4);
     put(L.kvtile, p->kvtile.data(), p->kvtile.size() * 4);
+    if (stored) put(L.kvpe, p->kvpe.data(), p->kvpe.size() * 4);
     if (cmask) {
       uint32_t *words = reinterpret_cast<uint32_t *>(p->image.data() + L.cmask);
       for (size_t row = 0; row < (size_t)B * S; ++row) {
@@ -729,6 +767,12 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     w.fwd_total = dtype == HCA_BF16 ? off : 0;
     w.delta = place((uint64_t)B * H * S * 4);
     w.part = place((uint64_t)std::max<int64_t>(1, nblocks * kvb * D) * 4);
+    if (stored) {
+      // per qent entry: P and dS of bq * H rows x 32 keys, bf16
+      w.pds_bytes = (uint64_t)std::max<size_t>(1, p->qent.size()) * 2 * bq * H * 32 * 2;
+      w.pds = place(w.pds_bytes);
+      in.ws_pds_bytes = w.pds_bytes;
+    }
     w.bwd_total = off;
     in.ws_fwd_bytes = w.fwd_total;
     in.ws_bwd_bytes = w.bwd_total;

@@ -135,6 +135,9 @@ typedef struct hca_plan_info {
   int32_t comp_masked;             /* 1: compressed visibility from a given mask (see
                                       hca_block_mask_build_masked) */
   int32_t kv_keys;                 /* keys per key tile of the key-stationary backward */
+  uint64_t ws_pds_bytes;           /* of ws_bwd_bytes: the bfloat16 P and dS tiles the dQ
+                                      pass stores for the key-stationary pass (64-key
+                                      tiles at head dim 512; 0 otherwise) */
 } hca_plan_info;
 
 /*

@@ -358,18 +358,33 @@ def test_compressed_item_chunks_knob(chunks):
 
 
 def test_workspace_grows_linearly():
-    """The backward workspace is O(S): compressed-tile items are merged once
-    their partial blocks would pass twice the raw tiles' (which grow as S), so
-    doubling S at most about doubles it (it grew as S^2 / r when every
-    64-position chunk of a compressed tile's rows was always an item)."""
+    """Without stored P and dS (128-key tiles) the backward workspace is O(S):
+    compressed-tile items are merged once their partial blocks would pass
+    twice the raw tiles' (which grow as S), so doubling S at most about doubles
+    it (it grew as S^2 / r when every 64-position chunk of a compressed tile's
+    rows was always an item).  With 64-key tiles the workspace adds the stored
+    P and dS: exactly one 2 x (bq H) x 32 bf16 block per listed (query tile,
+    32-key tile) pair, O(visible pairs)."""
+    lean = (0, 0, 0, 0, 0, 128)
     ws = {}
     for S in (131072, 262144):
         p = hca.hca_block_mask_build(1, S, 128, 128, S // 128, None, None, 64, 512,
-                                     hca.HCA_BF16)
-        ws[S] = hca.hca_plan_get_info(p).ws_bwd_bytes
+                                     hca.HCA_BF16, tiles=lean)
+        info = hca.hca_plan_get_info(p)
+        assert info.ws_pds_bytes == 0
+        ws[S] = info.ws_bwd_bytes
     assert ws[262144] <= 2.05 * ws[131072]
     # S = 65536 keeps one-chunk compressed items (its compressed partials fit
     # in twice the raw ones) and needs less than before (1.27 GiB)
-    p = hca.hca_block_mask_build(1, 65536, 128, 128, 512, None, None, 64, 512, hca.HCA_BF16)
+    p = hca.hca_block_mask_build(1, 65536, 128, 128, 512, None, None, 64, 512, hca.HCA_BF16,
+                                 tiles=lean)
     info = hca.hca_plan_get_info(p)
     assert info.comp_item_chunks == 1 and info.ws_bwd_bytes < 1.2 * 2**30
+    # stored P / dS: the listed pairs times one block each
+    p = hca.hca_block_mask_build(1, 16384, 128, 128, 128, None, None, 64, 512, hca.HCA_BF16)
+    info = hca.hca_plan_get_info(p)
+    raw, comp = hca.hca_plan_export_tiles(p)
+    listed = int((raw > 0).sum() + (comp > 0).sum())
+    assert info.kv_keys == 64
+    assert info.ws_pds_bytes == listed * 2 * info.bq * info.H * 32 * 2
+    assert info.ws_bwd_bytes > info.ws_pds_bytes
