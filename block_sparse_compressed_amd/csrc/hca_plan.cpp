@@ -465,6 +465,9 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     // one workgroup's waves each own 32 of them); for each, the query tiles
     // that see any of its keys, classified from the same intervals.
     const int64_t kvb = p->kv_bk;
+    // With stored P and dS (see below) the key-stationary pass needs no half
+    // items: a 32-key quarter that a query tile does not list is skipped.
+    const bool stored = dtype == HCA_BF16 && D == 512 && kvb == 64;
     const int64_t nkvr = ceil_div(S, kvb), nkvc = ceil_div(S_c, kvb);
     const int64_t nkv = nkvr + nkvc;
     // Query tiles per 64-position chunk.
@@ -547,7 +550,7 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
           p->kvent.insert(p->kvent.end(), list.begin() + s0, list.begin() + s1);
           it.e1 = (int32_t)p->kvent.size();
           it.halves = 3;
-          if (kvb == 128) {
+          if (kvb == 128 && !stored) {
             // Which 64-key halves of the tile any row of the item sees, from
             // the same per-position intervals as the tile states.
             it.halves = 0;
@@ -680,10 +683,10 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     // them instead of recomputing S and dP.  A 64-key tile's entry for query
     // tile qt names the stored blocks of its two 32-key halves: their indices
     // in qt's list (the qent CSR), -1 where qt does not list that half.
-    const bool stored = dtype == HCA_BF16 && D == 512 && kvb == 64;
     if (stored) {
       p->pds_rows = (int32_t)(bq * H);
-      p->kvpe.assign(p->kvent.size() * 2, -1);
+      const int64_t nqk = kvb / 32;  // 32-key tiles of the forward per key tile
+      p->kvpe.assign(p->kvent.size() * nqk, -1);
       std::vector<std::pair<uint64_t, int32_t>> keyed;  // (qt, kind, tile) -> qent index
       for (int b = 0; b < B; ++b) {
         keyed.clear();
@@ -703,8 +706,8 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
           if (it.b != b) continue;
           for (int32_t e = it.e0; e < it.e1; ++e) {
             const int64_t qt = p->kvent[e] & kEntIdx;
-            p->kvpe[2 * (size_t)e] = find(qt, it.kind, 2 * (int64_t)it.kt);
-            p->kvpe[2 * (size_t)e + 1] = find(qt, it.kind, 2 * (int64_t)it.kt + 1);
+            for (int64_t h = 0; h < nqk; ++h)
+              p->kvpe[nqk * (size_t)e + h] = find(qt, it.kind, nqk * (int64_t)it.kt + h);
           }
         }
       }
