@@ -30,10 +30,12 @@ PEAK_HBM_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_sparse_compressed_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
-# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE counters
-# (scaled by a plain copy of known size): "traffic:" JSON lines, one per kernel and
-# workload, in profiles/hbm_traffic_<workload>.md.  MFMA and LDS utilisation from
-# rocprofv3's derived counters: "mfma:" JSON lines in profiles/mfma_util.md.
+# HBM bytes per launch measured with rocprofv3's L2-to-memory request counters
+# (TCC_EA0_RDREQ_32B / _64B / _128B times their sizes for reads, TCC_EA0_WRREQ_64B
+# and TCC_EA0_WRREQ for writes; the same arithmetic on a plain copy of known size
+# gives its size back): "traffic:" JSON lines, one per kernel and workload, in
+# profiles/hbm_traffic_<workload>.md.  MFMA and LDS utilisation from rocprofv3's
+# derived counters: "mfma:" JSON lines in profiles/mfma_util.md.
 MFMA_FILE = os.path.join(PROFILES, "mfma_util.md")
 KERNEL_SOURCES = {"fwd": "hca_fwd.hip", "bwd_dq": "hca_bwd.hip", "bwd_dkv": "hca_bwd.hip",
                   "dkv_reduce": "hca_bwd.hip", "transpose": "hca_fwd.hip"}
@@ -108,7 +110,7 @@ def parse():
                     help="print the source hash of each kernel and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), the "
-                         "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
+                         "reference kernel that checks the HBM request-counter arithmetic")
     return ap.parse_args()
 
 
