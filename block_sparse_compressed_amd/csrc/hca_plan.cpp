@@ -93,13 +93,15 @@ int classify_tile_mask(const uint8_t *m, int64_t S, int64_t Sc, int64_t qt, int 
 }  // namespace
 
 // Keys per key tile of the key-stationary backward (a work item covers one
-// tile).  Head dim 512, bf16: 64 (four waves x 16 keys) for plans from the
-// rule, whose visible keys form intervals that narrower tiles follow more
-// closely; 128 (eight waves x 16 keys) for plans from a given mask, whose
-// scattered entries leave few tiles empty at either width, so wider tiles
-// stream each query row half as often.  Other kernels: the forward's 32-key
-// tile.  `want` (the tile configuration's kv_keys) overrides where the width
-// has a kernel; 0 if it has none.
+// tile).  Head dim 512, bf16: 64 for plans from the rule -- the backward then
+// stores P and dS in the dQ pass and the key-stationary pass reads them (see
+// the key-tile section of build_plan; above kPdsBudget of stored tiles the
+// library's choice falls back to 128); 128 (recomputing S and dP) for plans
+// from a given mask, whose scattered entries list nearly every tile pair, so
+// a store would be large and wider tiles stream each query row half as often.
+// Other kernels: the forward's 32-key tile.  `want` (the tile configuration's
+// kv_keys) overrides where the width has a kernel; 0 if it has none.
+constexpr uint64_t kPdsBudget = 32ull << 30;  // bytes of stored P and dS, library choice
 static int kv_tile_keys(int dtype, int D, bool masked, int want) {
   if (dtype == HCA_BF16 && D == 512) {
     if (want == 0) return masked ? 128 : 64;
@@ -461,12 +463,19 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     }
 
     // ---- key-tile work lists for the key-stationary backward ------------ //
-    // Key tiles of kv_bk keys (wider than the forward's tiles at D = 512, so
-    // one workgroup's waves each own 32 of them); for each, the query tiles
-    // that see any of its keys, classified from the same intervals.
+    // Library choice of 64-key tiles with stored P and dS: one bq * H x 32
+    // block of each per listed (query tile, 32-key tile) pair, O(S (W + S / r))
+    // bytes; past kPdsBudget the recomputing 128-key backward is used.
+    if (p->kv_bk == 64 && !(tiles && tiles->kv_keys) &&
+        (uint64_t)p->qent.size() * 2 * bq * H * 32 * 2 > kPdsBudget) {
+      p->kv_bk = 128;
+      in.kv_keys = 128;
+    }
+    // Key tiles of kv_bk keys (64 or 128 at D = 512, wider than the forward's
+    // 32); for each, the query tiles that see any of its keys, classified from
+    // the same intervals.
     const int64_t kvb = p->kv_bk;
-    // With stored P and dS (see below) the key-stationary pass needs no half
-    // items: a 32-key quarter that a query tile does not list is skipped.
+    // 64-key tiles at D = 512: P and dS stored by the dQ pass (see below).
     const bool stored = dtype == HCA_BF16 && D == 512 && kvb == 64;
     const int64_t nkvr = ceil_div(S, kvb), nkvc = ceil_div(S_c, kvb);
     const int64_t nkv = nkvr + nkvc;

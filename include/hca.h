@@ -81,10 +81,17 @@ enum { HCA_TILE_EMPTY = 0, HCA_TILE_PARTIAL = 1, HCA_TILE_FULL = 2 };
  * Three further fields shape the work items of the key-stationary backward
  * (they change the schedule, never the result beyond float summation order):
  *   kv_keys           keys per key tile of that backward; 0 = library choice.
- *                     Head dim 512, bfloat16: 64 or 128 (library choice 64 for
- *                     plans built from the rule, 128 for plans built from a
- *                     given mask, whose scattered entries fill wider tiles);
- *                     other kernels: 32.  Any other value is rejected.
+ *                     Head dim 512, bfloat16: 64 or 128.  With 64 the dQ pass
+ *                     stores P and dS (bf16, one bq * H x 32 block each per
+ *                     listed (query tile, 32-key tile) pair, in the backward
+ *                     workspace: hca_plan_info.ws_pds_bytes) and the key-
+ *                     stationary pass reads them instead of recomputing S and
+ *                     dP: faster, with a workspace of O(S (W + S / r)).  With
+ *                     128 both are recomputed and the workspace is O(S).
+ *                     Library choice: 64 for plans built from the rule while
+ *                     the store needs at most 32 GiB, else 128; 128 for plans
+ *                     built from a given mask.  Other kernels: 32.  Any other
+ *                     value is rejected.
  *   half_items_min    with 128-key items (head dim 512, bfloat16): an item whose
  *                     rows see only one 64-key half of its key tile runs over
  *                     that half alone once the plan has at least this many

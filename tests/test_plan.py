@@ -328,6 +328,13 @@ def test_kv_keys_choice():
     assert hca.hca_plan_get_info(masked64).kv_keys == 64
     d128 = hca.hca_block_mask_build(1, S, r, W, S // r, None, None, H, 128, hca.HCA_BF16)
     assert hca.hca_plan_get_info(d128).kv_keys == 32
+    # the library's 64-key choice stores P / dS only while that takes <= 32 GiB
+    big = hca.hca_plan_get_info(hca.hca_block_mask_build(1, 262144, 128, 128, 2048, None, None,
+                                                         64, 512, hca.HCA_BF16))
+    assert big.kv_keys == 128 and big.ws_pds_bytes == 0
+    forced = hca.hca_plan_get_info(hca.hca_block_mask_build(
+        1, 262144, 128, 128, 2048, None, None, 64, 512, hca.HCA_BF16, tiles=(0, 0, 0, 0, 0, 64)))
+    assert forced.kv_keys == 64 and forced.ws_pds_bytes > 32 * 2**30
     for D, bad in ((512, 32), (512, 96), (512, 256), (128, 64), (64, 128)):
         with pytest.raises(hca.HcaError, match="kv_keys"):
             hca.hca_block_mask_build(1, S, r, W, S // r, None, None, H, D, hca.HCA_BF16,
