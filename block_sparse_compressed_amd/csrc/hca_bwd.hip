@@ -33,6 +33,18 @@
 #include "hca_internal.h"
 #include "hca_stage.h"
 
+// Stored-P backward at D = 512: waves of the P / dS pass and of the streaming
+// dQ pass, and the streaming pass's stages in flight.
+#ifndef HCA_PDS_NW
+#define HCA_PDS_NW 4
+#endif
+#ifndef HCA_DQS_NW
+#define HCA_DQS_NW 8
+#endif
+#ifndef HCA_DQS_STAGES
+#define HCA_DQS_STAGES 3
+#endif
+
 namespace hca {
 
 namespace {
@@ -281,20 +293,17 @@ __global__ void __launch_bounds__(NW * 64, 1)
 //     matrix-core work.
 // ---------------------------------------------------------------------------
 // MASKED: compressed visibility from the plan's mask bits (separate
-// instantiation, as for the forward).  STORE: P and scale * dS of every tile
-// also go to the stored-P/dS area (bf16), for the key-stationary pass: list
-// entry e of a query tile owns the block pds + e * 2 R * 64 bytes (R = bq H
-// rows), P rows then dS rows, 64 bytes per row (32 keys), the 16-byte chunk
-// c of row rho at chunk position c ^ ((rho >> 3) & 3).
-template <int NW, bool MASKED, bool STORE>
+// instantiation, as for the forward).  Used by plans whose key-stationary
+// pass recomputes S and dP (128-key tiles); with stored P and dS the two
+// passes 1c and 1d replace it.
+template <int NW, bool MASKED>
 __global__ void __launch_bounds__(NW * 64, 1)
     hca_bwd_dq512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                          const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
                          const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
                          const bf16raw *__restrict__ o, const float *__restrict__ lse,
                          const bf16raw *__restrict__ dout, float scale_log2, float scale,
-                         bf16raw *__restrict__ dq, float *__restrict__ delta,
-                         char *__restrict__ pds) {
+                         bf16raw *__restrict__ dq, float *__restrict__ delta) {
   constexpr int D = 512, KS = D / 32, DB = D / 16;
   constexpr int M = NW * 16;
   __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes512];
@@ -371,7 +380,6 @@ __global__ void __launch_bounds__(NW * 64, 1)
   for (;;) {
     const int b = item / d.nqt, qt = item - b * d.nqt;
     const int rho = sl * M + wave * 16 + j;
-    const int eb = e_begin;  // this unit's first list entry (fetch() moves e_begin on)
     const int pos = qt * d.bq + (rho & (d.bq - 1)), hh = rho >> lbq;
     const bool valid = pos < d.S;
     const size_t row = ((size_t)b * d.H + hh) * d.S + pos;
@@ -498,28 +506,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
         }
       }
 #pragma unroll
-      for (int v4 = 0; v4 < 8; ++v4) x[v4] = fast_exp2(x[v4]);
-      if constexpr (STORE) {
-        float y[8];
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          y[v4] = x[v4] * (pc[0][v4] - dl) * scale;
-          y[4 + v4] = x[4 + v4] * (pc[1][v4] - dl) * scale;
-        }
-        char *blk = pds + (size_t)(eb + it) * (2 * (size_t)d.pds_rows * 64) +
-                    (size_t)rho * 64 + ((g ^ ((rho >> 3) & 3)) << 4);
-        // Non-temporal: the blocks are read back only by the next kernel, long
-        // after they have left the L2 (dQ 8.72 -> 8.61 ms at S = 65536).
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, pack8(x)),
-                                    reinterpret_cast<u32x4 *>(blk));
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, pack8(y)),
-                                    reinterpret_cast<u32x4 *>(blk + (size_t)d.pds_rows * 64));
-      }
-#pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        x[v4] = x[v4] * (pc[0][v4] - dl);
-        x[4 + v4] = x[4 + v4] * (pc[1][v4] - dl);
+        x[v4] = fast_exp2(x[v4]) * (pc[0][v4] - dl);
+        x[4 + v4] = fast_exp2(x[4 + v4]) * (pc[1][v4] - dl);
       }
       const bf16x8 dsb = pack8(x);
       __builtin_amdgcn_sched_barrier(0);
@@ -591,9 +580,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
       // least kRowLoads vector-memory loads after it (its list, row-interval
       // and LSE loads, then the row fragments).  Loads complete in issue
       // order, so leaving kRowLoads outstanding still waits for the copy while
-      // the row loads stay in flight (with STORE, the two stores of the tile
-      // above also count: they only make the wait stricter).  The barrier
-      // orders LDS only.
+      // the row loads stay in flight.  The barrier orders LDS only.
       asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kRowLoads) : "memory");
       lds_barrier();
       ent = ent_last;
@@ -626,7 +613,309 @@ __global__ void __launch_bounds__(NW * 64, 1)
   }
 }
 
+// ---------------------------------------------------------------------------
+// 1c. Stored-P backward at D = 512, first pass: P and dS only.  With 64-key
+//     key tiles the key-stationary pass reads P and dS from the backward
+//     workspace, and dQ = scale sum_k dS kv_k is formed by a second streaming
+//     pass (1d) from the same stored dS, so this pass carries no dQ
+//     accumulator: Q and dO fragments (128 registers) and the scores fit in
+//     256 registers and two workgroups run per CU.  A workgroup is one slice
+//     of 64 rows (4 waves x 16 consecutive positions of one head) of a query
+//     tile; it walks the tile's list, K tiles double-buffered in LDS (copied
+//     from the tile images), S^T and dP^T from shared K fragments, delta from
+//     O and dO.  P and scale dS of tile t (bf16) are stored by each lane as
+//     one 16-byte non-temporal store each, issued at the top of tile t + 1
+//     so the tile-end wait does not wait for them: list entry e of the query
+//     tile owns the block pds + e * 2 R * 64 bytes (R = bq H rows), P rows
+//     then dS rows, 64 bytes per row, chunk c of row rho at position
+//     c ^ ((rho >> 3) & 3).
+// ---------------------------------------------------------------------------
+template <int NW, bool MASKED>
+__global__ void __launch_bounds__(NW * 64, 8 / NW)
+    hca_bwd_pds512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
+                          const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
+                          const bf16raw *__restrict__ o, const float *__restrict__ lse,
+                          const bf16raw *__restrict__ dout, float scale_log2, float scale,
+                          float *__restrict__ delta, char *__restrict__ pds) {
+  constexpr int D = 512, KS = D / 32, M = NW * 16;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes512];  // K, double-buffered
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  const int nslices = d.bq * d.H / M;
+  const int lbq = __builtin_ctz(d.bq);
+  const int u = xcd_remap(blockIdx.x, d.B * d.nqt * nslices, 2 * nslices);
+  const int li = u / nslices, sl = u - li * nslices;
+  const int item = p.qorder[li];
+  const int b = item / d.nqt, qt = item - b * d.nqt;
+  const int rho = sl * M + wave * 16 + j;
+  const int pos = qt * d.bq + (rho & (d.bq - 1)), hh = rho >> lbq;
+  const bool valid = pos < d.S;
+  const int pc = min(pos, d.S - 1);
+  const size_t row = ((size_t)b * d.H + hh) * d.S + pc;
+
+  const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
+  const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
+  auto entry = [&](int t) -> uint32_t {
+    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
+                  : uniform_load(p.qent, e_begin + t);
+  };
+  __builtin_amdgcn_s_waitcnt(0);
+  const rsrc_t r_img =
+      make_rsrc(kvt + (size_t)b * 2 * D * d.S_pad, (uint32_t)d.S_pad * D * 4);
+  const rsrc_t r_imgc =
+      make_rsrc(kvct + (size_t)b * 2 * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 4);
+  auto stage_k = [&](int t) {
+    if (t >= nent) return;
+    const uint32_t ent = entry(t);
+    stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 0,
+                     smem + (t & 1) * kTileBytes512, wave, lane);
+  };
+  stage_k(0);
+
+  // Rows (padded rows read row S - 1; their intervals are empty, so their P
+  // and dS are zero), delta from O and dO.
+  const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pc];
+  const float lv = lse[row];
+  uint4 qv[KS], dv[KS];
+  float part = 0.f;
+  {
+    const bf16raw *qr = q + row * D + 8 * g, *dr = dout + row * D + 8 * g, *orow = o + row * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qv[ks] = *reinterpret_cast<const uint4 *>(qr + 32 * ks);
+      dv[ks] = *reinterpret_cast<const uint4 *>(dr + 32 * ks);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      part += dot8(dv[ks], *reinterpret_cast<const uint4 *>(orow + 32 * ks));
+  }
+  const float dl = group_sum(part);
+  if (valid && g == 0) delta[row] = dl;
+  const int rlo = valid ? rw.x : INT_MAX;
+  const int clo = valid ? rw.y : 0;
+  const int chi = valid ? rw.z : 0;
+  const float lse2 = valid ? lv * kLog2e : -INFINITY;
+  wait_all_loads();
+  __syncthreads();
+
+  const int frag_off = 16 * lane;
+  const size_t blk_bytes = 2 * (size_t)d.pds_rows * 64;
+  char *const prow = pds + (size_t)rho * 64 + ((g ^ ((rho >> 3) & 3)) << 4);
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 pend_p = {0u, 0u, 0u, 0u}, pend_s = {0u, 0u, 0u, 0u};
+  auto put = [&](int t) {  // P and dS of tile t, held since it was formed
+    char *blk = prow + (size_t)(e_begin + t) * blk_bytes;
+    __builtin_nontemporal_store(pend_p, reinterpret_cast<u32x4 *>(blk));
+    __builtin_nontemporal_store(pend_s, reinterpret_cast<u32x4 *>(blk + (size_t)d.pds_rows * 64));
+  };
+  for (int it = 0; it < nent; ++it) {
+    if (it > 0) put(it - 1);
+    stage_k(it + 1);
+    const uint32_t ent = entry(it);
+    uint32_t mw = 0u;
+    if constexpr (MASKED) {
+      if ((ent & kEntComp) && !(ent & kEntFull) && valid)
+        mw = p.cmask[((size_t)b * d.S + pos) * d.cmask_ldw + (ent & kEntIdx)];
+    }
+    // S^T and dP^T of tile it (shared K A-operands), K fragments read three
+    // k-steps ahead of their MFMAs.
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+    {
+      constexpr int PF = 3;
+      const char *kb = smem + (it & 1) * kTileBytes512 + frag_off;
+      bf16x8 a0[KS], a1[KS];
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) {
+        a0[ks] = lds_frag(kb + 2048 * ks);
+        a1[ks] = lds_frag(kb + 2048 * ks + 1024);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) {
+          a0[ks + PF] = lds_frag(kb + 2048 * (ks + PF));
+          a1[ks + PF] = lds_frag(kb + 2048 * (ks + PF) + 1024);
+        }
+        s0 = mfma16x16x32(a0[ks], as_bf16x8(qv[ks]), s0);
+        s1 = mfma16x16x32(a1[ks], as_bf16x8(qv[ks]), s1);
+        p0 = mfma16x16x32(a0[ks], as_bf16x8(dv[ks]), p0);
+        p1 = mfma16x16x32(a1[ks], as_bf16x8(dv[ks]), p1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+    }
+    // P = 2^(S scale log2e - LSE log2e) on visible keys, dS = scale P (dP - delta).
+    {
+      const bool comp = ent & kEntComp;
+      const int k0 = (int)(ent & kEntIdx) * kBK;
+      float x[8], y[8];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[v] = s0[v] * scale_log2 - lse2;
+        x[4 + v] = s1[v] * scale_log2 - lse2;
+      }
+      if (!(ent & kEntFull)) {
+        if (MASKED && comp) {
+          const uint32_t bits = mw >> (8 * g);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = ((bits >> t) & 1u) ? x[t] : -INFINITY;
+        } else {
+          const int lo = (comp ? clo : rlo) - (k0 + 8 * g);
+          const int hi = (comp ? chi : pos + 1) - (k0 + 8 * g);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = (t >= lo && t < hi) ? x[t] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[v] = fast_exp2(x[v]);
+        x[4 + v] = fast_exp2(x[4 + v]);
+        y[v] = x[v] * (p0[v] - dl) * scale;
+        y[4 + v] = x[4 + v] * (p1[v] - dl) * scale;
+      }
+      pend_p = __builtin_bit_cast(u32x4, pack8(x));
+      pend_s = __builtin_bit_cast(u32x4, pack8(y));
+    }
+    wait_all_loads();  // K of tile it + 1 (and the stores of tile it - 1)
+    __syncthreads();   // K buffer it & 1 free
+  }
+  if (nent > 0) put(nent - 1);
+}
+
+// ---------------------------------------------------------------------------
+// 1d. Stored-P backward at D = 512, second pass: dQ = sum over the listed
+//     tiles of (scale dS) K, streamed from the stored dS.  A workgroup is a
+//     slice of M = 16 NW rows of a query tile.  The product is split over D:
+//     wave w accumulates dQ^T for columns (512 / NW) w .. of all M rows (128
+//     registers), so each K^T fragment it reads from LDS feeds M / 16 MFMAs;
+//     the dS B fragments are the stored rows themselves, copied to LDS with
+//     the K^T tile (double-buffered) and read in place.  dQ is staged in LDS
+//     at the end and stored as whole rows.
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW)
+    hca_bwd_dqs512_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ kvt,
+                          const bf16raw *__restrict__ kvct, const char *__restrict__ pds,
+                          bf16raw *__restrict__ dq) {
+  constexpr int D = 512, M = NW * 16, RB = M / 16, CB = D / 16 / NW;
+  constexpr int DSB = M * 64;                   // the slice's dS rows of one tile
+  constexpr int STAGE = kTileBytes512 + DSB;    // K^T | dS
+  constexpr int NST = HCA_DQS_STAGES;           // stages in flight
+  constexpr int SMEM = NST * STAGE > M * 1024 ? NST * STAGE : M * 1024;
+  constexpr int kCopies = 32 / NW + 1;          // copies per wave and stage
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];  // NST stages; dQ rows at the end
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  const int nslices = d.bq * d.H / M;
+  const int lbq = __builtin_ctz(d.bq);
+  const int u = xcd_remap(blockIdx.x, d.B * d.nqt * nslices, 2 * nslices);
+  const int li = u / nslices, sl = u - li * nslices;
+  const int item = p.qorder[li];
+  const int b = item / d.nqt, qt = item - b * d.nqt;
+  const int e_begin = p.qptr[item], nent = p.qptr[item + 1] - e_begin;
+  const uint32_t ent_lane = lane < nent ? p.qent[e_begin + lane] : 0u;
+  auto entry = [&](int t) -> uint32_t {
+    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
+                  : uniform_load(p.qent, e_begin + t);
+  };
+  __builtin_amdgcn_s_waitcnt(0);
+  const rsrc_t r_img =
+      make_rsrc(kvt + (size_t)b * 2 * D * d.S_pad, (uint32_t)d.S_pad * D * 4);
+  const rsrc_t r_imgc =
+      make_rsrc(kvct + (size_t)b * 2 * D * d.Sc_pad, (uint32_t)d.Sc_pad * D * 4);
+  const size_t blk_bytes = 2 * (size_t)d.pds_rows * 64;
+  // Stage of tile t: its K^T tile, and the slice's rows of its stored dS
+  // (M x 64 bytes, contiguous; wave w copies rows 16 w .. 16 w + 15).
+  auto stage = [&](int t) {
+    if (t >= nent) return;
+    const uint32_t ent = entry(t);
+    char *st = smem + (t % NST) * STAGE;
+    stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 1, st,
+                     wave, lane);
+    dma16(pds + (size_t)(e_begin + t) * blk_bytes + (size_t)d.pds_rows * 64 +
+              (size_t)(sl * M + 16 * wave) * 64,
+          16 * lane, lds_addr(st + kTileBytes512 + wave * 1024));
+  };
+
+  floatx4 acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int c = 0; c < CB; ++c) acc[rb][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Stages of tiles 0 .. NST - 2 go out first; tile it + NST - 1 is copied at
+  // the top of iteration it, into the stage tile it - 1 used.
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) stage(t);
+  const int frag_off = 16 * lane;
+  // dS B fragment of row block rb: row 16 rb + j, stored chunk g at position
+  // g ^ ((row >> 3) & 3) (the slice starts on a multiple of 64 rows).
+  auto ds_off = [&](int rb) { return rb * 1024 + j * 64 + ((g ^ ((2 * rb + (j >> 3)) & 3)) << 4); };
+  for (int it = 0; it < nent; ++it) {
+    // This wave's copies of tile it have landed once at most the later
+    // stages' copies are outstanding (copies complete in issue order); the
+    // barrier covers the other waves' and frees the stage tile it - 1 used.
+    const int later = min(NST - 2, nent - 1 - it);
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * kCopies) : "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kCopies) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    stage(it + NST - 1);
+    const char *st = smem + (it % NST) * STAGE;
+    const char *tb = st + wave * CB * 1024 + frag_off;
+    bf16x8 kt[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) kt[c] = lds_frag(tb + c * 1024);
+    bf16x8 df = lds_frag(st + kTileBytes512 + ds_off(0));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bf16x8 cur = df;
+      if (rb + 1 < RB) df = lds_frag(st + kTileBytes512 + ds_off(rb + 1));
+#pragma unroll
+      for (int c = 0; c < CB; ++c) acc[rb][c] = mfma16x16x32(kt[c], cur, acc[rb][c]);
+    }
+  }
+  __syncthreads();  // every stage read before the rows are staged over them
+
+  // dQ rows as bf16 into LDS (row r at r * 1024, chunk c at c ^ (r & 15)),
+  // then every wave stores 16 whole rows.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * 16 + j;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      ushort4 w;
+      w.x = f2bf(acc[rb][c][0]);
+      w.y = f2bf(acc[rb][c][1]);
+      w.z = f2bf(acc[rb][c][2]);
+      w.w = f2bf(acc[rb][c][3]);
+      const int chunk = 2 * (CB * wave + c) + (g >> 1);
+      *reinterpret_cast<ushort4 *>(smem + r * 1024 + ((chunk ^ j) << 4) + ((g & 1) << 3)) = w;
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int r = wave * 16 + i;
+    const int rr = sl * M + r;
+    const int pr = qt * d.bq + (rr & (d.bq - 1)), hr = rr >> lbq;
+    if (pr < d.S) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(smem + r * 1024 + ((lane ^ (r & 15)) << 4));
+      *reinterpret_cast<uint4 *>(dq + (((size_t)b * d.H + hr) * d.S + pr) * D + 8 * lane) = v;
+    }
+  }
+}
+
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+
 
 // Transposed A operand of an MFMA from two ds_read_b64_tr_b16 reads: the
 // second read is `four_rows` bytes after the first (four rows further down a
@@ -1358,12 +1647,6 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
                        (const bf16raw *)kvct, (const bf16raw *)o, lse, (const bf16raw *)dout, sl2,
                        scale, (bf16raw *)dq, delta);
   };
-  auto go512 = [&](auto kernel, int groups) {
-    hipLaunchKernelGGL(kernel, dim3(groups), dim3(256), 0, s, d, p, (const bf16raw *)q,
-                       (const bf16raw *)kv, (const bf16raw *)kvc, (const bf16raw *)kvt,
-                       (const bf16raw *)kvct, (const bf16raw *)o, lse, (const bf16raw *)dout, sl2,
-                       scale, (bf16raw *)dq, delta, (char *)pds);
-  };
   switch (d.D) {
     case 512: {
       // Persistent: one workgroup per compute unit (each takes 128 KiB of
@@ -1372,13 +1655,30 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
       const int cus = compute_units();
       if (cus <= 0) return (int)hipErrorInvalidDevice;
       const int grid = units < cus ? units : cus;
-      if (d.pds_rows && !pds) return (int)hipErrorInvalidValue;
+      if (d.pds_rows) {
+        // Stored P / dS: P and dS pass, then the streaming dQ pass.
+        if (!pds) return (int)hipErrorInvalidValue;
+        constexpr int PW = HCA_PDS_NW, QW = HCA_DQS_NW;
+        const int pu = d.B * d.nqt * (d.bq * d.H / (16 * PW));
+        const int qu = d.B * d.nqt * (d.bq * d.H / (16 * QW));
+        auto gp2 = [&](auto kernel) {
+          hipLaunchKernelGGL(kernel, dim3(pu), dim3(PW * 64), 0, s, d, p, (const bf16raw *)q,
+                             (const bf16raw *)kvt, (const bf16raw *)kvct, (const bf16raw *)o,
+                             lse, (const bf16raw *)dout, sl2, scale, delta, (char *)pds);
+        };
+        if (d.cmask_ldw)
+          gp2(hca_bwd_pds512_kernel<PW, true>);
+        else
+          gp2(hca_bwd_pds512_kernel<PW, false>);
+        hipLaunchKernelGGL(hca_bwd_dqs512_kernel<QW>, dim3(qu), dim3(QW * 64), 0, s, d, p,
+                           (const bf16raw *)kvt, (const bf16raw *)kvct, (const char *)pds,
+                           (bf16raw *)dq);
+        break;
+      }
       if (d.cmask_ldw)
-        d.pds_rows ? go512(hca_bwd_dq512_kernel<4, true, true>, grid)
-                   : go512(hca_bwd_dq512_kernel<4, true, false>, grid);
+        go(hca_bwd_dq512_kernel<4, true>, 4, grid);
       else
-        d.pds_rows ? go512(hca_bwd_dq512_kernel<4, false, true>, grid)
-                   : go512(hca_bwd_dq512_kernel<4, false, false>, grid);
+        go(hca_bwd_dq512_kernel<4, false>, 4, grid);
       break;
     }
     case 128: go(hca_bwd_dq_kernel<128, 8, 1>, 8, d.B * d.nqt * (d.bq * d.H / 128)); break;
