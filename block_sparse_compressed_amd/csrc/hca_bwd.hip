@@ -1119,8 +1119,9 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *p) { return tr_frag_rows(p
 //     over all 128 keys (128 accumulation registers), so each wave needs at
 //     most 256 registers and a SIMD runs two waves.  (A four-wave version,
 //     32 score keys and 256 accumulators per wave, one wave per SIMD, ran
-//     8.9 ms at S = 65536 against 8.6 for this one.)  Plans from a given
-//     mask use this kernel by default; plans from the rule use 2c.  Items over
+//     8.9 ms at S = 65536 against 8.6 for this one.)  Used with 128-key
+//     tiles (plans whose stored P / dS would pass the planner's budget, or
+//     kv_keys = 128); 64-key plans use 2c.  Items over
 //     all keys of their tile and items over one 64-key half run in the same
 //     launch (a wave-uniform branch per item), so both kinds
 //     stream the rows of one chunk together through the L2.

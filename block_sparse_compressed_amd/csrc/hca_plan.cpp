@@ -93,18 +93,16 @@ int classify_tile_mask(const uint8_t *m, int64_t S, int64_t Sc, int64_t qt, int 
 }  // namespace
 
 // Keys per key tile of the key-stationary backward (a work item covers one
-// tile).  Head dim 512, bf16: 64 for plans from the rule -- the backward then
-// stores P and dS in the dQ pass and the key-stationary pass reads them (see
-// the key-tile section of build_plan; above kPdsBudget of stored tiles the
-// library's choice falls back to 128); 128 (recomputing S and dP) for plans
-// from a given mask, whose scattered entries list nearly every tile pair, so
-// a store would be large and wider tiles stream each query row half as often.
-// Other kernels: the forward's 32-key tile.  `want` (the tile configuration's
+// tile).  Head dim 512, bf16: 64 -- the backward then stores P and dS in its
+// first pass and the key-stationary pass reads them (see the key-tile section
+// of build_plan; above kPdsBudget of stored tiles the library's choice falls
+// back to 128, which recomputes S and dP with an O(S) workspace).  Other
+// kernels: the forward's 32-key tile.  `want` (the tile configuration's
 // kv_keys) overrides where the width has a kernel; 0 if it has none.
 constexpr uint64_t kPdsBudget = 32ull << 30;  // bytes of stored P and dS, library choice
-static int kv_tile_keys(int dtype, int D, bool masked, int want) {
+static int kv_tile_keys(int dtype, int D, int want) {
   if (dtype == HCA_BF16 && D == 512) {
-    if (want == 0) return masked ? 128 : 64;
+    if (want == 0) return 64;
     return want == 64 || want == 128 ? want : 0;
   }
   return want == 0 || want == 32 ? 32 : 0;
@@ -266,7 +264,7 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
   default_tiles(dtype, D, H, &bq, &bkr, &bkc);
   int64_t half_min = kHalfItemsMin;
   int64_t comp_chunks_cfg = 0;
-  const int kv_keys = kv_tile_keys(dtype, D, cmask != nullptr, tiles ? tiles->kv_keys : 0);
+  const int kv_keys = kv_tile_keys(dtype, D, tiles ? tiles->kv_keys : 0);
   if (kv_keys == 0) {
     set_error(F + ": kv_keys must be 0, 64 or 128 at head dim 512 bfloat16, else 0 or 32");
     return HCA_ERR_INVALID_ARG;

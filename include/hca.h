@@ -88,10 +88,9 @@ enum { HCA_TILE_EMPTY = 0, HCA_TILE_PARTIAL = 1, HCA_TILE_FULL = 2 };
  *                     stationary pass reads them instead of recomputing S and
  *                     dP: faster, with a workspace of O(S (W + S / r)).  With
  *                     128 both are recomputed and the workspace is O(S).
- *                     Library choice: 64 for plans built from the rule while
- *                     the store needs at most 32 GiB, else 128; 128 for plans
- *                     built from a given mask.  Other kernels: 32.  Any other
- *                     value is rejected.
+ *                     Library choice: 64 while the store needs at most 32
+ *                     GiB, else 128.  Other kernels: 32.  Any other value is
+ *                     rejected.
  *   half_items_min    with 128-key items (head dim 512, bfloat16): an item whose
  *                     rows see only one 64-key half of its key tile runs over
  *                     that half alone once the plan has at least this many

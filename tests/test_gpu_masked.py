@@ -70,10 +70,11 @@ def check_against_oracle(name, B, S, H, W, Sc, mask, lengths, plan, seed):
         assert not torch.isnan(t).any()
 
 
-@pytest.mark.parametrize("density,kv_keys", [(0.05, 0), (0.5, 0), (0.05, 64)])
+@pytest.mark.parametrize("density,kv_keys", [(0.05, 0), (0.5, 0), (0.05, 128)])
 def test_random_mask_every_element(density, kv_keys):
-    """Random masks over ragged documents; kv_keys = 64 runs the masked plan
-    through the 64-key key-stationary kernel instead of the 128-key one."""
+    """Random masks over ragged documents; the library's choice stores P and dS
+    (64-key tiles), kv_keys = 128 runs the recomputing 128-key backward with
+    the mask bits."""
     rng = np.random.default_rng(int(density * 1000))
     B, S, H, W, Sc = 1, 523, 64, 96, 150
     lengths = [random_lengths(rng, S, 60, 300)]
@@ -81,8 +82,8 @@ def test_random_mask_every_element(density, kv_keys):
     starts, counts = starts_csr(lengths, B)
     plan = hca.hca_block_mask_build_masked(B, S, W, Sc, mask, starts, counts, H=H, D=512,
                                            tiles=(0, 0, 0, 0, 0, kv_keys))
-    assert hca.hca_plan_get_info(plan).kv_keys == (kv_keys or 128)
-    check_against_oracle(f"masked_d{density}_k{kv_keys or 128}", B, S, H, W, Sc, mask, lengths,
+    assert hca.hca_plan_get_info(plan).kv_keys == (kv_keys or 64)
+    check_against_oracle(f"masked_d{density}_k{kv_keys or 64}", B, S, H, W, Sc, mask, lengths,
                          plan, seed=41)
 
 

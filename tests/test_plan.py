@@ -295,11 +295,11 @@ def test_half_items_knob():
 
 
 def test_kv_keys_choice():
-    """Key tile width of the key-stationary backward: 64 keys for D = 512
-    plans from the rule, 128 for plans from a given mask, 32 at other head
-    dims; kv_keys overrides it where a kernel of that width exists.  64-key
-    items always run over their whole tile (no half marks), and their partial
-    blocks are 64 x D."""
+    """Key tile width of the key-stationary backward: 64 keys at D = 512 (plans
+    from the rule or from a given mask), 32 at other head dims; kv_keys
+    overrides it where a kernel of that width exists.  64-key items always run
+    over their whole tile (no half marks), and their partial blocks are
+    64 x D."""
     S, H, r, W = 1536, 8, 16, 128
     rule, prob = build_both(1, S, H, 512, r, W, None, hca.HCA_COMPSEG_STRICT)
     info = hca.hca_plan_get_info(rule)
@@ -322,10 +322,11 @@ def test_kv_keys_choice():
     mask[0, :, ::3] = 1
     masked = hca.hca_block_mask_build_masked(1, S, W, S // r, mask, None, None, H, 512,
                                              hca.HCA_BF16)
-    assert hca.hca_plan_get_info(masked).kv_keys == 128
-    masked64 = hca.hca_block_mask_build_masked(1, S, W, S // r, mask, None, None, H, 512,
-                                               hca.HCA_BF16, tiles=(0, 0, 0, 0, 0, 64))
-    assert hca.hca_plan_get_info(masked64).kv_keys == 64
+    assert hca.hca_plan_get_info(masked).kv_keys == 64
+    masked128 = hca.hca_block_mask_build_masked(1, S, W, S // r, mask, None, None, H, 512,
+                                                hca.HCA_BF16, tiles=(0, 0, 0, 0, 0, 128))
+    info128 = hca.hca_plan_get_info(masked128)
+    assert info128.kv_keys == 128 and info128.ws_pds_bytes == 0
     d128 = hca.hca_block_mask_build(1, S, r, W, S // r, None, None, H, 128, hca.HCA_BF16)
     assert hca.hca_plan_get_info(d128).kv_keys == 32
     # the library's 64-key choice stores P / dS only while that takes <= 32 GiB
