@@ -28,6 +28,9 @@ namespace hca {
 
 constexpr int kBK = 32;  // keys per tile (raw and compressed)
 
+#ifndef HCA_FWD_NW
+#define HCA_FWD_NW 8  // waves of the D = 512 forward: 8 (one workgroup per CU) or 4 (two)
+#endif
 #ifndef HCA_FWD_QK_PF
 #define HCA_FWD_QK_PF 3  // k-steps of K fragments in flight ahead of the S^T MFMAs
 #endif
@@ -269,30 +272,34 @@ constexpr float kLazy = 8.f;
 // ---------------------------------------------------------------------------
 // D = 512 forward with the PV product split over the head dimension.
 // ---------------------------------------------------------------------------
-// Eight waves, 128 rows per workgroup (one workgroup per CU, two waves per
-// SIMD), K and K^T double-buffered (128 KiB).  The scores stay row-blocked:
-// wave w holds the Q fragments of rows 16 w .. 16 w + 15 and forms their S^T
-// and softmax.  The PV product is split over D instead: wave w accumulates
-// O^T for columns 64 w .. 64 w + 63 of all 128 rows, so each K^T fragment it
-// reads from LDS feeds eight MFMAs (one per row block) instead of one.  P goes
-// through LDS (one 1 KiB fragment per wave and tile, double-buffered), with
-// each row's lazy-rescale factor.  Per wave and tile the LDS reads fall from
-// 64 KiB (32 K and 32 K^T fragments) to 44 KiB (32 K, 4 K^T, 8 P fragments),
-// and one tile copy serves 128 rows instead of 64.
-template <bool MASKED>
-__global__ void __launch_bounds__(512, 1)
+// NW waves, 16 NW rows per workgroup.  NW = 4 (the default): two workgroups
+// per CU, K and K^T single-buffered (64 KiB), so one workgroup's copies and
+// barriers run under the other's math; NW = 8: one workgroup per CU, K and
+// K^T double-buffered (128 KiB), one barrier per tile.  The scores stay
+// row-blocked: wave w holds the Q fragments of rows 16 w .. 16 w + 15 and
+// forms their S^T and softmax.  The PV product is split over D instead: wave
+// w accumulates O^T for columns (512 / NW) w .. of all the workgroup's rows,
+// so each K^T fragment it reads from LDS feeds NW MFMAs (one per row block)
+// instead of one.  P goes through LDS (one 1 KiB fragment per wave and tile,
+// double-buffered), with each row's lazy-rescale factor.  Per wave and tile
+// the LDS reads fall from 64 KiB (32 K and 32 K^T fragments) to 44 KiB
+// (NW = 8: 32 K, 4 K^T, 8 P fragments; NW = 4: 32 K, 8 K^T, 4 P).
+template <int NW, bool MASKED>
+__global__ void __launch_bounds__(NW * 64, 8 / NW)
     hca_fwd512s_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                        const bf16raw *__restrict__ kvt, const bf16raw *__restrict__ kvct,
                        float scale_log2, bf16raw *__restrict__ o, float *__restrict__ lse) {
-  constexpr int D = 512, KS = D / 32, NW = 8, M = 128, RB = M / 16, CB = D / 16 / NW;
-  // [K 0][K 1][K^T 0][K^T 1]; after the tile walk, the output rows.
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes512];
+  constexpr int D = 512, KS = D / 32, M = NW * 16, RB = M / 16, CB = D / 16 / NW;
+  // NW = 8: [K 0][K 1][K^T 0][K^T 1], NW = 4: [K][K^T]; after the tile walk,
+  // the output rows.
+  constexpr int kBufs = NW == 8 ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufs * kTileBytes512];
   __shared__ __attribute__((aligned(1024))) char pbuf[2][RB * 1024];  // P fragments per row block
   __shared__ float alpha_s[2][M];  // per row: O rescale factor of the tile
   __shared__ int resc_s[2][RB];    // per row block: any row rescaled in the tile
   __shared__ float inv_s[M];       // per row: 1 / l
   char *const kbase = smem;
-  char *const tbase = smem + 2 * kTileBytes512;
+  char *const tbase = smem + kBufs * kTileBytes512;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
@@ -323,13 +330,13 @@ __global__ void __launch_bounds__(512, 1)
     if (t >= nent) return;
     const uint32_t ent = entry(t);
     stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 0,
-                     kbase + (t & 1) * kTileBytes512, wave, lane);
+                     kbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
   };
   auto stage_t = [&](int t) {
     if (t >= nent) return;
     const uint32_t ent = entry(t);
     stage_img512<NW>((ent & kEntComp) ? r_imgc : r_img, (int)(ent & kEntIdx) * kBK, 1,
-                     tbase + (t & 1) * kTileBytes512, wave, lane);
+                     tbase + (t & (kBufs - 1)) * kTileBytes512, wave, lane);
   };
   const int frag_off = 16 * lane;
 
@@ -353,7 +360,7 @@ __global__ void __launch_bounds__(512, 1)
   // QK_PF k-steps ahead of their MFMAs.
   auto qk = [&](int t, floatx4 (&s)[2]) {
     constexpr int PF = HCA_FWD_QK_PF;
-    const char *kb = kbase + (t & 1) * kTileBytes512 + frag_off;
+    const char *kb = kbase + (t & (kBufs - 1)) * kTileBytes512 + frag_off;
     s[0] = s[1] = floatx4{0.f, 0.f, 0.f, 0.f};
     bf16x8 a0[KS], a1[KS];
 #pragma unroll
@@ -444,18 +451,15 @@ __global__ void __launch_bounds__(512, 1)
     for (int c = 0; c < CB; ++c) oacc[rb][c] = floatx4{0.f, 0.f, 0.f, 0.f};
   auto pv = [&](int t) {
     const int bf = t & 1;
-    const int4 f0 = *reinterpret_cast<const int4 *>(&resc_s[bf][0]);
-    const int4 f1 = *reinterpret_cast<const int4 *>(&resc_s[bf][4]);
-    const int fl[RB] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      if (__builtin_amdgcn_readfirstlane(fl[rb])) {
+      if (__builtin_amdgcn_readfirstlane(resc_s[bf][rb])) {
         const float a = alpha_s[bf][rb * 16 + j];
 #pragma unroll
         for (int c = 0; c < CB; ++c) oacc[rb][c] *= a;
       }
     }
-    const char *tb = tbase + bf * kTileBytes512 + wave * CB * 1024 + frag_off;
+    const char *tb = tbase + (t & (kBufs - 1)) * kTileBytes512 + wave * CB * 1024 + frag_off;
     const char *pb = pbuf[bf] + frag_off;
     bf16x8 kt[CB], pf[RB];
 #pragma unroll
@@ -476,35 +480,69 @@ __global__ void __launch_bounds__(512, 1)
     }
   };
 
-  // K runs two tiles ahead, K^T one; the S^T of tile t + 1 is issued before
-  // the PV of tile t, its softmax after; one barrier per tile.
-  stage_k(0);
-  stage_k(1);
-  stage_t(0);
-  load_q();
-  wait_all_loads();
-  __syncthreads();
   floatx4 sc[2];
-  if (nent > 0) {
-    const uint32_t e0 = entry(0);
-    const uint32_t mw = load_mask(e0);
-    qk(0, sc);
-    softmax(0, sc, e0, mw);
-  }
-  __syncthreads();  // P of tile 0 visible; K buffer 0 free
-  stage_k(2);
-  stage_t(1);
-  for (int it = 0; it < nent; ++it) {
-    const bool more = it + 1 < nent;
-    const uint32_t en = more ? entry(it + 1) : 0u;
-    const uint32_t mw = load_mask(en);
-    if (more) qk(it + 1, sc);
-    pv(it);
-    if (more) softmax(it + 1, sc, en, mw);
+  if constexpr (NW == 8) {
+    // K runs two tiles ahead, K^T one; the S^T of tile t + 1 is issued before
+    // the PV of tile t, its softmax after; one barrier per tile.
+    stage_k(0);
+    stage_k(1);
+    stage_t(0);
+    load_q();
     wait_all_loads();
     __syncthreads();
-    stage_k(it + 3);
-    stage_t(it + 2);
+    if (nent > 0) {
+      const uint32_t e0 = entry(0);
+      const uint32_t mw = load_mask(e0);
+      qk(0, sc);
+      softmax(0, sc, e0, mw);
+    }
+    __syncthreads();  // P of tile 0 visible; K buffer 0 free
+    stage_k(2);
+    stage_t(1);
+    for (int it = 0; it < nent; ++it) {
+      const bool more = it + 1 < nent;
+      const uint32_t en = more ? entry(it + 1) : 0u;
+      const uint32_t mw = load_mask(en);
+      if (more) qk(it + 1, sc);
+      pv(it);
+      if (more) softmax(it + 1, sc, en, mw);
+      wait_all_loads();
+      __syncthreads();
+      stage_k(it + 3);
+      stage_t(it + 2);
+    }
+  } else {
+    // Single-buffered, two workgroups per CU: the K copy of tile t + 1 runs
+    // under the PV of tile t, the K^T copy of tile t + 1 under its scores and
+    // softmax; two barriers per tile.  The other workgroup covers the waits.
+    stage_k(0);
+    stage_t(0);
+    load_q();
+    wait_all_loads();
+    __syncthreads();
+    if (nent > 0) {
+      const uint32_t e0 = entry(0);
+      const uint32_t mw = load_mask(e0);
+      qk(0, sc);
+      softmax(0, sc, e0, mw);
+    }
+    __syncthreads();  // P of tile 0 visible; K buffer free
+    stage_k(1);
+    for (int it = 0; it < nent; ++it) {
+      pv(it);
+      wait_all_loads();  // K of tile it + 1
+      __syncthreads();   // K^T buffer free, K of tile it + 1 visible
+      if (it + 1 < nent) {
+        const uint32_t en = entry(it + 1);
+        const uint32_t mw = load_mask(en);
+        stage_t(it + 1);
+        qk(it + 1, sc);
+        softmax(it + 1, sc, en, mw);
+        wait_all_loads();  // K^T of tile it + 1
+        __syncthreads();   // K buffer free, K^T and P of tile it + 1 visible
+        stage_k(it + 2);
+      }
+    }
   }
 
   // Row statistics: 1 / l to LDS for every wave, LSE by the owner.
@@ -530,7 +568,7 @@ __global__ void __launch_bounds__(512, 1)
       w.y = f2bf(oacc[rb][c][1] * inv);
       w.z = f2bf(oacc[rb][c][2] * inv);
       w.w = f2bf(oacc[rb][c][3] * inv);
-      const int chunk = 8 * wave + 2 * c + (g >> 1);
+      const int chunk = 2 * (CB * wave + c) + (g >> 1);
       *reinterpret_cast<ushort4 *>(smem + r * 1024 + ((chunk ^ j) << 4) + ((g & 1) << 3)) = w;
     }
   }
@@ -659,16 +697,17 @@ int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *
   };
   switch (d.D) {
     case 512: {
-      // 128 rows per workgroup (bq * H is a power of two >= 128).
-      const dim3 gs(d.B * d.nqt * (d.bq * d.H / 128));
+      // 16 NW rows per workgroup (bq * H is a power of two >= 128).
+      constexpr int NW = HCA_FWD_NW;
+      const dim3 gs(d.B * d.nqt * (d.bq * d.H / (16 * NW)));
       auto gos = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, gs, dim3(512), 0, s, d, p, (const bf16raw *)q,
+        hipLaunchKernelGGL(kernel, gs, dim3(NW * 64), 0, s, d, p, (const bf16raw *)q,
                            (const bf16raw *)kvt, (const bf16raw *)kvct, sl2, (bf16raw *)o, lse);
       };
       if (d.cmask_ldw)
-        gos(hca_fwd512s_kernel<true>);
+        gos(hca_fwd512s_kernel<NW, true>);
       else
-        gos(hca_fwd512s_kernel<false>);
+        gos(hca_fwd512s_kernel<NW, false>);
       break;
     }
     case 128: args(hca_fwd_bf16_kernel<128, 8, 1>, 8); break;
