@@ -29,7 +29,7 @@ namespace hca {
 constexpr int kBK = 32;  // keys per tile (raw and compressed)
 
 #ifndef HCA_FWD_NW
-#define HCA_FWD_NW 8  // waves of the D = 512 forward: 8 (one workgroup per CU) or 4 (two)
+#define HCA_FWD_NW 4  // waves of the D = 512 forward: 4 (two workgroups per CU) or 8 (one)
 #endif
 #ifndef HCA_FWD_QK_PF
 #define HCA_FWD_QK_PF 3  // k-steps of K fragments in flight ahead of the S^T MFMAs
