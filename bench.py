@@ -37,8 +37,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 # profiles/hbm_traffic_<workload>.md.  MFMA and LDS utilisation from rocprofv3's
 # derived counters: "mfma:" JSON lines in profiles/mfma_util.md.
 MFMA_FILE = os.path.join(PROFILES, "mfma_util.md")
-KERNEL_SOURCES = {"fwd": "hca_fwd.hip", "bwd_dq": "hca_bwd.hip", "bwd_dkv": "hca_bwd.hip",
-                  "dkv_reduce": "hca_bwd.hip", "transpose": "hca_fwd.hip"}
+KERNEL_SOURCES = {"fwd": "hca_fwd.hip", "bwd_pds": "hca_bwd.hip", "bwd_dq": "hca_bwd.hip",
+                  "bwd_dkv": "hca_bwd.hip", "dkv_reduce": "hca_bwd.hip",
+                  "transpose": "hca_fwd.hip"}
 
 
 def source_hash(kernel):
@@ -293,13 +294,20 @@ def main():
     qb = wl.B * wl.H * wl.S * wl.D * e          # one [B,H,S,D] tensor
     kb = (wl.B * wl.S + wl.B * wl.Sc) * wl.D * e  # kv and kv_comp
     rb = 4 * wl.B * wl.H * wl.S                  # one fp32 value per row (LSE, delta)
+    DHP = wl.D * wl.H * P
     per_kernel = {  # kernel: (flops, bytes)
         "fwd": (fl_fwd, 2 * qb + kb + rb),                          # Q, K -> O, LSE
-        "bwd_dq": (6.0 * wl.D * wl.H * P, 4 * qb + kb + 2 * rb),    # Q, dO, O, LSE, K -> dQ, delta
-        "bwd_dkv": (4.0 * wl.D * wl.H * P, 2 * qb + kb + 2 * rb),   # Q, dO, LSE, delta, K
+        "bwd_dq": (6.0 * DHP, 4 * qb + kb + 2 * rb),                # Q, dO, O, LSE, K -> dQ, delta
+        "bwd_dkv": (4.0 * DHP, 2 * qb + kb + 2 * rb),               # Q, dO, LSE, delta, K
         "fwd_f32": (fl_fwd, 2 * qb + kb + rb),
-        "bwd_f32": (10.0 * wl.D * wl.H * P, 5 * qb + 2 * kb + rb),
+        "bwd_f32": (10.0 * DHP, 5 * qb + 2 * kb + rb),
     }
+    if info.ws_pds_bytes:
+        # Stored P / dS: the first pass forms S, dP, P and dS (Q, dO, O, LSE, K ->
+        # delta), the dQ pass only dQ = sum dS K (K -> dQ); the stored tiles are
+        # workspace, not algorithmic bytes.
+        per_kernel["bwd_pds"] = (4.0 * DHP, 3 * qb + kb + 2 * rb)
+        per_kernel["bwd_dq"] = (2.0 * DHP, qb + kb)
     kavg = {k: v[1] / v[0] for k, v in kernels.items() if v[0]}
     per_step = {k: kernels[k][1] / args.steps for k in kernels}
     dom = max((k for k in per_step if k in per_kernel), key=lambda k: per_step[k])

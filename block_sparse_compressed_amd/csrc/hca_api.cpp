@@ -86,9 +86,9 @@ hca_status check_common(const char *fn, const hca_plan *plan, float scale, void 
 
 // ---- kernel timing instrumentation ----------------------------------------
 enum KernelId { K_TRANSPOSE, K_FWD, K_BWD_DQ, K_BWD_DKV, K_DKV_REDUCE, K_FWD_F32, K_BWD_F32,
-                K_COUNT };
-const char *const kKernelNames[K_COUNT] = {"transpose", "fwd", "bwd_dq", "bwd_dkv",
-                                           "dkv_reduce", "fwd_f32", "bwd_f32"};
+                K_BWD_PDS, K_COUNT };
+const char *const kKernelNames[K_COUNT] = {"transpose", "fwd",     "bwd_dq",  "bwd_dkv",
+                                           "dkv_reduce", "fwd_f32", "bwd_f32", "bwd_pds"};
 struct TimingRec {
   int kid;
   hipEvent_t a, b;
@@ -288,6 +288,13 @@ extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const vo
                                d.Sc_pad, d.B, d.D, hip_stream);
   });
   if (err) return hip_fail("hca_attn_bwd (transpose)", err);
+  if (pds) {
+    err = timed(K_BWD_PDS, hip_stream, [&] {
+      return launch_bwd_pds_bf16(d, p, q, kvt, kvct, o, lse, dout, scale, delta, pds,
+                                 hip_stream);
+    });
+    if (err) return hip_fail("hca_attn_bwd (P / dS kernel)", err);
+  }
   err = timed(K_BWD_DQ, hip_stream, [&] {
     return launch_bwd_dq_bf16(d, p, q, kv, kvc, kvt, kvct, o, lse, dout, scale, dq, delta, pds,
                               hip_stream);

@@ -1657,20 +1657,10 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
       if (cus <= 0) return (int)hipErrorInvalidDevice;
       const int grid = units < cus ? units : cus;
       if (d.pds_rows) {
-        // Stored P / dS: P and dS pass, then the streaming dQ pass.
+        // Stored P / dS (written by launch_bwd_pds_bf16): the streaming dQ pass.
         if (!pds) return (int)hipErrorInvalidValue;
-        constexpr int PW = HCA_PDS_NW, QW = HCA_DQS_NW;
-        const int pu = d.B * d.nqt * (d.bq * d.H / (16 * PW));
+        constexpr int QW = HCA_DQS_NW;
         const int qu = d.B * d.nqt * (d.bq * d.H / (16 * QW));
-        auto gp2 = [&](auto kernel) {
-          hipLaunchKernelGGL(kernel, dim3(pu), dim3(PW * 64), 0, s, d, p, (const bf16raw *)q,
-                             (const bf16raw *)kvt, (const bf16raw *)kvct, (const bf16raw *)o,
-                             lse, (const bf16raw *)dout, sl2, scale, delta, (char *)pds);
-        };
-        if (d.cmask_ldw)
-          gp2(hca_bwd_pds512_kernel<PW, true>);
-        else
-          gp2(hca_bwd_pds512_kernel<PW, false>);
         hipLaunchKernelGGL(hca_bwd_dqs512_kernel<QW>, dim3(qu), dim3(QW * 64), 0, s, d, p,
                            (const bf16raw *)kvt, (const bf16raw *)kvct, (const char *)pds,
                            (bf16raw *)dq);
@@ -1686,6 +1676,26 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
     case 64: go(hca_bwd_dq_kernel<64, 8, 1>, 8, d.B * d.nqt * (d.bq * d.H / 128)); break;
     default: return (int)hipErrorInvalidValue;
   }
+  return (int)hipGetLastError();
+}
+
+int launch_bwd_pds_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kvt,
+                        const void *kvct, const void *o, const float *lse, const void *dout,
+                        float scale, float *delta, void *pds, void *stream) {
+  if (d.D != 512 || !d.pds_rows || !pds) return (int)hipErrorInvalidValue;
+  hipStream_t s = (hipStream_t)stream;
+  const float sl2 = scale * kLog2e;
+  constexpr int PW = HCA_PDS_NW;
+  const int pu = d.B * d.nqt * (d.bq * d.H / (16 * PW));
+  auto gp = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(pu), dim3(PW * 64), 0, s, d, p, (const bf16raw *)q,
+                       (const bf16raw *)kvt, (const bf16raw *)kvct, (const bf16raw *)o, lse,
+                       (const bf16raw *)dout, sl2, scale, delta, (char *)pds);
+  };
+  if (d.cmask_ldw)
+    gp(hca_bwd_pds512_kernel<PW, true>);
+  else
+    gp(hca_bwd_pds512_kernel<PW, false>);
   return (int)hipGetLastError();
 }
 

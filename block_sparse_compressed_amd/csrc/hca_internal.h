@@ -102,6 +102,11 @@ int launch_bwd_dq_bf16(const Dims &d, const DevPlan &p, const void *q, const voi
                        const void *kvc, const void *kvt, const void *kvct, const void *o,
                        const float *lse, const void *dout, float scale, void *dq, float *delta,
                        void *pds, void *stream);
+// Stored-P plans: the P / dS pass (launch_bwd_dq_bf16 then runs the streaming
+// dQ pass from the stored dS).
+int launch_bwd_pds_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kvt,
+                        const void *kvct, const void *o, const float *lse, const void *dout,
+                        float scale, float *delta, void *pds, void *stream);
 int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,
                         const void *kvc, const float *lse, const float *delta,
                         const void *dout, float scale, const void *pds, float *part,
