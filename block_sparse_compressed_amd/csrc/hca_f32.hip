@@ -18,13 +18,34 @@ namespace hca {
 
 namespace {
 
+// Sum over the 64 lanes, the result in every lane, without LDS round trips:
+// DPP within each 16-lane row (swap neighbours, swap pairs, mirror the half
+// row, mirror the row), then the gfx950 lane swaps across rows.  (A shuffle
+// ladder goes through the LDS crossbar once per step; with two sums per
+// visited key it was most of the float32 kernels' time.)
+template <int CTRL>
+__device__ __forceinline__ float dpp_plus(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, true));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  v = dpp_plus<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_plus<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_plus<0x141>(v);  // row_half_mirror
+  v = dpp_plus<0x140>(v);  // row_mirror
+  unsigned u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  u = __float_as_uint(v);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 }  // namespace
+
+// Loads of this many visits (keys of a row, heads of a position) are issued
+// together before any of them is used.
+constexpr int kBatch = 4;
 
 // Forward and dQ: one workgroup of kRowWaves wavefronts per query row; wave w
 // takes every kRowWaves-th visible key (raw window first, then compressed
@@ -54,13 +75,10 @@ __global__ void __launch_bounds__(kRowWaves * 64)
   }
   // Online softmax of this wave's keys (log2 units).
   float m = -INFINITY, l = 0.f;
-  auto visit = [&](const float *krow) {
-    float kr[NDU], s = 0.f;
+  auto visit = [&](const float (&kr)[NDU]) {
+    float s = 0.f;
 #pragma unroll
-    for (int u = 0; u < NDU; ++u) {
-      kr[u] = krow[lane + 64 * u];
-      s += qv[u] * kr[u];
-    }
+    for (int u = 0; u < NDU; ++u) s += qv[u] * kr[u];
     const float x = wave_sum(s) * scale_log2;
     const float mn = fmaxf(m, x);
     const float a = fast_exp2(m - mn), pr = fast_exp2(x - mn);
@@ -71,9 +89,23 @@ __global__ void __launch_bounds__(kRowWaves * 64)
   };
   const int nraw = max(i + 1 - rw.x, 0);
   const int nkeys = nraw + max(rw.z - rw.y, 0);
-  for (int n = wave; n < nkeys; n += kRowWaves)
-    visit(n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
-                   : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D);
+  // The wave's keys in order, kBatch rows loaded at a time.
+  for (int n0 = wave; n0 < nkeys; n0 += kBatch * kRowWaves) {
+    float kr[kBatch][NDU];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int n = n0 + t * kRowWaves;
+      if (n < nkeys) {
+        const float *krow = n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
+                                     : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D;
+#pragma unroll
+        for (int u = 0; u < NDU; ++u) kr[t][u] = krow[lane + 64 * u];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t)
+      if (n0 + t * kRowWaves < nkeys) visit(kr[t]);
+  }
   // Merge: M = max m_w, L = sum l_w 2^(m_w - M), acc = sum acc_w 2^(m_w - M).
 #pragma unroll
   for (int u = 0; u < NDU; ++u) red_acc[wave][lane + 64 * u] = acc[u];
@@ -128,11 +160,10 @@ __global__ void __launch_bounds__(kRowWaves * 64)
   dl = wave_sum(dl);  // every wave computes delta; wave 0 stores it
   if (wave == 0 && lane == 0) delta[row] = dl;
   const float lse2 = lse[row] * kLog2e;
-  auto visit = [&](const float *krow) {
-    float kr[NDU], s = 0.f, t = 0.f;
+  auto visit = [&](const float (&kr)[NDU]) {
+    float s = 0.f, t = 0.f;
 #pragma unroll
     for (int u = 0; u < NDU; ++u) {
-      kr[u] = krow[lane + 64 * u];
       s += qv[u] * kr[u];
       t += dv[u] * kr[u];
     }
@@ -145,9 +176,24 @@ __global__ void __launch_bounds__(kRowWaves * 64)
   };
   const int nraw = max(i + 1 - rw.x, 0);
   const int nkeys = nraw + max(rw.z - rw.y, 0);
-  for (int n = wave; n < nkeys; n += kRowWaves)
-    visit(n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
-                   : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D);
+  // The wave's keys n = wave, wave + kRowWaves, ... in order, kBatch at a time:
+  // their rows are loaded together, so one load latency covers the batch.
+  for (int n0 = wave; n0 < nkeys; n0 += kBatch * kRowWaves) {
+    float kr[kBatch][NDU];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int n = n0 + t * kRowWaves;
+      if (n < nkeys) {
+        const float *krow = n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
+                                     : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D;
+#pragma unroll
+        for (int u = 0; u < NDU; ++u) kr[t][u] = krow[lane + 64 * u];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t)
+      if (n0 + t * kRowWaves < nkeys) visit(kr[t]);
+  }
   if (wave > 0) {
 #pragma unroll
     for (int u = 0; u < NDU; ++u) red_acc[wave - 1][lane + 64 * u] = acc[u];
@@ -203,26 +249,51 @@ __global__ void __launch_bounds__(kDkvWaves * 64)
     i0 = k;
     i1 = d.W > 0 ? min(d.S - 1, k + d.W - 1) : k - 1;
   }
-  for (int i = i0 + wave; i <= i1; i += kDkvWaves) {
-    const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + i];
-    const bool vis = comp ? (rw.y <= k && k < rw.z) : (rw.x <= k);
-    if (!vis) continue;
-    for (int h = 0; h < d.H; ++h) {
-      const size_t row = ((size_t)b * d.H + h) * d.S + i;
-      float qv[NDU], dv[NDU], s = 0.f, t = 0.f;
+  // The wave's (position, head) visits in order -- positions i0 + wave,
+  // i0 + wave + kDkvWaves, ..., all heads of each -- VB at a time: the rows'
+  // visible intervals, Q and dO rows, LSE and delta of a batch are loaded
+  // together, so one load latency covers the batch (fewer for wide heads: a
+  // 16-wave workgroup has 128 registers per lane).  A position that does not
+  // see key k adds nothing.
+  constexpr int VB = NDU <= 1 ? 8 : NDU <= 2 ? 4 : NDU <= 4 ? 2 : 1;
+  const int npos = i1 >= i0 + wave ? (i1 - i0 - wave) / kDkvWaves + 1 : 0;
+  const int nvis = npos * d.H;
+  for (int v0 = 0; v0 < nvis; v0 += VB) {
+    float qv[VB][NDU], dv[VB][NDU], ls[VB], dt[VB];
+    bool on[VB];
+#pragma unroll
+    for (int t = 0; t < VB; ++t) {
+      const int v = v0 + t;
+      on[t] = false;
+      if (v < nvis) {
+        const int i = i0 + wave + (v / d.H) * kDkvWaves, h = v % d.H;
+        const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + i];
+        on[t] = comp ? (rw.y <= k && k < rw.z) : (rw.x <= k);
+        const size_t row = ((size_t)b * d.H + h) * d.S + i;
+#pragma unroll
+        for (int u = 0; u < NDU; ++u) {
+          qv[t][u] = q[row * D + lane + 64 * u];
+          dv[t][u] = dout[row * D + lane + 64 * u];
+        }
+        ls[t] = lse[row];
+        dt[t] = delta[row];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < VB; ++t) {
+      if (!on[t]) continue;
+      float s = 0.f, tt = 0.f;
 #pragma unroll
       for (int u = 0; u < NDU; ++u) {
-        qv[u] = q[row * D + lane + 64 * u];
-        dv[u] = dout[row * D + lane + 64 * u];
-        s += qv[u] * kr[u];
-        t += dv[u] * kr[u];
+        s += qv[t][u] * kr[u];
+        tt += dv[t][u] * kr[u];
       }
       s = wave_sum(s);
-      t = wave_sum(t);
-      const float pr = fast_exp2(s * scale_log2 - lse[row] * kLog2e);
-      const float ds = pr * (t - delta[row]) * scale;
+      tt = wave_sum(tt);
+      const float pr = fast_exp2(s * scale_log2 - ls[t] * kLog2e);
+      const float ds = pr * (tt - dt[t]) * scale;
 #pragma unroll
-      for (int u = 0; u < NDU; ++u) acc[u] += ds * qv[u] + pr * dv[u];
+      for (int u = 0; u < NDU; ++u) acc[u] += ds * qv[t][u] + pr * dv[t][u];
     }
   }
   if (wave > 0) {
