@@ -113,6 +113,58 @@ int timed(int kid, void *stream, F launch, bool allowed = true) {
   return err;
 }
 
+// The library's second stream on the current device: default priority,
+// non-blocking (ordered against the caller's stream by events only), created
+// on first use and kept until the process ends; nullptr if it cannot be made.
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
+    streams[dev] = nullptr;
+  return streams[dev];
+}
+
+// Fork of the second stream from a caller's stream and its join back: work
+// enqueued on `stream` after fork() starts after what the caller's stream
+// held at the fork, and the caller's stream waits, from join() on, for all of
+// it.  The destructor joins a fork left open by an early return.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipStream_t caller = nullptr;
+  int fork(void *caller_stream) {
+    hipStream_t s = side_stream();
+    if (!s) return (int)hipErrorOutOfMemory;
+    hipEvent_t ev = nullptr;
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(ev, (hipStream_t)caller_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, ev, 0);
+    if (ev) (void)hipEventDestroy(ev);  // released once the recorded work completes
+    if (e != hipSuccess) return (int)e;
+    stream = s;
+    caller = (hipStream_t)caller_stream;
+    return 0;
+  }
+  int join() {
+    if (!stream) return 0;
+    hipEvent_t ev = nullptr;
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(ev, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(caller, ev, 0);
+    if (ev) (void)hipEventDestroy(ev);
+    if (e != hipSuccess) {
+      // The caller's stream cannot be ordered after the second stream's work:
+      // wait for that work on the host instead.
+      (void)hipStreamSynchronize(stream);
+    }
+    stream = nullptr;
+    return (int)e;
+  }
+  ~SideStream() { join(); }
+};
+
 hca_status check_ptr(const char *fn, const char *name, const void *p) {
   if (!p) return fail(HCA_ERR_INVALID_ARG, std::string(fn) + ": " + name + " is NULL");
   if (!aligned16(p))
@@ -295,9 +347,17 @@ extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const vo
     });
     if (err) return hip_fail("hca_attn_bwd (P / dS kernel)", err);
   }
-  err = timed(K_BWD_DQ, hip_stream, [&] {
+  // With stored P / dS the dQ pass only reads the stored tiles and K^T, and
+  // writes dQ alone, so it runs on the library's second stream of the device,
+  // concurrently with the key-stationary pass, and fills the tail of that
+  // launch.  The second stream forks from the caller's stream after the P / dS
+  // pass and joins it again before the call returns (also on error paths).
+  SideStream side;
+  if (pds && (err = side.fork(hip_stream)) != 0) return hip_fail("hca_attn_bwd (second stream)", err);
+  void *dq_stream = side.stream ? (void *)side.stream : hip_stream;
+  err = timed(K_BWD_DQ, dq_stream, [&] {
     return launch_bwd_dq_bf16(d, p, q, kv, kvc, kvt, kvct, o, lse, dout, scale, dq, delta, pds,
-                              hip_stream);
+                              dq_stream);
   });
   if (err) return hip_fail("hca_attn_bwd (dQ kernel)", err);
   err = timed(K_BWD_DKV, hip_stream, [&] {
@@ -309,6 +369,7 @@ extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const vo
     return launch_dkv_reduce(d, p, part, HCA_BF16, dkv, dkv_comp, hip_stream);
   });
   if (err) return hip_fail("hca_attn_bwd (dKV reduction)", err);
+  if ((err = side.join()) != 0) return hip_fail("hca_attn_bwd (second stream)", err);
   return HCA_OK;
 }
 

@@ -522,7 +522,17 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
       return n;
     };
     int64_t cchunks = comp_chunks_cfg;
-    if (cchunks == 0) {
+    if (cchunks == 0 && stored) {
+      // With stored P / dS the workspace already holds 256 x bq x H bytes per
+      // listed (query tile, 64-key tile) pair, O(visible pairs); one-chunk
+      // items, whose partial blocks (kv_bk x D float32, 128 KiB) number at
+      // most the listed pairs over a chunk's query tiles, grow no faster.
+      // Longer runs only cost balance: with per-query top-k selections every
+      // query tile lists every compressed tile, and eight-chunk runs left the
+      // key-stationary pass at 7.7 ms against 5.9 with one-chunk items
+      // (S = 16384, H = 64, r = 4, 512 of 4096 entries per query).
+      cchunks = 1;
+    } else if (cchunks == 0) {
       const int64_t budget = std::max<int64_t>(2 * count_items(0, chunk), 4 * kCuTarget);
       cchunks = 1;
       while (cchunks < ceil_div(nqt, chunk) && count_items(1, chunk * cchunks) > budget)

@@ -39,6 +39,13 @@
  *   - Work is enqueued on the given HIP stream (NULL = default stream) and is
  *     asynchronous: results are ready after the caller synchronises.  Faults
  *     inside kernels surface at that synchronisation.
+ *   - One exception, inside hca_attn_bwd with stored P and dS (info.kv_keys
+ *     == 64): its dQ pass runs on a second stream that the library owns (one
+ *     per device, default priority, created on first use with the calling
+ *     thread's current device, which must be the stream's, and kept until the
+ *     process ends).  It is forked from the caller's stream and joined back
+ *     into it with events before the call returns, so the call as a whole
+ *     stays ordered on the caller's stream.
  *
  * Errors.  Every entry point validates all of its arguments before it makes
  * any HIP call, and returns a status; no exception crosses the ABI.  A
@@ -342,7 +349,9 @@ hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const void *kv, con
  * in a call (one launch, or two where the work is split: the key-stationary
  * backward's full-tile and half-tile items, the reduction's raw and
  * compressed tiles) is bracketed by a pair of HIP events recorded on the
- * call's stream.  hca_timing_read waits for the recorded events, writes
+ * call's stream (the dQ pass of a backward with stored P and dS: on the
+ * second stream, where its span overlaps the key-stationary pass's and is no
+ * exclusive time).  hca_timing_read waits for the recorded events, writes
  * per-family totals (up to `capacity` entries, *count = number of families
  * timed) and clears them.  Not thread-safe against concurrent hca_attn_* calls on
  * other threads while enabled.  Errors: HCA_ERR_INVALID_ARG on NULL output

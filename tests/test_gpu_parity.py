@@ -309,6 +309,39 @@ def test_deterministic_and_stream():
     bitwise_equal(a, b)
 
 
+def test_stored_backward_joins_caller_stream():
+    """With stored P and dS the backward's dQ pass runs on the library's second
+    stream.  Work the caller enqueues next on its own stream must see the
+    finished gradients (copied here before any host synchronisation), and a
+    second call that rewrites the same workspace must not overtake the first
+    call's dQ pass; both must equal the same calls run one at a time."""
+    case = Case(1, 4096, 64, 512, 128, 128, "bf16", seed=11)
+    info = case.att.info
+    assert info.kv_keys == 64 and info.ws_pds_bytes > 0
+    inputs = [(case.q, case.kv, case.kvc, case.dout),
+              draw(1, 4096, 64, 512, case.Sc, "bf16", 12, 1.0, device="cuda")]
+
+    def step(q, kv, kvc, dout, stream):
+        o, lse = case.att.new_outputs()
+        grads = case.att.new_grads()
+        for t in (o, lse) + tuple(grads):
+            t.fill_(float("nan"))
+        case.att.forward(q, kv, kvc, case.scale, o, lse, stream=stream)
+        case.att.backward(q, kv, kvc, o, lse, dout, case.scale, grads=grads, stream=stream)
+        return [t.clone() for t in grads]
+
+    want = []
+    for x in inputs:
+        want.append(step(*x, None))
+        torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = [step(*x, s) for x in inputs]
+    s.synchronize()
+    for g, w in zip(got, want):
+        bitwise_equal(g, w)
+
+
 def test_mid_workload_every_element_deterministic():
     """The mid-length workload (S = 16384, H = 64, D = 512) compared with the
     oracle on every element of O, LSE, dQ, dKV and dKV_comp, outputs
