@@ -953,8 +953,9 @@ __global__ void __launch_bounds__(256, 1)
   auto rsw = [](int r) { return ((r & 3) | (((r >> 3) & 3) << 2)) & (NCH - 1); };
   __shared__ __attribute__((aligned(16))) bf16raw q_lds[STEP * QROW];
   __shared__ __attribute__((aligned(16))) bf16raw o_lds[STEP * QROW];  // dO rows
-  __shared__ float lse_lds[STEP], dl_lds[STEP];
-  __shared__ int4 info_lds[STEP];  // rlo, clo, chi, pos (pos = INT_MAX if padded)
+  __shared__ __attribute__((aligned(16))) float lse_lds[STEP];
+  __shared__ __attribute__((aligned(16))) float dl_lds[STEP];
+  __shared__ __attribute__((aligned(16))) int2 vis_lds[STEP];  // the row's keys of this kind: [lo, hi]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
@@ -980,44 +981,77 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int rows_per_qt = d.bq * d.H;
+  // Steps of STEP rows: step s covers rows (s % spq) STEP .. + STEP - 1 of the
+  // query tile of entry e0 + s / spq (a query tile holds spq whole steps).
+  // The rows of step s + 1 are loaded into registers while step s computes.
+  // H and bq H / STEP are powers of two (bf16 plans), so row indices split
+  // into position and head by shifts.
+  const int lh = __builtin_ctz(d.H);
+  const int lspq = __builtin_ctz(d.bq * d.H / STEP);
+  const int spq = 1 << lspq;
+  const int nsteps = (it.e1 - it.e0) << lspq;
   const int r0 = 8 * (j >> 2) + (j & 3);  // A-operand row for the first 16-row block
-  for (int e = it.e0; e < it.e1; ++e) {
-    const uint32_t ent = p.kvent[e];
-    const int qt = (int)(ent & kEntIdx);
-    const bool full = ent & kEntFull;
-    for (int base = 0; base < rows_per_qt; base += STEP) {
-      __syncthreads();
-      // Stage rows base .. base+STEP-1 of query tile qt.
-      for (int c = tid; c < RCH; c += 256) {
-        const int r = c / (D / 8), col = c % (D / 8);
-        const int rho = base + r;
-        const int pos = qt * d.bq + rho / d.H, h = rho % d.H;
-        uint4 qv = make_uint4(0, 0, 0, 0), dv = qv;
-        if (pos < d.S) {
-          const size_t row = ((size_t)b * d.H + h) * d.S + pos;
-          qv = *reinterpret_cast<const uint4 *>(q + row * D + col * 8);
-          dv = *reinterpret_cast<const uint4 *>(dout + row * D + col * 8);
-        }
-        *reinterpret_cast<uint4 *>(q_lds + r * QROW + (col ^ rsw(r)) * 8) = qv;
-        *reinterpret_cast<uint4 *>(o_lds + r * QROW + (col ^ rsw(r)) * 8) = dv;
+  constexpr int CPT = RCH / 256;           // 16-B chunks per thread and tensor
+  static_assert(RCH % 256 == 0, "whole chunks per thread");
+  const bf16raw *qb = q + (size_t)b * d.H * d.S * D;
+  const bf16raw *ob = dout + (size_t)b * d.H * d.S * D;
+  uint4 nq[CPT], nd[CPT];
+  int2 nvis = make_int2(INT_MAX, -1);
+  float nlse = -INFINITY, ndl = 0.f;
+  auto fetch = [&](int st) {
+    const int qt = (int)(p.kvent[it.e0 + (st >> lspq)] & kEntIdx);
+    const int base = (st & (spq - 1)) * STEP;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * 256;
+      const int r = c / NCH, col = c % NCH;
+      const int rho = base + r;
+      const int pos = qt * d.bq + (rho >> lh), h = rho & (d.H - 1);
+      const bool ok = pos < d.S;
+      // Rows past the end read row 0 of the head and are zeroed.
+      const size_t off = ((size_t)h * d.S + (ok ? pos : 0)) * D + col * 8;
+      const uint4 vq = *reinterpret_cast<const uint4 *>(qb + off);
+      const uint4 vd = *reinterpret_cast<const uint4 *>(ob + off);
+      const uint32_t m = ok ? 0xffffffffu : 0u;
+      nq[u] = make_uint4(vq.x & m, vq.y & m, vq.z & m, vq.w & m);
+      nd[u] = make_uint4(vd.x & m, vd.y & m, vd.z & m, vd.w & m);
+    }
+    if (tid < STEP) {
+      const int rho = base + tid;
+      const int pos = qt * d.bq + (rho >> lh), h = rho & (d.H - 1);
+      nvis = make_int2(INT_MAX, -1);  // padded rows see no key
+      nlse = -INFINITY;
+      ndl = 0.f;
+      if (pos < d.S) {
+        const size_t row = ((size_t)b * d.H + h) * d.S + pos;
+        const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos];
+        // Raw keys rlo .. pos, compressed entries clo .. chi - 1.
+        nvis = comp ? make_int2(rw.y, rw.z - 1) : make_int2(rw.x, pos);
+        nlse = lse[row] * kLog2e;
+        ndl = delta[row];
+      }
+    }
+  };
+  if (nsteps > 0) fetch(0);
+  for (int st = 0; st < nsteps; ++st) {
+    {
+      const bool full = p.kvent[it.e0 + (st >> lspq)] & kEntFull;
+      // LDS-only barriers: the next step's row loads stay in flight.
+      lds_barrier();  // every wave is done with the previous step's rows
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = tid + u * 256;
+        const int r = c / NCH, col = c % NCH;
+        *reinterpret_cast<uint4 *>(q_lds + r * QROW + (col ^ rsw(r)) * 8) = nq[u];
+        *reinterpret_cast<uint4 *>(o_lds + r * QROW + (col ^ rsw(r)) * 8) = nd[u];
       }
       if (tid < STEP) {
-        const int rho = base + tid;
-        const int pos = qt * d.bq + rho / d.H, h = rho % d.H;
-        if (pos < d.S) {
-          const size_t row = ((size_t)b * d.H + h) * d.S + pos;
-          const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + pos];
-          info_lds[tid] = make_int4(rw.x, rw.y, rw.z, pos);
-          lse_lds[tid] = lse[row] * kLog2e;
-          dl_lds[tid] = delta[row];
-        } else {
-          info_lds[tid] = make_int4(INT_MAX, 0, 0, INT_MAX);
-          lse_lds[tid] = -INFINITY;
-          dl_lds[tid] = 0.f;
-        }
+        vis_lds[tid] = nvis;
+        lse_lds[tid] = nlse;
+        dl_lds[tid] = ndl;
       }
-      __syncthreads();
+      if (st + 1 < nsteps) fetch(st + 1);
+      lds_barrier();
 
       // S and dP for this wave's 32 rows x 16 keys.
       const int wr = rh * 32;  // first staged row of this wave
@@ -1037,20 +1071,34 @@ __global__ void __launch_bounds__(256, 1)
       }
       // Lane holds rows wr + 8g + {0..3} (rb 0) and wr + 8g + 4 + {0..3} (rb 1)
       // for key `mykey`.
+      // The lane's 8 rows are consecutive: their intervals, LSE and delta are
+      // read together, and invisible entries are dropped by selects.
       float pv[8], dsv[8];
+      {
+        const int rq = wr + 8 * g;
+        int4 vr[4];  // rows rq + 2 u and rq + 2 u + 1: lo, hi, lo, hi
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+        for (int u = 0; u < 4; ++u) vr[u] = *reinterpret_cast<const int4 *>(vis_lds + rq + 2 * u);
+        const float4 l0 = *reinterpret_cast<const float4 *>(lse_lds + rq);
+        const float4 l1 = *reinterpret_cast<const float4 *>(lse_lds + rq + 4);
+        const float4 q0 = *reinterpret_cast<const float4 *>(dl_lds + rq);
+        const float4 q1 = *reinterpret_cast<const float4 *>(dl_lds + rq + 4);
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float dv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int rr = wr + 8 * g + 4 * rb + v;
-          const int4 inf = info_lds[rr];
-          bool vis = true;
-          if (!full)
-            vis = comp ? (mykey >= inf.y && mykey < inf.z) : (mykey >= inf.x && mykey <= inf.w);
-          const float pr = vis ? fast_exp2(s[rb][v] * scale_log2 - lse_lds[rr]) : 0.f;
-          pv[4 * rb + v] = pr;
-          dsv[4 * rb + v] = pr * (t[rb][v] - dl_lds[rr]) * scale;
-        }
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int i = 4 * rb + v;
+            const int lo = (i & 1) ? vr[i >> 1].z : vr[i >> 1].x;
+            const int hi = (i & 1) ? vr[i >> 1].w : vr[i >> 1].y;
+            const bool in = (mykey >= lo) & (mykey <= hi);
+            const float e = fast_exp2(s[rb][v] * scale_log2 - lv[i]);
+            const float pr = (full | in) ? e : 0.f;
+            pv[i] = pr;
+            dsv[i] = pr * (t[rb][v] - dv[i]) * scale;
+          }
+      }
       const bf16x8 pb = pack8(pv), dsb = pack8(dsv);
       // dKV^T[d][key] += Q^T[d][rows] dS[rows][key] + dO^T[d][rows] P[rows][key].
       // Transposed A operand of column block db (d-row j, rows 8 g .. 8 g + 7
@@ -1732,8 +1780,15 @@ int launch_bwd_dkv_bf16(const Dims &d, const DevPlan &p, const void *q, const vo
                            p, (const bf16raw *)q, (const bf16raw *)kv, (const bf16raw *)kvc, lse,
                            delta, (const bf16raw *)dout, sl2, scale, part);
       break;
-    case 128: go(hca_bwd_dkv_kernel<128>); break;
-    case 64: go(hca_bwd_dkv_kernel<64>); break;
+    case 128:
+    case 64:
+      // The kernel stages whole 64-row steps of a query tile and splits rows
+      // by shifts.
+      if ((d.bq * d.H) % 64 || (d.H & (d.H - 1)) || ((d.bq * d.H / 64) & (d.bq * d.H / 64 - 1)))
+        return (int)hipErrorInvalidValue;
+      if (d.D == 128) go(hca_bwd_dkv_kernel<128>);
+      else go(hca_bwd_dkv_kernel<64>);
+      break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -596,26 +596,37 @@ struct KvCopy {
 // Tile-major transpose: dst[b][t / 32][d][t % 32] = src[b][t][d] for t < N, 0 for
 // N <= t < N_pad (N_pad a multiple of 32).  Each 32-key tile's transpose is one
 // contiguous D x 32 block, so a kernel stages it with contiguous copies.  One
-// launch covers the raw keys (blockIdx.x < ceil(raw.N_pad / 64)), then the
+// launch covers the raw tiles (blockIdx.x < raw.N_pad / 32), then the
 // compressed ones.
-__global__ void __launch_bounds__(256) hca_transpose_kernel(KvCopy raw, KvCopy cmp, int D) {
-  __shared__ bf16raw tile[64][66];
-  const int nraw = (raw.N_pad + 63) / 64;
+template <int D>
+__global__ void __launch_bounds__(256) hca_transpose_kernel(KvCopy raw, KvCopy cmp) {
+  // One 32-key tile per workgroup: its rows come in as 16-byte pieces, go
+  // through LDS, and leave as 16-byte pieces of 8 consecutive keys.
+  constexpr int PITCH = D + 8;  // bf16 per LDS row
+  constexpr int NCH = D / 8;    // 16-byte pieces per key row
+  __shared__ __attribute__((aligned(16))) bf16raw tile[kBK * PITCH];
+  const int nraw = raw.N_pad / kBK;
   const bool second = (int)blockIdx.x >= nraw;
   const KvCopy k = second ? cmp : raw;
-  const int N = k.N, N_pad = k.N_pad;
-  const int b = blockIdx.z, t0 = (second ? blockIdx.x - nraw : blockIdx.x) * 64,
-            d0 = blockIdx.y * 64;
+  const int b = blockIdx.y, t = second ? blockIdx.x - nraw : blockIdx.x;
+  const int N = k.N;
   const bf16raw *s = k.src + (size_t)b * N * D;
-  bf16raw *o = k.dst + (size_t)b * D * N_pad;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int tt = i / 64, dd = i % 64, t = t0 + tt, dx = d0 + dd;
-    tile[tt][dd] = (t < N && dx < D) ? s[(size_t)t * D + dx] : (bf16raw)0;
+  for (int c = threadIdx.x; c < kBK * NCH; c += 256) {
+    const int key = c / NCH, col = (c % NCH) * 8, gk = t * kBK + key;
+    *reinterpret_cast<uint4 *>(tile + key * PITCH + col) =
+        gk < N ? *reinterpret_cast<const uint4 *>(s + (size_t)gk * D + col)
+               : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int dd = i / 64, tt = i % 64, t = t0 + tt, dx = d0 + dd;
-    if (dx < D && t < N_pad) o[(size_t)(t / kBK) * D * kBK + (size_t)dx * kBK + t % kBK] = tile[tt][dd];
+  // Output piece c: column dx = c / 4, keys 8 (c % 4) .. + 7.
+  uint4 *out = reinterpret_cast<uint4 *>(k.dst + ((size_t)b * k.N_pad + (size_t)t * kBK) * D);
+  for (int c = threadIdx.x; c < D * kBK / 8; c += 256) {
+    const int dx = c / (kBK / 8), k8 = (c % (kBK / 8)) * 8;
+    ushort v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = tile[(k8 + i) * PITCH + dx];
+    out[c] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                        v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
   }
 }
 
@@ -677,10 +688,14 @@ int launch_transpose_kv(const void *kv, void *kvt, int N, int N_pad, const void 
     hipLaunchKernelGGL(hca_image512_kernel, dim3(tiles, B), dim3(256), 0, s, raw, cmp);
     return (int)hipGetLastError();
   }
-  const int blocks = (raw.N_pad + 63) / 64 + (cmp.N_pad + 63) / 64;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(hca_transpose_kernel, dim3(blocks, (D + 63) / 64, B), dim3(256), 0, s, raw,
-                     cmp, D);
+  if (raw.N_pad % kBK || cmp.N_pad % kBK) return (int)hipErrorInvalidValue;
+  const int tiles = raw.N_pad / kBK + cmp.N_pad / kBK;
+  if (tiles == 0) return hipSuccess;
+  switch (D) {
+    case 128: hipLaunchKernelGGL(hca_transpose_kernel<128>, dim3(tiles, B), dim3(256), 0, s, raw, cmp); break;
+    case 64: hipLaunchKernelGGL(hca_transpose_kernel<64>, dim3(tiles, B), dim3(256), 0, s, raw, cmp); break;
+    default: return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 
