@@ -1502,17 +1502,36 @@ __global__ void __launch_bounds__(256, 2)
   // c ^ sw(r), sw(r) = (r & 3) | ((r >> 3) << 2).  Wave w also copies stored
   // block w (P lo, P hi, dS lo, dS hi): 2 KiB, two 1 KiB copies.
   const uint32_t lane_sw = (uint32_t)(lane ^ (wave << 2));
+  // The wave's 8 rows of a step are 8 consecutive positions of one head (bq
+  // is a power of two >= 8), so away from the sequence end they are 8 KiB
+  // in a row: one base address, row i at i KiB.
+  uint32_t voff_row[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) voff_row[i] = ((lane_sw ^ (uint32_t)(i & 3)) << 4) + 1024u * i;
   auto stage = [&](int s) {
     const int e = s >> lspq, u = s & (SPQ - 1);
     const int qt = (int)(uniform_load(p.kvent, it.e0 + e) & kEntIdx);
+    const int rho0 = u * STEP + 8 * wave;
+    const int pos0 = qt * d.bq + (rho0 & (d.bq - 1)), h0 = rho0 >> lbq;
+    if (pos0 + 7 < d.S) {
+      const size_t rowoff = bat + ((size_t)h0 * d.S + pos0) * D;  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * wave + i, rho = u * STEP + r;
-      const int pos = min(qt * d.bq + (rho & (d.bq - 1)), d.S - 1), h = rho >> lbq;
-      const size_t rowoff = bat + ((size_t)h * d.S + pos) * D;  // wave-uniform
-      const uint32_t voff = (lane_sw ^ (uint32_t)(i & 3)) << 4;
-      dma16(q + rowoff, voff, qb_lds + r * 1024);
-      dma16(dout + rowoff, voff, qb_lds + STEP_BYTES + r * 1024);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lds = qb_lds + (8 * wave + i) * 1024;
+        dma16(q + rowoff, voff_row[i], lds);
+        dma16(dout + rowoff, voff_row[i], lds + STEP_BYTES);
+      }
+    } else {
+      // Last positions: rows past the end read the last row (never used).
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * wave + i;
+        const int pos = min(pos0 + i, d.S - 1);
+        const size_t rowoff = bat + ((size_t)h0 * d.S + pos) * D;  // wave-uniform
+        const uint32_t voff = (lane_sw ^ (uint32_t)(i & 3)) << 4;
+        dma16(q + rowoff, voff, qb_lds + r * 1024);
+        dma16(dout + rowoff, voff, qb_lds + STEP_BYTES + r * 1024);
+      }
     }
     const int ent = (int)uniform_load((const uint32_t *)p.kvpe, 2 * (it.e0 + e) + (wave & 1));
     // rows u * 32 .. u * 32 + 31 of the half's P (wave < 2) or dS (wave >= 2)
