@@ -244,16 +244,15 @@ __global__ void __launch_bounds__(NW * 64, 1)
         dp[v] = p0[mb][v];
         dp[4 + v] = p1[mb][v];
       }
+      // The row's visible keys of this tile's kind, [lo, hi]; invisible keys
+      // are dropped by selects.
+      const int lo = comp ? clo[mb] : rlo[mb], hi = comp ? chi[mb] - 1 : pos[mb];
       const int kb = k0 + 8 * g;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        bool vis = true;
-        if (!full) {
-          const int key = kb + t;
-          vis = comp ? (key >= clo[mb] && key < chi[mb]) : (key >= rlo[mb] && key <= pos[mb]);
-        }
-        const float pr = vis ? fast_exp2(x[t] - lse2[mb]) : 0.f;
-        x[t] = pr * (dp[t] - dl[mb]);
+        const bool vis = full | ((kb + t >= lo) & (kb + t <= hi));
+        const float pr = fast_exp2(x[t] - lse2[mb]);
+        x[t] = vis ? pr * (dp[t] - dl[mb]) : 0.f;
       }
       dsb[mb] = pack8(x);
     }

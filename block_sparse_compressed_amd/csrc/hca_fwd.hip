@@ -27,6 +27,7 @@
 namespace hca {
 
 constexpr int kBK = 32;  // keys per tile (raw and compressed)
+constexpr float kLazyF = 8.f;  // lazy-rescale margin of the D = 64 / 128 forward (log2 units)
 
 #ifndef HCA_FWD_NW
 #define HCA_FWD_NW 4  // waves of the D = 512 forward: 4 (two workgroups per CU) or 8 (one)
@@ -202,33 +203,39 @@ __global__ void __launch_bounds__(NW * 64, 1)
         x[4 + v] = s1[mb][v] * scale_log2;
       }
       if (!full) {
+        // The row's visible keys of this tile's kind, [lo, hi] (selects, no
+        // branches).
+        const int lo = comp ? clo[mb] : rlo[mb], hi = comp ? chi[mb] - 1 : pos[mb];
         const int kb = k0 + 8 * g;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int key = kb + t;
-          const bool vis = comp ? (key >= clo[mb] && key < chi[mb])
-                                : (key >= rlo[mb] && key <= pos[mb]);
-          if (!vis) x[t] = -INFINITY;
+          const bool vis = (kb + t >= lo) & (kb + t <= hi);
+          x[t] = vis ? x[t] : -INFINITY;
         }
       }
       float mx = x[0];
 #pragma unroll
       for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
-      mx = xor_max(mx, 16);
-      mx = xor_max(mx, 32);
-      const float m_new = fmaxf(m_run[mb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[mb] - m_use);
+      mx = group_max(mx);
+      // Lazy rescaling (as at D = 512): the reference max m_run only moves when
+      // the tile max passes it by more than kLazyF log2 units.
+      const bool up = mx > m_run[mb] + kLazyF;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float m_new = up ? mx : m_run[mb];
+        const float alpha = fast_exp2(m_run[mb] - (m_new == -INFINITY ? 0.f : m_new));
+        l_run[mb] *= alpha;
+        m_run[mb] = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[mb][db] *= alpha;
+      }
+      const float m_use = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
       float ps = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         x[t] = fast_exp2(x[t] - m_use);
         ps += x[t];
       }
-      l_run[mb] = l_run[mb] * alpha + ps;
-      m_run[mb] = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[mb][db] *= alpha;
+      l_run[mb] += ps;
       pb[mb] = pack8(x);
     }
 
@@ -242,9 +249,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    float l = l_run[mb];
-    l = xor_sum(l, 16);
-    l = xor_sum(l, 32);
+    const float l = group_sum(l_run[mb]);
     if (valid[mb]) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
       bf16raw *orow = o + (((size_t)b * d.H + hh[mb]) * d.S + pos[mb]) * D;
