@@ -936,7 +936,7 @@ __device__ __forceinline__ bf16x8 tr_frag_rows(const char *p, int four_rows) {
 //    ds_read_b64_tr_b16 reads each (sixteen 2-byte reads before).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 4)
     hca_bwd_dkv_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
                        const bf16raw *__restrict__ kv, const bf16raw *__restrict__ kvc,
                        const float *__restrict__ lse, const float *__restrict__ delta,
@@ -982,7 +982,9 @@ __global__ void __launch_bounds__(256, 1)
 
   // Steps of STEP rows: step s covers rows (s % spq) STEP .. + STEP - 1 of the
   // query tile of entry e0 + s / spq (a query tile holds spq whole steps).
-  // The rows of step s + 1 are loaded into registers while step s computes.
+  // Four workgroups share a CU (at most 128 registers per lane), so one
+  // workgroup's row loads run under the others' math; a step's loads are
+  // issued before the barrier that frees the LDS rows.
   // H and bq H / STEP are powers of two (bf16 plans), so row indices split
   // into position and head by shifts.
   const int lh = __builtin_ctz(d.H);
@@ -1031,11 +1033,10 @@ __global__ void __launch_bounds__(256, 1)
       }
     }
   };
-  if (nsteps > 0) fetch(0);
   for (int st = 0; st < nsteps; ++st) {
     {
       const bool full = p.kvent[it.e0 + (st >> lspq)] & kEntFull;
-      // LDS-only barriers: the next step's row loads stay in flight.
+      fetch(st);
       lds_barrier();  // every wave is done with the previous step's rows
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
@@ -1049,7 +1050,6 @@ __global__ void __launch_bounds__(256, 1)
         lse_lds[tid] = nlse;
         dl_lds[tid] = ndl;
       }
-      if (st + 1 < nsteps) fetch(st + 1);
       lds_barrier();
 
       // S and dP for this wave's 32 rows x 16 keys.
