@@ -1615,8 +1615,8 @@ __global__ void __launch_bounds__(256, 2)
 // ---------------------------------------------------------------------------
 // 3. Fixed-order sum of the partials of every key tile -> dKV / dKV_comp.
 // ---------------------------------------------------------------------------
-// One launch for the raw key tiles, one for the compressed ones; a workgroup
-// takes one (key tile, chunk of the tile's [kv_bk][D] block).  Thread (g, c)
+// One launch, the raw key tiles' workgroups first; a workgroup takes one
+// (key tile, chunk of the tile's [kv_bk][D] block).  Thread (g, c)
 // sums the float4 column c of the tile's partial blocks i = g, g + G, g + 2 G,
 // ... in increasing order (eight loads in flight), and the G group sums are
 // added in group order.  The grouping is fixed, so the result is bitwise
@@ -1624,15 +1624,15 @@ __global__ void __launch_bounds__(256, 2)
 // chunks); a compressed tile has tens to hundreds, streamed by G = 8 groups
 // over 128-element chunks.
 template <int G>
-__global__ void __launch_bounds__(256)
-    hca_dkv_reduce_kernel(Dims d, DevPlan p, const float *__restrict__ part, int dtype,
-                          void *__restrict__ dkv, void *__restrict__ dkvc, int comp) {
+__device__ __forceinline__ void dkv_reduce_block(const Dims &d, const DevPlan &p,
+                                                 const float *__restrict__ part, int dtype,
+                                                 void *__restrict__ dkv, void *__restrict__ dkvc,
+                                                 int comp, int blk, float4 (*red)[256 / G]) {
   constexpr int C = 256 / G, CHUNK = 4 * C;  // float4 columns per group, elements per workgroup
-  __shared__ float4 red[G][C];
   const int nkt = d.nkv_raw + d.nkv_comp;
   const int ntl = comp ? d.nkv_comp : d.nkv_raw;  // tiles of this launch per batch row
   const int per_tile = d.kv_bk * d.D / CHUNK;
-  const int tile = blockIdx.x / per_tile, chunk = blockIdx.x - tile * per_tile;
+  const int tile = blk / per_tile, chunk = blk - tile * per_tile;
   const int b = tile / ntl, kt = tile - b * ntl;
   const int t = comp ? d.nkv_raw + kt : kt;
   const int nk = comp ? d.Sc : d.S;
@@ -1683,6 +1683,19 @@ __global__ void __launch_bounds__(256)
   } else {
     *reinterpret_cast<float4 *>((float *)(comp ? dkvc : dkv) + off) = a;
   }
+}
+
+// Both kinds in one launch: blocks [0, raw_blk) reduce raw key tiles (G = 1),
+// the rest compressed ones (G = 8).
+__global__ void __launch_bounds__(256)
+    hca_dkv_reduce_kernel(Dims d, DevPlan p, const float *__restrict__ part, int dtype,
+                          void *__restrict__ dkv, void *__restrict__ dkvc, int raw_blk) {
+  __shared__ float4 red[8][32];
+  if ((int)blockIdx.x < raw_blk)
+    dkv_reduce_block<1>(d, p, part, dtype, dkv, dkvc, 0, blockIdx.x,
+                        reinterpret_cast<float4 (*)[256]>(&red[0][0]));
+  else
+    dkv_reduce_block<8>(d, p, part, dtype, dkv, dkvc, 1, blockIdx.x - raw_blk, red);
 }
 
 // Compute units of the current device rounded down to a multiple of 8 (the
@@ -1818,12 +1831,9 @@ int launch_dkv_reduce(const Dims &d, const DevPlan &p, const float *part, int dt
   hipStream_t s = (hipStream_t)stream;
   const int raw_blk = d.B * d.nkv_raw * (d.kv_bk * d.D / 1024);
   const int comp_blk = d.B * d.nkv_comp * (d.kv_bk * d.D / 128);
-  if (raw_blk > 0)
-    hipLaunchKernelGGL(hca_dkv_reduce_kernel<1>, dim3(raw_blk), dim3(256), 0, s, d, p, part,
-                       dtype, dkv, dkvc, 0);
-  if (comp_blk > 0)
-    hipLaunchKernelGGL(hca_dkv_reduce_kernel<8>, dim3(comp_blk), dim3(256), 0, s, d, p, part,
-                       dtype, dkv, dkvc, 1);
+  if (raw_blk + comp_blk > 0)
+    hipLaunchKernelGGL(hca_dkv_reduce_kernel, dim3(raw_blk + comp_blk), dim3(256), 0, s, d, p,
+                       part, dtype, dkv, dkvc, raw_blk);
   return (int)hipGetLastError();
 }
 

@@ -346,10 +346,8 @@ hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const void *kv, con
 
 /*
  * Kernel timing (instrumentation).  While enabled, each kernel family's work
- * in a call (one launch, or two where the work is split: the key-stationary
- * backward's full-tile and half-tile items, the reduction's raw and
- * compressed tiles) is bracketed by a pair of HIP events recorded on the
- * call's stream (the dQ pass of a backward with stored P and dS: on the
+ * in a call (one launch each) is bracketed by a pair of HIP events recorded
+ * on the call's stream (the dQ pass of a backward with stored P and dS: on the
  * second stream, where its span overlaps the key-stationary pass's and is no
  * exclusive time).  hca_timing_read waits for the recorded events, writes
  * per-family totals (up to `capacity` entries, *count = number of families
