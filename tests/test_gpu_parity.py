@@ -150,6 +150,9 @@ SMALL = [
     (1, 97, 4, 128, 4, 9, "f32", "random", 1),
     (1, 64, 64, 512, 1, 0, "bf16", None, 0),   # compressed only (W = 0, r = 1)
     (1, 70, 16, 128, 100, 70, "bf16", None, 0),  # no compressed entries, causal
+    # sliding window only at D = 512 (r > S: no compressed entry completes),
+    # two documents: the stored-P backward with raw key tiles alone
+    (1, 600, 64, 512, 1024, 128, "bf16", [[250, 350]], 0),
     # D = 512 tiles at other head counts: 16 x 8, 16 x 128 and 32 x 4 (positions x heads)
     (1, 250, 8, 512, 16, 40, "bf16", None, 0),
     (1, 100, 128, 512, 8, 30, "bf16", [[40, 60]], 1),
