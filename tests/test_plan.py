@@ -336,6 +336,17 @@ def test_kv_keys_choice():
     forced = hca.hca_plan_get_info(hca.hca_block_mask_build(
         1, 262144, 128, 128, 2048, None, None, 64, 512, hca.HCA_BF16, tiles=(0, 0, 0, 0, 0, 64)))
     assert forced.kv_keys == 64 and forced.ws_pds_bytes > 32 * 2**30
+    # stored P / dS keeps compressed items one chunk long (their partial sums
+    # grow no faster than the store), also where every query tile lists every
+    # compressed tile (top-k selections); the recomputing backward merges runs
+    rng = np.random.default_rng(5)
+    Sq, Sc = 16384, 4096
+    idx = rng.integers(0, Sc, size=(1, Sq, 32)).astype(np.int32)
+    tk = hca.hca_plan_get_info(hca.hca_block_mask_build_topk(1, Sq, 128, Sc, idx, H=8, D=512))
+    assert tk.kv_keys == 64 and tk.comp_item_chunks == 1
+    tk128 = hca.hca_plan_get_info(hca.hca_block_mask_build_topk(
+        1, Sq, 128, Sc, idx, H=8, D=512, tiles=(0, 0, 0, 0, 0, 128)))
+    assert tk128.kv_keys == 128 and tk128.comp_item_chunks > 1
     for D, bad in ((512, 32), (512, 96), (512, 256), (128, 64), (64, 128)):
         with pytest.raises(hca.HcaError, match="kv_keys"):
             hca.hca_block_mask_build(1, S, r, W, S // r, None, None, H, D, hca.HCA_BF16,
