@@ -208,39 +208,64 @@ __global__ void __launch_bounds__(kRowWaves * 64)
   }
 }
 
-// dKV: one workgroup of kDkvWaves wavefronts per key.  A compressed entry is
-// seen by every later position of its document, so a single wavefront walking
-// its rows one by one (each a chain of loads and wave-wide sums) took most of
-// the backward; the waves take interleaved positions and their partial sums are
-// added in a fixed order (wave 0, then 1, 2, ...), so the result is the same on
-// every run.
-constexpr int kDkvWaves = 16;
+// dKV, sixteen lanes per visit: one workgroup of kGroupWaves wavefronts per
+// key; each 16-lane row of a wavefront takes one (position, head) visit at a
+// time, a lane holding D / 16 columns of the visit's q and dO rows (16-byte
+// pieces c, c + 16, ... of the row, so a row's loads are whole and
+// contiguous).  <q, k> and <dO, k> need only a 16-lane sum (four DPP steps,
+// no lane swaps across rows), and dS q + P dO is added to the lane's own
+// columns.  At the end the four rows of each wavefront are added with the
+// lane swaps and the wavefronts' sums in a fixed order (wave 0, 1, ...), so the
+// result is the same on every run.  A compressed entry is seen by every later
+// position of its document; against one visit per wavefront (64 lanes over D,
+// two full wave sums per visit) a wavefront works on four visits at once with
+// a quarter of the cross-lane steps each.
+constexpr int kGroupWaves = 8;
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v = dpp_plus<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_plus<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_plus<0x141>(v);  // row_half_mirror
+  return dpp_plus<0x140>(v);  // row_mirror
+}
+
+__device__ __forceinline__ float rows4_sum(float v) {  // the 4 rows of a wave
+  unsigned u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  u = __float_as_uint(v);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int NDU>
-__global__ void __launch_bounds__(kDkvWaves * 64)
-    hca_bwd_dkv_f32_kernel(Dims d, DevPlan p, const float *__restrict__ q,
-                           const float *__restrict__ kv, const float *__restrict__ kvc,
-                           const float *__restrict__ lse, const float *__restrict__ delta,
-                           const float *__restrict__ dout, float scale_log2, float scale,
-                           float *__restrict__ dkv, float *__restrict__ dkvc) {
-  __shared__ float red[kDkvWaves - 1][NDU * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ void __launch_bounds__(kGroupWaves * 64)
+    hca_bwd_dkv_f32_rows_kernel(Dims d, DevPlan p, const float *__restrict__ q,
+                                const float *__restrict__ kv, const float *__restrict__ kvc,
+                                const float *__restrict__ lse, const float *__restrict__ delta,
+                                const float *__restrict__ dout, float scale_log2, float scale,
+                                float *__restrict__ dkv, float *__restrict__ dkvc) {
+  constexpr int D = NDU * 64, C4 = D / 4;     // 16-byte pieces per row
+  constexpr int NG = kGroupWaves * 4;          // 16-lane rows per workgroup
+  constexpr int VB = NDU <= 1 ? 8 : NDU <= 2 ? 4 : NDU <= 4 ? 2 : 1;  // visits per batch
+  __shared__ float4 red[kGroupWaves][C4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, grp = wave * 4 + (lane >> 4);
   const int per_b = d.S + d.Sc;
   const int64_t kk = blockIdx.x;  // whole workgroup: same key
   if (kk >= (int64_t)d.B * per_b) return;
-  const int D = NDU * 64;
   const int b = (int)(kk / per_b), idx = (int)(kk % per_b);
   const bool comp = idx >= d.S;
   const int k = comp ? idx - d.S : idx;
-  const float *krow = comp ? kvc + ((size_t)b * d.Sc + k) * D : kv + ((size_t)b * d.S + k) * D;
-  float kr[NDU], acc[NDU];
+  const float4 *krow = reinterpret_cast<const float4 *>(
+      comp ? kvc + ((size_t)b * d.Sc + k) * D : kv + ((size_t)b * d.S + k) * D);
+  float4 kr[NDU], acc[NDU];
 #pragma unroll
-  for (int u = 0; u < NDU; ++u) {
-    kr[u] = krow[lane + 64 * u];
-    acc[u] = 0.f;
+  for (int m = 0; m < NDU; ++m) {
+    kr[m] = krow[c + 16 * m];
+    acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  // Positions that can see key k: raw k .. k+W-1, compressed (k+1) r - 1 .. S-1;
-  // each is then checked against its own visible interval.
+  // Positions that can see key k (each then checked against its own interval).
   int i0, i1;
   if (comp) {
     i0 = (k + 1) * d.r - 1;
@@ -249,65 +274,76 @@ __global__ void __launch_bounds__(kDkvWaves * 64)
     i0 = k;
     i1 = d.W > 0 ? min(d.S - 1, k + d.W - 1) : k - 1;
   }
-  // The wave's (position, head) visits in order -- positions i0 + wave,
-  // i0 + wave + kDkvWaves, ..., all heads of each -- VB at a time: the rows'
-  // visible intervals, Q and dO rows, LSE and delta of a batch are loaded
-  // together, so one load latency covers the batch (fewer for wide heads: a
-  // 16-wave workgroup has 128 registers per lane).  A position that does not
-  // see key k adds nothing.
-  constexpr int VB = NDU <= 1 ? 8 : NDU <= 2 ? 4 : NDU <= 4 ? 2 : 1;
-  const int npos = i1 >= i0 + wave ? (i1 - i0 - wave) / kDkvWaves + 1 : 0;
-  const int nvis = npos * d.H;
-  for (int v0 = 0; v0 < nvis; v0 += VB) {
-    float qv[VB][NDU], dv[VB][NDU], ls[VB], dt[VB];
+  const int nvis = i1 >= i0 ? (i1 - i0 + 1) * d.H : 0;
+  // Row group g takes visits g, g + NG, g + 2 NG, ... (position-major), VB at
+  // a time with their loads issued together.
+  for (int v0 = grp; v0 < nvis; v0 += VB * NG) {
+    float4 qv[VB][NDU], dv[VB][NDU];
+    float ls[VB], dt[VB];
     bool on[VB];
 #pragma unroll
     for (int t = 0; t < VB; ++t) {
-      const int v = v0 + t;
-      on[t] = false;
-      if (v < nvis) {
-        const int i = i0 + wave + (v / d.H) * kDkvWaves, h = v % d.H;
-        const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + i];
-        on[t] = comp ? (rw.y <= k && k < rw.z) : (rw.x <= k);
-        const size_t row = ((size_t)b * d.H + h) * d.S + i;
+      const int v = v0 + t * NG;
+      on[t] = v < nvis;
+      const int vc = on[t] ? v : grp;  // (an in-range visit; its result is dropped)
+      const int i = i0 + vc / d.H, h = vc % d.H;
+      const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + i];
+      on[t] = on[t] && (comp ? (rw.y <= k && k < rw.z) : (rw.x <= k));
+      const size_t row = ((size_t)b * d.H + h) * d.S + i;
+      const float4 *qr = reinterpret_cast<const float4 *>(q + row * D);
+      const float4 *dr = reinterpret_cast<const float4 *>(dout + row * D);
 #pragma unroll
-        for (int u = 0; u < NDU; ++u) {
-          qv[t][u] = q[row * D + lane + 64 * u];
-          dv[t][u] = dout[row * D + lane + 64 * u];
-        }
-        ls[t] = lse[row];
-        dt[t] = delta[row];
+      for (int m = 0; m < NDU; ++m) {
+        qv[t][m] = qr[c + 16 * m];
+        dv[t][m] = dr[c + 16 * m];
       }
+      ls[t] = lse[row];
+      dt[t] = delta[row];
     }
 #pragma unroll
     for (int t = 0; t < VB; ++t) {
-      if (!on[t]) continue;
-      float s = 0.f, tt = 0.f;
+      float sv = 0.f, tv = 0.f;
 #pragma unroll
-      for (int u = 0; u < NDU; ++u) {
-        s += qv[t][u] * kr[u];
-        tt += dv[t][u] * kr[u];
+      for (int m = 0; m < NDU; ++m) {
+        sv += qv[t][m].x * kr[m].x + qv[t][m].y * kr[m].y + qv[t][m].z * kr[m].z +
+              qv[t][m].w * kr[m].w;
+        tv += dv[t][m].x * kr[m].x + dv[t][m].y * kr[m].y + dv[t][m].z * kr[m].z +
+              dv[t][m].w * kr[m].w;
       }
-      s = wave_sum(s);
-      tt = wave_sum(tt);
-      const float pr = fast_exp2(s * scale_log2 - ls[t] * kLog2e);
-      const float ds = pr * (tt - dt[t]) * scale;
+      sv = row16_sum(sv);
+      tv = row16_sum(tv);
+      const float pr = on[t] ? fast_exp2(sv * scale_log2 - ls[t] * kLog2e) : 0.f;
+      const float ds = pr * (tv - dt[t]) * scale;
 #pragma unroll
-      for (int u = 0; u < NDU; ++u) acc[u] += ds * qv[t][u] + pr * dv[t][u];
+      for (int m = 0; m < NDU; ++m) {
+        acc[m].x += ds * qv[t][m].x + pr * dv[t][m].x;
+        acc[m].y += ds * qv[t][m].y + pr * dv[t][m].y;
+        acc[m].z += ds * qv[t][m].z + pr * dv[t][m].z;
+        acc[m].w += ds * qv[t][m].w + pr * dv[t][m].w;
+      }
     }
   }
-  if (wave > 0) {
 #pragma unroll
-    for (int u = 0; u < NDU; ++u) red[wave - 1][lane + 64 * u] = acc[u];
+  for (int m = 0; m < NDU; ++m) {
+    acc[m].x = rows4_sum(acc[m].x);
+    acc[m].y = rows4_sum(acc[m].y);
+    acc[m].z = rows4_sum(acc[m].z);
+    acc[m].w = rows4_sum(acc[m].w);
+    if (lane < 16) red[wave][c + 16 * m] = acc[m];
   }
   __syncthreads();
-  if (wave == 0) {
-    for (int w = 0; w < kDkvWaves - 1; ++w)
-#pragma unroll
-      for (int u = 0; u < NDU; ++u) acc[u] += red[w][lane + 64 * u];
-    float *out = comp ? dkvc + ((size_t)b * d.Sc + k) * D : dkv + ((size_t)b * d.S + k) * D;
-#pragma unroll
-    for (int u = 0; u < NDU; ++u) out[lane + 64 * u] = acc[u];
+  if (tid < C4) {
+    float4 t = red[0][tid];
+    for (int w = 1; w < kGroupWaves; ++w) {
+      const float4 x = red[w][tid];
+      t.x += x.x;
+      t.y += x.y;
+      t.z += x.z;
+      t.w += x.w;
+    }
+    float4 *out = reinterpret_cast<float4 *>(comp ? dkvc + ((size_t)b * d.Sc + k) * D
+                                                  : dkv + ((size_t)b * d.S + k) * D);
+    out[tid] = t;
   }
 }
 
@@ -352,9 +388,10 @@ int launch_bwd_f32(const Dims &d, const DevPlan &p, const float *q, const float 
 #undef CALL
   int err = (int)hipGetLastError();
   if (err) return err;
-#define CALL(N)                                                                                \
-  hipLaunchKernelGGL(hca_bwd_dkv_f32_kernel<N>, dim3((unsigned)keys), dim3(kDkvWaves * 64), 0, \
-                     s, d, p, q, kv, kvc, lse, delta, dout, sl2, scale, dkv, dkvc)
+#define CALL(N)                                                                          \
+  hipLaunchKernelGGL(hca_bwd_dkv_f32_rows_kernel<N>, dim3((unsigned)keys),               \
+                     dim3(kGroupWaves * 64), 0, s, d, p, q, kv, kvc, lse, delta, dout, sl2, \
+                     scale, dkv, dkvc)
   HCA_F32_SWITCH(d.D, CALL)
 #undef CALL
   return (int)hipGetLastError();

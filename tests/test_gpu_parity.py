@@ -148,6 +148,10 @@ SMALL = [
     (1, 200, 128, 64, 9, 17, "bf16", [[1, 1, 198]], 0),
     (1, 333, 1, 64, 5, 12, "bf16", "random", 0),
     (1, 97, 4, 128, 4, 9, "f32", "random", 1),
+    # float32 at wide heads and an odd head count (dKV: 16 lanes per visit,
+    # D / 16 columns per lane)
+    (1, 150, 2, 512, 8, 16, "f32", [[60, 90]], 0),
+    (1, 180, 3, 256, 8, 20, "f32", None, 1),
     (1, 64, 64, 512, 1, 0, "bf16", None, 0),   # compressed only (W = 0, r = 1)
     (1, 70, 16, 128, 100, 70, "bf16", None, 0),  # no compressed entries, causal
     # sliding window only at D = 512 (r > S: no compressed entry completes),
