@@ -18,21 +18,27 @@ namespace hca {
 
 namespace {
 
-// Sum over the 64 lanes, the result in every lane, without LDS round trips:
-// DPP within each 16-lane row (swap neighbours, swap pairs, mirror the half
-// row, mirror the row), then the gfx950 lane swaps across rows.  (A shuffle
-// ladder goes through the LDS crossbar once per step; with two sums per
-// visited key it was most of the float32 kernels' time.)
+// Cross-lane sums without LDS round trips.  Within each 16-lane row: DPP
+// steps (swap neighbours, swap pairs, mirror the half row, mirror the row),
+// the row's sum in each of its lanes.  (A shuffle ladder goes through the LDS
+// crossbar once per step; with two sums per visited key it had been most of
+// the float32 kernels' time.)
 template <int CTRL>
 __device__ __forceinline__ float dpp_plus(float v) {
   return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
                                                                 0xF, 0xF, true));
 }
-__device__ __forceinline__ float wave_sum(float v) {
+
+__device__ __forceinline__ float row16_sum(float v) {
   v = dpp_plus<0xB1>(v);   // quad_perm [1, 0, 3, 2]
   v = dpp_plus<0x4E>(v);   // quad_perm [2, 3, 0, 1]
   v = dpp_plus<0x141>(v);  // row_half_mirror
-  v = dpp_plus<0x140>(v);  // row_mirror
+  return dpp_plus<0x140>(v);  // row_mirror
+}
+
+// Sum / max over the four 16-lane rows of a wavefront (lanes l, l ^ 16,
+// l ^ 32, l ^ 48) with the gfx950 lane swaps, the result in every lane.
+__device__ __forceinline__ float rows4_sum(float v) {
   unsigned u = __float_as_uint(v);
   auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -41,96 +47,126 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ float rows4_max(float v) {
+  unsigned u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  u = __float_as_uint(v);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 }  // namespace
 
-// Loads of this many visits (keys of a row, heads of a position) are issued
-// together before any of them is used.
-constexpr int kBatch = 4;
-
-// Forward and dQ: one workgroup of kRowWaves wavefronts per query row; wave w
-// takes every kRowWaves-th visible key (raw window first, then compressed
-// entries), so the chains of dependent loads and wave-wide sums run side by
-// side.  The waves' partial results are merged in a fixed order.
+// Forward and dQ: one workgroup of kRowWaves wavefronts per query row, and
+// sixteen lanes per visited key: each 16-lane row of a wavefront (group g =
+// 4 wave + lane / 16) takes keys g, g + 16, g + 32, ... of the row (raw window
+// first, then compressed entries), a lane holding D / 16 columns of the q, dO
+// and key rows as whole 16-byte pieces (c, c + 16, ... for lane c of the row),
+// so a key's dot products need only a 16-lane sum.  kBatch keys' rows are
+// loaded together.  The 16 groups' partial results are merged at the end in a
+// fixed order (the four rows of a wavefront with the lane swaps, then the
+// wavefronts), so every run gives the same result.
 constexpr int kRowWaves = 4;
+constexpr int kBatch = 4;
 
 template <int NDU>
 __global__ void __launch_bounds__(kRowWaves * 64)
     hca_fwd_f32_kernel(Dims d, DevPlan p, const float *__restrict__ q, const float *__restrict__ kv,
                        const float *__restrict__ kvc, float scale_log2, float *__restrict__ o,
                        float *__restrict__ lse) {
-  __shared__ float red_acc[kRowWaves][NDU * 64];
+  constexpr int D = NDU * 64, C4 = D / 4, NG = kRowWaves * 4;
+  __shared__ float4 red_acc[kRowWaves][C4];
   __shared__ float red_ml[kRowWaves][2];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 15, grp = wave * 4 + (lane >> 4);
   const int64_t row = blockIdx.x;  // whole workgroup: same row
   if (row >= (int64_t)d.B * d.H * d.S) return;
-  const int D = NDU * 64;
   const int i = (int)(row % d.S);
   const int b = (int)(row / d.S / d.H);
   const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + i];
-  float qv[NDU], acc[NDU];
+  const float4 *qr = reinterpret_cast<const float4 *>(q + row * D);
+  float4 qv[NDU], acc[NDU];
 #pragma unroll
-  for (int u = 0; u < NDU; ++u) {
-    qv[u] = q[row * D + lane + 64 * u];
-    acc[u] = 0.f;
+  for (int m = 0; m < NDU; ++m) {
+    qv[m] = qr[c + 16 * m];
+    acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  // Online softmax of this wave's keys (log2 units).
-  float m = -INFINITY, l = 0.f;
-  auto visit = [&](const float (&kr)[NDU]) {
-    float s = 0.f;
-#pragma unroll
-    for (int u = 0; u < NDU; ++u) s += qv[u] * kr[u];
-    const float x = wave_sum(s) * scale_log2;
-    const float mn = fmaxf(m, x);
-    const float a = fast_exp2(m - mn), pr = fast_exp2(x - mn);
-    l = l * a + pr;
-#pragma unroll
-    for (int u = 0; u < NDU; ++u) acc[u] = acc[u] * a + pr * kr[u];
-    m = mn;
-  };
+  // Online softmax of this group's keys (log2 units).
+  float mx = -INFINITY, l = 0.f;
   const int nraw = max(i + 1 - rw.x, 0);
   const int nkeys = nraw + max(rw.z - rw.y, 0);
-  // The wave's keys in order, kBatch rows loaded at a time.
-  for (int n0 = wave; n0 < nkeys; n0 += kBatch * kRowWaves) {
-    float kr[kBatch][NDU];
+  for (int n0 = grp; n0 < nkeys; n0 += kBatch * NG) {
+    float4 kr[kBatch][NDU];
 #pragma unroll
     for (int t = 0; t < kBatch; ++t) {
-      const int n = n0 + t * kRowWaves;
-      if (n < nkeys) {
-        const float *krow = n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
-                                     : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D;
+      const int n = min(n0 + t * NG, nkeys - 1);  // (past the end: a key that is dropped)
+      const float4 *krow = reinterpret_cast<const float4 *>(
+          n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
+                   : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D);
 #pragma unroll
-        for (int u = 0; u < NDU; ++u) kr[t][u] = krow[lane + 64 * u];
-      }
+      for (int m = 0; m < NDU; ++m) kr[t][m] = krow[c + 16 * m];
     }
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t)
-      if (n0 + t * kRowWaves < nkeys) visit(kr[t]);
-  }
-  // Merge: M = max m_w, L = sum l_w 2^(m_w - M), acc = sum acc_w 2^(m_w - M).
+    for (int t = 0; t < kBatch; ++t) {
+      if (n0 + t * NG >= nkeys) break;  // uniform within the group
+      float sv = 0.f;
 #pragma unroll
-  for (int u = 0; u < NDU; ++u) red_acc[wave][lane + 64 * u] = acc[u];
+      for (int m = 0; m < NDU; ++m)
+        sv += qv[m].x * kr[t][m].x + qv[m].y * kr[t][m].y + qv[m].z * kr[t][m].z +
+              qv[m].w * kr[t][m].w;
+      const float x = row16_sum(sv) * scale_log2;
+      const float mn = fmaxf(mx, x);
+      const float a = fast_exp2(mx - mn), pr = fast_exp2(x - mn);
+      l = l * a + pr;
+#pragma unroll
+      for (int m = 0; m < NDU; ++m) {
+        acc[m].x = acc[m].x * a + pr * kr[t][m].x;
+        acc[m].y = acc[m].y * a + pr * kr[t][m].y;
+        acc[m].z = acc[m].z * a + pr * kr[t][m].z;
+        acc[m].w = acc[m].w * a + pr * kr[t][m].w;
+      }
+      mx = mn;
+    }
+  }
+  // Merge the wavefront's four groups: M = max m_g, L = sum l_g 2^(m_g - M),
+  // acc = sum acc_g 2^(m_g - M); then the wavefronts the same way.
+  const float mw = rows4_max(mx);
+  const float f = mx == -INFINITY ? 0.f : fast_exp2(mx - mw);
+  const float lw = rows4_sum(l * f);
+#pragma unroll
+  for (int m = 0; m < NDU; ++m) {
+    acc[m].x = rows4_sum(acc[m].x * f);
+    acc[m].y = rows4_sum(acc[m].y * f);
+    acc[m].z = rows4_sum(acc[m].z * f);
+    acc[m].w = rows4_sum(acc[m].w * f);
+    if (lane < 16) red_acc[wave][c + 16 * m] = acc[m];
+  }
   if (lane == 0) {
-    red_ml[wave][0] = m;
-    red_ml[wave][1] = l;
+    red_ml[wave][0] = mw;
+    red_ml[wave][1] = lw;
   }
   __syncthreads();
-  if (wave == 0) {
+  if (threadIdx.x < C4) {
+    const int e = threadIdx.x;
     float M = -INFINITY;
     for (int w = 0; w < kRowWaves; ++w) M = fmaxf(M, red_ml[w][0]);
-    float L = 0.f, out[NDU];
-#pragma unroll
-    for (int u = 0; u < NDU; ++u) out[u] = 0.f;
+    float L = 0.f;
+    float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int w = 0; w < kRowWaves; ++w) {
-      const float mw = red_ml[w][0];
-      const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-      L += red_ml[w][1] * f;
-#pragma unroll
-      for (int u = 0; u < NDU; ++u) out[u] += red_acc[w][lane + 64 * u] * f;
+      const float m_w = red_ml[w][0];
+      const float fw = m_w == -INFINITY ? 0.f : fast_exp2(m_w - M);
+      L += red_ml[w][1] * fw;
+      const float4 x = red_acc[w][e];
+      out.x += x.x * fw;
+      out.y += x.y * fw;
+      out.z += x.z * fw;
+      out.w += x.w * fw;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-    for (int u = 0; u < NDU; ++u) o[row * D + lane + 64 * u] = out[u] * inv;
-    if (lane == 0) lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    reinterpret_cast<float4 *>(o + row * D)[e] =
+        make_float4(out.x * inv, out.y * inv, out.z * inv, out.w * inv);
+    if (e == 0) lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
   }
 }
 
@@ -141,70 +177,88 @@ __global__ void __launch_bounds__(kRowWaves * 64)
                           const float *__restrict__ o, const float *__restrict__ lse,
                           const float *__restrict__ dout, float scale_log2, float scale,
                           float *__restrict__ dq, float *__restrict__ delta) {
-  __shared__ float red_acc[kRowWaves - 1][NDU * 64];
+  constexpr int D = NDU * 64, C4 = D / 4, NG = kRowWaves * 4;
+  __shared__ float4 red_acc[kRowWaves][C4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 15, grp = wave * 4 + (lane >> 4);
   const int64_t row = blockIdx.x;  // whole workgroup: same row
   if (row >= (int64_t)d.B * d.H * d.S) return;
-  const int D = NDU * 64;
   const int i = (int)(row % d.S);
   const int b = (int)(row / d.S / d.H);
   const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + i];
-  float qv[NDU], dv[NDU], acc[NDU], dl = 0.f;
+  const float4 *qr = reinterpret_cast<const float4 *>(q + row * D);
+  const float4 *dr = reinterpret_cast<const float4 *>(dout + row * D);
+  const float4 *orow = reinterpret_cast<const float4 *>(o + row * D);
+  float4 qv[NDU], dv[NDU], acc[NDU];
+  float dl = 0.f;
 #pragma unroll
-  for (int u = 0; u < NDU; ++u) {
-    qv[u] = q[row * D + lane + 64 * u];
-    dv[u] = dout[row * D + lane + 64 * u];
-    dl += dv[u] * o[row * D + lane + 64 * u];
-    acc[u] = 0.f;
+  for (int m = 0; m < NDU; ++m) {
+    qv[m] = qr[c + 16 * m];
+    dv[m] = dr[c + 16 * m];
+    const float4 ov = orow[c + 16 * m];
+    dl += dv[m].x * ov.x + dv[m].y * ov.y + dv[m].z * ov.z + dv[m].w * ov.w;
+    acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  dl = wave_sum(dl);  // every wave computes delta; wave 0 stores it
-  if (wave == 0 && lane == 0) delta[row] = dl;
+  dl = row16_sum(dl);  // every group holds the whole row: delta in every lane
+  if (threadIdx.x == 0) delta[row] = dl;
   const float lse2 = lse[row] * kLog2e;
-  auto visit = [&](const float (&kr)[NDU]) {
-    float s = 0.f, t = 0.f;
-#pragma unroll
-    for (int u = 0; u < NDU; ++u) {
-      s += qv[u] * kr[u];
-      t += dv[u] * kr[u];
-    }
-    s = wave_sum(s);
-    t = wave_sum(t);
-    const float pr = fast_exp2(s * scale_log2 - lse2);
-    const float ds = pr * (t - dl) * scale;
-#pragma unroll
-    for (int u = 0; u < NDU; ++u) acc[u] += ds * kr[u];
-  };
   const int nraw = max(i + 1 - rw.x, 0);
   const int nkeys = nraw + max(rw.z - rw.y, 0);
-  // The wave's keys n = wave, wave + kRowWaves, ... in order, kBatch at a time:
-  // their rows are loaded together, so one load latency covers the batch.
-  for (int n0 = wave; n0 < nkeys; n0 += kBatch * kRowWaves) {
-    float kr[kBatch][NDU];
+  for (int n0 = grp; n0 < nkeys; n0 += kBatch * NG) {
+    float4 kr[kBatch][NDU];
 #pragma unroll
     for (int t = 0; t < kBatch; ++t) {
-      const int n = n0 + t * kRowWaves;
-      if (n < nkeys) {
-        const float *krow = n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
-                                     : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D;
+      const int n = min(n0 + t * NG, nkeys - 1);  // (past the end: a key that is dropped)
+      const float4 *krow = reinterpret_cast<const float4 *>(
+          n < nraw ? kv + ((size_t)b * d.S + rw.x + n) * D
+                   : kvc + ((size_t)b * d.Sc + rw.y + (n - nraw)) * D);
 #pragma unroll
-        for (int u = 0; u < NDU; ++u) kr[t][u] = krow[lane + 64 * u];
-      }
+      for (int m = 0; m < NDU; ++m) kr[t][m] = krow[c + 16 * m];
     }
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t)
-      if (n0 + t * kRowWaves < nkeys) visit(kr[t]);
-  }
-  if (wave > 0) {
+    for (int t = 0; t < kBatch; ++t) {
+      if (n0 + t * NG >= nkeys) break;  // uniform within the group
+      float sv = 0.f, tv = 0.f;
 #pragma unroll
-    for (int u = 0; u < NDU; ++u) red_acc[wave - 1][lane + 64 * u] = acc[u];
+      for (int m = 0; m < NDU; ++m) {
+        sv += qv[m].x * kr[t][m].x + qv[m].y * kr[t][m].y + qv[m].z * kr[t][m].z +
+              qv[m].w * kr[t][m].w;
+        tv += dv[m].x * kr[t][m].x + dv[m].y * kr[t][m].y + dv[m].z * kr[t][m].z +
+              dv[m].w * kr[t][m].w;
+      }
+      sv = row16_sum(sv);
+      tv = row16_sum(tv);
+      const float pr = fast_exp2(sv * scale_log2 - lse2);
+      const float ds = pr * (tv - dl) * scale;
+#pragma unroll
+      for (int m = 0; m < NDU; ++m) {
+        acc[m].x += ds * kr[t][m].x;
+        acc[m].y += ds * kr[t][m].y;
+        acc[m].z += ds * kr[t][m].z;
+        acc[m].w += ds * kr[t][m].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NDU; ++m) {
+    acc[m].x = rows4_sum(acc[m].x);
+    acc[m].y = rows4_sum(acc[m].y);
+    acc[m].z = rows4_sum(acc[m].z);
+    acc[m].w = rows4_sum(acc[m].w);
+    if (lane < 16) red_acc[wave][c + 16 * m] = acc[m];
   }
   __syncthreads();
-  if (wave == 0) {
-    for (int w = 0; w < kRowWaves - 1; ++w)
-#pragma unroll
-      for (int u = 0; u < NDU; ++u) acc[u] += red_acc[w][lane + 64 * u];
-#pragma unroll
-    for (int u = 0; u < NDU; ++u) dq[row * D + lane + 64 * u] = acc[u];
+  if (threadIdx.x < C4) {
+    const int e = threadIdx.x;
+    float4 t = red_acc[0][e];
+    for (int w = 1; w < kRowWaves; ++w) {
+      const float4 x = red_acc[w][e];
+      t.x += x.x;
+      t.y += x.y;
+      t.z += x.z;
+      t.w += x.w;
+    }
+    reinterpret_cast<float4 *>(dq + row * D)[e] = t;
   }
 }
 
@@ -221,22 +275,6 @@ __global__ void __launch_bounds__(kRowWaves * 64)
 // two full wave sums per visit) a wavefront works on four visits at once with
 // a quarter of the cross-lane steps each.
 constexpr int kGroupWaves = 8;
-
-__device__ __forceinline__ float row16_sum(float v) {
-  v = dpp_plus<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v = dpp_plus<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v = dpp_plus<0x141>(v);  // row_half_mirror
-  return dpp_plus<0x140>(v);  // row_mirror
-}
-
-__device__ __forceinline__ float rows4_sum(float v) {  // the 4 rows of a wave
-  unsigned u = __float_as_uint(v);
-  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  u = __float_as_uint(v);
-  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int NDU>
 __global__ void __launch_bounds__(kGroupWaves * 64)
