@@ -153,8 +153,16 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const bf16raw *kvct_b = kvct + (size_t)b * D * d.Sc_pad;
 
   uint4 pk[St::KPT], pt[St::TPT];
+  // The query tile's list entries: the first 64 held one per lane (read with
+  // readlane, no memory round trip per tile), later ones loaded.
+  const uint32_t ent_lane = lane < e_end - e_begin ? p.qent[e_begin + lane] : 0u;
+  auto entry = [&](int e) -> uint32_t {
+    const int t = e - e_begin;
+    return t < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)ent_lane, t)
+                  : uniform_load(p.qent, e);
+  };
   auto issue = [&](int e) {
-    const uint32_t ent = p.qent[e];
+    const uint32_t ent = entry(e);
     const bool comp = ent & kEntComp;
     const int k0 = (int)(ent & kEntIdx) * kBK;
     St::load(pk, pt, tid, comp ? kvc_b : kv_b, comp ? d.Sc : d.S, comp ? kvct_b : kvt_b,
@@ -167,7 +175,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const int r0 = 8 * (j >> 2) + (j & 3), r1 = r0 + 4;
 
   for (int e = e_begin; e < e_end; ++e) {
-    const uint32_t ent = p.qent[e];
+    const uint32_t ent = entry(e);
     const bool comp = ent & kEntComp;
     const bool full = ent & kEntFull;
     const int k0 = (int)(ent & kEntIdx) * kBK;
