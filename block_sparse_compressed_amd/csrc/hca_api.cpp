@@ -241,11 +241,15 @@ hca_status run_fwd(const char *fn, const hca_plan *plan, const void *q, const vo
   }
   uint8_t *w = static_cast<uint8_t *>(ws);
   void *kvt = w + plan->ws.kvt, *kvct = w + plan->ws.kvct;
-  err = timed(K_TRANSPOSE, hip_stream, [&] {
-    return launch_transpose_kv(kv, kvt, d.S, d.S_pad, d.Sc > 0 ? kv_comp : nullptr, kvct, d.Sc,
-                               d.Sc_pad, d.B, d.D, hip_stream);
-  }, timing);
-  if (err) return hip_fail((std::string(fn) + " (transpose)").c_str(), err);
+  // The D = 512 kernels stage K tiles from tile images made here; the D = 64
+  // / 128 kernels stage the row-major tensor itself.
+  if (d.D == 512) {
+    err = timed(K_TRANSPOSE, hip_stream, [&] {
+      return launch_transpose_kv(kv, kvt, d.S, d.S_pad, d.Sc > 0 ? kv_comp : nullptr, kvct, d.Sc,
+                                 d.Sc_pad, d.B, d.D, hip_stream);
+    }, timing);
+    if (err) return hip_fail((std::string(fn) + " (transpose)").c_str(), err);
+  }
   err = timed(K_FWD, hip_stream, [&] {
     return launch_fwd_bf16(d, p, q, kv, kv_comp ? kv_comp : kv, kvt, kvct, scale, o, lse,
                            hip_stream);
@@ -335,11 +339,13 @@ extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const vo
   float *part = reinterpret_cast<float *>(w + plan->ws.part);
   void *pds = plan->pds_rows ? w + plan->ws.pds : nullptr;
   const void *kvc = kv_comp ? kv_comp : kv;
-  err = timed(K_TRANSPOSE, hip_stream, [&] {
-    return launch_transpose_kv(kv, kvt, d.S, d.S_pad, d.Sc > 0 ? kv_comp : nullptr, kvct, d.Sc,
-                               d.Sc_pad, d.B, d.D, hip_stream);
-  });
-  if (err) return hip_fail("hca_attn_bwd (transpose)", err);
+  if (d.D == 512) {  // tile images (see the forward)
+    err = timed(K_TRANSPOSE, hip_stream, [&] {
+      return launch_transpose_kv(kv, kvt, d.S, d.S_pad, d.Sc > 0 ? kv_comp : nullptr, kvct, d.Sc,
+                                 d.Sc_pad, d.B, d.D, hip_stream);
+    });
+    if (err) return hip_fail("hca_attn_bwd (transpose)", err);
+  }
   if (pds) {
     err = timed(K_BWD_PDS, hip_stream, [&] {
       return launch_bwd_pds_bf16(d, p, q, kvt, kvct, o, lse, dout, scale, delta, pds,

@@ -51,59 +51,6 @@ namespace {
 
 constexpr int kBK = 32;
 
-template <int D, int NT>
-struct StageB {
-  static constexpr int KROW = D + 8;
-  static constexpr int TROW = kBK + 8;
-  static constexpr int KCH = kBK * D / 8;
-  static constexpr int TCH = D * kBK / 8;
-  static constexpr int KPT = (KCH + NT - 1) / NT;
-  static constexpr int TPT = (TCH + NT - 1) / NT;
-
-  __device__ __forceinline__ static void load(uint4 (&pk)[KPT], uint4 (&pt)[TPT], int tid,
-                                              const bf16raw *src, int nk, const bf16raw *srct,
-                                              int ts, int k0) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * NT;
-      if (KCH % NT == 0 || c < KCH) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        const int key = k0 + row;
-        pk[u] = key < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)key * D + col * 8)
-                         : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int c = tid + u * NT;
-      if (TCH % NT == 0 || c < TCH) {
-        const int dd = c / (kBK / 8), col = c % (kBK / 8);
-        pt[u] = *reinterpret_cast<const uint4 *>(srct + (size_t)k0 * D + dd * kBK + col * 8);
-      }
-    }
-  }
-
-  __device__ __forceinline__ static void store(const uint4 (&pk)[KPT], const uint4 (&pt)[TPT],
-                                               int tid, bf16raw *k_lds, bf16raw *t_lds) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * NT;
-      if (KCH % NT == 0 || c < KCH) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        *reinterpret_cast<uint4 *>(k_lds + row * KROW + col * 8) = pk[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int c = tid + u * NT;
-      if (TCH % NT == 0 || c < TCH) {
-        const int dd = c / (kBK / 8), col = c % (kBK / 8);
-        *reinterpret_cast<uint4 *>(t_lds + dd * TROW + col * 8) = pt[u];
-      }
-    }
-  }
-};
-
 __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
   const bf16raw *x = reinterpret_cast<const bf16raw *>(&a);
   const bf16raw *y = reinterpret_cast<const bf16raw *>(&b);
@@ -130,9 +77,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
   constexpr int M = NW * MB * 16;
-  using St = StageB<D, NT>;
-  __shared__ __attribute__((aligned(16))) bf16raw k_lds[kBK * St::KROW];
-  __shared__ __attribute__((aligned(16))) bf16raw t_lds[D * St::TROW];
+  using St = KTile<D, NT>;
+  __shared__ __attribute__((aligned(16))) bf16raw k_lds[kBK * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
@@ -193,9 +139,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const int e_begin = p.qptr[item], e_end = p.qptr[item + 1];
   const bf16raw *kv_b = kv + (size_t)b * d.S * D;
   const bf16raw *kvc_b = kvc + (size_t)b * d.Sc * D;
-  const bf16raw *kvt_b = kvt + (size_t)b * D * d.S_pad;
-  const bf16raw *kvct_b = kvct + (size_t)b * D * d.Sc_pad;
-  uint4 pk[St::KPT], pt[St::TPT];
+  uint4 pk[St::KPT];
   // The query tile's list entries: the first 64 held one per lane (read with
   // readlane, no memory round trip per tile), later ones loaded.
   const uint32_t ent_lane = lane < e_end - e_begin ? p.qent[e_begin + lane] : 0u;
@@ -208,8 +152,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     const uint32_t ent = entry(e);
     const bool comp = ent & kEntComp;
     const int k0 = (int)(ent & kEntIdx) * kBK;
-    St::load(pk, pt, tid, comp ? kvc_b : kv_b, comp ? d.Sc : d.S, comp ? kvct_b : kvt_b,
-             comp ? d.Sc_pad : d.S_pad, k0);
+    St::load(pk, tid, comp ? kvc_b : kv_b, comp ? d.Sc : d.S, k0);
   };
   if (e_begin < e_end) issue(e_begin);
   const int r0 = 8 * (j >> 2) + (j & 3), r1 = r0 + 4;
@@ -220,7 +163,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     const bool full = ent & kEntFull;
     const int k0 = (int)(ent & kEntIdx) * kBK;
     __syncthreads();
-    St::store(pk, pt, tid, k_lds, t_lds);
+    St::store(pk, tid, k_lds);
     __syncthreads();
     if (e + 1 < e_end) issue(e + 1);
 
@@ -231,8 +174,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a0 = as_bf16x8(lds_load16(k_lds + r0 * St::KROW + 32 * ks + 8 * g));
-      const bf16x8 a1 = as_bf16x8(lds_load16(k_lds + r1 * St::KROW + 32 * ks + 8 * g));
+      const bf16x8 a0 = St::kfrag(k_lds, r0, ks, g);
+      const bf16x8 a1 = St::kfrag(k_lds, r1, ks, g);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         s0[mb] = mfma16x16x32(a0, qf[mb][ks], s0[mb]);
@@ -266,7 +209,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = as_bf16x8(lds_load16(t_lds + (16 * db + j) * St::TROW + 8 * g));
+      const bf16x8 a = St::tfrag(k_lds, db, g, j);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[mb][db] = mfma16x16x32(a, dsb[mb], acc[mb][db]);
     }
@@ -921,19 +864,6 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
   }
 }
 
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-
-
-// Transposed A operand of an MFMA from two ds_read_b64_tr_b16 reads: the
-// second read is `four_rows` bytes after the first (four rows further down a
-// row-major LDS tile).
-__device__ __forceinline__ bf16x8 tr_frag_rows(const char *p, int four_rows) {
-  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4 *)(p));
-  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4 *)(p + four_rows));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
 
 // ---------------------------------------------------------------------------
 // 2. dKV, key-stationary.  4 waves: wave & 1 selects 16 of the tile's 32 keys,
@@ -1196,7 +1126,7 @@ __global__ void __launch_bounds__(512, 1)
                             const float *__restrict__ lse, const float *__restrict__ delta,
                             const bf16raw *__restrict__ dout, float scale_log2, float scale,
                             float *__restrict__ part) {
-  constexpr int D = 512, KS = D / 32, NW = 8;
+  constexpr int D = 512, KS = D / 32;
   constexpr int STEP = 32, STEP_BYTES = STEP * 1024, XBYTES = 128 * STEP * 2;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * STEP_BYTES];  // [buf][Q | dO]
   __shared__ __attribute__((aligned(16))) char xs[2 * XBYTES];             // [P | dS]
@@ -1385,7 +1315,7 @@ __global__ void __launch_bounds__(512, 1)
               vis = full | ((((word >> (kk & 31)) & 1u) != 0) &
                             (__float_as_int(rr.z) != INT_MAX));
             } else {
-              vis = full | ((key >= __float_as_int(rr.z)) & (key < __float_as_int(rr.w)));
+              vis = full | ((int)(key >= __float_as_int(rr.z)) & (int)(key < __float_as_int(rr.w)));
             }
             const float ex = fast_exp2(sv[rb][v] * scale_log2 - rr.x);
             const float e = vis ? ex : 0.f;

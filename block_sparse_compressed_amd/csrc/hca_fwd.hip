@@ -11,7 +11,9 @@
 // runs
 //   S^T = K Q^T      (v_mfma_f32_16x16x32_bf16, Q fragments held in VGPRs)
 //   online softmax   (PARTIAL tiles masked in registers from per-row intervals)
-//   O^T += K^T P^T   (P rounded to bf16, K^T read from a transposed LDS copy)
+//   O^T += K^T P^T   (P rounded to bf16; K^T fragments: at D = 512 from a
+//                     transposed copy staged from the tile images, at D = 64 /
+//                     128 by transpose reads of the one staged K tile)
 // Computing S transposed leaves each lane holding one query row and 8
 // consecutive keys, which is exactly the B operand layout the PV product
 // needs: at D = 64 / 128 P stays in registers; at D = 512 each wave's P
@@ -37,60 +39,6 @@ constexpr float kLazyF = 8.f;  // lazy-rescale margin of the D = 64 / 128 forwar
 #endif
 
 
-// K tile chunks: BK rows x D; transposed tile chunks: D rows x BK.  16 B each.
-template <int D, int NT>
-struct Stage {
-  static constexpr int KROW = D + 8;    // padded LDS row of the K tile (bf16)
-  static constexpr int TROW = kBK + 8;  // padded LDS row of the transposed tile
-  static constexpr int KCH = kBK * D / 8;
-  static constexpr int TCH = D * kBK / 8;
-  static constexpr int KPT = (KCH + NT - 1) / NT;
-  static constexpr int TPT = (TCH + NT - 1) / NT;
-
-  __device__ __forceinline__ static void load(uint4 (&pk)[KPT], uint4 (&pt)[TPT], int tid,
-                                              const bf16raw *src, int nk, const bf16raw *srct,
-                                              int ts, int k0) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * NT;
-      if (KCH % NT == 0 || c < KCH) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        const int key = k0 + row;
-        pk[u] = key < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)key * D + col * 8)
-                         : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int c = tid + u * NT;
-      if (TCH % NT == 0 || c < TCH) {
-        const int dd = c / (kBK / 8), col = c % (kBK / 8);
-        pt[u] = *reinterpret_cast<const uint4 *>(srct + (size_t)k0 * D + dd * kBK + col * 8);
-      }
-    }
-  }
-
-  __device__ __forceinline__ static void store(const uint4 (&pk)[KPT], const uint4 (&pt)[TPT],
-                                               int tid, bf16raw *k_lds, bf16raw *t_lds) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * NT;
-      if (KCH % NT == 0 || c < KCH) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        *reinterpret_cast<uint4 *>(k_lds + row * KROW + col * 8) = pk[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int c = tid + u * NT;
-      if (TCH % NT == 0 || c < TCH) {
-        const int dd = c / (kBK / 8), col = c % (kBK / 8);
-        *reinterpret_cast<uint4 *>(t_lds + dd * TROW + col * 8) = pt[u];
-      }
-    }
-  }
-};
-
 template <int D, int NW, int MB>
 __global__ void __launch_bounds__(NW * 64, 1)
     hca_fwd_bf16_kernel(Dims d, DevPlan p, const bf16raw *__restrict__ q,
@@ -100,9 +48,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
   constexpr int NT = NW * 64;
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
-  using St = Stage<D, NT>;
-  __shared__ __attribute__((aligned(16))) bf16raw k_lds[kBK * St::KROW];
-  __shared__ __attribute__((aligned(16))) bf16raw t_lds[D * St::TROW];
+  using St = KTile<D, NT>;
+  __shared__ __attribute__((aligned(16))) bf16raw k_lds[kBK * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
@@ -149,10 +96,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const int e_begin = p.qptr[item], e_end = p.qptr[item + 1];
   const bf16raw *kv_b = kv + (size_t)b * d.S * D;
   const bf16raw *kvc_b = kvc + (size_t)b * d.Sc * D;
-  const bf16raw *kvt_b = kvt + (size_t)b * D * d.S_pad;
-  const bf16raw *kvct_b = kvct + (size_t)b * D * d.Sc_pad;
 
-  uint4 pk[St::KPT], pt[St::TPT];
+  uint4 pk[St::KPT];
   // The query tile's list entries: the first 64 held one per lane (read with
   // readlane, no memory round trip per tile), later ones loaded.
   const uint32_t ent_lane = lane < e_end - e_begin ? p.qent[e_begin + lane] : 0u;
@@ -165,8 +110,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     const uint32_t ent = entry(e);
     const bool comp = ent & kEntComp;
     const int k0 = (int)(ent & kEntIdx) * kBK;
-    St::load(pk, pt, tid, comp ? kvc_b : kv_b, comp ? d.Sc : d.S, comp ? kvct_b : kvt_b,
-             comp ? d.Sc_pad : d.S_pad, k0);
+    St::load(pk, tid, comp ? kvc_b : kv_b, comp ? d.Sc : d.S, k0);
   };
   if (e_begin < e_end) issue(e_begin);
 
@@ -180,7 +124,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
     const bool full = ent & kEntFull;
     const int k0 = (int)(ent & kEntIdx) * kBK;
     __syncthreads();
-    St::store(pk, pt, tid, k_lds, t_lds);
+    St::store(pk, tid, k_lds);
     __syncthreads();
     if (e + 1 < e_end) issue(e + 1);
 
@@ -192,8 +136,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a0 = as_bf16x8(lds_load16(k_lds + r0 * St::KROW + 32 * ks + 8 * g));
-      const bf16x8 a1 = as_bf16x8(lds_load16(k_lds + r1 * St::KROW + 32 * ks + 8 * g));
+      const bf16x8 a0 = St::kfrag(k_lds, r0, ks, g);
+      const bf16x8 a1 = St::kfrag(k_lds, r1, ks, g);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         s0[mb] = mfma16x16x32(a0, qf[mb][ks], s0[mb]);
@@ -249,7 +193,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = as_bf16x8(lds_load16(t_lds + (16 * db + j) * St::TROW + 8 * g));
+      const bf16x8 a = St::tfrag(k_lds, db, g, j);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb][db] = mfma16x16x32(a, pb[mb], oacc[mb][db]);
     }
@@ -606,43 +550,6 @@ struct KvCopy {
   int N, N_pad;
 };
 
-// Tile-major transpose: dst[b][t / 32][d][t % 32] = src[b][t][d] for t < N, 0 for
-// N <= t < N_pad (N_pad a multiple of 32).  Each 32-key tile's transpose is one
-// contiguous D x 32 block, so a kernel stages it with contiguous copies.  One
-// launch covers the raw tiles (blockIdx.x < raw.N_pad / 32), then the
-// compressed ones.
-template <int D>
-__global__ void __launch_bounds__(256) hca_transpose_kernel(KvCopy raw, KvCopy cmp) {
-  // One 32-key tile per workgroup: its rows come in as 16-byte pieces, go
-  // through LDS, and leave as 16-byte pieces of 8 consecutive keys.
-  constexpr int PITCH = D + 8;  // bf16 per LDS row
-  constexpr int NCH = D / 8;    // 16-byte pieces per key row
-  __shared__ __attribute__((aligned(16))) bf16raw tile[kBK * PITCH];
-  const int nraw = raw.N_pad / kBK;
-  const bool second = (int)blockIdx.x >= nraw;
-  const KvCopy k = second ? cmp : raw;
-  const int b = blockIdx.y, t = second ? blockIdx.x - nraw : blockIdx.x;
-  const int N = k.N;
-  const bf16raw *s = k.src + (size_t)b * N * D;
-  for (int c = threadIdx.x; c < kBK * NCH; c += 256) {
-    const int key = c / NCH, col = (c % NCH) * 8, gk = t * kBK + key;
-    *reinterpret_cast<uint4 *>(tile + key * PITCH + col) =
-        gk < N ? *reinterpret_cast<const uint4 *>(s + (size_t)gk * D + col)
-               : make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-  // Output piece c: column dx = c / 4, keys 8 (c % 4) .. + 7.
-  uint4 *out = reinterpret_cast<uint4 *>(k.dst + ((size_t)b * k.N_pad + (size_t)t * kBK) * D);
-  for (int c = threadIdx.x; c < D * kBK / 8; c += 256) {
-    const int dx = c / (kBK / 8), k8 = (c % (kBK / 8)) * 8;
-    ushort v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = tile[(k8 + i) * PITCH + dx];
-    out[c] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
-                        v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
-  }
-}
-
 // Tile images at D = 512: dst[b][t] (64 KiB) = the K tile t (keys 32 t ..
 // 32 t + 31, zero past N) in MFMA fragment order, then its transpose in
 // fragment order (block and lane layout as the D = 512 kernels read them).
@@ -701,15 +608,8 @@ int launch_transpose_kv(const void *kv, void *kvt, int N, int N_pad, const void 
     hipLaunchKernelGGL(hca_image512_kernel, dim3(tiles, B), dim3(256), 0, s, raw, cmp);
     return (int)hipGetLastError();
   }
-  if (raw.N_pad % kBK || cmp.N_pad % kBK) return (int)hipErrorInvalidValue;
-  const int tiles = raw.N_pad / kBK + cmp.N_pad / kBK;
-  if (tiles == 0) return hipSuccess;
-  switch (D) {
-    case 128: hipLaunchKernelGGL(hca_transpose_kernel<128>, dim3(tiles, B), dim3(256), 0, s, raw, cmp); break;
-    case 64: hipLaunchKernelGGL(hca_transpose_kernel<64>, dim3(tiles, B), dim3(256), 0, s, raw, cmp); break;
-    default: return (int)hipErrorInvalidValue;
-  }
-  return (int)hipGetLastError();
+  // (Only the D = 512 kernels read staged copies of K.)
+  return (int)hipErrorInvalidValue;
 }
 
 int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,

@@ -56,8 +56,8 @@ struct DevLayout {
 
 // Byte offsets inside the caller's workspaces.
 struct WsLayout {
-  uint64_t kvt = 0;     // raw kv tile images (bf16 path): D = 512 [B][S_pad/32][K | K^T
-                        // fragments, 64 KiB], else transposed [B][S_pad/32][D][32]
+  uint64_t kvt = 0;     // raw kv tile images (bf16, D = 512 only): [B][S_pad/32][K | K^T
+                        // fragments, 64 KiB]
   uint64_t kvct = 0;    // the same for compressed kv, Sc_pad entries
   uint64_t delta = 0;   // float32 [B][H][S] (backward)
   uint64_t part = 0;    // float32 partial key gradients (backward)
@@ -93,6 +93,8 @@ struct DevPlan {
 };
 
 // Launchers (defined in the .hip files).  Each returns a hipError_t as int.
+// launch_transpose_kv writes the D = 512 tile images (other head dims: an
+// error; their kernels stage the row-major tensor).
 int launch_transpose_kv(const void *kv, void *kvt, int N, int N_pad, const void *kvc,
                         void *kvct, int Nc, int Nc_pad, int B, int D, void *stream);
 int launch_fwd_bf16(const Dims &d, const DevPlan &p, const void *q, const void *kv,

@@ -777,14 +777,13 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     // ---- workspaces ------------------------------------------------------- //
     WsLayout &w = p->ws;
     off = 0;
-    if (dtype == HCA_BF16) {
-      // D = 512: K and K^T of every tile in MFMA fragment order (two copies);
-      // other head dims: K^T only.
-      const uint64_t copies = D == 512 ? 2 : 1;
-      w.kvt = place(copies * B * D * (nktr * bkr) * 2);
-      w.kvct = place(copies * B * D * std::max<int64_t>(1, nktc * bkc) * 2);
+    if (dtype == HCA_BF16 && D == 512) {
+      // K and K^T of every tile in MFMA fragment order (the tile images).  The
+      // D = 64 / 128 kernels stage the row-major tensor itself.
+      w.kvt = place(2 * B * D * (nktr * bkr) * 2);
+      w.kvct = place(2 * B * D * std::max<int64_t>(1, nktc * bkc) * 2);
     }
-    w.fwd_total = dtype == HCA_BF16 ? off : 0;
+    w.fwd_total = off;
     w.delta = place((uint64_t)B * H * S * 4);
     w.part = place((uint64_t)std::max<int64_t>(1, nblocks * kvb * D) * 4);
     if (stored) {

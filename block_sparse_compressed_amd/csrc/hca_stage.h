@@ -141,6 +141,71 @@ __device__ __forceinline__ void store_rows512(const floatx4 (&acc)[32], float mu
   }
 }
 
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// Transposed A operand of an MFMA from two ds_read_b64_tr_b16 reads: the
+// second read is `four_rows` bytes after the first (four rows further down a
+// row-major LDS tile).
+__device__ __forceinline__ bf16x8 tr_frag_rows(const char *p, int four_rows) {
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(p));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(p + four_rows));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A 32-key tile of the row-major K = V tensor at head dim D (64 or 128) in
+// LDS, for kernels of NT threads: rows unpadded, the 16-byte chunk c of row r
+// at slot c ^ sw(r), sw(r) = (r & 3) | ((r >> 3) & 3) << 2 (within the row's
+// D / 8 chunks).  Both MFMA operands come from this one copy: the K
+// A-operand of S^T = K Q^T as flat 16-byte reads (the eight rows a read
+// instruction touches fall in distinct bank groups), and the K^T A-operand of
+// a product over keys (O^T += K^T P^T, dQ^T += K^T dS^T) as two transpose
+// reads, so no transposed copy of K is staged.
+template <int D, int NT>
+struct KTile {
+  static constexpr int NCH = D / 8;  // 16-byte chunks per row
+  static constexpr int KCH = 32 * NCH;
+  static constexpr int KPT = (KCH + NT - 1) / NT;
+  __device__ __forceinline__ static int sw(int r) { return ((r & 3) | (((r >> 3) & 3) << 2)) & (NCH - 1); }
+  // Rows k0 .. k0 + 31 of src (nk rows; zero past the end) into registers.
+  __device__ __forceinline__ static void load(uint4 (&pk)[KPT], int tid, const bf16raw *src,
+                                              int nk, int k0) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int c = tid + u * NT;
+      if (KCH % NT == 0 || c < KCH) {
+        const int row = c / NCH, col = c % NCH;
+        const int key = k0 + row;
+        pk[u] = key < nk ? *reinterpret_cast<const uint4 *>(src + (size_t)key * D + col * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ static void store(const uint4 (&pk)[KPT], int tid, bf16raw *k_lds) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int c = tid + u * NT;
+      if (KCH % NT == 0 || c < KCH) {
+        const int row = c / NCH, col = c % NCH;
+        *reinterpret_cast<uint4 *>(k_lds + row * D + (col ^ sw(row)) * 8) = pk[u];
+      }
+    }
+  }
+  // K A-operand for k-step ks: row `row` (16 keys of the tile: rows r0 and
+  // r0 + 4 of lane (g, j)), columns 32 ks + 8 g .. + 7.
+  __device__ __forceinline__ static bf16x8 kfrag(const bf16raw *k_lds, int row, int ks, int g) {
+    return *reinterpret_cast<const bf16x8 *>(k_lds + row * D + ((4 * ks + g) ^ sw(row)) * 8);
+  }
+  // K^T A-operand of column block db: lane (g, j) gets column 16 db + j of
+  // keys 8 g .. 8 g + 7.
+  __device__ __forceinline__ static bf16x8 tfrag(const bf16raw *k_lds, int db, int g, int j) {
+    const int tr_row = 8 * g + (j >> 2);  // rows tr_row + 4 share its swizzle
+    const int off = tr_row * D * 2 + (((2 * db + ((j & 3) >> 1)) ^ sw(tr_row)) << 4) + (j & 1) * 8;
+    return tr_frag_rows(reinterpret_cast<const char *>(k_lds) + off, 4 * D * 2);
+  }
+};
+
 __device__ __forceinline__ bf16x8 lds_frag(const char *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }

@@ -136,7 +136,8 @@ typedef struct hca_plan_info {
   int64_t pairs_raw, pairs_comp;   /* visible (query position, key) pairs, summed over the
                                       batch; multiply by H for (query row, key) pairs */
   uint64_t device_bytes;           /* size of the plan's device image */
-  uint64_t ws_fwd_bytes;           /* workspace hca_attn_fwd needs */
+  uint64_t ws_fwd_bytes;           /* workspace hca_attn_fwd needs (0 for float32 and for
+                                      bfloat16 below head dim 512) */
   uint64_t ws_bwd_bytes;           /* workspace hca_attn_bwd needs (>= ws_fwd_bytes; the
                                       backward's layout starts with the forward's, so one
                                       buffer of ws_bwd_bytes serves both calls in turn) */
@@ -318,6 +319,8 @@ hca_status hca_attn_fwd(const hca_plan *plan, const void *q, const void *kv, con
  * All calls on one GPU share its scratch: calls that overlap in time on one
  * GPU (on different streams, or from different threads) race and must not be
  * issued; calls in sequence on one stream are fine.
+ * Plans with ws_fwd_bytes == 0 (float32, bfloat16 below head dim 512) do not
+ * touch the scratch.
  * Errors: as hca_attn_fwd, plus HCA_ERR_WORKSPACE (before any HIP call) when
  * the plan's ws_fwd_bytes exceeds HCA_NOALLOC_SCRATCH_BYTES, and HCA_ERR_HIP
  * when the device or the scratch address cannot be queried.

@@ -113,12 +113,28 @@ def test_plan_is_kernel_ready(plan):
     (dict(kvc=None), hca.HCA_ERR_INVALID_ARG), (dict(o=None), hca.HCA_ERR_INVALID_ARG),
     (dict(lse=FAKE + 4), hca.HCA_ERR_INVALID_ARG), (dict(scale=0.0), hca.HCA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), hca.HCA_ERR_INVALID_ARG),
-    (dict(ws_bytes=16), hca.HCA_ERR_WORKSPACE), (dict(ws=None), hca.HCA_ERR_INVALID_ARG),
     (dict(), hca.HCA_ERR_STATE),
 ])
 def test_fwd_error_paths(plan, over, status):
     assert lib.hca_attn_fwd(*fwd_args(plan, **over)) == status
     assert lib.hca_last_error().decode()
+
+
+def test_fwd_workspace_size_checked():
+    """The head dim 512 forward needs its tile-image workspace; a head dim 64
+    forward needs none (it stages the row-major K itself)."""
+    p512 = hca.hca_block_mask_build(1, 64, 8, 4, 8, H=4, D=512, dtype=hca.HCA_BF16,
+                                    tiles=(32, 32, 32))
+    assert hca.hca_plan_get_info(p512).ws_fwd_bytes > 16
+    assert lib.hca_attn_fwd(*fwd_args(p512, ws_bytes=16)) == hca.HCA_ERR_WORKSPACE
+    assert "workspace" in lib.hca_last_error().decode()
+    assert lib.hca_attn_fwd(*fwd_args(p512, ws=None)) == hca.HCA_ERR_INVALID_ARG
+    p64 = hca.hca_block_mask_build(1, 64, 8, 4, 8, H=4, D=64, dtype=hca.HCA_BF16,
+                                   tiles=(32, 32, 32))
+    assert hca.hca_plan_get_info(p64).ws_fwd_bytes == 0
+    # no workspace needed: any size and a NULL pointer pass (next: not uploaded)
+    assert lib.hca_attn_fwd(*fwd_args(p64, ws_bytes=0)) == hca.HCA_ERR_STATE
+    assert lib.hca_attn_fwd(*fwd_args(p64, ws=None)) == hca.HCA_ERR_STATE
 
 
 @pytest.mark.parametrize("over,status", [

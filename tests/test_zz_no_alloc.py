@@ -37,14 +37,18 @@ def run_pair(B, S, H, D, r, W, dtype, lengths, seed):
     return att.info.ws_fwd_bytes
 
 
-@pytest.mark.parametrize("dtype_d", [("bf16", 512), ("bf16", 128)])
-def test_noalloc_matches_workspace_forward_two_calls(dtype_d):
+def test_noalloc_matches_workspace_forward_two_calls():
+    """Head dim 512 (the forward's tile images live in the scratch array): two
+    calls in a row, the second smaller, each equal to the workspace forward."""
+    big = run_pair(1, 12000, 64, 512, 64, 128, "bf16", [[5000, 7000]], seed=31)
+    small = run_pair(1, 1500, 64, 512, 16, 100, "bf16", None, seed=32)
+    assert 0 < small < big
+
+
+@pytest.mark.parametrize("dtype_d", [("f32", 64), ("bf16", 128)])
+def test_noalloc_needs_no_scratch_below_d512(dtype_d):
+    """float32 and head dim 64 / 128 forwards use no workspace: the entry point
+    runs them without touching the scratch array."""
     dtype, D = dtype_d
-    H = 64 if D == 512 else 16
-    big = run_pair(1, 12000, H, D, 64, 128, dtype, [[5000, 7000]], seed=31)
-    small = run_pair(1, 1500, H, D, 16, 100, dtype, None, seed=32)
-    assert small < big
-
-
-def test_noalloc_float32_needs_no_scratch():
-    assert run_pair(1, 489, 4, 64, 16, 64, "f32", None, seed=33) == 0
+    H = 4 if dtype == "f32" else 16
+    assert run_pair(1, 489, H, D, 16, 64, dtype, None, seed=33) == 0
