@@ -134,9 +134,11 @@ hipStream_t side_stream() {
 struct SideStream {
   hipStream_t stream = nullptr;
   hipStream_t caller = nullptr;
+  // Without a second stream (it could not be created) the work stays on the
+  // caller's stream: `stream` remains nullptr and the call runs serially.
   int fork(void *caller_stream) {
     hipStream_t s = side_stream();
-    if (!s) return (int)hipErrorOutOfMemory;
+    if (!s) return 0;
     hipEvent_t ev = nullptr;
     hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventRecord(ev, (hipStream_t)caller_stream);

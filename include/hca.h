@@ -45,7 +45,8 @@
  *     thread's current device, which must be the stream's, and kept until the
  *     process ends).  It is forked from the caller's stream and joined back
  *     into it with events before the call returns, so the call as a whole
- *     stays ordered on the caller's stream.
+ *     stays ordered on the caller's stream.  If that stream cannot be
+ *     created, the dQ pass runs on the caller's stream instead.
  *
  * Errors.  Every entry point validates all of its arguments before it makes
  * any HIP call, and returns a status; no exception crosses the ABI.  A
