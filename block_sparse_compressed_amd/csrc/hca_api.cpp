@@ -90,26 +90,56 @@ enum KernelId { K_TRANSPOSE, K_FWD, K_BWD_DQ, K_BWD_DKV, K_DKV_REDUCE, K_FWD_F32
 const char *const kKernelNames[K_COUNT] = {"transpose", "fwd",     "bwd_dq",  "bwd_dkv",
                                            "dkv_reduce", "fwd_f32", "bwd_f32", "bwd_pds"};
 struct TimingRec {
-  int kid;
+  int kid, dev;
   hipEvent_t a, b;
 };
 std::mutex g_tmu;
 bool g_timing = false;
 std::vector<TimingRec> g_recs;
+// Events read back and ready for reuse, per device (an event is recorded only
+// on streams of the device it was created on).
+std::vector<std::vector<hipEvent_t>> g_free_events;
+
+// An event for a timed region on device `dev`: a reused one when
+// available (creating events costs host time inside the region being
+// measured), else a new one.
+hipEvent_t take_event(int dev) {
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if ((size_t)dev < g_free_events.size() && !g_free_events[dev].empty()) {
+      hipEvent_t e = g_free_events[dev].back();
+      g_free_events[dev].pop_back();
+      return e;
+    }
+  }
+  hipEvent_t e = nullptr;
+  return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
+
+void give_event(int dev, hipEvent_t e) {  // caller holds g_tmu
+  if (g_free_events.size() <= (size_t)dev) g_free_events.resize(dev + 1);
+  g_free_events[dev].push_back(e);
+}
 
 // Runs `launch` (which enqueues one library kernel on `stream`), bracketed by
 // events when timing is enabled and `allowed` (the allocation-free entry
 // point never creates events).
 template <class F>
 int timed(int kid, void *stream, F launch, bool allowed = true) {
-  if (!g_timing || !allowed) return launch();
-  hipEvent_t a = nullptr, b = nullptr;
-  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return launch();
+  int dev = 0;
+  if (!g_timing || !allowed || hipGetDevice(&dev) != hipSuccess || dev < 0) return launch();
+  hipEvent_t a = take_event(dev), b = take_event(dev);
+  if (!a || !b) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (a) give_event(dev, a);
+    if (b) give_event(dev, b);
+    return launch();
+  }
   hipEventRecord(a, (hipStream_t)stream);
   int err = launch();
   hipEventRecord(b, (hipStream_t)stream);
   std::lock_guard<std::mutex> lk(g_tmu);
-  g_recs.push_back({kid, a, b});
+  g_recs.push_back({kid, dev, a, b});
   return err;
 }
 
@@ -398,14 +428,30 @@ extern "C" hca_status hca_timing_read(hca_kernel_time *out, int32_t capacity, in
   double ms[K_COUNT] = {0};
   int64_t n[K_COUNT] = {0};
   hca_status st = HCA_OK;
-  for (const TimingRec &r : recs) {
+  std::vector<bool> ok(recs.size(), true);
+  for (size_t i = 0; i < recs.size(); ++i) {
+    const TimingRec &r = recs[i];
     float t = 0.f;
-    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
       st = fail(HCA_ERR_HIP, "hca_timing_read: event query failed");
+      ok[i] = false;
+    }
     ms[r.kid] += t;
     n[r.kid] += 1;
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+  }
+  {
+    // Completed pairs go back to the pool; a pair whose query failed is
+    // destroyed instead of being reused.
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (size_t i = 0; i < recs.size(); ++i) {
+      if (ok[i]) {
+        give_event(recs[i].dev, recs[i].a);
+        give_event(recs[i].dev, recs[i].b);
+      } else {
+        (void)hipEventDestroy(recs[i].a);
+        (void)hipEventDestroy(recs[i].b);
+      }
+    }
   }
   int32_t c = 0;
   for (int k = 0; k < K_COUNT; ++k) {

@@ -355,9 +355,11 @@ hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const void *kv, con
  * second stream, where its span overlaps the key-stationary pass's and is no
  * exclusive time).  hca_timing_read waits for the recorded events, writes
  * per-family totals (up to `capacity` entries, *count = number of families
- * timed) and clears them.  Not thread-safe against concurrent hca_attn_* calls on
- * other threads while enabled.  Errors: HCA_ERR_INVALID_ARG on NULL output
- * pointers, HCA_ERR_HIP if an event cannot be created or read.
+ * timed) and clears them.  Events that have been read are kept in a per-device
+ * pool and reused, so timed calls after the first create none; a kernel whose
+ * events cannot be created runs untimed.  Not thread-safe against concurrent
+ * hca_attn_* calls on other threads while enabled.  Errors: HCA_ERR_INVALID_ARG
+ * on NULL output pointers, HCA_ERR_HIP if a recorded event cannot be read.
  */
 typedef struct hca_kernel_time {
   char name[32];    /* kernel family, e.g. "fwd", "bwd_dq", "bwd_dkv" */
