@@ -1406,11 +1406,12 @@ __global__ void __launch_bounds__(512, 1)
 //     the query tiles of a run of 64-position chunks that see it), two
 //     workgroups per CU.  Per 32-row step, Q and dO rows (64 KiB, chunks
 //     XOR-swizzled) and the P / dS rows of the tile's two 32-key halves
-//     (8 KiB, as stored) are copied straight to LDS, single-buffered (the
-//     other workgroup on the CU covers the copy).  Wave w accumulates columns
-//     d in [128 w, 128 w + 128) of all 64 keys (128 fp32 sums per lane); the A
-//     operands are transpose reads of the row tiles, the B operands transpose
-//     reads of the P / dS tiles.  A half that the query tile does not list is
+//     (8 KiB, as stored) are copied straight to LDS, single-buffered, in two
+//     halves: Q with dS, dO with P.  Each half's copy runs under the math of
+//     the other half (and the other workgroup on the CU covers the rest of
+//     the wait).  Wave w accumulates columns d in [128 w, 128 w + 128) of all
+//     64 keys (128 fp32 sums per lane); the A operands are transpose reads of
+//     the row tiles, the B operands transpose reads of the P / dS tiles.  A half that the query tile does not list is
 //     read as zeros (an empty buffer range).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256, 2)
@@ -1419,6 +1420,11 @@ __global__ void __launch_bounds__(256, 2)
                            float *__restrict__ part) {
   constexpr int D = 512, STEP = 32, STEP_BYTES = STEP * 1024;
   constexpr int PT = STEP * 64;  // bytes of one stored half-tile step (32 rows x 32 keys)
+  // Copy instructions per wave and half-step: kRowCopies rows of Q or dO and
+  // one KiB of dS or P.  The hand-counted waits below rely on these being the
+  // only vector-memory instructions between them.
+  constexpr int kRowCopies = 8, kHalfCopies = kRowCopies + 1;
+  static_assert(4 * kRowCopies == STEP, "four waves copy the step's rows, one per copy");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STEP_BYTES];  // [Q | dO]
   __shared__ __attribute__((aligned(1024))) char ps[4 * PT];           // [P lo|P hi|dS lo|dS hi]
 
@@ -1442,41 +1448,43 @@ __global__ void __launch_bounds__(256, 2)
   // The wave's 8 rows of a step are 8 consecutive positions of one head (bq
   // is a power of two >= 8), so away from the sequence end they are 8 KiB
   // in a row: one base address, row i at i KiB.
-  uint32_t voff_row[8];
+  uint32_t voff_row[kRowCopies];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) voff_row[i] = ((lane_sw ^ (uint32_t)(i & 3)) << 4) + 1024u * i;
-  auto stage = [&](int s) {
+  for (int i = 0; i < kRowCopies; ++i)
+    voff_row[i] = ((lane_sw ^ (uint32_t)(i & 3)) << 4) + 1024u * i;
+  // Half-step copies: tensor 0 = the Q rows and both dS halves, tensor 1 =
+  // the dO rows and both P halves.
+  auto stage = [&](int s, int tensor) {
     const int e = s >> lspq, u = s & (SPQ - 1);
     const int qt = (int)(uniform_load(p.kvent, it.e0 + e) & kEntIdx);
     const int rho0 = u * STEP + 8 * wave;
     const int pos0 = qt * d.bq + (rho0 & (d.bq - 1)), h0 = rho0 >> lbq;
-    if (pos0 + 7 < d.S) {
+    const bf16raw *src_rows = tensor ? dout : q;
+    const uint32_t rows_lds = qb_lds + tensor * STEP_BYTES;
+    if (pos0 + kRowCopies - 1 < d.S) {
       const size_t rowoff = bat + ((size_t)h0 * d.S + pos0) * D;  // wave-uniform
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lds = qb_lds + (8 * wave + i) * 1024;
-        dma16(q + rowoff, voff_row[i], lds);
-        dma16(dout + rowoff, voff_row[i], lds + STEP_BYTES);
-      }
+      for (int i = 0; i < kRowCopies; ++i)
+        dma16(src_rows + rowoff, voff_row[i], rows_lds + (8 * wave + i) * 1024);
     } else {
       // Last positions: rows past the end read the last row (never used).
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kRowCopies; ++i) {
         const int r = 8 * wave + i;
         const int pos = min(pos0 + i, d.S - 1);
         const size_t rowoff = bat + ((size_t)h0 * d.S + pos) * D;  // wave-uniform
         const uint32_t voff = (lane_sw ^ (uint32_t)(i & 3)) << 4;
-        dma16(q + rowoff, voff, qb_lds + r * 1024);
-        dma16(dout + rowoff, voff, qb_lds + STEP_BYTES + r * 1024);
+        dma16(src_rows + rowoff, voff, rows_lds + r * 1024);
       }
     }
-    const int ent = (int)uniform_load((const uint32_t *)p.kvpe, 2 * (it.e0 + e) + (wave & 1));
-    // rows u * 32 .. u * 32 + 31 of the half's P (wave < 2) or dS (wave >= 2)
+    // Wave w: KiB (w & 1) of half (w >> 1) of the step's dS (tensor 0) or P.
+    const int half = wave >> 1;
+    const int ent = (int)uniform_load((const uint32_t *)p.kvpe, 2 * (it.e0 + e) + half);
     const char *src = pds + (ent >= 0 ? (size_t)ent * blk_bytes : 0) +
-                      (size_t)(wave >> 1) * d.pds_rows * 64 + (size_t)u * PT;
+                      (size_t)(1 - tensor) * d.pds_rows * 64 + (size_t)u * PT;
     const rsrc_t r = make_rsrc(src, ent >= 0 ? PT : 0);
-    buf_load16(r, lds_addr(ps + wave * PT), 16 * lane);
-    buf_load16(r, lds_addr(ps + wave * PT + 1024), 1024 + 16 * lane);
+    const int blk = 2 * (1 - tensor) + half;
+    buf_load16(r, lds_addr(ps + blk * PT + (wave & 1) * 1024), (wave & 1) * 1024 + 16 * lane);
   };
   // Transposed A operands of column block 8 wave + dl: chunk 16 wave + 2 dl +
   // c0 of rows 8 g + (j >> 2) (and + 4) of the swizzled row tiles.
@@ -1498,40 +1506,47 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
     for (int dl = 0; dl < 8; ++dl) acc[kb][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (nsteps > 0) stage(0);
-  for (int s = 0; s < nsteps; ++s) {
-    wait_all_loads();
-    __syncthreads();  // rows and P / dS of step s in LDS
+  // One half-step: acc += (row tile of `tensor`)^T x (its stored partner),
+  // Q with dS (tensor 0), dO with P (tensor 1).
+  auto half_step = [&](int tensor) {
     int trb = tr_base;
     asm volatile("" : "+v"(trb));
-    const char *qb = smem, *ob = smem + STEP_BYTES;
-    bf16x8 xp[4], xd[4];
+    const char *rb = smem + tensor * STEP_BYTES;
+    bf16x8 x[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      xp[kb] = xfrag(0, kb);
-      xd[kb] = xfrag(1, kb);
-    }
-    // Two passes of four column blocks: the pass's transposed row fragments
-    // are held while the key blocks stream through.
+    for (int kb = 0; kb < 4; ++kb) x[kb] = xfrag(1 - tensor, kb);
 #pragma unroll
     for (int ps_ = 0; ps_ < 2; ++ps_) {
-      bf16x8 tq[4], to[4];
+      bf16x8 tr[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int to_ = trb + ((tr_sw ^ (2 * (4 * ps_ + c))) << 4);
-        tq[c] = tr_frag(qb + to_);
-        to[c] = tr_frag(ob + to_);
-      }
+      for (int c = 0; c < 4; ++c) tr[c] = tr_frag(rb + trb + ((tr_sw ^ (2 * (4 * ps_ + c))) << 4));
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[kb][4 * ps_ + c] = mfma16x16x32(tq[c], xd[kb], acc[kb][4 * ps_ + c]);
-          acc[kb][4 * ps_ + c] = mfma16x16x32(to[c], xp[kb], acc[kb][4 * ps_ + c]);
-        }
+        for (int c = 0; c < 4; ++c)
+          acc[kb][4 * ps_ + c] = mfma16x16x32(tr[c], x[kb], acc[kb][4 * ps_ + c]);
     }
-    __syncthreads();  // step s no longer read
-    if (s + 1 < nsteps) stage(s + 1);
+  };
+  // Each half-step's copy runs under the other half-step's math: the dO / P
+  // copy of step s under the Q / dS half of step s, the Q / dS copy of step
+  // s + 1 under the dO / P half of step s.  Per element the sums keep the
+  // order dS Q (s), P dO (s), dS Q (s + 1), ...
+  if (nsteps > 0) {
+    stage(0, 0);
+    stage(0, 1);
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    if (s == 0)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kHalfCopies) : "memory");
+    else
+      wait_all_loads();
+    __syncthreads();  // Q / dS of step s visible; the dO / P buffers are free
+    if (s > 0) stage(s, 1);
+    half_step(0);
+    wait_all_loads();
+    __syncthreads();  // dO / P of step s visible; the Q / dS buffers are free
+    if (s + 1 < nsteps) stage(s + 1, 0);
+    half_step(1);
   }
 
   // Partial [64 keys][512]: this wave's 128 columns of every key.
