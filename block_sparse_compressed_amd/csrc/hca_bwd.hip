@@ -671,6 +671,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     // S^T and dP^T of tile it (shared K A-operands), K fragments read three
     // k-steps ahead of their MFMAs.
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+    mfma_phase_begin();
     {
       constexpr int PF = 3;
       const char *kb = smem + (it & 1) * kTileBytes512 + frag_off;
@@ -699,6 +700,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
     }
+    mfma_phase_end();
     // P = 2^(S scale log2e - LSE log2e) on visible keys, dS = scale P (dP - delta).
     {
       const bool comp = ent & kEntComp;
@@ -821,6 +823,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     stage(it + NST - 1);
     const char *st = smem + (it % NST) * STAGE;
     const char *tb = st + wave * CB * 1024 + frag_off;
+    mfma_phase_begin();
     bf16x8 kt[CB];
 #pragma unroll
     for (int c = 0; c < CB; ++c) kt[c] = lds_frag(tb + c * 1024);
@@ -832,6 +835,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
 #pragma unroll
       for (int c = 0; c < CB; ++c) acc[rb][c] = mfma16x16x32(kt[c], cur, acc[rb][c]);
     }
+    mfma_phase_end();
   }
   __syncthreads();  // every stage read before the rows are staged over them
 
@@ -1509,6 +1513,7 @@ __global__ void __launch_bounds__(256, 2)
   // One half-step: acc += (row tile of `tensor`)^T x (its stored partner),
   // Q with dS (tensor 0), dO with P (tensor 1).
   auto half_step = [&](int tensor) {
+    mfma_phase_begin();
     int trb = tr_base;
     asm volatile("" : "+v"(trb));
     const char *rb = smem + tensor * STEP_BYTES;
@@ -1526,6 +1531,7 @@ __global__ void __launch_bounds__(256, 2)
         for (int c = 0; c < 4; ++c)
           acc[kb][4 * ps_ + c] = mfma16x16x32(tr[c], x[kb], acc[kb][4 * ps_ + c]);
     }
+    mfma_phase_end();
   };
   // Each half-step's copy runs under the other half-step's math: the dO / P
   // copy of step s under the Q / dS half of step s, the Q / dS copy of step

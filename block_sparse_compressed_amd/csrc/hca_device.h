@@ -19,6 +19,13 @@ __device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Wave issue priority around a block of matrix instructions: while it is
+// raised, the SIMD's arbiter picks this wave ahead of waves that are issuing
+// copies, softmax or address arithmetic, so the matrix unit stays fed while
+// the other waves of the CU do that work.  It orders issue only.
+__device__ __forceinline__ void mfma_phase_begin() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mfma_phase_end() { __builtin_amdgcn_s_setprio(0); }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ uint4 lds_load16(const void *p) {

@@ -319,6 +319,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
     constexpr int PF = HCA_FWD_QK_PF;
     const char *kb = kbase + (t & (kBufs - 1)) * kTileBytes512 + frag_off;
     s[0] = s[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    mfma_phase_begin();
     bf16x8 a0[KS], a1[KS];
 #pragma unroll
     for (int ks = 0; ks < PF; ++ks) {
@@ -340,6 +341,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
       if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
+    mfma_phase_end();
   };
 
   // Masked plans: the row's 32 visibility bits for the compressed tile of
@@ -416,6 +418,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
         for (int c = 0; c < CB; ++c) oacc[rb][c] *= a;
       }
     }
+    mfma_phase_begin();
     const char *tb = tbase + (t & (kBufs - 1)) * kTileBytes512 + wave * CB * 1024 + frag_off;
     const char *pb = pbuf[bf] + frag_off;
     bf16x8 kt[CB], pf[RB];
@@ -435,6 +438,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
       if (rb + 2 < RB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
     }
+    mfma_phase_end();
   };
 
   floatx4 sc[2];
