@@ -175,7 +175,7 @@ def cpu_baseline(wl, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported"
+        print("bench.py: the library runs on exactly one GPU; --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.source_hashes:

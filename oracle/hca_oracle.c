@@ -13,7 +13,7 @@
  *   of raw keys plus every compression window that has completed before it;
  *   the pattern is deterministic (no indexer, no top-k).  The precise
  *   conventions used here (window bounds, completion boundary, segment rule)
- *   are the ones fixed for this library and listed in the design doc:
+ *   are the ones this library fixes where the pages leave them open:
  *     raw key t is visible to query i   iff  i - W < t <= i  and seg(t) == seg(i)
  *     compressed entry c (covering raw positions [c*r, (c+1)*r)) is visible
  *     to query i  iff  (c+1)*r <= i+1  and  segc(c) == seg(i)
