@@ -112,7 +112,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), the "
                          "reference kernel that checks the HBM request-counter arithmetic")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+    return args
 
 
 def copy_probe(mib):
