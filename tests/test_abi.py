@@ -269,3 +269,16 @@ def test_binding_binds_to_torch_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                          cwd=ROOT, check=True).stdout
     assert out.strip().splitlines()[-1] == "True"
+
+
+def test_timing_read_checks_and_empty():
+    """hca_timing_read: NULL count (or NULL output with a capacity) is an
+    invalid argument; with nothing timed it reports zero kernel families, and
+    enabling / disabling makes no HIP call."""
+    n = ctypes.c_int32(-1)
+    assert lib.hca_timing_read(None, 4, ctypes.byref(n)) == hca.HCA_ERR_INVALID_ARG
+    assert lib.hca_timing_read(None, 0, None) == hca.HCA_ERR_INVALID_ARG
+    assert lib.hca_timing_enable(1) == hca.HCA_OK
+    assert lib.hca_timing_enable(0) == hca.HCA_OK
+    assert lib.hca_timing_read(None, 0, ctypes.byref(n)) == hca.HCA_OK and n.value == 0
+    assert hca.hca_timing_read() == {}
