@@ -289,12 +289,14 @@ __global__ void __launch_bounds__(kGroupWaves * 64)
   __shared__ float4 red[kGroupWaves][C4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, grp = wave * 4 + (lane >> 4);
-  const int per_b = d.S + d.Sc;
-  const int64_t kk = blockIdx.x;  // whole workgroup: same key
-  if (kk >= (int64_t)d.B * per_b) return;
-  const int b = (int)(kk / per_b), idx = (int)(kk % per_b);
-  const bool comp = idx >= d.S;
-  const int k = comp ? idx - d.S : idx;
+  // Whole workgroup: one key.  The compressed entries (each seen by every
+  // later position of its document: the longest walks) take the first
+  // workgroup ids, so they start first and the raw keys fill in beside them.
+  const int64_t x = blockIdx.x, ncomp = (int64_t)d.B * d.Sc;
+  if (x >= ncomp + (int64_t)d.B * d.S) return;
+  const bool comp = x < ncomp;
+  const int b = comp ? (int)(x / d.Sc) : (int)((x - ncomp) / d.S);
+  const int k = comp ? (int)(x % d.Sc) : (int)((x - ncomp) % d.S);
   const float4 *krow = reinterpret_cast<const float4 *>(
       comp ? kvc + ((size_t)b * d.Sc + k) * D : kv + ((size_t)b * d.S + k) * D);
   float4 kr[NDU], acc[NDU];
