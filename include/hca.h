@@ -339,8 +339,11 @@ hca_status hca_attn_fwd_noalloc(const hca_plan *plan, const void *q, const void 
  * with dS_k = P_k (<dout, kv_k> - <dout, o>).  Key K and value V are one
  * tensor, so each key's two gradient paths are summed ("[DeepSeek-V4]
  * Implement Compressed Attention Layers", review suggestions: k = kv, v = kv).
- * dQ is accumulated in registers, never through atomics to device memory.
- *   ws   device workspace of at least info.ws_bwd_bytes
+ * dQ is accumulated in registers, never through atomics to device memory;
+ * the key gradients are summed from per-item partial sums in a fixed order,
+ * so the same inputs and plan give bitwise the same outputs on every call.
+ *   ws   device workspace of at least info.ws_bwd_bytes (its contents on
+ *        return are unspecified; nothing needs to be kept between calls)
  *   dkv_comp / kv_comp may be NULL only when S_c == 0.
  * Errors as for hca_attn_fwd.
  */
