@@ -154,7 +154,7 @@ def hca_last_error() -> str:
     return _lib.hca_last_error().decode()
 
 
-@dataclass
+@dataclass(frozen=True)
 class PlanInfo:
     B: int; S: int; H: int; D: int; r: int; W: int; S_c: int
     dtype: int; comp_mode: int; bq: int; bk_raw: int; bk_comp: int
@@ -175,6 +175,7 @@ class Plan:
         # the module's globals are cleared, can still be released.
         self._destroy = _lib.hca_plan_destroy
         self.device_buffer = None  # keeps the uploaded torch buffer alive
+        self.info_cache = None  # PlanInfo (a plan never changes after it is built)
 
     @property
     def handle(self):
@@ -264,9 +265,11 @@ def hca_block_mask_build_topk(B, S, W, S_c, idx, seg_starts=None, seg_counts=Non
 
 
 def hca_plan_get_info(plan: Plan) -> PlanInfo:
-    info = _PlanInfo()
-    _check(_lib.hca_plan_get_info(plan.handle, ctypes.byref(info)))
-    return PlanInfo(**{n: getattr(info, n) for n, _ in _PlanInfo._fields_})
+    if plan.info_cache is None:
+        info = _PlanInfo()
+        _check(_lib.hca_plan_get_info(plan.handle, ctypes.byref(info)))
+        plan.info_cache = PlanInfo(**{n: getattr(info, n) for n, _ in _PlanInfo._fields_})
+    return plan.info_cache
 
 
 def hca_plan_export_tiles(plan: Plan):
@@ -327,6 +330,10 @@ def _expect(t, name, shape, dtype):
     import torch
 
     if t is None:
+        return
+    # Fast path: the checks below, in one expression, for the common case.
+    if (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.shape == shape
+            and t.is_contiguous()):
         return
     if not isinstance(t, torch.Tensor):
         raise HcaInvalidArgument(HCA_ERR_INVALID_ARG, "%s must be a torch tensor" % name)

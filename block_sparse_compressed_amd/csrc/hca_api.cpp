@@ -38,6 +38,7 @@ Dims make_dims(const hca_plan *plan) {
   d.nkv_comp = plan->nkv_comp;
   d.cmask_ldw = plan->cmask_ldw;
   d.pds_rows = plan->pds_rows;
+  d.f32_split = plan->f32_split;
   return d;
 }
 
@@ -362,7 +363,8 @@ extern "C" hca_status hca_attn_bwd(const hca_plan *plan, const void *q, const vo
     err = timed(K_BWD_F32, hip_stream, [&] {
       return launch_bwd_f32(d, p, (const float *)q, (const float *)kv, (const float *)kv_comp,
                             (const float *)o, lse, (const float *)dout, scale, (float *)dq,
-                            (float *)dkv, (float *)dkv_comp, delta, hip_stream);
+                            (float *)dkv, (float *)dkv_comp, delta,
+                            reinterpret_cast<float *>(w + plan->ws.f32_part), hip_stream);
     });
     if (err) return hip_fail("hca_attn_bwd (float32 kernels)", err);
     return HCA_OK;

@@ -282,21 +282,26 @@ __global__ void __launch_bounds__(kGroupWaves * 64)
                                 const float *__restrict__ kv, const float *__restrict__ kvc,
                                 const float *__restrict__ lse, const float *__restrict__ delta,
                                 const float *__restrict__ dout, float scale_log2, float scale,
-                                float *__restrict__ dkv, float *__restrict__ dkvc) {
+                                float *__restrict__ dkv, float *__restrict__ dkvc,
+                                float *__restrict__ part) {
   constexpr int D = NDU * 64, C4 = D / 4;     // 16-byte pieces per row
   constexpr int NG = kGroupWaves * 4;          // 16-lane rows per workgroup
   constexpr int VB = NDU <= 1 ? 8 : NDU <= 2 ? 4 : NDU <= 4 ? 2 : 1;  // visits per batch
   __shared__ float4 red[kGroupWaves][C4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, grp = wave * 4 + (lane >> 4);
-  // Whole workgroup: one key.  The compressed entries (each seen by every
-  // later position of its document: the longest walks) take the first
-  // workgroup ids, so they start first and the raw keys fill in beside them.
-  const int64_t x = blockIdx.x, ncomp = (int64_t)d.B * d.Sc;
+  // Whole workgroup: one key, or one of the f32_split parts of a compressed
+  // entry's visits.  The compressed entries (each seen by every later
+  // position of its document: the longest walks) take the first workgroup
+  // ids, so they start first and the raw keys fill in beside them.
+  const int nsplit = d.f32_split;
+  const int64_t x = blockIdx.x, ncomp = (int64_t)d.B * d.Sc * nsplit;
   if (x >= ncomp + (int64_t)d.B * d.S) return;
   const bool comp = x < ncomp;
-  const int b = comp ? (int)(x / d.Sc) : (int)((x - ncomp) / d.S);
-  const int k = comp ? (int)(x % d.Sc) : (int)((x - ncomp) % d.S);
+  const int64_t centry = comp ? x / nsplit : 0;  // b * Sc + k
+  const int split = comp ? (int)(x % nsplit) : 0;
+  const int b = comp ? (int)(centry / d.Sc) : (int)((x - ncomp) / d.S);
+  const int k = comp ? (int)(centry % d.Sc) : (int)((x - ncomp) % d.S);
   const float4 *krow = reinterpret_cast<const float4 *>(
       comp ? kvc + ((size_t)b * d.Sc + k) * D : kv + ((size_t)b * d.S + k) * D);
   float4 kr[NDU], acc[NDU];
@@ -314,10 +319,15 @@ __global__ void __launch_bounds__(kGroupWaves * 64)
     i0 = k;
     i1 = d.W > 0 ? min(d.S - 1, k + d.W - 1) : k - 1;
   }
-  const int nvis = i1 >= i0 ? (i1 - i0 + 1) * d.H : 0;
-  // Row group g takes visits g, g + NG, g + 2 NG, ... (position-major), VB at
-  // a time with their loads issued together.
-  for (int v0 = grp; v0 < nvis; v0 += VB * NG) {
+  const int nvis_all = i1 >= i0 ? (i1 - i0 + 1) * d.H : 0;
+  // This workgroup's visits [vlo, nvis): all of them, or split `split` of
+  // nsplit equal ranges.
+  const int per = (nvis_all + nsplit - 1) / nsplit;
+  const int vlo = comp ? min(nvis_all, split * per) : 0;
+  const int nvis = comp ? min(nvis_all, vlo + per) : nvis_all;
+  // Row group g takes visits vlo + g, vlo + g + NG, ... (position-major), VB
+  // at a time with their loads issued together.
+  for (int v0 = vlo + grp; v0 < nvis; v0 += VB * NG) {
     float4 qv[VB][NDU], dv[VB][NDU];
     float ls[VB], dt[VB];
     bool on[VB];
@@ -325,7 +335,7 @@ __global__ void __launch_bounds__(kGroupWaves * 64)
     for (int t = 0; t < VB; ++t) {
       const int v = v0 + t * NG;
       on[t] = v < nvis;
-      const int vc = on[t] ? v : grp;  // (an in-range visit; its result is dropped)
+      const int vc = on[t] ? v : vlo + grp;  // (an in-range visit; its result is dropped)
       const int i = i0 + vc / d.H, h = vc % d.H;
       const int4 rw = reinterpret_cast<const int4 *>(p.rows)[(size_t)b * d.S + i];
       on[t] = on[t] && (comp ? (rw.y <= k && k < rw.z) : (rw.x <= k));
@@ -381,10 +391,34 @@ __global__ void __launch_bounds__(kGroupWaves * 64)
       t.z += x.z;
       t.w += x.w;
     }
-    float4 *out = reinterpret_cast<float4 *>(comp ? dkvc + ((size_t)b * d.Sc + k) * D
-                                                  : dkv + ((size_t)b * d.S + k) * D);
+    // A split's sum goes to the partial area; hca_dkv_f32_split_sum_kernel
+    // adds the splits of each entry in split order.
+    float4 *out = reinterpret_cast<float4 *>(
+        comp ? (nsplit > 1 ? part + ((size_t)centry * nsplit + split) * D
+                           : dkvc + ((size_t)b * d.Sc + k) * D)
+             : dkv + ((size_t)b * d.S + k) * D);
     out[tid] = t;
   }
+}
+
+// Compressed entries' dKV from their split partial sums: one workgroup per
+// entry, thread e adds 16-byte piece e of the f32_split partials in split
+// order.
+__global__ void __launch_bounds__(128)
+    hca_dkv_f32_split_sum_kernel(Dims d, const float *__restrict__ part, float *__restrict__ dkvc) {
+  const int C4 = d.D / 4, e = threadIdx.x;
+  if (e >= C4) return;
+  const size_t entry = blockIdx.x;  // b * Sc + k
+  const float4 *pe = reinterpret_cast<const float4 *>(part + entry * d.f32_split * d.D);
+  float4 t = pe[e];
+  for (int s = 1; s < d.f32_split; ++s) {
+    const float4 x = pe[s * C4 + e];
+    t.x += x.x;
+    t.y += x.y;
+    t.z += x.z;
+    t.w += x.w;
+  }
+  reinterpret_cast<float4 *>(dkvc + entry * d.D)[e] = t;
 }
 
 #define HCA_F32_SWITCH(D, CALL) \
@@ -416,9 +450,10 @@ int launch_fwd_f32(const Dims &d, const DevPlan &p, const float *q, const float 
 
 int launch_bwd_f32(const Dims &d, const DevPlan &p, const float *q, const float *kv,
                    const float *kvc, const float *o, const float *lse, const float *dout,
-                   float scale, float *dq, float *dkv, float *dkvc, float *delta, void *stream) {
+                   float scale, float *dq, float *dkv, float *dkvc, float *delta,
+                   float *f32_part, void *stream) {
   const int64_t rows = (int64_t)d.B * d.H * d.S;
-  const int64_t keys = (int64_t)d.B * (d.S + d.Sc);
+  const int64_t keys = (int64_t)d.B * (d.S + (int64_t)d.Sc * d.f32_split);
   hipStream_t s = (hipStream_t)stream;
   const float sl2 = scale * kLog2e;
 #define CALL(N)                                                                              \
@@ -431,9 +466,13 @@ int launch_bwd_f32(const Dims &d, const DevPlan &p, const float *q, const float 
 #define CALL(N)                                                                          \
   hipLaunchKernelGGL(hca_bwd_dkv_f32_rows_kernel<N>, dim3((unsigned)keys),               \
                      dim3(kGroupWaves * 64), 0, s, d, p, q, kv, kvc, lse, delta, dout, sl2, \
-                     scale, dkv, dkvc)
+                     scale, dkv, dkvc, f32_part)
   HCA_F32_SWITCH(d.D, CALL)
 #undef CALL
+  err = (int)hipGetLastError();
+  if (err || d.f32_split <= 1 || d.Sc == 0) return err;
+  hipLaunchKernelGGL(hca_dkv_f32_split_sum_kernel, dim3((unsigned)(d.B * d.Sc)),
+                     dim3(d.D / 4 < 64 ? 64 : d.D / 4), 0, s, d, (const float *)f32_part, dkvc);
   return (int)hipGetLastError();
 }
 

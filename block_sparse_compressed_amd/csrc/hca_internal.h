@@ -64,6 +64,8 @@ struct WsLayout {
   uint64_t pds = 0;     // bf16 P and dS per query-tile entry e: [e][P | dS][bq * H rows]
                         // [32 keys], chunks swizzled (64-key tiles at D = 512 only)
   uint64_t pds_bytes = 0;
+  uint64_t f32_part = 0;  // float32 plans: partial dKV of the compressed entries'
+                          // split workgroups, [B][Sc][f32_split][D]
   uint64_t fwd_total = 0;
   uint64_t bwd_total = 0;
 };
@@ -77,6 +79,7 @@ struct Dims {
   int32_t kv_bk, nkv_raw, nkv_comp;  // key tiles of the key-stationary backward
   int32_t cmask_ldw;  // words per position of the compressed-key mask; 0: interval rule
   int32_t pds_rows;   // rows per stored P/dS block (bq * H); 0: dKV recomputes S and dP
+  int32_t f32_split;  // float32 dKV: workgroups per compressed entry (1: one)
 };
 
 struct DevPlan {
@@ -117,9 +120,11 @@ int launch_dkv_reduce(const Dims &d, const DevPlan &p, const float *part, int dt
                       void *dkvc, void *stream);
 int launch_fwd_f32(const Dims &d, const DevPlan &p, const float *q, const float *kv,
                    const float *kvc, float scale, float *o, float *lse, void *stream);
+// f32_part: the workspace section of that name (used when d.f32_split > 1).
 int launch_bwd_f32(const Dims &d, const DevPlan &p, const float *q, const float *kv,
                    const float *kvc, const float *o, const float *lse, const float *dout,
-                   float scale, float *dq, float *dkv, float *dkvc, float *delta, void *stream);
+                   float scale, float *dq, float *dkv, float *dkvc, float *delta,
+                   float *f32_part, void *stream);
 
 // Scratch of the allocation-free forward: a file-scope device array in
 // hca_fwd.hip of this many bytes (the limit hca.h states).
@@ -151,6 +156,7 @@ struct hca_plan {
   int32_t rows_b = 0;  // rows of the plan's tables: batch rows x kv heads
   int32_t cmask_ldw = 0;  // masked plans: words per position of the device mask
   int32_t pds_rows = 0;   // stored-P/dS plans: rows per stored block (bq * H)
+  int32_t f32_split = 1;  // float32 plans: dKV workgroups per compressed entry
   hca::DevLayout lay;
   hca::WsLayout ws;
   std::string unsupported;     // why kernel_ok is 0 ("" when it is 1)

@@ -52,6 +52,10 @@ constexpr int64_t kItemPositions = 64;
 // of 4 kCuTarget blocks: the workspace stays O(S) and shorter problems keep
 // one-chunk items.
 constexpr int64_t kCuTarget = 256;
+// float32 dKV: visits per workgroup of a compressed entry, and at most this
+// many workgroups per entry.
+constexpr int64_t kF32SplitVisits = 256;
+constexpr int64_t kF32SplitMax = 64;
 
 // Half-tile items (128-key tiles whose item sees one 64-key half) share the
 // key-stationary launch with the items over whole tiles, so by default they
@@ -786,6 +790,15 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     w.fwd_total = off;
     w.delta = place((uint64_t)B * H * S * 4);
     w.part = place((uint64_t)std::max<int64_t>(1, nblocks * kvb * D) * 4);
+    if (dtype == HCA_F32 && S_c > 0) {
+      // float32 dKV: the visits of a compressed entry (up to S x H rows) are
+      // split over f32_split workgroups of about kF32SplitVisits each, whose
+      // partial sums a second kernel adds in split order.
+      const int64_t split = std::min<int64_t>(
+          kF32SplitMax, std::max<int64_t>(1, ceil_div((int64_t)S * H, kF32SplitVisits)));
+      p->f32_split = (int32_t)split;
+      if (split > 1) w.f32_part = place((uint64_t)B * S_c * split * D * 4);
+    }
     if (stored) {
       // per qent entry: P and dS of bq * H rows x 32 keys, bf16
       w.pds_bytes = (uint64_t)std::max<size_t>(1, p->qent.size()) * 2 * bq * H * 32 * 2;
