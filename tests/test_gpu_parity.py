@@ -152,6 +152,9 @@ SMALL = [
     # D / 16 columns per lane)
     (1, 150, 2, 512, 8, 16, "f32", [[60, 90]], 0),
     (1, 180, 3, 256, 8, 20, "f32", None, 1),
+    # float32 with S x H <= 256: each compressed entry's dKV in one workgroup
+    # (larger problems split an entry's visits over several and add the parts)
+    (1, 120, 2, 64, 8, 16, "f32", None, 0),
     (1, 64, 64, 512, 1, 0, "bf16", None, 0),   # compressed only (W = 0, r = 1)
     (1, 70, 16, 128, 100, 70, "bf16", None, 0),  # no compressed entries, causal
     # sliding window only at D = 512 (r > S: no compressed entry completes),
