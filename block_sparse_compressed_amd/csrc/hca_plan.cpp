@@ -56,6 +56,7 @@ constexpr int64_t kCuTarget = 256;
 // many workgroups per entry.
 constexpr int64_t kF32SplitVisits = 256;
 constexpr int64_t kF32SplitMax = 64;
+constexpr int64_t kF32PartBudget = 256ll << 20;
 
 // Half-tile items (128-key tiles whose item sees one 64-key half) share the
 // key-stationary launch with the items over whole tiles, so by default they
@@ -789,13 +790,17 @@ static hca_status build_plan(const char *fn, int32_t B, int32_t G, int32_t S, in
     }
     w.fwd_total = off;
     w.delta = place((uint64_t)B * H * S * 4);
-    w.part = place((uint64_t)std::max<int64_t>(1, nblocks * kvb * D) * 4);
+    // (the float32 kernels write dKV directly: no key-tile partials)
+    if (dtype != HCA_F32) w.part = place((uint64_t)std::max<int64_t>(1, nblocks * kvb * D) * 4);
     if (dtype == HCA_F32 && S_c > 0) {
       // float32 dKV: the visits of a compressed entry (up to S x H rows) are
       // split over f32_split workgroups of about kF32SplitVisits each, whose
       // partial sums a second kernel adds in split order.
-      const int64_t split = std::min<int64_t>(
+      int64_t split = std::min<int64_t>(
           kF32SplitMax, std::max<int64_t>(1, ceil_div((int64_t)S * H, kF32SplitVisits)));
+      // ... and at most kF32PartBudget bytes of partial sums in all
+      split = std::max<int64_t>(
+          1, std::min<int64_t>(split, kF32PartBudget / ((int64_t)B * S_c * D * 4)));
       p->f32_split = (int32_t)split;
       if (split > 1) w.f32_part = place((uint64_t)B * S_c * split * D * 4);
     }

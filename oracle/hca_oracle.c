@@ -256,17 +256,20 @@ void hco_keys(const hco_problem *p, const void *q, const void *kv, const void *k
               const int32_t *kinds, const int32_t *bs, const int32_t *idx, double *dkv) {
   const int32_t D = p->D;
   const int64_t nk = (int64_t)p->S + p->Sc + 1;
+  const int64_t nrow = (int64_t)p->H * p->S;
+  /* The rows are summed in fixed blocks of kRowBlock (rows in order inside a
+   * block, then the blocks in order), so the result does not depend on the
+   * thread count or on which thread took which block. */
+  enum { kRowBlock = 64 };
+  const int64_t nblk = (nrow + kRowBlock - 1) / kRowBlock;
+  double *bpart = (double *)malloc(sizeof(double) * (size_t)(nblk > 0 ? nblk : 1) * D);
   for (int64_t j = 0; j < nkeys; ++j) {
     keyref key = {kinds[j], idx[j]};
     int32_t b = bs[j];
     double *out = dkv + j * D;
     for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
-    const void *kb = key_base(kv, kvc, key.kind);
-    int64_t koff = key_row_offset(p, b, key);
-    const int64_t nrow = (int64_t)p->H * p->S;
 #pragma omp parallel
     {
-      double *acc = (double *)calloc((size_t)D, sizeof(double));
       keyref *keys = NULL;
       double *s = NULL, *dp = NULL;
       if (!lse_all) {
@@ -274,38 +277,41 @@ void hco_keys(const hco_problem *p, const void *q, const void *kv, const void *k
         s = (double *)malloc(sizeof(double) * nk);
         dp = (double *)malloc(sizeof(double) * nk);
       }
-#pragma omp for schedule(dynamic, 64)
-      for (int64_t hi = 0; hi < nrow; ++hi) {
-        int32_t h = (int32_t)(hi / p->S);
-        int64_t i = hi % p->S;
-        int vis = key.kind == 0 ? hco_vis_raw(p, b, i, key.idx) : hco_vis_comp(p, b, i, key.idx);
-        if (!vis) continue;
-        int64_t qoff = (((int64_t)b * p->H + h) * p->S + i) * D;
-        double lse, delta;
-        if (lse_all) {
-          lse = lse_all[((int64_t)b * p->H + h) * p->S + i];
-          delta = delta_all[((int64_t)b * p->H + h) * p->S + i];
-        } else {
-          row_compute(p, q, kv, kvc, dout, b, h, i, keys, s, dp, NULL, &lse, &delta, NULL);
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t blk = 0; blk < nblk; ++blk) {
+        double *acc = bpart + blk * D;
+        for (int32_t d = 0; d < D; ++d) acc[d] = 0.0;
+        const int64_t hi_end = (blk + 1) * kRowBlock < nrow ? (blk + 1) * kRowBlock : nrow;
+        for (int64_t hi = blk * kRowBlock; hi < hi_end; ++hi) {
+          int32_t h = (int32_t)(hi / p->S);
+          int64_t i = hi % p->S;
+          int vis = key.kind == 0 ? hco_vis_raw(p, b, i, key.idx) : hco_vis_comp(p, b, i, key.idx);
+          if (!vis) continue;
+          int64_t qoff = (((int64_t)b * p->H + h) * p->S + i) * D;
+          double lse, delta;
+          if (lse_all) {
+            lse = lse_all[((int64_t)b * p->H + h) * p->S + i];
+            delta = delta_all[((int64_t)b * p->H + h) * p->S + i];
+          } else {
+            row_compute(p, q, kv, kvc, dout, b, h, i, keys, s, dp, NULL, &lse, &delta, NULL);
+          }
+          double sk = p->scale * dot_row(p, q, qoff, kv, kvc, b, key);
+          double pk = exp(sk - lse);
+          double dpk = dot_row(p, dout, qoff, kv, kvc, b, key);
+          double dsk = pk * (dpk - delta);
+          for (int32_t d = 0; d < D; ++d)
+            acc[d] += p->scale * dsk * load_val(q, p->in_dtype, qoff + d) +
+                      pk * load_val(dout, p->in_dtype, qoff + d);
         }
-        double sk = p->scale * dot_row(p, q, qoff, kv, kvc, b, key);
-        double pk = exp(sk - lse);
-        double dpk = dot_row(p, dout, qoff, kv, kvc, b, key);
-        double dsk = pk * (dpk - delta);
-        for (int32_t d = 0; d < D; ++d)
-          acc[d] += p->scale * dsk * load_val(q, p->in_dtype, qoff + d) +
-                    pk * load_val(dout, p->in_dtype, qoff + d);
       }
-#pragma omp critical
-      for (int32_t d = 0; d < D; ++d) out[d] += acc[d];
-      free(acc);
       free(keys);
       free(s);
       free(dp);
     }
-    (void)kb;
-    (void)koff;
+    for (int64_t blk = 0; blk < nblk; ++blk)
+      for (int32_t d = 0; d < D; ++d) out[d] += bpart[blk * D + d];
   }
+  free(bpart);
 }
 
 /* ---- tile states, brute force --------------------------------------------- */

@@ -40,12 +40,12 @@ MUTANTS = {
     "dq_unscaled": ("dq[d] += p->scale * ds * load_val(kb, p->in_dtype, koff + d);",
                     "dq[d] += ds * load_val(kb, p->in_dtype, koff + d);"),
     "dkv_drops_value_path": ("acc[d] += p->scale * dsk * load_val(q, p->in_dtype, qoff + d) +\n"
-                             "                    pk * load_val(dout, p->in_dtype, qoff + d);",
+                             "                      pk * load_val(dout, p->in_dtype, qoff + d);",
                              "acc[d] += p->scale * dsk * load_val(q, p->in_dtype, qoff + d);"),
     "dkv_swaps_q_and_dout": ("acc[d] += p->scale * dsk * load_val(q, p->in_dtype, qoff + d) +\n"
-                             "                    pk * load_val(dout, p->in_dtype, qoff + d);",
+                             "                      pk * load_val(dout, p->in_dtype, qoff + d);",
                              "acc[d] += p->scale * dsk * load_val(dout, p->in_dtype, qoff + d) +\n"
-                             "                    pk * load_val(q, p->in_dtype, qoff + d);"),
+                             "                      pk * load_val(q, p->in_dtype, qoff + d);"),
     "lse_drops_max": ("if (lse) *lse = m + log(l);", "if (lse) *lse = log(l);"),
     "tile_rows_one_past": ("for (int64_t i = qt * bq; i < (qt + 1) * bq; ++i) {",
                            "for (int64_t i = qt * bq; i <= (qt + 1) * bq; ++i) {"),

@@ -26,6 +26,8 @@ import pytest
 import torch
 
 import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 from hca_inputs import segment_ids
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -505,3 +507,36 @@ def test_bf16_and_f32_inputs_widen_exactly():
     for k in a:
         assert np.array_equal(a[k], b[k]), k
         assert np.array_equal(a[k], c[k]), k
+
+
+def test_results_independent_of_thread_count():
+    """The oracle's per-key gradient sums rows in fixed blocks and adds the
+    blocks in order, so its outputs are bitwise the same for any number of
+    threads (two fresh processes, one and five threads)."""
+    import hashlib
+    import subprocess
+    import sys as _sys
+
+    code = (
+        "import sys, hashlib, numpy as np\n"
+        "sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+        "import oracle\n"
+        "from test_oracle_pins import make_problem, rnd\n"
+        "rng = np.random.default_rng(5)\n"
+        "B, S, H, D, r, W = 1, 300, 4, 16, 8, 20\n"
+        "q, kv, kvc, dout = (rnd(rng, B, H, S, D), rnd(rng, B, S, D), rnd(rng, B, S // r, D),"
+        " rnd(rng, B, H, S, D))\n"
+        "out = oracle.full(make_problem(B, S, H, D, r, W, [[120, 180]]), q, kv, kvc, dout)\n"
+        "print(oracle.num_threads(), hashlib.sha1(b''.join(np.ascontiguousarray(out[k]).tobytes()"
+        " for k in sorted(out))).hexdigest())\n"
+    ) % (ROOT, os.path.join(ROOT, "tests"))
+    got = {}
+    for t in (1, 5):
+        env = dict(os.environ, OMP_NUM_THREADS=str(t))
+        r = subprocess.run([_sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=120)
+        assert r.returncode == 0, r.stderr
+        n, h = r.stdout.split()
+        assert int(n) == t
+        got[t] = h
+    assert got[1] == got[5]
