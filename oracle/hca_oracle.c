@@ -263,6 +263,7 @@ void hco_keys(const hco_problem *p, const void *q, const void *kv, const void *k
   enum { kRowBlock = 64 };
   const int64_t nblk = (nrow + kRowBlock - 1) / kRowBlock;
   double *bpart = (double *)malloc(sizeof(double) * (size_t)(nblk > 0 ? nblk : 1) * D);
+  unsigned char *bused = (unsigned char *)malloc((size_t)(nblk > 0 ? nblk : 1));
   for (int64_t j = 0; j < nkeys; ++j) {
     keyref key = {kinds[j], idx[j]};
     int32_t b = bs[j];
@@ -281,12 +282,14 @@ void hco_keys(const hco_problem *p, const void *q, const void *kv, const void *k
       for (int64_t blk = 0; blk < nblk; ++blk) {
         double *acc = bpart + blk * D;
         for (int32_t d = 0; d < D; ++d) acc[d] = 0.0;
+        bused[blk] = 0;
         const int64_t hi_end = (blk + 1) * kRowBlock < nrow ? (blk + 1) * kRowBlock : nrow;
         for (int64_t hi = blk * kRowBlock; hi < hi_end; ++hi) {
           int32_t h = (int32_t)(hi / p->S);
           int64_t i = hi % p->S;
           int vis = key.kind == 0 ? hco_vis_raw(p, b, i, key.idx) : hco_vis_comp(p, b, i, key.idx);
           if (!vis) continue;
+          bused[blk] = 1;
           int64_t qoff = (((int64_t)b * p->H + h) * p->S + i) * D;
           double lse, delta;
           if (lse_all) {
@@ -308,9 +311,12 @@ void hco_keys(const hco_problem *p, const void *q, const void *kv, const void *k
       free(s);
       free(dp);
     }
+    /* blocks without a visible row hold zeros and are skipped */
     for (int64_t blk = 0; blk < nblk; ++blk)
-      for (int32_t d = 0; d < D; ++d) out[d] += bpart[blk * D + d];
+      if (bused[blk])
+        for (int32_t d = 0; d < D; ++d) out[d] += bpart[blk * D + d];
   }
+  free(bused);
   free(bpart);
 }
 
